@@ -1,0 +1,147 @@
+"""Seeded synthetic workloads.
+
+This module holds the workload shapes and the seeded random inputs that both
+the HIP path's tests/benchmark and the CPU oracle consume.  It holds none of
+the method's arithmetic: only shapes, graph parameters (T, W, offsets) and
+random draws.  It imports nothing from the rest of the package.
+
+Shapes stand in for the pages' workloads (no corpus or trained weight is
+available or needed): the 16,384-token training context of the SpatialLM-Mini
+news page ("What the comparison on 8 GB showed"), the 256-token chunked window
+at the longest context MiniGPT (Part 6) trained ("The raw numbers" table), and
+the very long single-GPU sequences of the sparse-graph-processing abstract
+(arXiv 2502.01659).  Values are i.i.d. N(0, 1) drawn in fp32 and rounded to
+bf16 (round-to-nearest-even) where the workload is bf16.
+
+Seed of tensor t of workload c: 1000 * c + t with t = 0 q, 1 k, 2 v, 3 dO,
+4 c_q, 5 c_k, 6 gamma, 7 beta, 8 sampled rows.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import torch
+
+SEED_Q, SEED_K, SEED_V, SEED_DO, SEED_CQ, SEED_CK, SEED_GAMMA, SEED_BETA, SEED_ROWS = range(9)
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    index: int  # c in the seed formula
+    B: int
+    H: int
+    T: int
+    D: int
+    dtype: torch.dtype
+    window: int
+    offsets: tuple = field(default_factory=tuple)
+    coord: bool = False
+    backward: bool = True
+
+    @property
+    def dtype_name(self) -> str:
+        return {torch.float32: "f32", torch.bfloat16: "bf16"}[self.dtype]
+
+
+def _pow2(lo: int, hi: int) -> tuple:
+    return tuple(2 ** k for k in range(lo, hi + 1))
+
+
+WORKLOADS = {
+    # tiny fp32 forward/backward: window 8 + distances 16..128
+    "tiny": Workload("tiny", 1, 1, 2, 256, 32, torch.float32, 8, (16, 32, 64, 128)),
+    "tiny_dense": Workload("tiny_dense", 1, 1, 2, 256, 32, torch.float32, 256, ()),
+    # sliding window only, W = 256, T = 16384
+    "band": Workload("band", 2, 1, 8, 16384, 64, torch.bfloat16, 256, ()),
+    "band_dense": Workload("band_dense", 2, 1, 8, 2048, 64, torch.bfloat16, 2048, ()),
+    # local window 4 + distances 2^0..2^13, training shape B=4, H=8, T=16384
+    "dilated": Workload("dilated", 3, 4, 8, 16384, 64, torch.bfloat16, 4, _pow2(0, 13)),
+    # coordinate-distance score on the dilated graph
+    "coord": Workload("coord", 4, 4, 8, 16384, 64, torch.bfloat16, 4, _pow2(0, 13), coord=True),
+    # coordinate-distance score on the W = 256 band graph (secondary)
+    "coord_band": Workload("coord_band", 4, 1, 8, 16384, 64, torch.bfloat16, 256, (), coord=True),
+    # ultra-long single head, forward only: window 64 + distances 2^6..2^25
+    "ultra": Workload("ultra", 5, 1, 1, 2 ** 26, 64, torch.bfloat16, 64, _pow2(6, 25),
+                      backward=False),
+}
+
+
+def seed_of(w: Workload, t: int) -> int:
+    return 1000 * w.index + t
+
+
+def _randn(shape, seed: int) -> torch.Tensor:
+    g = torch.Generator().manual_seed(seed)
+    return torch.randn(shape, generator=g, dtype=torch.float32)
+
+
+def _uniform(shape, lo: float, hi: float, seed: int) -> torch.Tensor:
+    g = torch.Generator().manual_seed(seed)
+    return torch.rand(shape, generator=g, dtype=torch.float32) * (hi - lo) + lo
+
+
+def make_inputs(w: Workload, device="cpu", backward: bool | None = None,
+                B: int | None = None, H: int | None = None, T: int | None = None,
+                D: int | None = None) -> dict:
+    """CPU-generated seeded inputs, moved to `device`.  Shape overrides allow
+    small variants of a workload with the same recipe."""
+    B = w.B if B is None else B
+    H = w.H if H is None else H
+    T = w.T if T is None else T
+    D = w.D if D is None else D
+    backward = w.backward if backward is None else backward
+    shp = (B, H, T, D)
+    out = {}
+    if w.coord:
+        out["cq"] = _randn((B, H, T, 3), seed_of(w, SEED_CQ))
+        out["ck"] = _randn((B, H, T, 3), seed_of(w, SEED_CK))
+        out["gamma"] = _uniform((H,), 0.5, 2.0, seed_of(w, SEED_GAMMA))
+        out["beta"] = _randn((H,), seed_of(w, SEED_BETA)) * 0.1
+    else:
+        out["q"] = _randn(shp, seed_of(w, SEED_Q)).to(w.dtype)
+        out["k"] = _randn(shp, seed_of(w, SEED_K)).to(w.dtype)
+    out["v"] = _randn(shp, seed_of(w, SEED_V)).to(w.dtype)
+    if backward:
+        out["do"] = _randn(shp, seed_of(w, SEED_DO)).to(w.dtype)
+    return {k: t.to(device) for k, t in out.items()}
+
+
+def make_device_inputs_chunked(w: Workload, device, chunk_rows: int = 1 << 22) -> dict:
+    """Device-generated inputs for workloads too large to draw on the host
+    (the 2^26-token single head): fp32 normal draws from a seeded device
+    generator, chunk by chunk, rounded to the workload dtype."""
+    assert w.B == 1 and w.H == 1
+    out = {}
+    for name, t in (("q", SEED_Q), ("k", SEED_K), ("v", SEED_V)):
+        x = torch.empty((1, 1, w.T, w.D), dtype=w.dtype, device=device)
+        g = torch.Generator(device=device).manual_seed(seed_of(w, t))
+        for r0 in range(0, w.T, chunk_rows):
+            r1 = min(w.T, r0 + chunk_rows)
+            x[0, 0, r0:r1].copy_(torch.randn((r1 - r0, w.D), generator=g, device=device,
+                                             dtype=torch.float32))
+        out[name] = x
+    return out
+
+
+def sample_rows(w: Workload, n: int = 4096, boundary=None) -> torch.Tensor:
+    """n rows uniform in [0, T) from the workload's row seed, plus boundary rows."""
+    g = torch.Generator().manual_seed(seed_of(w, SEED_ROWS))
+    r = torch.randint(0, w.T, (n,), generator=g, dtype=torch.int64)
+    if boundary:
+        r = torch.cat([r, torch.tensor([b for b in boundary if 0 <= b < w.T], dtype=torch.int64)])
+    return torch.unique(r)
+
+
+def bf16_bits(t: torch.Tensor):
+    """numpy uint16 view of a bf16 CPU tensor (exact stored bits)."""
+    assert t.dtype == torch.bfloat16
+    return t.contiguous().view(torch.int16).numpy().view("uint16")
+
+
+def host_view(t: torch.Tensor):
+    """numpy view with exact stored values: fp32 stays fp32, bf16 becomes bits."""
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return bf16_bits(t)
+    return t.numpy()
