@@ -1,0 +1,310 @@
+"""Throughput of the sparse causal attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workloads band,dilated,coord,ultra]
+
+One step = one forward (sa_fwd) plus one backward (sa_bwd) over one batch of
+seeded synthetic inputs already resident in HBM (the 2^26-token workload is
+forward only).  The headline line is the sliding-window workload (B=1, H=8,
+T=16384, D=64, W=256, bf16); the other workloads are measured in the same run
+and reported under "extra".  Prints exactly one JSON line.
+
+Roofline: algorithmic bytes per call (each tensor once: q, k, v, o, lse
+forward; q, k, v, o, dout, lse, dq, dk, dv backward; plus a K and V row per
+long-range edge forward and q, dout, k, v rows plus lse, Delta per long-range
+edge backward) divided by the call's average duration, measured with HIP
+events recorded on the stream the kernels run on.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+MFMA_BF16_PEAK_TFS = 2500.0  # dense bf16 MFMA
+METRIC = "attention edges/s and tokens/s fwd+bwd at T=16384; % of HBM/MFMA roofline"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workloads", default="band,dilated,coord,ultra")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample length")
+    ap.add_argument("--algo", default="auto")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 1 GiB device copy (scales profiler byte counters)")
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------------ byte and flop models
+def edge_counts(w):
+    """(total edges per (b, h), long-range edges per (b, h))."""
+    T, Wc = w.T, min(w.window, w.T)
+    dil = sorted({d for d in w.offsets if Wc <= d < T})
+    band = Wc * (Wc + 1) // 2 + Wc * (T - Wc)
+    long_range = sum(T - d for d in dil)
+    return band + long_range, long_range
+
+
+def models(w, grad_bytes=4):
+    """Algorithmic bytes and flops per call for workload w (all heads)."""
+    E, Ed = edge_counts(w)
+    rows = w.B * w.H * w.T
+    eb = 2 if w.dtype_name == "bf16" else 4
+    D = w.D
+    if w.coord:
+        # forward: c_q, c_k (12 B), v, o rows, lse; backward: + dout, dv, dcq, dck
+        fwd = rows * (12 + 12 + 2 * D * eb + 4) + w.B * w.H * Ed * (12 + D * eb)
+        bwd = rows * (12 + 12 + D * eb + D * eb + D * eb + 4 + D * grad_bytes + 12 + 12) + \
+            w.B * w.H * Ed * 2 * (12 + D * eb + 8)
+        ffl = w.B * w.H * E * (2 * D + 11)
+        bfl = w.B * w.H * E * (4 * D + 35)
+    else:
+        fwd = rows * (4 * D * eb + 4) + w.B * w.H * Ed * 2 * D * eb
+        bwd = rows * (5 * D * eb + 4 + 3 * D * grad_bytes) + w.B * w.H * Ed * (4 * D * eb + 8)
+        ffl = w.B * w.H * E * 4 * D
+        bfl = w.B * w.H * E * 10 * D
+    return {"edges": w.B * w.H * E, "fwd_bytes": fwd, "bwd_bytes": bwd, "fwd_flops": ffl,
+            "bwd_flops": bfl}
+
+
+# ------------------------------------------------------------------ timing
+def run_workload(w, steps, warmup, algo, with_backward=True):
+    import torch
+
+    from sparse_causal_attention_amd import (sa_build_graph, sa_bwd_prepared, sa_describe_plan,
+                                             sa_fwd_prepared)
+    from sparse_causal_attention_amd.inputs import make_device_inputs_chunked, make_inputs
+
+    dev = "cuda"
+    if w.T * w.D * w.B * w.H > (1 << 30):
+        x = make_device_inputs_chunked(w, dev)
+    else:
+        x = {k: t.to(dev) for k, t in make_inputs(w, backward=with_backward and w.backward).items()}
+    g = sa_build_graph(w.T, w.window, w.offsets)
+    bwd = with_backward and w.backward
+    coord = w.coord
+    o = torch.empty_like(x["v"])
+    lse = torch.empty((w.B, w.H, w.T), dtype=torch.float32, device=dev)
+    fkw = dict(v=x["v"], cq=x.get("cq"), ck=x.get("ck"), gamma=x.get("gamma"), beta=x.get("beta"),
+               o=o, lse=lse, algo=algo)
+    if not coord:
+        fkw.update(q=x["q"], k=x["k"])
+    grads = None
+    if bwd:
+        gshape = (w.B, w.H, w.T, w.D)
+        grads = {"dv": torch.empty(gshape, dtype=torch.float32, device=dev)}
+        if coord:
+            grads.update(dcq=torch.empty((w.B, w.H, w.T, 3), dtype=torch.float32, device=dev),
+                         dck=torch.empty((w.B, w.H, w.T, 3), dtype=torch.float32, device=dev),
+                         dgamma=torch.empty((w.H,), dtype=torch.float32, device=dev),
+                         dbeta=torch.empty((w.H,), dtype=torch.float32, device=dev))
+        else:
+            grads.update(dq=torch.empty(gshape, dtype=torch.float32, device=dev),
+                         dk=torch.empty(gshape, dtype=torch.float32, device=dev))
+        from sparse_causal_attention_amd import sa_bwd_workspace_size
+        ws = torch.empty(sa_bwd_workspace_size(g, x["v"]), dtype=torch.uint8, device=dev)
+        bkw = dict(v=x["v"], o=o, lse=lse, dout=x["do"], cq=x.get("cq"), ck=x.get("ck"),
+                   gamma=x.get("gamma"), beta=x.get("beta"), workspace=ws, algo=algo, **grads)
+        if not coord:
+            bkw.update(q=x["q"], k=x["k"])
+
+    fwd_call = sa_fwd_prepared(g, **fkw)
+    bwd_call = sa_bwd_prepared(g, **bkw) if bwd else None
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        fwd_call()
+        if ev is not None:
+            ev[1].record()
+        if bwd:
+            bwd_call()
+            if ev is not None:
+                ev[2].record()
+
+    for _ in range(warmup):
+        step()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        step(evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    f_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    b_ms = [e[1].elapsed_time(e[2]) for e in evs] if bwd else [0.0]
+    res = {
+        "wall_s": wall, "ms_per_step": 1e3 * wall / steps,
+        "fwd_ms": sum(f_ms) / len(f_ms), "bwd_ms": sum(b_ms) / len(b_ms),
+        "fwd_ms_min": min(f_ms), "bwd_ms_min": min(b_ms),
+        "plan_fwd": sa_describe_plan(g, x["v"], coord=coord, algo=algo, which="fwd"),
+        "plan_bwd": sa_describe_plan(g, x["v"], coord=coord, algo=algo, which="bwd") if bwd else None,
+        "inputs": {k: t for k, t in x.items()},
+    }
+    del o, lse, grads
+    return res
+
+
+def summarize(w, r, steps):
+    m = models(w)
+    tokens = w.B * w.T
+    fb = r["fwd_ms"] + r["bwd_ms"]
+    wall = r["wall_s"]
+    out = {
+        "workload": w.name,
+        "shape": {"B": w.B, "H": w.H, "T": w.T, "D": w.D, "window": w.window,
+                  "offsets": list(w.offsets), "dtype": w.dtype_name,
+                  "score": "coord" if w.coord else "dot", "backward": w.backward},
+        "tokens_per_s": tokens * steps / wall,
+        "edges_per_s": m["edges"] * steps / wall,
+        "ms_per_step": r["ms_per_step"],
+        "fwd_ms": r["fwd_ms"], "bwd_ms": r["bwd_ms"],
+        "fwd_GBs": m["fwd_bytes"] / (r["fwd_ms"] * 1e6),
+        "bwd_GBs": m["bwd_bytes"] / (r["bwd_ms"] * 1e6) if r["bwd_ms"] > 0 else None,
+        "fwd_TFLOPs": m["fwd_flops"] / (r["fwd_ms"] * 1e9),
+        "bwd_TFLOPs": m["bwd_flops"] / (r["bwd_ms"] * 1e9) if r["bwd_ms"] > 0 else None,
+        "kernels": {"fwd": r["plan_fwd"], "bwd": r["plan_bwd"]},
+        "event_ms_fwd_plus_bwd": fb,
+    }
+    return out, m
+
+
+def roofline_for(w, r, m):
+    """Roofline entry for the longer of the two calls."""
+    use_bwd = r["bwd_ms"] > r["fwd_ms"]
+    ms = r["bwd_ms"] if use_bwd else r["fwd_ms"]
+    byt = m["bwd_bytes"] if use_bwd else m["fwd_bytes"]
+    fl = m["bwd_flops"] if use_bwd else m["fwd_flops"]
+    achieved = byt / (ms * 1e6)
+    return {
+        "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+        "kernel": r["plan_bwd"] if use_bwd else r["plan_fwd"],
+        "call": "sa_bwd" if use_bwd else "sa_fwd",
+        "avg_ms": round(ms, 5), "algorithmic_bytes": byt,
+        "mfma_bf16_frac": round(fl / (ms * 1e9) / MFMA_BF16_PEAK_TFS, 4),
+    }
+
+
+# ------------------------------------------------------------------ CPU baseline (oracle)
+def cpu_baseline(w, inputs, target_s):
+    """The fp64 oracle, as it stands, on a bounded sample of the same inputs:
+    whole (b, h) slices (forward + backward) until target_s seconds elapse.
+    Scaled to tokens/s of the full workload."""
+    import oracle
+    from sparse_causal_attention_amd.inputs import host_view
+
+    hv = {k: host_view(t) for k, t in inputs.items()}
+    slices = [(b, h) for b in range(w.B) for h in range(w.H)]
+    done = 0
+    t0 = time.perf_counter()
+    while True:  # whole passes over the (batch, head) slices until target_s
+        b, h = slices[done % len(slices)]
+        if w.coord:
+            oracle.fwd(w.T, w.window, w.offsets, hv["v"][b, h], cq=hv["cq"][b, h], ck=hv["ck"][b, h],
+                       gamma=float(hv["gamma"][h]), beta=float(hv["beta"][h]))
+            oracle.bwd(w.T, w.window, w.offsets, hv["v"][b, h], hv["do"][b, h], cq=hv["cq"][b, h],
+                       ck=hv["ck"][b, h], gamma=float(hv["gamma"][h]), beta=float(hv["beta"][h]))
+        else:
+            oracle.fwd(w.T, w.window, w.offsets, hv["v"][b, h], q=hv["q"][b, h], k=hv["k"][b, h])
+            oracle.bwd(w.T, w.window, w.offsets, hv["v"][b, h], hv["do"][b, h], q=hv["q"][b, h],
+                       k=hv["k"][b, h])
+        done += 1
+        if time.perf_counter() - t0 >= target_s:
+            break
+    el = time.perf_counter() - t0
+    frac = done / len(slices)
+    tokens_per_s = w.B * w.T * frac / el
+    return {"value": tokens_per_s, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "%d (batch, head) slices (%.2f passes over the %d slices of the %s workload), "
+                      "forward + backward, fp64, %.1f s; tokens/s scaled by the slice fraction"
+                      % (done, frac, len(slices), w.name, el),
+            "edges_per_s": edge_counts(w)[0] * done / el}
+
+
+def copy_probe():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        sys.stderr.write("bench.py measures one GPU only: this build has no multi-GPU path "
+                         "(independent (batch, head) slices would shard without communication; "
+                         "see the sharding notes in the design document).\n")
+        sys.exit(2)
+    import torch
+
+    from sparse_causal_attention_amd import _abi
+    from sparse_causal_attention_amd.inputs import WORKLOADS
+
+    _abi.lib()
+    if args.copy_probe:
+        copy_probe()
+    names = [n for n in args.workloads.split(",") if n]
+    headline = names[0]
+    results = {}
+    for name in names:
+        w = WORKLOADS[name]
+        steps = args.steps if name != "ultra" else max(2, min(args.steps, 5))
+        warm = args.warmup if name != "ultra" else min(args.warmup, 2)
+        print("[bench] %s: %d warmup + %d timed steps" % (name, warm, steps), file=sys.stderr, flush=True)
+        r = run_workload(w, steps, warm, args.algo)
+        s, m = summarize(w, r, steps)
+        s["roofline"] = roofline_for(w, r, m)
+        s["steps"] = steps
+        results[name] = (w, r, s)
+        if name != headline:
+            del r["inputs"]
+            torch.cuda.empty_cache()
+    w, r, s = results[headline]
+    line = {
+        "metric": METRIC,
+        "value": s["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": s["steps"],
+        "warmup": args.warmup,
+        "ms_per_step": s["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype_name,
+        "data": "synthetic: seeded N(0,1) inputs shaped like the pages' workloads",
+        "config": {"workload": "%s: B=%d H=%d T=%d D=%d W=%d offsets=%s %s, %s" % (
+            w.name, w.B, w.H, w.T, w.D, w.window, list(w.offsets), w.dtype_name,
+            "fwd+bwd" if w.backward else "fwd"),
+            "global_batch": w.B, "seq_len": w.T, "heads": w.H, "head_dim": w.D},
+        "edges_per_s": s["edges_per_s"],
+        "roofline": s["roofline"],
+        "detail": {k: v for k, v in s.items() if k not in ("roofline",)},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] cpu baseline (oracle) on %s" % w.name, file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(w, r["inputs"], args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    line["extra"] = {n: s2 for n, (_, _, s2) in results.items() if n != headline}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

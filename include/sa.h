@@ -1,0 +1,190 @@
+/*
+ * sa.h -- C ABI of the MI355X (gfx950) sparse causal attention library.
+ *
+ * The operation: every query row i of a sequence of length T attends only to
+ * a fixed neighbour set
+ *
+ *     N(i) = { i - delta : delta in {0, ..., W-1} U Dil, i - delta >= 0 }
+ *
+ * made of its local window (itself and the W-1 rows before it) and a set Dil
+ * of long-range distances (typically 1, 2, 4, 8, ...).  The weights are a
+ * softmax over N(i) only; no T x T score matrix is formed anywhere.
+ *
+ * Sources (the pages this library implements):
+ *  - SpatialLM-Mini news page, section "How tokens choose whom to listen to":
+ *    the admissible list of each token is fixed in advance (itself, nearby
+ *    predecessors, positions at distances 1, 2, 4, 8, ...), nothing ahead of
+ *    the token is visible, and the weights are distributed within that list;
+ *    weights come from learnable 3-D query/key coordinates, nearer pairs
+ *    weighing more, adjusted by extra learnable parameters.
+ *  - Same page, section "What to check before adopting it in your project":
+ *    the same graph with a standard dot product is the comparison to run,
+ *    hence the score-mode switch.
+ *  - MiniGPT (Part 6), section "A mask is not enough": the sliding-window
+ *    predicate (key j kept for query i iff j <= i and i - j < w), the
+ *    requirement that the O(T*W) cost come from never forming the T x T
+ *    matrix, and exact equality with causal attention when w >= T.
+ *  - "Longer Attention Span: Increasing Transformer Context Length with
+ *    Sparse Graph Processing Techniques" (arXiv 2502.01659), abstract: tokens
+ *    are graph nodes, the mask gives the edges, and the work done is
+ *    proportional to the edges.
+ *
+ * Conventions shared by every entry point:
+ *  - All sizes and strides are counts of elements (not bytes), int64.
+ *  - Tensors q, k, v, o, dout, dq, dk, dv are [B, H, T, D] with arbitrary
+ *    (b, h, t) strides and the D elements of a row contiguous.  Every row must
+ *    start on a 16-byte boundary (base pointer and strides times element size
+ *    divisible by 16).
+ *  - lse is [B, H, T] fp32, contiguous: lse[(b*H + h)*T + t].
+ *  - Coordinates c_q, c_k (and their gradients) are [B, H, T, 3] fp32,
+ *    contiguous.  gamma, beta (and dgamma, dbeta) are [H] fp32.
+ *  - Every pointer passed to sa_fwd / sa_bwd is a device pointer owned by the
+ *    caller.  The library never allocates, frees or retains device memory.
+ *  - Calls are asynchronous on the given stream (a hipStream_t; NULL is the
+ *    null stream).  SA_OK means the work was validated and enqueued.
+ *  - All validation happens before any HIP call, and nothing is written when
+ *    validation fails.  No entry point aborts, throws or prints.
+ *  - The library does not touch the GPU when it is loaded; sa_build_graph,
+ *    sa_graph_* and the validation paths run on hosts without a GPU.
+ */
+#ifndef SPARSE_CAUSAL_ATTENTION_SA_H
+#define SPARSE_CAUSAL_ATTENTION_SA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SA_OK = 0,
+  SA_ERR_INVALID_ARG = 1,    /* null pointer, size < 1, negative offset, bad alignment, ... */
+  SA_ERR_UNSUPPORTED = 2,    /* a valid request this build does not implement (e.g. D = 48) */
+  SA_ERR_SHAPE_MISMATCH = 3, /* graph T differs from the descriptor's T */
+  SA_ERR_WORKSPACE = 4,      /* backward workspace missing or too small */
+  SA_ERR_HIP = 5             /* a kernel launch reported an error */
+} sa_status;
+
+typedef enum { SA_F32 = 0, SA_BF16 = 1 } sa_dtype;
+
+/* Score of edge (i, j):
+ *  SA_SCORE_DOT:   s_ij = scale * <q_i, k_j>
+ *  SA_SCORE_COORD: s_ij = -gamma_h * ||c_q,i - c_k,j||^2 + beta_h
+ * (SpatialLM-Mini news page, "How tokens choose whom to listen to", and the
+ * dot-product comparison asked for in "What to check before adopting it"). */
+typedef enum { SA_SCORE_DOT = 0, SA_SCORE_COORD = 1 } sa_score;
+
+/* Kernel family.  AUTO picks the LDS/MFMA band kernels for the window when
+ * they apply (bf16, dot score, D = 64, W >= 16) and the gather kernels
+ * otherwise.  GATHER forces the gather kernels for every edge; BAND requests
+ * the band kernels and fails with SA_ERR_UNSUPPORTED where they do not apply. */
+typedef enum { SA_ALGO_AUTO = 0, SA_ALGO_GATHER = 1, SA_ALGO_BAND = 2 } sa_algo;
+
+#define SA_MAX_DILATED 64 /* distinct long-range distances kept by a graph */
+
+typedef struct sa_graph sa_graph; /* opaque, host memory, immutable once built */
+typedef void* sa_stream;          /* hipStream_t */
+
+/* ------------------------------------------------------------------ graph */
+
+/* Builds the neighbour graph of a length-T sequence with window `window`
+ * (W >= 1; W >= T means every j <= i, i.e. dense causal attention) and
+ * long-range distances `offsets[0..n_offsets)` (SpatialLM-Mini news page,
+ * "How tokens choose whom to listen to"; MiniGPT Part 6 window predicate).
+ * Offsets may be unsorted and repeated; offsets below W (already inside the
+ * window) and offsets >= T (never a valid key) are dropped, the rest sorted
+ * and deduplicated, so each edge exists once.  A negative offset would look
+ * ahead and is SA_ERR_INVALID_ARG.  More than SA_MAX_DILATED distinct kept
+ * offsets is SA_ERR_UNSUPPORTED; T >= 2^31 is SA_ERR_UNSUPPORTED.  On success
+ * *out receives a handle the caller releases with sa_graph_free.  Integer
+ * only, host only, bit-exact. */
+sa_status sa_build_graph(int64_t T, int64_t window, const int64_t* offsets, int32_t n_offsets,
+                         sa_graph** out);
+
+/* Normalised descriptor: T, the effective window min(W, T), the kept
+ * long-range distances ascending (dil may be NULL; else SA_MAX_DILATED
+ * entries of room) and the edge count per (batch, head)
+ *   E = W'(W'+1)/2 + W'(T-W') + sum_{d in Dil} (T - d),  W' = min(W, T).
+ * Any output pointer may be NULL. */
+sa_status sa_graph_info(const sa_graph* g, int64_t* T, int64_t* window, int32_t* n_dil,
+                        int64_t* dil, int64_t* n_edges);
+
+/* CSR rows [row_begin, row_end) of the graph: row_ptr receives
+ * row_end - row_begin + 1 offsets starting at 0, cols the key indices of each
+ * row in ascending order.  cols_cap is the room in cols; too little room is
+ * SA_ERR_INVALID_ARG with row_ptr filled (so row_ptr[last] is the size
+ * needed) and cols untouched. */
+sa_status sa_graph_rows(const sa_graph* g, int64_t row_begin, int64_t row_end, int64_t* row_ptr,
+                        int64_t* cols, int64_t cols_cap);
+
+/* The reverse graph in the same format: row j lists, ascending, the queries
+ * i with j in N(i) (i = j + delta, delta in {0..W-1} U Dil, i < T). */
+sa_status sa_graph_rows_reverse(const sa_graph* g, int64_t row_begin, int64_t row_end,
+                                int64_t* row_ptr, int64_t* cols, int64_t cols_cap);
+
+void sa_graph_free(sa_graph* g);
+
+/* ------------------------------------------------------------------ attention */
+
+typedef struct {
+  int64_t B, H, T, D;  /* D in {16, 32, 64, 128} */
+  int32_t dtype;       /* sa_dtype of q, k, v, o, dout */
+  int32_t grad_dtype;  /* sa_dtype of dq, dk, dv (fp32 recommended) */
+  int32_t score;       /* sa_score */
+  int32_t algo;        /* sa_algo */
+  float scale;         /* dot mode; <= 0 selects 1/sqrt(D).  Unused in coordinate mode. */
+  int64_t stride_q[3], stride_k[3], stride_v[3], stride_o[3], stride_do[3]; /* (b, h, t) */
+  int64_t stride_dq[3], stride_dk[3], stride_dv[3];                          /* (b, h, t) */
+} sa_attn_desc;
+
+/* Forward (SpatialLM-Mini news page, "How tokens choose whom to listen to";
+ * MiniGPT Part 6, "A mask is not enough"): for every (b, h, i)
+ *   m_i = max_{j in N(i)} s_ij,  l_i = sum_{j in N(i)} exp(s_ij - m_i),
+ *   o_i = sum_{j in N(i)} exp(s_ij - m_i) v_j / l_i,   lse_i = m_i + ln l_i.
+ * Dot mode reads q, k, v (cq, ck, gamma, beta ignored, may be NULL);
+ * coordinate mode reads cq, ck, gamma, beta, v (q, k ignored).  Writes o in
+ * `dtype` (bf16 rounded to nearest even) and lse in fp32 (natural log).
+ * Arithmetic is fp32 with fp32 accumulation; bf16 MFMA products for the band. */
+sa_status sa_fwd(const sa_graph* g, const sa_attn_desc* desc, const void* q, const void* k,
+                 const void* v, const float* cq, const float* ck, const float* gamma,
+                 const float* beta, void* o, float* lse, sa_stream stream);
+
+/* Bytes of device workspace sa_bwd needs for this graph and descriptor
+ * (per-row Delta_i plus per-block partial sums of the coordinate-mode
+ * parameter gradients). */
+sa_status sa_bwd_workspace_size(const sa_graph* g, const sa_attn_desc* desc, size_t* bytes);
+
+/* Backward of L = sum <dout, o> through sa_fwd, given the forward's o and
+ * lse:  dP_ij = <dout_i, v_j>,  Delta_i = <dout_i, o_i>,
+ *       dS_ij = P_ij (dP_ij - Delta_i),  P_ij = exp(s_ij - lse_i),
+ *   dot mode:   dq_i = scale sum_j dS_ij k_j,   dk_j = scale sum_i dS_ij q_i,
+ *   both modes: dv_j = sum_i P_ij dout_i,
+ *   coordinate: dcq_i = -2 gamma sum_j dS_ij (c_q,i - c_k,j),
+ *               dck_j =  2 gamma sum_i dS_ij (c_q,i - c_k,j),
+ *               dgamma_h = -sum dS_ij ||c_q,i - c_k,j||^2,  dbeta_h = sum dS_ij.
+ * Every output element is written (not accumulated into).  Deterministic: no
+ * atomics, fixed summation order, bitwise identical across runs.  Dot mode
+ * writes dq, dk, dv (dcq, dck, dgamma, dbeta may be NULL); coordinate mode
+ * writes dv, dcq, dck, dgamma, dbeta (dq, dk may be NULL).  The workspace
+ * (at least sa_bwd_workspace_size bytes, 256-byte aligned) is scratch owned
+ * by the caller and must not be shared by concurrent calls. */
+sa_status sa_bwd(const sa_graph* g, const sa_attn_desc* desc, const void* q, const void* k,
+                 const void* v, const float* cq, const float* ck, const float* gamma,
+                 const float* beta, const void* o, const float* lse, const void* dout, void* dq,
+                 void* dk, void* dv, float* dcq, float* dck, float* dgamma, float* dbeta,
+                 void* workspace, size_t workspace_bytes, sa_stream stream);
+
+/* Names the kernels sa_fwd (which = 0) or sa_bwd (which = 1) would launch for
+ * this graph and descriptor, as a NUL-terminated string in buf[0..cap).
+ * Validates like the call itself. */
+sa_status sa_describe_plan(const sa_graph* g, const sa_attn_desc* desc, int32_t which, char* buf,
+                           size_t cap);
+
+/* Static description of a status code. */
+const char* sa_status_str(sa_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

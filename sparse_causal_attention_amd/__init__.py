@@ -1,0 +1,291 @@
+"""Sparse causal attention over a fixed per-query neighbour graph, for MI355X.
+
+Thin Python binding of the C ABI in ``include/sa.h`` (same names).  It only
+marshals arguments: torch supplies device memory and the current stream;
+every step of the computation runs in the HIP kernels of ``libsa.so``.  There
+is no CPU or PyTorch fallback: tensors must live on the GPU and the library
+must be built (``python -m sparse_causal_attention_amd.build``).
+
+    g = sa_build_graph(T, window=4, offsets=[2**k for k in range(14)])
+    o, lse = sa_fwd(g, q, k, v)                 # [B, H, T, D], [B, H, T]
+    grads = sa_bwd(g, q, k, v, o, lse, dout)    # {"dq", "dk", "dv"}
+
+Coordinate score (-gamma_h ||c_q - c_k||^2 + beta_h): pass ``cq``, ``ck``
+([B, H, T, 3] fp32), ``gamma``, ``beta`` ([H] fp32) instead of ``q``, ``k``.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+
+from . import _abi
+from ._abi import (SA_ALGO_AUTO, SA_ALGO_BAND, SA_ALGO_GATHER, SA_BF16, SA_F32,
+                   SA_MAX_DILATED, SA_SCORE_COORD, SA_SCORE_DOT, SaError)
+
+__all__ = ["sa_build_graph", "sa_fwd", "sa_bwd", "sa_fwd_prepared", "sa_bwd_prepared",
+           "sa_bwd_workspace_size", "sa_describe_plan", "Graph", "SaError"]
+
+_ALGOS = {"auto": SA_ALGO_AUTO, "gather": SA_ALGO_GATHER, "band": SA_ALGO_BAND}
+
+
+class Graph:
+    """Owns an ``sa_graph`` handle (host memory)."""
+
+    def __init__(self, handle: int):
+        self._h = ctypes.c_void_p(handle)
+        L = _abi.lib()
+        T, W, nd, ne = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int64()
+        dil = (ctypes.c_int64 * SA_MAX_DILATED)()
+        _abi.check(L.sa_graph_info(self._h, ctypes.byref(T), ctypes.byref(W), ctypes.byref(nd),
+                                   dil, ctypes.byref(ne)), "sa_graph_info")
+        self.T, self.window, self.n_edges = T.value, W.value, ne.value
+        self.dilations = tuple(dil[t] for t in range(nd.value))
+
+    @property
+    def handle(self):
+        return self._h
+
+    def _rows(self, fn, r0, r1):
+        L = _abi.lib()
+        r1 = self.T if r1 is None else r1
+        rp = np.zeros(max(r1 - r0, 0) + 1, dtype=np.int64)
+        st = fn(self._h, r0, r1, rp.ctypes.data, None, 0)
+        need = int(rp[-1])
+        if st != _abi.SA_OK and need == 0:
+            _abi.check(st, "graph rows")
+        cols = np.empty(max(need, 1), dtype=np.int64)
+        _abi.check(fn(self._h, r0, r1, rp.ctypes.data, cols.ctypes.data, need), "graph rows")
+        return rp, cols[:need]
+
+    def rows(self, r0: int = 0, r1: int | None = None):
+        """CSR (row_ptr, cols) of rows [r0, r1), keys ascending."""
+        return self._rows(_abi.lib().sa_graph_rows, r0, r1)
+
+    def rows_reverse(self, r0: int = 0, r1: int | None = None):
+        """CSR of the reverse graph: for key j, the queries that attend to it."""
+        return self._rows(_abi.lib().sa_graph_rows_reverse, r0, r1)
+
+    def __del__(self):
+        if getattr(self, "_h", None) is not None and self._h.value and _abi._lib is not None:
+            _abi._lib.sa_graph_free(self._h)
+            self._h = None
+
+    def __repr__(self):
+        return "Graph(T=%d, window=%d, dilations=%s, edges/head=%d)" % (
+            self.T, self.window, list(self.dilations), self.n_edges)
+
+
+def sa_build_graph(T: int, window: int, offsets=()) -> Graph:
+    L = _abi.lib()
+    offs = np.ascontiguousarray(np.asarray(list(offsets), dtype=np.int64).reshape(-1))
+    h = ctypes.c_void_p()
+    _abi.check(L.sa_build_graph(int(T), int(window), offs.ctypes.data if len(offs) else None,
+                                len(offs), ctypes.byref(h)), "sa_build_graph")
+    return Graph(h.value)
+
+
+# ------------------------------------------------------------------ marshalling
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return SA_F32
+    if t.dtype == torch.bfloat16:
+        return SA_BF16
+    raise TypeError("tensors are float32 or bfloat16, got %s" % t.dtype)
+
+
+def _strides(t, name):
+    if t is None:
+        return (0, 0, 0)
+    if t.dim() != 4 or t.stride(3) != 1:
+        raise ValueError("%s must be [B, H, T, D] with a contiguous last dimension" % name)
+    return tuple(int(s) for s in t.stride()[:3])
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _require_gpu(**ts):
+    for name, t in ts.items():
+        if t is not None and not t.is_cuda:
+            raise ValueError("%s must be a GPU tensor (there is no CPU path)" % name)
+
+
+def _stream(stream):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _make_desc(ref, *, score, algo, scale, grad_dtype, q=None, k=None, v=None, o=None, dout=None,
+               dq=None, dk=None, dv=None) -> _abi.SaAttnDesc:
+    B, H, T, D = ref.shape
+    d = _abi.SaAttnDesc()
+    d.B, d.H, d.T, d.D = B, H, T, D
+    d.dtype = _dtype_code(ref)
+    d.grad_dtype = grad_dtype
+    d.score = score
+    d.algo = _ALGOS[algo] if isinstance(algo, str) else int(algo)
+    d.scale = 0.0 if scale is None else float(scale)
+    for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", dout), ("dq", dq), ("dk", dk),
+                    ("dv", dv)):
+        if t is not None and tuple(t.shape) != (B, H, T, D):
+            raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), (B, H, T, D)))
+        getattr(d, "stride_" + name)[:] = _strides(t, name)
+    return d
+
+
+def _coord_args(cq, ck, gamma, beta, B, H, T):
+    torch = _torch()
+    for name, t, shp in (("cq", cq, (B, H, T, 3)), ("ck", ck, (B, H, T, 3)), ("gamma", gamma, (H,)),
+                         ("beta", beta, (H,))):
+        if t is None or t.dtype != torch.float32 or tuple(t.shape) != shp or not t.is_contiguous():
+            raise ValueError("%s must be a contiguous float32 tensor of shape %s" % (name, shp))
+
+
+def _fwd_args(graph, q, k, v, cq, ck, gamma, beta, scale, o, lse, algo, stream):
+    torch = _torch()
+    coord = cq is not None
+    _require_gpu(q=q, k=k, v=v, cq=cq, ck=ck, gamma=gamma, beta=beta, o=o, lse=lse)
+    B, H, T, D = v.shape
+    if coord:
+        _coord_args(cq, ck, gamma, beta, B, H, T)
+    if o is None:
+        o = torch.empty_like(v, memory_format=torch.contiguous_format)
+    if lse is None:
+        lse = torch.empty((B, H, T), dtype=torch.float32, device=v.device)
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, T) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H, T] tensor")
+    d = _make_desc(v, score=SA_SCORE_COORD if coord else SA_SCORE_DOT, algo=algo, scale=scale,
+                   grad_dtype=SA_F32, q=None if coord else q, k=None if coord else k, v=v, o=o)
+    args = (graph.handle, ctypes.byref(d), _ptr(None if coord else q), _ptr(None if coord else k),
+            _ptr(v), _ptr(cq), _ptr(ck), _ptr(gamma), _ptr(beta), _ptr(o), _ptr(lse), _stream(stream))
+    return args, (d, o, lse)
+
+
+def sa_fwd(graph: Graph, q=None, k=None, v=None, *, cq=None, ck=None, gamma=None, beta=None,
+           scale=None, o=None, lse=None, algo="auto", stream=None):
+    """Returns (o, lse).  o has v's dtype and shape, lse is [B, H, T] fp32."""
+    args, (_d, o, lse) = _fwd_args(graph, q, k, v, cq, ck, gamma, beta, scale, o, lse, algo, stream)
+    _abi.check(_abi.lib().sa_fwd(*args), "sa_fwd")
+    return o, lse
+
+
+def sa_fwd_prepared(graph: Graph, q=None, k=None, v=None, *, cq=None, ck=None, gamma=None,
+                    beta=None, scale=None, o=None, lse=None, algo="auto", stream=None):
+    """Marshals the arguments of sa_fwd once and returns a zero-argument
+    callable that enqueues the same call again (same tensors, same stream).
+    For tight loops where per-call Python marshalling would dominate."""
+    args, keep = _fwd_args(graph, q, k, v, cq, ck, gamma, beta, scale, o, lse, algo, stream)
+    fn = _abi.lib().sa_fwd
+
+    def call():
+        _abi.check(fn(*args), "sa_fwd")
+        return keep[1], keep[2]
+
+    call.keepalive = (keep, graph)
+    return call
+
+
+def sa_bwd_workspace_size(graph: Graph, v, grad_dtype=None) -> int:
+    d = _make_desc(v, score=SA_SCORE_DOT, algo="auto", scale=None,
+                   grad_dtype=SA_F32 if grad_dtype is None else _dtype_code_of(grad_dtype))
+    n = ctypes.c_size_t()
+    _abi.check(_abi.lib().sa_bwd_workspace_size(graph.handle, ctypes.byref(d), ctypes.byref(n)),
+               "sa_bwd_workspace_size")
+    return n.value
+
+
+def _dtype_code_of(dt) -> int:
+    torch = _torch()
+    return {torch.float32: SA_F32, torch.bfloat16: SA_BF16}[dt]
+
+
+def _bwd_args(graph, q, k, v, o, lse, dout, cq, ck, gamma, beta, scale, grad_dtype, dq, dk, dv,
+              dcq, dck, dgamma, dbeta, workspace, algo, stream):
+    torch = _torch()
+    coord = cq is not None
+    _require_gpu(q=q, k=k, v=v, o=o, lse=lse, dout=dout, cq=cq, ck=ck, gamma=gamma, beta=beta)
+    B, H, T, D = v.shape
+    gdt = torch.float32 if grad_dtype is None else grad_dtype
+    gcode = _dtype_code_of(gdt)
+    dev = v.device
+    if coord:
+        _coord_args(cq, ck, gamma, beta, B, H, T)
+        dcq = torch.empty((B, H, T, 3), dtype=torch.float32, device=dev) if dcq is None else dcq
+        dck = torch.empty((B, H, T, 3), dtype=torch.float32, device=dev) if dck is None else dck
+        dgamma = torch.empty((H,), dtype=torch.float32, device=dev) if dgamma is None else dgamma
+        dbeta = torch.empty((H,), dtype=torch.float32, device=dev) if dbeta is None else dbeta
+    else:
+        dq = torch.empty((B, H, T, D), dtype=gdt, device=dev) if dq is None else dq
+        dk = torch.empty((B, H, T, D), dtype=gdt, device=dev) if dk is None else dk
+    dv = torch.empty((B, H, T, D), dtype=gdt, device=dev) if dv is None else dv
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if t is not None and t.dtype != gdt:
+            raise ValueError("%s must have the gradient dtype %s" % (name, gdt))
+    d = _make_desc(v, score=SA_SCORE_COORD if coord else SA_SCORE_DOT, algo=algo, scale=scale,
+                   grad_dtype=gcode, q=None if coord else q, k=None if coord else k, v=v, o=o,
+                   dout=dout, dq=None if coord else dq, dk=None if coord else dk, dv=dv)
+    L = _abi.lib()
+    n = ctypes.c_size_t()
+    _abi.check(L.sa_bwd_workspace_size(graph.handle, ctypes.byref(d), ctypes.byref(n)),
+               "sa_bwd_workspace_size")
+    if workspace is None:
+        workspace = torch.empty(max(n.value, 256), dtype=torch.uint8, device=dev)
+    args = (graph.handle, ctypes.byref(d), _ptr(None if coord else q), _ptr(None if coord else k),
+            _ptr(v), _ptr(cq), _ptr(ck), _ptr(gamma), _ptr(beta), _ptr(o), _ptr(lse), _ptr(dout),
+            _ptr(None if coord else dq), _ptr(None if coord else dk), _ptr(dv),
+            _ptr(dcq if coord else None), _ptr(dck if coord else None),
+            _ptr(dgamma if coord else None), _ptr(dbeta if coord else None),
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    if coord:
+        out = {"dv": dv, "dcq": dcq, "dck": dck, "dgamma": dgamma, "dbeta": dbeta}
+    else:
+        out = {"dq": dq, "dk": dk, "dv": dv}
+    return args, (d, workspace, out)
+
+
+def sa_bwd(graph: Graph, q=None, k=None, v=None, o=None, lse=None, dout=None, *, cq=None, ck=None,
+           gamma=None, beta=None, scale=None, grad_dtype=None, dq=None, dk=None, dv=None,
+           dcq=None, dck=None, dgamma=None, dbeta=None, workspace=None, algo="auto", stream=None):
+    """Gradients of sum <dout, o>.  Dot mode returns {dq, dk, dv}; coordinate
+    mode {dv, dcq, dck, dgamma, dbeta}.  Gradients default to fp32."""
+    args, (_d, _ws, out) = _bwd_args(graph, q, k, v, o, lse, dout, cq, ck, gamma, beta, scale,
+                                     grad_dtype, dq, dk, dv, dcq, dck, dgamma, dbeta, workspace,
+                                     algo, stream)
+    _abi.check(_abi.lib().sa_bwd(*args), "sa_bwd")
+    return out
+
+
+def sa_bwd_prepared(graph: Graph, q=None, k=None, v=None, o=None, lse=None, dout=None, *, cq=None,
+                    ck=None, gamma=None, beta=None, scale=None, grad_dtype=None, dq=None, dk=None,
+                    dv=None, dcq=None, dck=None, dgamma=None, dbeta=None, workspace=None,
+                    algo="auto", stream=None):
+    """Like sa_fwd_prepared, for sa_bwd."""
+    args, keep = _bwd_args(graph, q, k, v, o, lse, dout, cq, ck, gamma, beta, scale, grad_dtype,
+                           dq, dk, dv, dcq, dck, dgamma, dbeta, workspace, algo, stream)
+    fn = _abi.lib().sa_bwd
+
+    def call():
+        _abi.check(fn(*args), "sa_bwd")
+        return keep[2]
+
+    call.keepalive = (keep, graph)
+    return call
+
+
+def sa_describe_plan(graph: Graph, v, *, coord=False, algo="auto", which="fwd") -> str:
+    """Names of the kernels sa_fwd ("fwd") or sa_bwd ("bwd") would launch."""
+    d = _make_desc(v, score=SA_SCORE_COORD if coord else SA_SCORE_DOT, algo=algo, scale=None,
+                   grad_dtype=SA_F32)
+    buf = ctypes.create_string_buffer(256)
+    _abi.check(_abi.lib().sa_describe_plan(graph.handle, ctypes.byref(d), 0 if which == "fwd" else 1,
+                                           buf, 256), "sa_describe_plan")
+    return buf.value.decode()

@@ -1,0 +1,243 @@
+// C ABI: argument validation, parameter packing and kernel selection.
+//
+// Every check runs on the host before the first HIP call, so a rejected call
+// has no side effect and the library works for validation on machines with
+// no GPU.  Nothing here allocates device memory.
+#include <math.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "sa_internal.h"
+
+namespace {
+
+bool bad_dtype(int32_t dt) { return dt != SA_F32 && dt != SA_BF16; }
+int esize(int32_t dt) { return dt == SA_BF16 ? 2 : 4; }
+
+// Row starts 16-byte aligned for 16-byte vector accesses.
+bool aligned_rows(const void* p, const int64_t st[3], int es) {
+  if ((reinterpret_cast<uintptr_t>(p) & 15u) != 0) return false;
+  for (int c = 0; c < 3; ++c)
+    if (st[c] < 0 || (st[c] * es) % 16 != 0) return false;
+  return true;
+}
+
+// Largest element offset touched by a [B, H, T, D] tensor with these strides.
+bool offsets_fit(const sa_attn_desc* d, const int64_t st[3]) {
+  const double last = (double)(d->B - 1) * st[0] + (double)(d->H - 1) * st[1] +
+                      (double)(d->T - 1) * st[2] + (double)d->D;
+  return last < 9.0e18;
+}
+
+enum class Path { Gather, Band };
+
+struct Plan {
+  Path path;
+};
+
+sa_status check_common(const sa_graph* g, const sa_attn_desc* d, const void* q, const void* k,
+                       const void* v, const float* cq, const float* ck, const float* gamma,
+                       const float* beta, Plan* plan) {
+  if (g == nullptr || d == nullptr) return SA_ERR_INVALID_ARG;
+  if (d->B < 1 || d->H < 1 || d->T < 1 || d->D < 1) return SA_ERR_INVALID_ARG;
+  if (bad_dtype(d->dtype) || bad_dtype(d->grad_dtype)) return SA_ERR_INVALID_ARG;
+  if (d->score != SA_SCORE_DOT && d->score != SA_SCORE_COORD) return SA_ERR_INVALID_ARG;
+  if (d->algo != SA_ALGO_AUTO && d->algo != SA_ALGO_GATHER && d->algo != SA_ALGO_BAND)
+    return SA_ERR_INVALID_ARG;
+  if (d->T != g->T) return SA_ERR_SHAPE_MISMATCH;
+  if (d->D != 16 && d->D != 32 && d->D != 64 && d->D != 128) return SA_ERR_UNSUPPORTED;
+  if (d->B * d->H > (int64_t)1 << 24) return SA_ERR_UNSUPPORTED;
+  // blocks of the smallest row tile must be countable in int32
+  if ((double)d->B * d->H * (double)d->T > 1.0e12) return SA_ERR_UNSUPPORTED;
+  const bool coord = d->score == SA_SCORE_COORD;
+  const int es = esize(d->dtype);
+  if (v == nullptr || !aligned_rows(v, d->stride_v, es) || !offsets_fit(d, d->stride_v))
+    return SA_ERR_INVALID_ARG;
+  if (!coord) {
+    if (q == nullptr || k == nullptr) return SA_ERR_INVALID_ARG;
+    if (!aligned_rows(q, d->stride_q, es) || !aligned_rows(k, d->stride_k, es))
+      return SA_ERR_INVALID_ARG;
+    if (!offsets_fit(d, d->stride_q) || !offsets_fit(d, d->stride_k)) return SA_ERR_INVALID_ARG;
+  } else {
+    if (cq == nullptr || ck == nullptr || gamma == nullptr || beta == nullptr)
+      return SA_ERR_INVALID_ARG;
+  }
+  if (!coord && !(d->scale == d->scale)) return SA_ERR_INVALID_ARG;  // NaN scale
+  const bool band_ok = sa::band_supported(d->dtype, (int)d->D, coord, g->W);
+  if (d->algo == SA_ALGO_BAND && !band_ok) return SA_ERR_UNSUPPORTED;
+  plan->path = (d->algo != SA_ALGO_GATHER && band_ok) ? Path::Band : Path::Gather;
+  return SA_OK;
+}
+
+void fill_common(sa::Params* p, const sa_graph* g, const sa_attn_desc* d) {
+  memset(p, 0, sizeof(*p));
+  p->B = (int32_t)d->B;
+  p->H = (int32_t)d->H;
+  p->T = (int32_t)d->T;
+  p->D = (int32_t)d->D;
+  p->W = (int32_t)g->W;
+  p->n_dil = g->n_dil;
+  for (int t = 0; t < g->n_dil; ++t) p->dil[t] = (int32_t)g->dil[t];
+  p->scale = d->scale > 0.f ? d->scale : (float)(1.0 / sqrt((double)d->D));
+  p->scale_log2 = p->scale * 1.4426950408889634f;
+  p->grad_bf16 = d->grad_dtype == SA_BF16;
+}
+
+#define SET_STRIDES(prefix, arr) \
+  p.prefix##_b = (arr)[0];       \
+  p.prefix##_h = (arr)[1];       \
+  p.prefix##_t = (arr)[2]
+
+hipStream_t as_stream(sa_stream s) { return reinterpret_cast<hipStream_t>(s); }
+
+const char* fwd_kernel_name(const sa_attn_desc* d, Path path) {
+  if (path == Path::Band) return "band_fwd_mfma_bf16";
+  return d->score == SA_SCORE_COORD ? "gather_fwd_coord" : "gather_fwd_dot";
+}
+
+}  // namespace
+
+extern "C" sa_status sa_fwd(const sa_graph* g, const sa_attn_desc* d, const void* q, const void* k,
+                            const void* v, const float* cq, const float* ck, const float* gamma,
+                            const float* beta, void* o, float* lse, sa_stream stream) {
+  Plan plan;
+  sa_status st = check_common(g, d, q, k, v, cq, ck, gamma, beta, &plan);
+  if (st != SA_OK) return st;
+  if (o == nullptr || lse == nullptr) return SA_ERR_INVALID_ARG;
+  if (!aligned_rows(o, d->stride_o, esize(d->dtype)) || !offsets_fit(d, d->stride_o))
+    return SA_ERR_INVALID_ARG;
+  sa::Params p;
+  fill_common(&p, g, d);
+  p.q = q; SET_STRIDES(sq, d->stride_q);
+  p.k = k; SET_STRIDES(sk, d->stride_k);
+  p.v = v; SET_STRIDES(sv, d->stride_v);
+  p.o = o; SET_STRIDES(so, d->stride_o);
+  p.cq = cq; p.ck = ck; p.gamma = gamma; p.beta = beta;
+  p.lse = lse;
+  hipError_t e = plan.path == Path::Band
+                     ? sa::launch_band_fwd(p, as_stream(stream))
+                     : sa::launch_gather_fwd(p, d->dtype == SA_BF16 ? sa::DT_BF16 : sa::DT_F32,
+                                             d->score == SA_SCORE_COORD, as_stream(stream));
+  return e == hipSuccess ? SA_OK : SA_ERR_HIP;
+}
+
+namespace {
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+size_t workspace_bytes_for(const sa_attn_desc* d) {
+  const size_t rows = (size_t)d->B * d->H * d->T;
+  const int rpb = sa::gather_rows_per_block(d->dtype == SA_BF16 ? sa::DT_BF16 : sa::DT_F32,
+                                            (int)d->D);
+  const size_t nblk = (size_t)((d->T + rpb - 1) / rpb);
+  return align256(rows * sizeof(float)) + align256((size_t)d->B * d->H * nblk * 2 * sizeof(float));
+}
+
+}  // namespace
+
+extern "C" sa_status sa_bwd_workspace_size(const sa_graph* g, const sa_attn_desc* d,
+                                           size_t* bytes) {
+  if (bytes == nullptr || g == nullptr || d == nullptr) return SA_ERR_INVALID_ARG;
+  if (d->B < 1 || d->H < 1 || d->T < 1) return SA_ERR_INVALID_ARG;
+  if (bad_dtype(d->dtype)) return SA_ERR_INVALID_ARG;
+  if (d->D != 16 && d->D != 32 && d->D != 64 && d->D != 128) return SA_ERR_UNSUPPORTED;
+  if (d->T != g->T) return SA_ERR_SHAPE_MISMATCH;
+  *bytes = workspace_bytes_for(d);
+  return SA_OK;
+}
+
+extern "C" sa_status sa_bwd(const sa_graph* g, const sa_attn_desc* d, const void* q, const void* k,
+                            const void* v, const float* cq, const float* ck, const float* gamma,
+                            const float* beta, const void* o, const float* lse, const void* dout,
+                            void* dq, void* dk, void* dv, float* dcq, float* dck, float* dgamma,
+                            float* dbeta, void* workspace, size_t workspace_bytes,
+                            sa_stream stream) {
+  Plan plan;
+  sa_status st = check_common(g, d, q, k, v, cq, ck, gamma, beta, &plan);
+  if (st != SA_OK) return st;
+  const bool coord = d->score == SA_SCORE_COORD;
+  const int es = esize(d->dtype), gs = esize(d->grad_dtype);
+  if (o == nullptr || lse == nullptr || dout == nullptr || dv == nullptr) return SA_ERR_INVALID_ARG;
+  if (!aligned_rows(o, d->stride_o, es) || !aligned_rows(dout, d->stride_do, es))
+    return SA_ERR_INVALID_ARG;
+  if (!offsets_fit(d, d->stride_o) || !offsets_fit(d, d->stride_do)) return SA_ERR_INVALID_ARG;
+  // gradient rows: 16-byte aligned starts, like the inputs
+  auto grad_ok = [&](const void* ptr, const int64_t s[3]) {
+    if ((reinterpret_cast<uintptr_t>(ptr) & 15u) != 0) return false;
+    for (int c = 0; c < 3; ++c)
+      if (s[c] < 0 || (s[c] * gs) % 16 != 0) return false;
+    return offsets_fit(d, s);
+  };
+  if (!grad_ok(dv, d->stride_dv)) return SA_ERR_INVALID_ARG;
+  if (!coord) {
+    if (dq == nullptr || dk == nullptr) return SA_ERR_INVALID_ARG;
+    if (!grad_ok(dq, d->stride_dq) || !grad_ok(dk, d->stride_dk)) return SA_ERR_INVALID_ARG;
+  } else {
+    if (dcq == nullptr || dck == nullptr || dgamma == nullptr || dbeta == nullptr)
+      return SA_ERR_INVALID_ARG;
+  }
+  if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return SA_ERR_WORKSPACE;
+  const size_t need = workspace_bytes_for(d);
+  if (workspace_bytes < need) return SA_ERR_WORKSPACE;
+
+  sa::Params p;
+  fill_common(&p, g, d);
+  p.q = q; SET_STRIDES(sq, d->stride_q);
+  p.k = k; SET_STRIDES(sk, d->stride_k);
+  p.v = v; SET_STRIDES(sv, d->stride_v);
+  p.o = const_cast<void*>(o); SET_STRIDES(so, d->stride_o);
+  p.dout = dout; SET_STRIDES(sdo, d->stride_do);
+  p.dq = dq; SET_STRIDES(sdq, d->stride_dq);
+  p.dk = dk; SET_STRIDES(sdk, d->stride_dk);
+  p.dv = dv; SET_STRIDES(sdv, d->stride_dv);
+  p.cq = cq; p.ck = ck; p.gamma = gamma; p.beta = beta;
+  p.dcq = dcq; p.dck = dck; p.dgamma = dgamma; p.dbeta = dbeta;
+  p.lse = const_cast<float*>(lse);
+  char* ws = static_cast<char*>(workspace);
+  p.delta = reinterpret_cast<float*>(ws);
+  p.partials = reinterpret_cast<float*>(ws + align256((size_t)d->B * d->H * d->T * sizeof(float)));
+  hipError_t e = plan.path == Path::Band
+                     ? sa::launch_band_bwd(p, as_stream(stream))
+                     : sa::launch_gather_bwd(p, d->dtype == SA_BF16 ? sa::DT_BF16 : sa::DT_F32,
+                                             coord, as_stream(stream));
+  return e == hipSuccess ? SA_OK : SA_ERR_HIP;
+}
+
+extern "C" sa_status sa_describe_plan(const sa_graph* g, const sa_attn_desc* d, int32_t which,
+                                      char* buf, size_t cap) {
+  if (buf == nullptr || cap == 0 || (which != 0 && which != 1)) return SA_ERR_INVALID_ARG;
+  if (d == nullptr) return SA_ERR_INVALID_ARG;
+  Plan plan;
+  // validates the shape, dtype and mode parts; pointers and strides are not
+  // needed to choose kernels, so stand-ins are used for them
+  alignas(16) static const float dummy[4] = {0.f, 0.f, 0.f, 0.f};
+  sa_attn_desc tmp = *d;
+  for (int c = 0; c < 3; ++c) tmp.stride_q[c] = tmp.stride_k[c] = tmp.stride_v[c] = 0;
+  sa_status st = check_common(g, &tmp, dummy, dummy, dummy, dummy, dummy, dummy, dummy, &plan);
+  if (st != SA_OK) return st;
+  const bool coord = d->score == SA_SCORE_COORD;
+  const char* txt;
+  if (which == 0) {
+    txt = fwd_kernel_name(d, plan.path);
+  } else if (plan.path == Path::Band) {
+    txt = "band_bwd_dq_mfma_bf16+band_bwd_dkdv_mfma_bf16";
+  } else {
+    txt = coord ? "gather_bwd_q_coord+gather_bwd_kv_coord+coord_param_reduce"
+                : "gather_bwd_q_dot+gather_bwd_kv_dot";
+  }
+  snprintf(buf, cap, "%s", txt);
+  return SA_OK;
+}
+
+extern "C" const char* sa_status_str(sa_status s) {
+  switch (s) {
+    case SA_OK: return "ok";
+    case SA_ERR_INVALID_ARG: return "invalid argument";
+    case SA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case SA_ERR_SHAPE_MISMATCH: return "graph length differs from descriptor length";
+    case SA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case SA_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}

@@ -1,0 +1,281 @@
+// Band kernels: the sliding-window part of the graph as dense LDS-staged
+// tiles on the bf16 matrix cores, with the long-range edges of the same
+// query rows gathered in the same workgroup.
+//
+// The window of query i is keys (i-W, i] (MiniGPT Part 6, "A mask is not
+// enough": keep j iff j <= i and i - j < w).  A block of consecutive queries
+// therefore needs one contiguous key range, and within it the scores form a
+// dense matrix product with a band mask -- the part of the computation that
+// really is a contraction, so it runs on MFMA.  Unlike the page's chunked
+// version (stacked 2W-wide copies of K and V, a [T/W, W, 2W] score tensor),
+// nothing is materialised in HBM: 64-key tiles of K and V pass through LDS,
+// the scores live in MFMA accumulators, and key tiles that lie wholly outside
+// a wavefront's band are skipped, so the work stays proportional to the
+// band's edges.
+//
+// Layouts (v_mfma_f32_32x32x16_bf16; lane l, half = l / 32, l32 = l % 32):
+//   A operand: A[m = l32][k = 8*half + e]        (8 bf16, e = 0..7)
+//   B operand: B[k = 8*half + e][n = l32]
+//   C (16 fp32): C[m = 8*(r/4) + 4*half + r%4][n = l32], r = 0..15
+// Scores are computed transposed, S^T = K Q^T, so that C's column index is
+// the query: lane l owns query row l32 of its wavefront, and its 16 values
+// per 32-key block are keys 8*(r/4) + 4*half + r%4.  The output is computed
+// transposed too, O^T = V^T P^T: P^T is the B operand, which lane l supplies
+// from its own score registers (keys in the order above), and V^T comes from
+// a transposed copy of the V tile in LDS.  Each lane therefore keeps the
+// running max, sum and output accumulator of exactly one query row, and the
+// two lanes l, l+32 of a row combine with one cross-half exchange per tile.
+#include "device_util.h"
+#include "sa_internal.h"
+
+namespace sa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kD = 64;
+constexpr int kBQ = 128;        // query rows per workgroup: 4 wavefronts x 32
+constexpr int kBK = 64;         // keys per LDS tile
+constexpr int kKRow = kD + 8;   // K tile row stride, bf16 elements (144 B)
+constexpr int kVRow = kBK + 4;  // V^T tile row stride, bf16 elements (136 B)
+constexpr int kThreads = 256;
+constexpr int kG = 2;           // long-range edges in flight per lane
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8, u); }
+
+__device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float xhalf(float x) { return __shfl_xor(x, 32, 64); }
+
+__global__ __launch_bounds__(kThreads) void band_fwd_kernel(Params p) {
+  __shared__ __align__(16) __bf16 Ks[kBK * kKRow];
+  __shared__ __align__(16) __bf16 Vt[kD * kVRow];
+
+  const int nblk = (p.T + kBQ - 1) / kBQ;
+  const int logical = xcd_logical_block(p.B * p.H * nblk);
+  if (logical < 0) return;
+  const int bh = logical / nblk;
+  const int rb = nblk - 1 - (logical - bh * nblk);  // late (longest) query blocks first
+  const int b = bh / p.H, h = bh - b * p.H;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, half = lane >> 5;
+  const int q0 = rb * kBQ;
+  const int qw = q0 + wave * 32;
+  const int m = qw + l32;
+  const int mc = m < p.T ? m : p.T - 1;
+
+  const char* qbase = static_cast<const char*>(p.q) + (b * p.sq_b + h * p.sq_h) * 2;
+  const char* kbase = static_cast<const char*>(p.k) + (b * p.sk_b + h * p.sk_h) * 2;
+  const char* vbase = static_cast<const char*>(p.v) + (b * p.sv_b + h * p.sv_h) * 2;
+  const int64_t sqt = p.sq_t * 2, skt = p.sk_t * 2, svt = p.sv_t * 2;
+
+  // Q^T as B operand: lane holds q[m][16*kk + 8*half + e]
+  bf16x8 qf[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) qf[kk] = as_bf16x8(ld16(qbase + mc * sqt + (16 * kk + 8 * half) * 2));
+
+  float mrun = -INFINITY, lrun = 0.f;
+  f32x16 oacc[2];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) oacc[0][r] = oacc[1][r] = 0.f;
+
+  const int W = p.W;
+  const int lo = q0 - W + 1 > 0 ? q0 - W + 1 : 0;
+  const int hi = q0 + kBQ - 1 < p.T - 1 ? q0 + kBQ - 1 : p.T - 1;
+  const int wlo = qw - W + 1, whi = qw + 31;  // this wavefront's key range
+  const float sl2 = p.scale_log2;
+
+  for (int kt0 = (lo / kBK) * kBK; kt0 <= hi; kt0 += kBK) {
+    __syncthreads();  // previous tile fully consumed
+    {
+      // stage rows [kt0, kt0 + 64): K as is, V transposed; 4 threads per row
+      const int r = tid >> 2, c = (tid & 3) * 2;
+      const int key = kt0 + r < p.T ? kt0 + r : p.T - 1;
+      const uint4 k0 = ld16(kbase + key * skt + c * 16);
+      const uint4 k1 = ld16(kbase + key * skt + (c + 1) * 16);
+      const uint4 v0 = ld16(vbase + key * svt + c * 16);
+      const uint4 v1 = ld16(vbase + key * svt + (c + 1) * 16);
+      *reinterpret_cast<uint4*>(&Ks[r * kKRow + c * 8]) = k0;
+      *reinterpret_cast<uint4*>(&Ks[r * kKRow + (c + 1) * 8]) = k1;
+      const bf16x8 a0 = as_bf16x8(v0), a1 = as_bf16x8(v1);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        Vt[(c * 8 + e) * kVRow + r] = a0[e];
+        Vt[((c + 1) * 8 + e) * kVRow + r] = a1[e];
+      }
+    }
+    __syncthreads();
+    if (kt0 + kBK - 1 < wlo || kt0 > whi) continue;  // tile outside this wavefront's band
+
+    f32x16 sacc[2];
+    bool on[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int nb0 = kt0 + nb * 32;
+      on[nb] = !(nb0 + 31 < wlo || nb0 > whi);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[nb][r] = 0.f;
+      if (on[nb]) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Ks[(nb * 32 + l32) * kKRow + 16 * kk + 8 * half]);
+          sacc[nb] = mfma32(a, qf[kk], sacc[nb]);
+        }
+      }
+    }
+    // band mask, scale to log2 units, tile max
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int n = kt0 + nb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+        const bool ok = on[nb] && n <= m && m - n < W;
+        const float s = ok ? sacc[nb][r] * sl2 : -INFINITY;
+        sacc[nb][r] = s;
+        tmax = fmaxf(tmax, s);
+      }
+    tmax = fmaxf(tmax, xhalf(tmax));
+    const float mnew = fmaxf(mrun, tmax);
+    const float mref = mnew == -INFINITY ? 0.f : mnew;
+    const float alpha = fast_exp2(mrun - mref);
+    float psum = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float pv = fast_exp2(sacc[nb][r] - mref);
+        sacc[nb][r] = pv;
+        psum += pv;
+      }
+    lrun = fmaf(lrun, alpha, psum);
+    mrun = mnew;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      oacc[0][r] *= alpha;
+      oacc[1][r] *= alpha;
+    }
+    // O^T += V^T P^T, 16 keys per step
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      const int nb = ks >> 1;
+      if (!on[nb]) continue;
+      bf16x8 pb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[e] = static_cast<__bf16>(sacc[nb][8 * (ks & 1) + e]);
+#pragma unroll
+      for (int dblk = 0; dblk < 2; ++dblk) {
+        const __bf16* row = &Vt[(dblk * 32 + l32) * kVRow + 16 * ks + 4 * half];
+        const uint2 x0 = *reinterpret_cast<const uint2*>(row);
+        const uint2 x1 = *reinterpret_cast<const uint2*>(row + 8);
+        oacc[dblk] = mfma32(as_bf16x8(make_uint4(x0.x, x0.y, x1.x, x1.y)), pb, oacc[dblk]);
+      }
+    }
+  }
+
+  // ---- long-range edges j = m - d: row gathers in the accumulator layout
+  if (p.n_dil > 0) {
+    float qv[32];  // q[m][16*kk + 8*half + e] in fp32
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qv[8 * kk + e] = static_cast<float>(qf[kk][e]);
+    for (int t0 = 0; t0 < p.n_dil; t0 += kG) {
+      uint4 kr[kG][4];
+      uint2 vr[kG][8];
+      int j[kG];
+#pragma unroll
+      for (int g = 0; g < kG; ++g) {
+        const int t = t0 + g;
+        j[g] = t < p.n_dil ? mc - p.dil[t] : -1;
+        const int jj = j[g] < 0 ? 0 : j[g];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) kr[g][kk] = ld16(kbase + jj * skt + (16 * kk + 8 * half) * 2);
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          vr[g][c] = *reinterpret_cast<const uint2*>(vbase + jj * svt +
+                                                     ((c >> 2) * 32 + 8 * (c & 3) + 4 * half) * 2);
+      }
+      float s[kG];
+#pragma unroll
+      for (int g = 0; g < kG; ++g) {
+        float part = 0.f;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const bf16x8 kv = as_bf16x8(kr[g][kk]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) part = fmaf(qv[8 * kk + e], static_cast<float>(kv[e]), part);
+        }
+        s[g] = part;
+      }
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int g = 0; g < kG; ++g) {
+        s[g] = (s[g] + xhalf(s[g])) * sl2;
+        s[g] = j[g] >= 0 ? s[g] : -INFINITY;
+        tmax = fmaxf(tmax, s[g]);
+      }
+      const float mnew = fmaxf(mrun, tmax);
+      const float mref = mnew == -INFINITY ? 0.f : mnew;
+      const float alpha = fast_exp2(mrun - mref);
+      float pg[kG], psum = 0.f;
+#pragma unroll
+      for (int g = 0; g < kG; ++g) {
+        pg[g] = fast_exp2(s[g] - mref);
+        psum += pg[g];
+      }
+      // both halves see the same edge: count its weight once in the row sum
+      lrun = fmaf(lrun, alpha, half == 0 ? psum : 0.f);
+      mrun = mnew;
+#pragma unroll
+      for (int dblk = 0; dblk < 2; ++dblk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float acc = oacc[dblk][r] * alpha;
+#pragma unroll
+          for (int g = 0; g < kG; ++g) {
+            const uint2 w2 = vr[g][dblk * 4 + (r >> 2)];
+            const uint32_t word = (r & 2) ? w2.y : w2.x;
+            const float vv = (r & 1) ? bf16_hi(word) : bf16_lo(word);
+            acc = fmaf(pg[g], vv, acc);
+          }
+          oacc[dblk][r] = acc;
+        }
+    }
+  }
+
+  // ---- finish: O = acc / l, lse = m + log l (natural log)
+  const float ltot = lrun + xhalf(lrun);
+  if (m >= p.T) return;
+  const float inv = 1.f / ltot;
+  char* orow = static_cast<char*>(p.o) + (b * p.so_b + h * p.so_h + (int64_t)m * p.so_t) * 2;
+#pragma unroll
+  for (int dblk = 0; dblk < 2; ++dblk)
+#pragma unroll
+    for (int g4 = 0; g4 < 4; ++g4) {
+      const uint2 w2 = make_uint2(pack_bf16x2(oacc[dblk][4 * g4] * inv, oacc[dblk][4 * g4 + 1] * inv),
+                                  pack_bf16x2(oacc[dblk][4 * g4 + 2] * inv, oacc[dblk][4 * g4 + 3] * inv));
+      *reinterpret_cast<uint2*>(orow + (dblk * 32 + 8 * g4 + 4 * half) * 2) = w2;
+    }
+  if (half == 0) p.lse[(int64_t)bh * p.T + m] = (mrun + fast_log2(ltot)) * kLn2;
+}
+
+}  // namespace
+
+bool band_supported(int dtype, int D, bool coord, int64_t W) {
+  return dtype == DT_BF16 && D == kD && !coord && W >= 16;
+}
+
+int band_rows_per_block() { return kBQ; }
+
+hipError_t launch_band_fwd(const Params& p, hipStream_t s) {
+  const int nblk = (p.T + kBQ - 1) / kBQ;
+  const int grid = xcd_grid(p.B * p.H * nblk);
+  hipLaunchKernelGGL(band_fwd_kernel, dim3(grid), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace sa

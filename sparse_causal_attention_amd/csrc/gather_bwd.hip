@@ -1,0 +1,420 @@
+// Gather backward: the gradients of sum <dout, o> through the forward, on
+// the vector ALUs, deterministic and without atomics.
+//
+// Two passes share the lane-group layout of the forward (one row per LG
+// lanes, 16 bytes per lane, DPP reductions):
+//  1. query side, one row i per lane group, over the forward graph
+//     j = i - delta: P_ij = exp(s_ij - lse_i), dP_ij = <dout_i, v_j>, and in
+//     the same single pass Delta_i = sum_j P_ij dP_ij (kept in the workspace
+//     for pass 2) together with sum_j P_ij dP_ij x_j and sum_j P_ij x_j, so
+//     that dq_i = scale (sum_j P dP k_j - Delta_i sum_j P k_j) needs no second
+//     pass over the edges (coordinate mode: dc_q,i and per-block partial sums
+//     of dgamma, dbeta the same way).  Delta_i comes from the edges, not from
+//     <dout_i, o_i>, so a bf16-rounded o does not perturb it;
+//  2. key side, one row j per lane group, over the reverse graph
+//     i = j + delta < T: dv_j = sum_i P_ij dout_i, dk_j = scale sum_i dS_ij q_i
+//     (coordinate mode: dc_k,j).  For a fixed delta the query rows of
+//     consecutive keys are consecutive, so these reads coalesce exactly like
+//     the forward's.
+// Each output row has exactly one writer, so the result is bitwise
+// reproducible.  A final pass reduces the coordinate-mode partials per head
+// in fp64 in a fixed order.
+#include "device_util.h"
+#include "sa_internal.h"
+
+namespace sa {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+
+template <int DT, int D>
+struct Geo {
+  static constexpr int EPL = Frag<DT>::EPL;
+  static constexpr int LG = D / EPL;
+  static constexpr int RPW = 64 / LG;
+  static constexpr int RPB = RPW * kWaves;
+};
+
+__device__ __forceinline__ int distance_of(const Params& p, int t) {
+  return t < p.W ? t : p.dil[t - p.W];
+}
+
+// ------------------------------------------------------------------ pass 1
+template <int DT, int D, bool COORD, int G>
+__global__ __launch_bounds__(kThreads) void gather_bwd_q_kernel(Params p) {
+  using F = Frag<DT>;
+  using Gm = Geo<DT, D>;
+  constexpr int EPL = Gm::EPL, LG = Gm::LG, RPW = Gm::RPW, RPB = Gm::RPB;
+  constexpr int EB = F::BYTES;
+
+  const int nblk = (p.T + RPB - 1) / RPB;
+  const int logical = xcd_logical_block(p.B * p.H * nblk);
+  if (logical < 0) return;
+  const int bh = logical / nblk, rb = logical - bh * nblk;
+  const int b = bh / p.H, h = bh - b * p.H;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane % LG;
+  int i = rb * RPB + wave * RPW + lane / LG;
+  const bool row_ok = i < p.T;
+  if (!row_ok) i = p.T - 1;
+
+  const char* kb = static_cast<const char*>(p.k) + (b * p.sk_b + h * p.sk_h) * EB + sub * 16;
+  const char* vb = static_cast<const char*>(p.v) + (b * p.sv_b + h * p.sv_h) * EB + sub * 16;
+  const int64_t skt = p.sk_t * EB, svt = p.sv_t * EB;
+
+  float dof[EPL], qf[EPL];
+  {
+    const char* dorow = static_cast<const char*>(p.dout) +
+                        (b * p.sdo_b + h * p.sdo_h + i * p.sdo_t) * EB + sub * 16;
+    F::unpack(ld16(dorow), dof);
+  }
+  // lse includes beta in coordinate mode; the scores below omit it
+  const float lse2 =
+      (p.lse[(int64_t)bh * p.T + i] - (COORD ? p.beta[h] : 0.f)) * kLog2e;
+
+  float cqi[3] = {0.f, 0.f, 0.f};
+  float gl2 = 0.f, gam = 0.f;
+  const float* ckb = nullptr;
+  if constexpr (!COORD) {
+    const char* qrow = static_cast<const char*>(p.q) + (b * p.sq_b + h * p.sq_h + i * p.sq_t) * EB +
+                       sub * 16;
+    F::unpack(ld16(qrow), qf);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qf[e] *= p.scale_log2;
+  } else {
+    const float* cqr = p.cq + ((int64_t)bh * p.T + i) * 3;
+    cqi[0] = cqr[0]; cqi[1] = cqr[1]; cqi[2] = cqr[2];
+    gam = p.gamma[h];
+    gl2 = gam * kLog2e;
+    ckb = p.ck + (int64_t)bh * p.T * 3;
+  }
+
+  // running sums over the row's edges: Delta = sum P dP, and per term x
+  // (k_j in dot mode; c_q,i - c_k,j and ||.||^2 in coordinate mode)
+  // sum P dP x and sum P x
+  float delta = 0.f;
+  float pdx[EPL], px[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) pdx[e] = px[e] = 0.f;
+  float cdx[3] = {0.f, 0.f, 0.f}, cx[3] = {0.f, 0.f, 0.f};
+  float r2dx = 0.f, r2x = 0.f, psum = 0.f;
+
+  const int nd = p.W + p.n_dil;
+  for (int t0 = 0; t0 < nd; t0 += G) {
+    int j[G];
+    uint4 kraw[G], vraw[G];
+    float s[G], dp[G], r2[G], dif[G][3];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int t = t0 + g;
+      j[g] = (t < nd) ? i - distance_of(p, t) : -1;
+      const int jj = j[g] < 0 ? 0 : j[g];
+      if constexpr (!COORD) kraw[g] = ld16(kb + jj * skt);
+      vraw[g] = ld16(vb + jj * svt);
+      if constexpr (COORD) {
+        const float* c = ckb + (int64_t)jj * 3;
+        dif[g][0] = cqi[0] - c[0];
+        dif[g][1] = cqi[1] - c[1];
+        dif[g][2] = cqi[2] - c[2];
+        r2[g] = dif[g][0] * dif[g][0] + dif[g][1] * dif[g][1] + dif[g][2] * dif[g][2];
+        s[g] = -gl2 * r2[g];
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float vf[EPL];
+      F::unpack(vraw[g], vf);
+      float part = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) part = fmaf(dof[e], vf[e], part);
+      dp[g] = part;
+      if constexpr (!COORD) {
+        float kf[EPL];
+        F::unpack(kraw[g], kf);
+        float ps = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) ps = fmaf(qf[e], kf[e], ps);
+        s[g] = ps;
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      dp[g] = group_sum<LG>(dp[g]);
+      if constexpr (!COORD) s[g] = group_sum<LG>(s[g]);
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float pr = j[g] >= 0 ? fast_exp2(s[g] - lse2) : 0.f;
+      const float pd = pr * dp[g];
+      delta += pd;
+      if constexpr (!COORD) {
+        float kf[EPL];
+        F::unpack(kraw[g], kf);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) {
+          pdx[e] = fmaf(pd, kf[e], pdx[e]);
+          px[e] = fmaf(pr, kf[e], px[e]);
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < 3; ++c) {
+          cdx[c] = fmaf(pd, dif[g][c], cdx[c]);
+          cx[c] = fmaf(pr, dif[g][c], cx[c]);
+        }
+        r2dx = fmaf(pd, r2[g], r2dx);
+        r2x = fmaf(pr, r2[g], r2x);
+        psum += pr;
+      }
+    }
+  }
+  if (row_ok && sub == 0) p.delta[(int64_t)bh * p.T + i] = delta;
+
+  if constexpr (!COORD) {
+    if (row_ok) {
+      float dq[EPL];
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) dq[e] = p.scale * (pdx[e] - delta * px[e]);
+      const int gb = p.grad_bf16 ? 2 : 4;
+      char* dqrow = static_cast<char*>(p.dq) + (b * p.sdq_b + h * p.sdq_h + i * p.sdq_t) * gb +
+                    sub * EPL * gb;
+      store_vals<EPL>(dqrow, dq, p.grad_bf16 != 0);
+    }
+  } else {
+    if (row_ok && sub == 0) {
+      float* o = p.dcq + ((int64_t)bh * p.T + i) * 3;
+#pragma unroll
+      for (int c = 0; c < 3; ++c) o[c] = -2.f * gam * (cdx[c] - delta * cx[c]);
+    }
+    // dgamma_i = -sum_j dS_ij r2_ij,  dbeta_i = sum_j dS_ij = Delta_i (1 - sum_j P_ij)
+    const float gpart = -(r2dx - delta * r2x);
+    const float bpart = delta * (1.f - psum);
+    // per-block partial sums, one value per row (lane sub == 0), reduced in
+    // a fixed order through LDS
+    __shared__ float red[2][kThreads];
+    const bool counts = row_ok && sub == 0;
+    red[0][threadIdx.x] = counts ? gpart : 0.f;
+    red[1][threadIdx.x] = counts ? bpart : 0.f;
+    __syncthreads();
+    for (int w = kThreads / 2; w > 0; w >>= 1) {
+      if (threadIdx.x < w) {
+        red[0][threadIdx.x] += red[0][threadIdx.x + w];
+        red[1][threadIdx.x] += red[1][threadIdx.x + w];
+      }
+      __syncthreads();
+    }
+    if (threadIdx.x == 0) {
+      float* pp = p.partials + ((int64_t)bh * nblk + rb) * 2;
+      pp[0] = red[0][0];
+      pp[1] = red[1][0];
+    }
+  }
+}
+
+// ------------------------------------------------------------------ pass 2
+template <int DT, int D, bool COORD, int G>
+__global__ __launch_bounds__(kThreads) void gather_bwd_kv_kernel(Params p) {
+  using F = Frag<DT>;
+  using Gm = Geo<DT, D>;
+  constexpr int EPL = Gm::EPL, LG = Gm::LG, RPW = Gm::RPW, RPB = Gm::RPB;
+  constexpr int EB = F::BYTES;
+
+  const int nblk = (p.T + RPB - 1) / RPB;
+  const int logical = xcd_logical_block(p.B * p.H * nblk);
+  if (logical < 0) return;
+  const int bh = logical / nblk, rb = logical - bh * nblk;
+  const int b = bh / p.H, h = bh - b * p.H;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane % LG;
+  int j = rb * RPB + wave * RPW + lane / LG;
+  const bool row_ok = j < p.T;
+  if (!row_ok) j = p.T - 1;
+
+  const char* qb = static_cast<const char*>(p.q) + (b * p.sq_b + h * p.sq_h) * EB + sub * 16;
+  const char* dob = static_cast<const char*>(p.dout) + (b * p.sdo_b + h * p.sdo_h) * EB + sub * 16;
+  const int64_t sqt = p.sq_t * EB, sdot = p.sdo_t * EB;
+  const float* lseb = p.lse + (int64_t)bh * p.T;
+  const float* delb = p.delta + (int64_t)bh * p.T;
+  const float bsub = COORD ? p.beta[h] : 0.f;  // lse includes beta in coordinate mode
+
+  float kf[EPL], vf[EPL];
+  {
+    const char* vrow = static_cast<const char*>(p.v) + (b * p.sv_b + h * p.sv_h + j * p.sv_t) * EB +
+                       sub * 16;
+    F::unpack(ld16(vrow), vf);
+  }
+  float ckj[3] = {0.f, 0.f, 0.f};
+  float gl2 = 0.f, gam = 0.f;
+  const float* cqb = nullptr;
+  if constexpr (!COORD) {
+    const char* krow = static_cast<const char*>(p.k) + (b * p.sk_b + h * p.sk_h + j * p.sk_t) * EB +
+                       sub * 16;
+    F::unpack(ld16(krow), kf);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) kf[e] *= p.scale_log2;
+  } else {
+    const float* ckr = p.ck + ((int64_t)bh * p.T + j) * 3;
+    ckj[0] = ckr[0]; ckj[1] = ckr[1]; ckj[2] = ckr[2];
+    gam = p.gamma[h];
+    gl2 = gam * kLog2e;
+    cqb = p.cq + (int64_t)bh * p.T * 3;
+  }
+
+  float dk[EPL], dv[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) dk[e] = dv[e] = 0.f;
+  float dc[3] = {0.f, 0.f, 0.f};
+
+  const int nd = p.W + p.n_dil;
+  for (int t0 = 0; t0 < nd; t0 += G) {
+    int i[G];
+    uint4 qraw[G], doraw[G];
+    float s[G], dp[G], lse2[G], del[G], dif[G][3];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int t = t0 + g;
+      i[g] = (t < nd) ? j + distance_of(p, t) : p.T;
+      const int ii = i[g] < p.T ? i[g] : p.T - 1;  // clamped address, masked below
+      if constexpr (!COORD) qraw[g] = ld16(qb + ii * sqt);
+      doraw[g] = ld16(dob + ii * sdot);
+      lse2[g] = (lseb[ii] - bsub) * kLog2e;
+      del[g] = delb[ii];
+      if constexpr (COORD) {
+        const float* c = cqb + (int64_t)ii * 3;
+        dif[g][0] = c[0] - ckj[0];
+        dif[g][1] = c[1] - ckj[1];
+        dif[g][2] = c[2] - ckj[2];
+        s[g] = -gl2 * (dif[g][0] * dif[g][0] + dif[g][1] * dif[g][1] + dif[g][2] * dif[g][2]);
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float dof[EPL];
+      F::unpack(doraw[g], dof);
+      float part = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) part = fmaf(dof[e], vf[e], part);
+      dp[g] = part;
+      if constexpr (!COORD) {
+        float qf[EPL];
+        F::unpack(qraw[g], qf);
+        float ps = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) ps = fmaf(qf[e], kf[e], ps);
+        s[g] = ps;
+      }
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      dp[g] = group_sum<LG>(dp[g]);
+      if constexpr (!COORD) s[g] = group_sum<LG>(s[g]);
+    }
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const float pr = i[g] < p.T ? fast_exp2(s[g] - lse2[g]) : 0.f;
+      const float ds = pr * (dp[g] - del[g]);
+      float dof[EPL];
+      F::unpack(doraw[g], dof);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) dv[e] = fmaf(pr, dof[e], dv[e]);
+      if constexpr (!COORD) {
+        float qf[EPL];
+        F::unpack(qraw[g], qf);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) dk[e] = fmaf(ds, qf[e], dk[e]);
+      } else {
+        dc[0] = fmaf(ds, dif[g][0], dc[0]);
+        dc[1] = fmaf(ds, dif[g][1], dc[1]);
+        dc[2] = fmaf(ds, dif[g][2], dc[2]);
+      }
+    }
+  }
+
+  if (!row_ok) return;
+  const int gb = p.grad_bf16 ? 2 : 4;
+  char* dvrow = static_cast<char*>(p.dv) + (b * p.sdv_b + h * p.sdv_h + j * p.sdv_t) * gb +
+                sub * EPL * gb;
+  store_vals<EPL>(dvrow, dv, p.grad_bf16 != 0);
+  if constexpr (!COORD) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) dk[e] *= p.scale;
+    char* dkrow = static_cast<char*>(p.dk) + (b * p.sdk_b + h * p.sdk_h + j * p.sdk_t) * gb +
+                  sub * EPL * gb;
+    store_vals<EPL>(dkrow, dk, p.grad_bf16 != 0);
+  } else {
+    if (sub == 0) {
+      float* o = p.dck + ((int64_t)bh * p.T + j) * 3;
+      o[0] = 2.f * gam * dc[0];
+      o[1] = 2.f * gam * dc[1];
+      o[2] = 2.f * gam * dc[2];
+    }
+  }
+}
+
+// ------------------------------------------------------------------ pass 3
+// dgamma_h, dbeta_h: sum of the per-block partials of every batch for head
+// h, in fp64, in a fixed order (strided per thread, then a fixed tree).
+__global__ __launch_bounds__(256) void coord_param_reduce_kernel(const float* partials, int B, int H,
+                                                                 int nblk, float* dgamma,
+                                                                 float* dbeta) {
+  const int h = blockIdx.x;
+  __shared__ double red[2][256];
+  double g = 0.0, bsum = 0.0;
+  const int per_head = B * nblk;
+  for (int t = threadIdx.x; t < per_head; t += 256) {
+    const int b = t / nblk, r = t - b * nblk;
+    const float* pp = partials + (((int64_t)b * H + h) * nblk + r) * 2;
+    g += (double)pp[0];
+    bsum += (double)pp[1];
+  }
+  red[0][threadIdx.x] = g;
+  red[1][threadIdx.x] = bsum;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w) {
+      red[0][threadIdx.x] += red[0][threadIdx.x + w];
+      red[1][threadIdx.x] += red[1][threadIdx.x + w];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    dgamma[h] = (float)red[0][0];
+    dbeta[h] = (float)red[1][0];
+  }
+}
+
+template <int DT, int D, bool COORD>
+hipError_t launch_one(const Params& p, hipStream_t s) {
+  constexpr int RPB = Geo<DT, D>::RPB;
+  const int nblk = (p.T + RPB - 1) / RPB;
+  const int grid = xcd_grid(p.B * p.H * nblk);
+  hipLaunchKernelGGL((gather_bwd_q_kernel<DT, D, COORD, 4>), dim3(grid), dim3(kThreads), 0, s, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((gather_bwd_kv_kernel<DT, D, COORD, 4>), dim3(grid), dim3(kThreads), 0, s, p);
+  e = hipGetLastError();
+  if (e != hipSuccess || !COORD) return e;
+  hipLaunchKernelGGL(coord_param_reduce_kernel, dim3(p.H), dim3(256), 0, s, p.partials, p.B, p.H,
+                     nblk, p.dgamma, p.dbeta);
+  return hipGetLastError();
+}
+
+template <int DT, bool COORD>
+hipError_t launch_d(const Params& p, hipStream_t s) {
+  switch (p.D) {
+    case 16: return launch_one<DT, 16, COORD>(p, s);
+    case 32: return launch_one<DT, 32, COORD>(p, s);
+    case 64: return launch_one<DT, 64, COORD>(p, s);
+    case 128: return launch_one<DT, 128, COORD>(p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_gather_bwd(const Params& p, int dtype, bool coord, hipStream_t s) {
+  if (dtype == DT_BF16) return coord ? launch_d<DT_BF16, true>(p, s) : launch_d<DT_BF16, false>(p, s);
+  return coord ? launch_d<DT_F32, true>(p, s) : launch_d<DT_F32, false>(p, s);
+}
+
+}  // namespace sa

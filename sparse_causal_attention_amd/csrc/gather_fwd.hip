@@ -1,0 +1,187 @@
+// Gather forward: every edge of the neighbour graph handled on the vector
+// ALUs, one lane group per query row.
+//
+// The graph is translation invariant (SpatialLM-Mini news page, "How tokens
+// choose whom to listen to": a fixed list of distances per token), so for a
+// fixed distance delta the keys of consecutive query rows are consecutive
+// rows of K and V.  A wavefront holds 64/LG consecutive query rows, each row
+// spread over LG lanes with 16 bytes (8 bf16 or 4 fp32 elements) per lane,
+// so the K or V rows one distance needs form one contiguous, fully coalesced
+// block of 64 x 16 bytes.  Scores are reduced across the lane group with DPP,
+// and the softmax over the row's neighbours runs online (running max, sum
+// and weighted value accumulator, rescaled once per group of G distances).
+// Work and traffic are proportional to the number of edges (page "Longer
+// Attention Span ...", abstract: work-optimal graph processing); no score
+// matrix and no gathered copy of K or V is ever formed.
+#include "device_util.h"
+#include "sa_internal.h"
+
+namespace sa {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+
+template <int DT, int D>
+struct Geo {
+  static constexpr int EPL = Frag<DT>::EPL;  // elements per lane
+  static constexpr int LG = D / EPL;         // lanes per row
+  static constexpr int RPW = 64 / LG;        // rows per wavefront
+  static constexpr int RPB = RPW * kWaves;   // rows per workgroup
+  static_assert(LG >= 1 && LG <= 32 && (LG & (LG - 1)) == 0, "row must span 1..32 lanes");
+};
+
+// Distance of slot t in the concatenated list [0, 1, ..., W-1, dil...].
+__device__ __forceinline__ int distance_of(const Params& p, int t) {
+  return t < p.W ? t : p.dil[t - p.W];
+}
+
+template <int DT, int D, bool COORD, int G>
+__global__ __launch_bounds__(kThreads) void gather_fwd_kernel(Params p) {
+  using F = Frag<DT>;
+  using Gm = Geo<DT, D>;
+  constexpr int EPL = Gm::EPL, LG = Gm::LG, RPW = Gm::RPW, RPB = Gm::RPB;
+  constexpr int EB = F::BYTES;
+
+  const int nblk = (p.T + RPB - 1) / RPB;
+  const int logical = xcd_logical_block(p.B * p.H * nblk);
+  if (logical < 0) return;
+  const int bh = logical / nblk, rb = logical - bh * nblk;
+  const int b = bh / p.H, h = bh - b * p.H;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane % LG;
+  int i = rb * RPB + wave * RPW + lane / LG;
+  const bool row_ok = i < p.T;
+  if (!row_ok) i = p.T - 1;  // compute a valid row, store nothing
+
+  const char* kb = static_cast<const char*>(p.k) + (b * p.sk_b + h * p.sk_h) * EB + sub * 16;
+  const char* vb = static_cast<const char*>(p.v) + (b * p.sv_b + h * p.sv_h) * EB + sub * 16;
+  const int64_t skt = p.sk_t * EB, svt = p.sv_t * EB;
+
+  float qf[EPL];
+  float cqi[3] = {0.f, 0.f, 0.f};
+  float gl2 = 0.f;  // gamma * log2(e)
+  const float* ckb = nullptr;
+  if constexpr (!COORD) {
+    const char* qrow = static_cast<const char*>(p.q) + (b * p.sq_b + h * p.sq_h + i * p.sq_t) * EB +
+                       sub * 16;
+    F::unpack(ld16(qrow), qf);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qf[e] *= p.scale_log2;
+  } else {
+    const float* cqr = p.cq + ((int64_t)bh * p.T + i) * 3;
+    cqi[0] = cqr[0]; cqi[1] = cqr[1]; cqi[2] = cqr[2];
+    gl2 = p.gamma[h] * kLog2e;
+    ckb = p.ck + (int64_t)bh * p.T * 3;
+  }
+
+  float m = -INFINITY, l = 0.f;
+  float acc[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+
+  const int nd = p.W + p.n_dil;
+  for (int t0 = 0; t0 < nd; t0 += G) {
+    int j[G];
+    uint4 kraw[G], vraw[G];
+    float s[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int t = t0 + g;
+      j[g] = (t < nd) ? i - distance_of(p, t) : -1;
+      const int jj = j[g] < 0 ? 0 : j[g];  // clamped address, masked below
+      if constexpr (!COORD) kraw[g] = ld16(kb + jj * skt);
+      vraw[g] = ld16(vb + jj * svt);
+      if constexpr (COORD) {
+        const float* c = ckb + (int64_t)jj * 3;
+        const float d0 = cqi[0] - c[0], d1 = cqi[1] - c[1], d2 = cqi[2] - c[2];
+        s[g] = -gl2 * (d0 * d0 + d1 * d1 + d2 * d2);
+      }
+    }
+    if constexpr (!COORD) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float kf[EPL];
+        F::unpack(kraw[g], kf);
+        float part = 0.f;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) part = fmaf(qf[e], kf[e], part);
+        s[g] = part;
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) s[g] = group_sum<LG>(s[g]);
+    }
+    float mx = m;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      s[g] = j[g] >= 0 ? s[g] : -INFINITY;
+      mx = fmaxf(mx, s[g]);
+    }
+    const float mref = mx == -INFINITY ? 0.f : mx;
+    const float alpha = fast_exp2(m - mref);
+    float pg[G];
+    float psum = 0.f;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      pg[g] = fast_exp2(s[g] - mref);
+      psum += pg[g];
+    }
+    l = fmaf(l, alpha, psum);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[e] *= alpha;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float vf[EPL];
+      F::unpack(vraw[g], vf);
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(pg[g], vf[e], acc[e]);
+    }
+    m = mx;
+  }
+
+  if (!row_ok) return;
+  const float inv_l = 1.f / l;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) acc[e] *= inv_l;
+  char* orow = static_cast<char*>(p.o) + (b * p.so_b + h * p.so_h + i * p.so_t) * EB + sub * 16;
+  st16(orow, F::pack(acc));
+  if (sub == 0) {
+    float lse = (m + fast_log2(l)) * kLn2;
+    if constexpr (COORD) lse += p.beta[h];
+    p.lse[(int64_t)bh * p.T + i] = lse;
+  }
+}
+
+template <int DT, int D, bool COORD>
+hipError_t launch_one(const Params& p, hipStream_t s) {
+  constexpr int RPB = Geo<DT, D>::RPB;
+  const int nblk = (p.T + RPB - 1) / RPB;
+  const int grid = xcd_grid(p.B * p.H * nblk);
+  hipLaunchKernelGGL((gather_fwd_kernel<DT, D, COORD, 4>), dim3(grid), dim3(kThreads), 0, s, p);
+  return hipGetLastError();
+}
+
+template <int DT, bool COORD>
+hipError_t launch_d(const Params& p, hipStream_t s) {
+  switch (p.D) {
+    case 16: return launch_one<DT, 16, COORD>(p, s);
+    case 32: return launch_one<DT, 32, COORD>(p, s);
+    case 64: return launch_one<DT, 64, COORD>(p, s);
+    case 128: return launch_one<DT, 128, COORD>(p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+int gather_rows_per_block(int dtype, int D) {
+  const int epl = dtype == DT_BF16 ? 8 : 4;
+  return (64 / (D / epl)) * kWaves;
+}
+
+hipError_t launch_gather_fwd(const Params& p, int dtype, bool coord, hipStream_t s) {
+  if (dtype == DT_BF16) return coord ? launch_d<DT_BF16, true>(p, s) : launch_d<DT_BF16, false>(p, s);
+  return coord ? launch_d<DT_F32, true>(p, s) : launch_d<DT_F32, false>(p, s);
+}
+
+}  // namespace sa

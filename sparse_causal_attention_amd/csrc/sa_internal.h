@@ -1,0 +1,64 @@
+// Internal declarations shared by the C ABI layer and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/sa.h"
+
+// Normalised translation-invariant graph (see graph.cpp).
+struct sa_graph {
+  int64_t T;                    // sequence length
+  int64_t W;                    // effective window, min(W, T)
+  int32_t n_dil;                // kept long-range distances
+  int64_t dil[SA_MAX_DILATED];  // ascending, W <= d < T
+  int64_t n_edges;              // per (batch, head)
+};
+
+namespace sa {
+
+enum { DT_F32 = 0, DT_BF16 = 1 };  // same values as sa_dtype
+
+// Everything a kernel needs, passed by value as one kernel argument.  Row
+// addresses are base + b*s_b + h*s_h + t*s_t elements (D contiguous).
+struct Params {
+  int32_t B, H, T, D;
+  int32_t W;      // effective window
+  int32_t n_dil;  // long-range distances
+  int32_t dil[SA_MAX_DILATED];
+  float scale;       // dot-mode scale
+  float scale_log2;  // scale * log2(e)
+  int32_t grad_bf16; // dq/dk/dv stored as bf16 (else fp32)
+  int32_t rows_per_block_q;  // query-side block height (partials layout)
+
+  const void* q;  int64_t sq_b, sq_h, sq_t;
+  const void* k;  int64_t sk_b, sk_h, sk_t;
+  const void* v;  int64_t sv_b, sv_h, sv_t;
+  void* o;        int64_t so_b, so_h, so_t;
+  const void* dout; int64_t sdo_b, sdo_h, sdo_t;
+  void* dq;       int64_t sdq_b, sdq_h, sdq_t;
+  void* dk;       int64_t sdk_b, sdk_h, sdk_t;
+  void* dv;       int64_t sdv_b, sdv_h, sdv_t;
+
+  const float* cq; const float* ck;  // [B, H, T, 3]
+  const float* gamma; const float* beta;  // [H]
+  float* dcq; float* dck;
+  float* dgamma; float* dbeta;
+
+  float* lse;       // [B, H, T]
+  float* delta;     // workspace [B, H, T]
+  float* partials;  // workspace [B, H, nblk_q, 2]
+};
+
+// Launchers (defined in the .hip files).  Each validates nothing: the C ABI
+// layer has already checked every argument.  Return the launch status.
+hipError_t launch_gather_fwd(const Params& p, int dtype, bool coord, hipStream_t s);
+hipError_t launch_gather_bwd(const Params& p, int dtype, bool coord, hipStream_t s);
+int gather_rows_per_block(int dtype, int D);
+
+hipError_t launch_band_fwd(const Params& p, hipStream_t s);
+hipError_t launch_band_bwd(const Params& p, hipStream_t s);
+int band_rows_per_block();
+bool band_supported(int dtype, int D, bool coord, int64_t W);
+
+}  // namespace sa

@@ -1,0 +1,136 @@
+"""The C ABI library on a host without a GPU: it loads, exports every entry
+point include/sa.h declares, and rejects every invalid request with its
+status before any HIP call (the pointers below are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_causal_attention_amd import _abi, sa_build_graph
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "sa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sa_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(_abi.EXPORTED)
+    L = _abi.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    L = _abi.lib()
+    for s in range(6):
+        assert L.sa_status_str(s)
+    assert L.sa_status_str(99) == b"unknown status"
+
+
+FAKE = 0x10000  # 16-byte aligned stand-in; never dereferenced on these paths
+
+
+def desc(B=1, H=2, T=64, D=32, dtype=0, score=0, algo=0, grad=0):
+    d = _abi.SaAttnDesc()
+    d.B, d.H, d.T, d.D = B, H, T, D
+    d.dtype, d.grad_dtype, d.score, d.algo = dtype, grad, score, algo
+    es = 2 if dtype == 1 else 4
+    for name in ("q", "k", "v", "o", "do"):
+        getattr(d, "stride_" + name)[:] = (H * T * D, T * D, D)
+    for name in ("dq", "dk", "dv"):
+        getattr(d, "stride_" + name)[:] = (H * T * D, T * D, D)
+    _ = es
+    return d
+
+
+def fwd(g, d, q=FAKE, k=FAKE, v=FAKE, cq=None, ck=None, gm=None, bt=None, o=FAKE, lse=FAKE):
+    return _abi.lib().sa_fwd(g.handle if g is not None else None, ctypes.byref(d) if d is not None else None,
+                             q, k, v, cq, ck, gm, bt, o, lse, None)
+
+
+def bwd(g, d, ws=FAKE, ws_bytes=1 << 30, **kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, cq=None, ck=None, gm=None, bt=None, o=FAKE, lse=FAKE, do=FAKE,
+                dq=FAKE, dk=FAKE, dv=FAKE, dcq=None, dck=None, dg=None, db=None)
+    args.update(kw)
+    return _abi.lib().sa_bwd(g.handle, ctypes.byref(d), *args.values(), ws, ws_bytes, None)
+
+
+@pytest.fixture
+def g64():
+    return sa_build_graph(64, 4, [4, 8, 16, 32])
+
+
+def test_fwd_validation(g64):
+    E = _abi
+    assert fwd(None, desc()) == E.SA_ERR_INVALID_ARG
+    assert fwd(g64, None) == E.SA_ERR_INVALID_ARG
+    assert fwd(g64, desc(T=65)) == E.SA_ERR_SHAPE_MISMATCH
+    assert fwd(g64, desc(D=48)) == E.SA_ERR_UNSUPPORTED
+    assert fwd(g64, desc(D=256)) == E.SA_ERR_UNSUPPORTED
+    assert fwd(g64, desc(B=0)) == E.SA_ERR_INVALID_ARG
+    assert fwd(g64, desc(H=-1)) == E.SA_ERR_INVALID_ARG
+    assert fwd(g64, desc(dtype=7)) == E.SA_ERR_INVALID_ARG
+    assert fwd(g64, desc(score=3)) == E.SA_ERR_INVALID_ARG
+    assert fwd(g64, desc(algo=9)) == E.SA_ERR_INVALID_ARG
+    assert fwd(g64, desc(), q=None) == E.SA_ERR_INVALID_ARG
+    assert fwd(g64, desc(), v=None) == E.SA_ERR_INVALID_ARG
+    assert fwd(g64, desc(), o=None) == E.SA_ERR_INVALID_ARG
+    assert fwd(g64, desc(), lse=None) == E.SA_ERR_INVALID_ARG
+    assert fwd(g64, desc(), q=FAKE + 4) == E.SA_ERR_INVALID_ARG  # misaligned row start
+    d = desc()
+    d.stride_k[2] = 33  # 132-byte rows: not 16-byte aligned
+    assert fwd(g64, d) == E.SA_ERR_INVALID_ARG
+    d = desc()
+    d.stride_v[0] = -64
+    assert fwd(g64, d) == E.SA_ERR_INVALID_ARG
+    # coordinate mode needs c_q, c_k, gamma, beta
+    assert fwd(g64, desc(score=1), q=None, k=None) == E.SA_ERR_INVALID_ARG
+    assert fwd(g64, desc(score=1), q=None, k=None, cq=FAKE, ck=FAKE, gm=FAKE) == E.SA_ERR_INVALID_ARG
+    # the band kernels do not apply to fp32 inputs
+    assert fwd(g64, desc(algo=2)) == E.SA_ERR_UNSUPPORTED
+
+
+def test_bwd_validation(g64):
+    E = _abi
+    d = desc()
+    assert bwd(g64, d, ws=None) == E.SA_ERR_WORKSPACE
+    assert bwd(g64, d, ws=FAKE + 16) == E.SA_ERR_WORKSPACE  # not 256-byte aligned
+    need = ctypes.c_size_t()
+    assert _abi.lib().sa_bwd_workspace_size(g64.handle, ctypes.byref(d), ctypes.byref(need)) == 0
+    assert need.value >= 1 * 2 * 64 * 4
+    assert bwd(g64, d, ws_bytes=need.value - 1) == E.SA_ERR_WORKSPACE
+    assert bwd(g64, d, do=None) == E.SA_ERR_INVALID_ARG
+    assert bwd(g64, d, dq=None) == E.SA_ERR_INVALID_ARG
+    assert bwd(g64, d, dv=None) == E.SA_ERR_INVALID_ARG
+    assert bwd(g64, d, lse=None) == E.SA_ERR_INVALID_ARG
+    assert bwd(g64, d, dk=FAKE + 8) == E.SA_ERR_INVALID_ARG
+    assert bwd(g64, desc(T=32)) == E.SA_ERR_SHAPE_MISMATCH
+    dc = desc(score=1)
+    assert bwd(g64, dc, q=None, k=None, cq=FAKE, ck=FAKE, gm=FAKE, bt=FAKE, dq=None, dk=None,
+               dcq=FAKE, dck=FAKE, dg=FAKE) == E.SA_ERR_INVALID_ARG  # dbeta missing
+    assert _abi.lib().sa_bwd_workspace_size(g64.handle, ctypes.byref(desc(T=8)),
+                                            ctypes.byref(need)) == E.SA_ERR_SHAPE_MISMATCH
+
+
+def plan(g, d, which):
+    buf = ctypes.create_string_buffer(128)
+    st = _abi.lib().sa_describe_plan(g.handle, ctypes.byref(d), which, buf, 128)
+    return st, buf.value.decode()
+
+
+def test_plan_selection():
+    g = sa_build_graph(16384, 256, ())
+    st, name = plan(g, desc(B=1, H=8, T=16384, D=64, dtype=1), 0)
+    assert st == 0 and name
+    st, name = plan(g, desc(B=1, H=8, T=16384, D=64, dtype=0), 0)
+    assert st == 0 and name.startswith("gather")
+    st, name = plan(g, desc(B=1, H=8, T=16384, D=64, dtype=1, algo=1), 1)
+    assert st == 0 and name.startswith("gather_bwd")
+    st, name = plan(g, desc(B=1, H=8, T=16384, D=64, dtype=1, score=1), 0)
+    assert st == 0 and name == "gather_fwd_coord"

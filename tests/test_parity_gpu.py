@@ -1,0 +1,246 @@
+"""HIP path against the fp64 oracle, element by element, through the C ABI.
+
+Tolerances (max-abs over every output element): 1e-4 for fp32 inputs and
+2e-2 for bf16 inputs with fp32 accumulation.  The per-head coordinate-score
+parameter gradients (sums over up to 8M edges) use
+|err| <= max(tol, 1e-6 * sum_edges |dS| (1 + ||c_q - c_k||^2)).
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from sparse_causal_attention_amd import sa_build_graph, sa_bwd, sa_describe_plan, sa_fwd
+from sparse_causal_attention_amd.inputs import (WORKLOADS, Workload, host_view, make_device_inputs_chunked,
+                                                make_inputs, sample_rows)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def _say(msg):
+    print("\n[parity] " + msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    from sparse_causal_attention_amd import _abi
+    _abi.lib()  # loud failure when libsa.so is missing
+
+
+def tol_of(w_dtype):
+    return 1e-4 if w_dtype == torch.float32 else 2e-2
+
+
+def maxabs(t, ref):
+    return float(np.max(np.abs(t.detach().double().cpu().numpy() - ref))) if ref.size else 0.0
+
+
+def run_and_compare(w: Workload, algo="auto", backward=True, grad_dtype=None, **shape):
+    x = make_inputs(w, device="cpu", backward=backward, **shape)
+    B, H, T, D = x["v"].shape
+    g = sa_build_graph(T, w.window, w.offsets)
+    xd = {k: v.to(DEV) for k, v in x.items()}
+    _say("%s algo=%s shape=%s plan=%s" % (w.name, algo, (B, H, T, D),
+                                          sa_describe_plan(g, xd["v"], coord=w.coord, algo=algo)))
+    if w.coord:
+        o, lse = sa_fwd(g, v=xd["v"], cq=xd["cq"], ck=xd["ck"], gamma=xd["gamma"], beta=xd["beta"],
+                        algo=algo)
+    else:
+        o, lse = sa_fwd(g, xd["q"], xd["k"], xd["v"], algo=algo)
+    torch.cuda.synchronize()
+    hv = {k: host_view(v) for k, v in x.items()}
+    tol = tol_of(w.dtype)
+    if w.coord:
+        O, L = oracle.fwd_bh(w.window, w.offsets, hv["v"], cq=hv["cq"], ck=hv["ck"], gamma=hv["gamma"],
+                             beta=hv["beta"])
+    else:
+        O, L = oracle.fwd_bh(w.window, w.offsets, hv["v"], q=hv["q"], k=hv["k"])
+    errs = {"o": maxabs(o, O), "lse": maxabs(lse, L)}
+    if backward:
+        if w.coord:
+            gr = sa_bwd(g, v=xd["v"], o=o, lse=lse, dout=xd["do"], cq=xd["cq"], ck=xd["ck"],
+                        gamma=xd["gamma"], beta=xd["beta"], algo=algo, grad_dtype=grad_dtype)
+            ref = oracle.bwd_bh(w.window, w.offsets, hv["v"], hv["do"], cq=hv["cq"], ck=hv["ck"],
+                                gamma=hv["gamma"], beta=hv["beta"])
+            torch.cuda.synchronize()
+            for key in ("dv", "dcq", "dck"):
+                errs[key] = maxabs(gr[key], ref[key])
+            for key in ("dgamma", "dbeta"):
+                err = np.abs(gr[key].double().cpu().numpy() - ref[key])
+                bound = np.maximum(tol, 1e-6 * ref["l1"])
+                errs[key] = float(np.max(err / bound)) * tol  # scaled so that <= tol passes
+        else:
+            gr = sa_bwd(g, xd["q"], xd["k"], xd["v"], o, lse, xd["do"], algo=algo, grad_dtype=grad_dtype)
+            ref = oracle.bwd_bh(w.window, w.offsets, hv["v"], hv["do"], q=hv["q"], k=hv["k"])
+            torch.cuda.synchronize()
+            for key in ("dq", "dk", "dv"):
+                errs[key] = maxabs(gr[key], ref[key])
+    _say("%s errors %s (tol %g)" % (w.name, {k: "%.2e" % v for k, v in errs.items()}, tol))
+    gtol = tol if grad_dtype in (None, torch.float32) else max(tol, 5e-2)
+    for key, e in errs.items():
+        assert e <= (tol if key in ("o", "lse") else gtol), (w.name, key, e)
+    return o, lse
+
+
+# ------------------------------------------------------------------ the workloads
+@pytest.mark.parametrize("name", ["tiny", "tiny_dense"])
+def test_tiny_fp32(name):
+    run_and_compare(WORKLOADS[name])
+
+
+def test_tiny_dense_equals_causal():
+    w = WORKLOADS["tiny_dense"]
+    x = make_inputs(w, backward=False)
+    g = sa_build_graph(w.T, w.T, ())
+    o, lse = sa_fwd(g, *(x[k].to(DEV) for k in ("q", "k", "v")))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        *(x[k].double() for k in ("q", "k", "v")), is_causal=True)
+    assert float((o.cpu().double() - ref).abs().max()) <= 1e-4
+
+
+@pytest.mark.parametrize("algo", ["auto", "gather"])
+def test_band_full_size(algo):
+    run_and_compare(WORKLOADS["band"], algo=algo)
+
+
+@pytest.mark.parametrize("algo", ["auto", "gather"])
+def test_band_dense_full_size(algo):
+    run_and_compare(WORKLOADS["band_dense"], algo=algo)
+
+
+def test_dilated_full_size():
+    run_and_compare(WORKLOADS["dilated"])
+
+
+def test_coord_full_size():
+    run_and_compare(WORKLOADS["coord"])
+
+
+def test_coord_band_graph():
+    run_and_compare(WORKLOADS["coord_band"])
+
+
+def test_dilated_bf16_gradients():
+    run_and_compare(WORKLOADS["dilated"], grad_dtype=torch.bfloat16, B=1, H=4)
+
+
+def test_ultra_long_sampled_rows():
+    w = WORKLOADS["ultra"]
+    _say("ultra: generating %d x %d bf16 inputs on device" % (w.T, w.D))
+    x = make_device_inputs_chunked(w, DEV)
+    g = sa_build_graph(w.T, w.window, w.offsets)
+    _say("ultra: plan %s" % sa_describe_plan(g, x["v"]))
+    o, lse = sa_fwd(g, x["q"], x["k"], x["v"])
+    torch.cuda.synchronize()
+    rows = sample_rows(w, 4096, boundary=[0, 1, 63, 64, 65, 2 ** 25 - 1, 2 ** 25, 2 ** 25 + 1, w.T - 1])
+    # host copies hold only the rows the sampled queries touch (lazy zero pages elsewhere)
+    need = set()
+    for i in rows.tolist():
+        need.update(oracle.row(w.T, w.window, w.offsets, i).tolist())
+    need = torch.tensor(sorted(need | set(rows.tolist())), dtype=torch.int64)
+    host = {}
+    for name in ("q", "k", "v"):
+        arr = np.zeros((w.T, w.D), dtype=np.uint16)
+        arr[need.numpy()] = host_view(x[name][0, 0].index_select(0, need.to(DEV)))
+        host[name] = arr
+    O, L = oracle.fwd(w.T, w.window, w.offsets, host["v"], q=host["q"], k=host["k"], rows=rows.numpy())
+    og = o[0, 0].index_select(0, rows.to(DEV))
+    lg = lse[0, 0].index_select(0, rows.to(DEV))
+    eo, el = maxabs(og, O), maxabs(lg, L)
+    _say("ultra: %d rows, errors o %.2e lse %.2e" % (len(rows), eo, el))
+    assert eo <= 2e-2 and el <= 2e-2
+    del x, o, lse
+    torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------ shapes and edge cases
+RAGGED = [
+    (1, 1, 1, 16, torch.float32, 1, ()),
+    (2, 3, 17, 32, torch.float32, 4, (4, 8, 16)),
+    (1, 2, 1000, 64, torch.bfloat16, 4, tuple(2 ** k for k in range(10))),
+    (1, 1, 4097, 64, torch.bfloat16, 256, (512, 1024, 2048)),
+    (2, 2, 333, 128, torch.float32, 9, (16, 32, 64, 128, 256)),
+    (1, 3, 257, 128, torch.bfloat16, 40, (64, 128)),
+    (3, 1, 95, 16, torch.bfloat16, 200, ()),
+    (1, 1, 4097, 64, torch.bfloat16, 5000, ()),
+]
+
+
+@pytest.mark.parametrize("B,H,T,D,dt,W,offs", RAGGED)
+def test_ragged_shapes(B, H, T, D, dt, W, offs):
+    w = Workload("ragged", 9, B, H, T, D, dt, W, offs)
+    run_and_compare(w)
+
+
+@pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
+def test_coord_small(dt):
+    w = Workload("coord_small", 8, 2, 3, 300, 32, dt, 3, (4, 8, 16, 32, 64, 128), coord=True)
+    run_and_compare(w)
+
+
+def test_strided_inputs():
+    """q, k, v, dout as [B, T, H, D] storage viewed as [B, H, T, D]."""
+    B, H, T, D, W, offs = 2, 4, 777, 64, 6, (8, 16, 32, 64, 128, 256)
+    gen = torch.Generator().manual_seed(77)
+    base = {n: torch.randn((B, T, H, D), generator=gen).to(torch.bfloat16) for n in ("q", "k", "v", "do")}
+    xd = {n: t.to(DEV).permute(0, 2, 1, 3) for n, t in base.items()}
+    g = sa_build_graph(T, W, offs)
+    o, lse = sa_fwd(g, xd["q"], xd["k"], xd["v"])
+    gr = sa_bwd(g, xd["q"], xd["k"], xd["v"], o, lse, xd["do"])
+    hv = {n: host_view(t.permute(0, 2, 1, 3).contiguous()) for n, t in base.items()}
+    O, L = oracle.fwd_bh(W, offs, hv["v"], q=hv["q"], k=hv["k"])
+    ref = oracle.bwd_bh(W, offs, hv["v"], hv["do"], q=hv["q"], k=hv["k"])
+    assert maxabs(o, O) <= 2e-2 and maxabs(lse, L) <= 2e-2
+    for key in ("dq", "dk", "dv"):
+        assert maxabs(gr[key], ref[key]) <= 2e-2, key
+
+
+def test_row_zero_identity_and_determinism():
+    w = WORKLOADS["dilated"]
+    x = {k: v.to(DEV) for k, v in make_inputs(w, B=1, H=2, T=4096).items()}
+    g = sa_build_graph(4096, w.window, w.offsets)
+    o1, l1 = sa_fwd(g, x["q"], x["k"], x["v"])
+    o2, l2 = sa_fwd(g, x["q"], x["k"], x["v"])
+    # row 0 has one key: o_0 = v_0 exactly, lse_0 = s_00
+    assert torch.equal(o1[:, :, 0], x["v"][:, :, 0])
+    s00 = (x["q"][:, :, 0].float() * x["k"][:, :, 0].float()).sum(-1) / 8.0
+    assert float((l1[:, :, 0] - s00).abs().max()) < 1e-5
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    g1 = sa_bwd(g, x["q"], x["k"], x["v"], o1, l1, x["do"])
+    g2 = sa_bwd(g, x["q"], x["k"], x["v"], o1, l1, x["do"])
+    for key in ("dq", "dk", "dv"):
+        assert torch.equal(g1[key], g2[key]), key
+
+
+def test_outputs_stay_in_bounds():
+    """Canaries around every output: nothing outside the tensors is written."""
+    B, H, T, D, W, offs = 1, 2, 1001, 64, 4, (4, 8, 16, 32, 64)
+    x = {k: v.to(DEV) for k, v in make_inputs(WORKLOADS["dilated"], B=B, H=H, T=T).items()}
+    g = sa_build_graph(T, W, offs)
+    n = B * H * T * D
+    pad = 4096
+    canary = -1536.0  # exact in bf16 and fp32
+
+    def guarded(numel, dtype):
+        buf = torch.full((numel + 2 * pad,), canary, dtype=dtype, device=DEV)
+        return buf, buf[pad:pad + numel]
+
+    ob, o = guarded(n, torch.bfloat16)
+    lb, lse = guarded(B * H * T, torch.float32)
+    sa_fwd(g, x["q"], x["k"], x["v"], o=o.view(B, H, T, D), lse=lse.view(B, H, T))
+    grads = {}
+    bufs = {}
+    for key in ("dq", "dk", "dv"):
+        bufs[key], grads[key] = guarded(n, torch.float32)
+    sa_bwd(g, x["q"], x["k"], x["v"], o.view(B, H, T, D), lse.view(B, H, T), x["do"],
+           dq=grads["dq"].view(B, H, T, D), dk=grads["dk"].view(B, H, T, D), dv=grads["dv"].view(B, H, T, D))
+    torch.cuda.synchronize()
+    for buf in [ob, lb] + list(bufs.values()):
+        assert bool((buf[:pad].float() == canary).all()) and bool((buf[-pad:].float() == canary).all())
