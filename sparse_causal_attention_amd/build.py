@@ -30,7 +30,10 @@ COMMON = [
 # Device code: gfx950 only; no packed-fp32 instructions (hipcc warns that the
 # host pass does not know the feature; harmless).
 DEVICE = ["-x", "hip", "--offload-arch=" + ARCH, "-Xclang", "-target-feature",
-          "-Xclang", "-packed-fp32-ops", "-munsafe-fp-atomics"]
+          "-Xclang", "-packed-fp32-ops", "-munsafe-fp-atomics",
+          # MFMA accumulators in ordinary VGPRs: the softmax works on them
+          # directly instead of copying through AGPRs
+          "-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 
 
 def sources():

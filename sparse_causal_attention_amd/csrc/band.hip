@@ -50,9 +50,56 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
 
 __device__ __forceinline__ float xhalf(float x) { return __shfl_xor(x, 32, 64); }
 
+// Global -> register staging of one 64-key tile (K row-major, V as key
+// pairs for the transposed LDS copy), then register -> LDS.
+struct TileRegs {
+  uint4 k0, k1, v0, v1;
+};
+
+__device__ __forceinline__ void tile_load(TileRegs& t, const char* kbase, const char* vbase, int64_t skt,
+                                          int64_t svt, int kt0, int T) {
+  const int tid = threadIdx.x;
+  {  // K: 4 threads per row, 2 x 16 B each
+    const int r = tid >> 2, c = (tid & 3) * 2;
+    const int key = kt0 + r < T ? kt0 + r : T - 1;
+    t.k0 = ld16(kbase + key * skt + c * 16);
+    t.k1 = ld16(kbase + key * skt + (c + 1) * 16);
+  }
+  {  // V: key pair (2 kp, 2 kp + 1), 16-byte chunk c
+    const int kp = tid >> 3, c = tid & 7;
+    const int k0 = kt0 + 2 * kp < T ? kt0 + 2 * kp : T - 1;
+    const int k1 = kt0 + 2 * kp + 1 < T ? kt0 + 2 * kp + 1 : T - 1;
+    t.v0 = ld16(vbase + k0 * svt + c * 16);
+    t.v1 = ld16(vbase + k1 * svt + c * 16);
+  }
+}
+
+__device__ __forceinline__ void tile_store(const TileRegs& t, __bf16* Ks, __bf16* Vt) {
+  const int tid = threadIdx.x;
+  {
+    const int r = tid >> 2, c = (tid & 3) * 2;
+    *reinterpret_cast<uint4*>(&Ks[r * kKRow + c * 8]) = t.k0;
+    *reinterpret_cast<uint4*>(&Ks[r * kKRow + (c + 1) * 8]) = t.k1;
+  }
+  {
+    const int kp = tid >> 3, c = tid & 7;
+    const uint32_t a[4] = {t.v0.x, t.v0.y, t.v0.z, t.v0.w};
+    const uint32_t bb[4] = {t.v1.x, t.v1.y, t.v1.z, t.v1.w};
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      // elements 2w (low halves) and 2w + 1 (high halves) of the two keys
+      const uint32_t lo = (a[w] & 0xffffu) | (bb[w] << 16);
+      const uint32_t hi = (a[w] >> 16) | (bb[w] & 0xffff0000u);
+      *reinterpret_cast<uint32_t*>(&Vt[(c * 8 + 2 * w) * kVRow + 2 * kp]) = lo;
+      *reinterpret_cast<uint32_t*>(&Vt[(c * 8 + 2 * w + 1) * kVRow + 2 * kp]) = hi;
+    }
+  }
+}
+
+template <bool HAS_DIL>
 __global__ __launch_bounds__(kThreads) void band_fwd_kernel(Params p) {
-  __shared__ __align__(16) __bf16 Ks[kBK * kKRow];
-  __shared__ __align__(16) __bf16 Vt[kD * kVRow];
+  __shared__ __align__(16) __bf16 Ks[2][kBK * kKRow];
+  __shared__ __align__(16) __bf16 Vt[2][kD * kVRow];
 
   const int nblk = (p.T + kBQ - 1) / kBQ;
   const int logical = xcd_logical_block(p.B * p.H * nblk);
@@ -72,112 +119,119 @@ __global__ __launch_bounds__(kThreads) void band_fwd_kernel(Params p) {
   const char* vbase = static_cast<const char*>(p.v) + (b * p.sv_b + h * p.sv_h) * 2;
   const int64_t sqt = p.sq_t * 2, skt = p.sk_t * 2, svt = p.sv_t * 2;
 
+  const int W = p.W;
+  const int lo = q0 - W + 1 > 0 ? q0 - W + 1 : 0;
+  const int hi = q0 + kBQ - 1 < p.T - 1 ? q0 + kBQ - 1 : p.T - 1;
+  const int kfirst = (lo / kBK) * kBK;
+  const int ntiles = (hi - kfirst) / kBK + 1;
+
+  TileRegs pre;
+  tile_load(pre, kbase, vbase, skt, svt, kfirst, p.T);
+
   // Q^T as B operand: lane holds q[m][16*kk + 8*half + e]
   bf16x8 qf[4];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) qf[kk] = as_bf16x8(ld16(qbase + mc * sqt + (16 * kk + 8 * half) * 2));
 
+  tile_store(pre, Ks[0], Vt[0]);
+  if (ntiles > 1) tile_load(pre, kbase, vbase, skt, svt, kfirst + kBK, p.T);
+  __syncthreads();
+
+  // running max (raw score units), row sum (this lane's keys), O^T accumulator
   float mrun = -INFINITY, lrun = 0.f;
   f32x16 oacc[2];
 #pragma unroll
   for (int r = 0; r < 16; ++r) oacc[0][r] = oacc[1][r] = 0.f;
 
-  const int W = p.W;
-  const int lo = q0 - W + 1 > 0 ? q0 - W + 1 : 0;
-  const int hi = q0 + kBQ - 1 < p.T - 1 ? q0 + kBQ - 1 : p.T - 1;
   const int wlo = qw - W + 1, whi = qw + 31;  // this wavefront's key range
-  const float sl2 = p.scale_log2;
+  const float sl2 = p.scale_log2;             // > 0
 
-  for (int kt0 = (lo / kBK) * kBK; kt0 <= hi; kt0 += kBK) {
-    __syncthreads();  // previous tile fully consumed
-    {
-      // stage rows [kt0, kt0 + 64): K as is, V transposed; 4 threads per row
-      const int r = tid >> 2, c = (tid & 3) * 2;
-      const int key = kt0 + r < p.T ? kt0 + r : p.T - 1;
-      const uint4 k0 = ld16(kbase + key * skt + c * 16);
-      const uint4 k1 = ld16(kbase + key * skt + (c + 1) * 16);
-      const uint4 v0 = ld16(vbase + key * svt + c * 16);
-      const uint4 v1 = ld16(vbase + key * svt + (c + 1) * 16);
-      *reinterpret_cast<uint4*>(&Ks[r * kKRow + c * 8]) = k0;
-      *reinterpret_cast<uint4*>(&Ks[r * kKRow + (c + 1) * 8]) = k1;
-      const bf16x8 a0 = as_bf16x8(v0), a1 = as_bf16x8(v1);
+  for (int it = 0; it < ntiles; ++it) {
+    const int cur = it & 1;
+    const int kt0 = kfirst + it * kBK;
+    if (!(kt0 + kBK - 1 < wlo || kt0 > whi)) {
+      const __bf16* ks = Ks[cur];
+      const __bf16* vt = Vt[cur];
+      f32x16 sacc[2];
+      bool on[2], full[2];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        Vt[(c * 8 + e) * kVRow + r] = a0[e];
-        Vt[((c + 1) * 8 + e) * kVRow + r] = a1[e];
+      for (int nb = 0; nb < 2; ++nb) {
+        const int nb0 = kt0 + nb * 32;
+        on[nb] = !(nb0 + 31 < wlo || nb0 > whi);
+        // every (query, key) of the 32 x 32 block inside the band
+        full[nb] = nb0 + 31 <= qw && qw + 31 - nb0 < W && qw + 31 < p.T;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sacc[nb][r] = 0.f;
+        if (on[nb]) {
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) {
+            const bf16x8 a =
+                *reinterpret_cast<const bf16x8*>(&ks[(nb * 32 + l32) * kKRow + 16 * kk + 8 * half]);
+            sacc[nb] = mfma32(a, qf[kk], sacc[nb]);
+          }
+        }
       }
-    }
-    __syncthreads();
-    if (kt0 + kBK - 1 < wlo || kt0 > whi) continue;  // tile outside this wavefront's band
-
-    f32x16 sacc[2];
-    bool on[2];
+      float tmax = -INFINITY;
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const int nb0 = kt0 + nb * 32;
-      on[nb] = !(nb0 + 31 < wlo || nb0 > whi);
+      for (int nb = 0; nb < 2; ++nb) {
+        if (!full[nb]) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sacc[nb][r] = 0.f;
-      if (on[nb]) {
+          for (int r = 0; r < 16; ++r) {
+            const int n = kt0 + nb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
+            const bool ok = on[nb] && n <= m && m - n < W;
+            sacc[nb][r] = ok ? sacc[nb][r] : -INFINITY;
+          }
+        }
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Ks[(nb * 32 + l32) * kKRow + 16 * kk + 8 * half]);
-          sacc[nb] = mfma32(a, qf[kk], sacc[nb]);
+        for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sacc[nb][r]);
+      }
+      tmax = fmaxf(tmax, xhalf(tmax));
+      const float mnew = fmaxf(mrun, tmax);
+      const float mref = mnew == -INFINITY ? 0.f : mnew;
+      const float alpha = fast_exp2((mrun - mref) * sl2);
+      const float neg = -mref * sl2;
+      float psum = 0.f;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float pv = fast_exp2(fmaf(sacc[nb][r], sl2, neg));
+          sacc[nb][r] = pv;
+          psum += pv;
+        }
+      lrun = fmaf(lrun, alpha, psum);
+      mrun = mnew;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        oacc[0][r] *= alpha;
+        oacc[1][r] *= alpha;
+      }
+      // O^T += V^T P^T, 16 keys per step
+#pragma unroll
+      for (int ks4 = 0; ks4 < 4; ++ks4) {
+        const int nb = ks4 >> 1;
+        if (!on[nb]) continue;
+        bf16x8 pb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) pb[e] = static_cast<__bf16>(sacc[nb][8 * (ks4 & 1) + e]);
+#pragma unroll
+        for (int dblk = 0; dblk < 2; ++dblk) {
+          const __bf16* row = &vt[(dblk * 32 + l32) * kVRow + 16 * ks4 + 4 * half];
+          const uint2 x0 = *reinterpret_cast<const uint2*>(row);
+          const uint2 x1 = *reinterpret_cast<const uint2*>(row + 8);
+          oacc[dblk] = mfma32(as_bf16x8(make_uint4(x0.x, x0.y, x1.x, x1.y)), pb, oacc[dblk]);
         }
       }
     }
-    // band mask, scale to log2 units, tile max
-    float tmax = -INFINITY;
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int n = kt0 + nb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        const bool ok = on[nb] && n <= m && m - n < W;
-        const float s = ok ? sacc[nb][r] * sl2 : -INFINITY;
-        sacc[nb][r] = s;
-        tmax = fmaxf(tmax, s);
-      }
-    tmax = fmaxf(tmax, xhalf(tmax));
-    const float mnew = fmaxf(mrun, tmax);
-    const float mref = mnew == -INFINITY ? 0.f : mnew;
-    const float alpha = fast_exp2(mrun - mref);
-    float psum = 0.f;
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pv = fast_exp2(sacc[nb][r] - mref);
-        sacc[nb][r] = pv;
-        psum += pv;
-      }
-    lrun = fmaf(lrun, alpha, psum);
-    mrun = mnew;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      oacc[0][r] *= alpha;
-      oacc[1][r] *= alpha;
+    if (it + 1 < ntiles) {
+      tile_store(pre, Ks[cur ^ 1], Vt[cur ^ 1]);  // last read in iteration it - 1
+      if (it + 2 < ntiles) tile_load(pre, kbase, vbase, skt, svt, kt0 + 2 * kBK, p.T);
     }
-    // O^T += V^T P^T, 16 keys per step
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int nb = ks >> 1;
-      if (!on[nb]) continue;
-      bf16x8 pb;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) pb[e] = static_cast<__bf16>(sacc[nb][8 * (ks & 1) + e]);
-#pragma unroll
-      for (int dblk = 0; dblk < 2; ++dblk) {
-        const __bf16* row = &Vt[(dblk * 32 + l32) * kVRow + 16 * ks + 4 * half];
-        const uint2 x0 = *reinterpret_cast<const uint2*>(row);
-        const uint2 x1 = *reinterpret_cast<const uint2*>(row + 8);
-        oacc[dblk] = mfma32(as_bf16x8(make_uint4(x0.x, x0.y, x1.x, x1.y)), pb, oacc[dblk]);
-      }
-    }
+    __syncthreads();
   }
 
   // ---- long-range edges j = m - d: row gathers in the accumulator layout
-  if (p.n_dil > 0) {
+  if constexpr (HAS_DIL) {
     float qv[32];  // q[m][16*kk + 8*half + e] in fp32
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk)
@@ -214,17 +268,18 @@ __global__ __launch_bounds__(kThreads) void band_fwd_kernel(Params p) {
       float tmax = -INFINITY;
 #pragma unroll
       for (int g = 0; g < kG; ++g) {
-        s[g] = (s[g] + xhalf(s[g])) * sl2;
+        s[g] = s[g] + xhalf(s[g]);
         s[g] = j[g] >= 0 ? s[g] : -INFINITY;
         tmax = fmaxf(tmax, s[g]);
       }
       const float mnew = fmaxf(mrun, tmax);
       const float mref = mnew == -INFINITY ? 0.f : mnew;
-      const float alpha = fast_exp2(mrun - mref);
+      const float alpha = fast_exp2((mrun - mref) * sl2);
+      const float neg = -mref * sl2;
       float pg[kG], psum = 0.f;
 #pragma unroll
       for (int g = 0; g < kG; ++g) {
-        pg[g] = fast_exp2(s[g] - mref);
+        pg[g] = fast_exp2(fmaf(s[g], sl2, neg));
         psum += pg[g];
       }
       // both halves see the same edge: count its weight once in the row sum
@@ -260,7 +315,7 @@ __global__ __launch_bounds__(kThreads) void band_fwd_kernel(Params p) {
                                   pack_bf16x2(oacc[dblk][4 * g4 + 2] * inv, oacc[dblk][4 * g4 + 3] * inv));
       *reinterpret_cast<uint2*>(orow + (dblk * 32 + 8 * g4 + 4 * half) * 2) = w2;
     }
-  if (half == 0) p.lse[(int64_t)bh * p.T + m] = (mrun + fast_log2(ltot)) * kLn2;
+  if (half == 0) p.lse[(int64_t)bh * p.T + m] = (mrun * sl2 + fast_log2(ltot)) * kLn2;
 }
 
 }  // namespace
@@ -274,7 +329,10 @@ int band_rows_per_block() { return kBQ; }
 hipError_t launch_band_fwd(const Params& p, hipStream_t s) {
   const int nblk = (p.T + kBQ - 1) / kBQ;
   const int grid = xcd_grid(p.B * p.H * nblk);
-  hipLaunchKernelGGL(band_fwd_kernel, dim3(grid), dim3(kThreads), 0, s, p);
+  if (p.n_dil > 0)
+    hipLaunchKernelGGL(band_fwd_kernel<true>, dim3(grid), dim3(kThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL(band_fwd_kernel<false>, dim3(grid), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 

@@ -17,6 +17,11 @@
 // straight from the score registers, with the contraction index ordered as
 // the accumulator rows (8*(r/4) + 4*half + r%4).
 //
+// Streamed 64-row tiles are double-buffered in LDS: the global loads of tile
+// t+1 are in flight while tile t is computed, one barrier per tile.  Within a
+// tile the two 32-row blocks are processed one after the other to keep the
+// score registers at 32 per lane; blocks wholly inside the band skip the mask.
+//
 // Delta_i = <dout_i, o_i> equals sum_j P_ij dP_ij up to the rounding of o;
 // with the dot-product score the resulting gradient error is far inside the
 // bf16 tolerance (the score's 1/sqrt(D) scale damps it).
@@ -30,38 +35,53 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kD = 64;
-constexpr int kRows = 128;      // rows (queries or keys) owned per workgroup
-constexpr int kTile = 64;       // streamed rows per LDS tile
-constexpr int kRow = kD + 8;    // row-major tile stride, bf16 (144 B)
+constexpr int kRows = 128;        // rows (queries or keys) owned per workgroup
+constexpr int kTile = 64;         // streamed rows per LDS tile
+constexpr int kRow = kD + 8;      // row-major tile stride, bf16 (144 B)
 constexpr int kTRow = kTile + 4;  // transposed tile stride, bf16 (136 B)
 constexpr int kThreads = 256;
+constexpr int kRM = kTile * kRow;  // elements of a row-major tile
+constexpr int kTR = kD * kTRow;    // elements of a transposed tile
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8, u); }
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 __device__ __forceinline__ float xhalf(float x) { return __shfl_xor(x, 32, 64); }
+__device__ __forceinline__ float bf(const bf16x8& v, int e) { return static_cast<float>(v[e]); }
 
-// Stage rows [r0, r0 + 64) of a [T, 64] bf16 tensor into LDS: row-major
-// (when rm != nullptr) and transposed (when tr != nullptr).  Rows past T are
-// clamped to T - 1 (their products are masked by the callers).
-__device__ __forceinline__ void stage_tile(const char* base, int64_t st, int r0, int T, __bf16* rm,
-                                           __bf16* tr) {
+// One thread's share of a 64-row tile of a [T, 64] bf16 tensor: rows
+// (2 kp, 2 kp + 1), 16-byte chunk c, kp = tid / 8, c = tid % 8 (a wavefront
+// reads 16 whole consecutive rows).  Rows past T are clamped to T - 1; their
+// products are masked by the callers.
+struct PairRegs {
+  uint4 a, b;
+};
+
+__device__ __forceinline__ void pair_load(PairRegs& r, const char* base, int64_t st, int r0, int T) {
   const int tid = threadIdx.x;
-  const int r = tid >> 2, c = (tid & 3) * 2;
-  const int row = r0 + r < T ? r0 + r : T - 1;
-  const uint4 x0 = ld16(base + row * st + c * 16);
-  const uint4 x1 = ld16(base + row * st + (c + 1) * 16);
+  const int kp = tid >> 3, c = tid & 7;
+  const int x0 = r0 + 2 * kp < T ? r0 + 2 * kp : T - 1;
+  const int x1 = r0 + 2 * kp + 1 < T ? r0 + 2 * kp + 1 : T - 1;
+  r.a = ld16(base + x0 * st + c * 16);
+  r.b = ld16(base + x1 * st + c * 16);
+}
+
+__device__ __forceinline__ void pair_store(const PairRegs& r, __bf16* rm, __bf16* tr) {
+  const int tid = threadIdx.x;
+  const int kp = tid >> 3, c = tid & 7;
   if (rm != nullptr) {
-    *reinterpret_cast<uint4*>(&rm[r * kRow + c * 8]) = x0;
-    *reinterpret_cast<uint4*>(&rm[r * kRow + (c + 1) * 8]) = x1;
+    *reinterpret_cast<uint4*>(&rm[(2 * kp) * kRow + c * 8]) = r.a;
+    *reinterpret_cast<uint4*>(&rm[(2 * kp + 1) * kRow + c * 8]) = r.b;
   }
   if (tr != nullptr) {
-    const bf16x8 a0 = as_bf16x8(x0), a1 = as_bf16x8(x1);
+    const uint32_t a[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
+    const uint32_t b[4] = {r.b.x, r.b.y, r.b.z, r.b.w};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      tr[(c * 8 + e) * kTRow + r] = a0[e];
-      tr[((c + 1) * 8 + e) * kTRow + r] = a1[e];
+    for (int w = 0; w < 4; ++w) {
+      *reinterpret_cast<uint32_t*>(&tr[(c * 8 + 2 * w) * kTRow + 2 * kp]) = (a[w] & 0xffffu) | (b[w] << 16);
+      *reinterpret_cast<uint32_t*>(&tr[(c * 8 + 2 * w + 1) * kTRow + 2 * kp]) =
+          (a[w] >> 16) | (b[w] & 0xffff0000u);
     }
   }
 }
@@ -75,10 +95,8 @@ __device__ __forceinline__ bf16x8 tr_operand(const __bf16* tr, int d, int ks, in
   return as_bf16x8(make_uint4(x0.x, x0.y, x1.x, x1.y));
 }
 
-__device__ __forceinline__ float bf(const bf16x8& v, int e) { return static_cast<float>(v[e]); }
-
 // Accumulator-layout element (dblk, r) of a 64-element bf16 row fetched as
-// 8 x 8 bytes: c = 4*dblk + r/4 picks the 4-element run, r%4 the element.
+// 8 x 8 bytes: run c = 4*dblk + r/4, element r%4.
 __device__ __forceinline__ float acc_elem(const uint2* runs, int dblk, int r) {
   const uint2 w2 = runs[dblk * 4 + (r >> 2)];
   const uint32_t word = (r & 2) ? w2.y : w2.x;
@@ -107,11 +125,11 @@ __device__ __forceinline__ void store_acc_row(void* base, int64_t off_elems, con
 }
 
 // ------------------------------------------------------------------ dq
-template <bool GRAD_BF16>
+template <bool GRAD_BF16, bool HAS_DIL>
 __global__ __launch_bounds__(kThreads) void band_bwd_dq_kernel(Params p) {
-  __shared__ __align__(16) __bf16 Ks[kTile * kRow];
-  __shared__ __align__(16) __bf16 Kt[kD * kTRow];
-  __shared__ __align__(16) __bf16 Vs[kTile * kRow];
+  __shared__ __align__(16) __bf16 Ks[2][kRM];
+  __shared__ __align__(16) __bf16 Kt[2][kTR];
+  __shared__ __align__(16) __bf16 Vs[2][kRM];
 
   const int nblk = (p.T + kRows - 1) / kRows;
   const int logical = xcd_logical_block(p.B * p.H * nblk);
@@ -132,6 +150,16 @@ __global__ __launch_bounds__(kThreads) void band_bwd_dq_kernel(Params p) {
   const char* dob = static_cast<const char*>(p.dout) + (b * p.sdo_b + h * p.sdo_h) * 2;
   const int64_t sqt = p.sq_t * 2, skt = p.sk_t * 2, svt = p.sv_t * 2, sot = p.so_t * 2,
                 sdot = p.sdo_t * 2;
+  const int W = p.W;
+
+  const int lo = q0 - W + 1 > 0 ? q0 - W + 1 : 0;
+  const int hi = q0 + kRows - 1 < p.T - 1 ? q0 + kRows - 1 : p.T - 1;
+  const int kfirst = (lo / kTile) * kTile;
+  const int ntiles = (hi - kfirst) / kTile + 1;
+
+  PairRegs pk, pv;
+  pair_load(pk, kb, skt, kfirst, p.T);
+  pair_load(pv, vb, svt, kfirst, p.T);
 
   bf16x8 qf[4], df[4];
   float delta = 0.f;
@@ -148,91 +176,98 @@ __global__ __launch_bounds__(kThreads) void band_bwd_dq_kernel(Params p) {
   if (half == 0 && m < p.T) p.delta[(int64_t)bh * p.T + m] = delta;
   const float lse2 = p.lse[(int64_t)bh * p.T + mc] * kLog2e;
   const float sl2 = p.scale_log2;
-  const int W = p.W;
+
+  pair_store(pk, Ks[0], Kt[0]);
+  pair_store(pv, Vs[0], nullptr);
+  if (ntiles > 1) {
+    pair_load(pk, kb, skt, kfirst + kTile, p.T);
+    pair_load(pv, vb, svt, kfirst + kTile, p.T);
+  }
+  __syncthreads();
 
   f32x16 acc[2];
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[0][r] = acc[1][r] = 0.f;
-
-  const int lo = q0 - W + 1 > 0 ? q0 - W + 1 : 0;
-  const int hi = q0 + kRows - 1 < p.T - 1 ? q0 + kRows - 1 : p.T - 1;
   const int wlo = qw - W + 1, whi = qw + 31;
 
-  for (int kt0 = (lo / kTile) * kTile; kt0 <= hi; kt0 += kTile) {
-    __syncthreads();
-    stage_tile(kb, skt, kt0, p.T, Ks, Kt);
-    stage_tile(vb, svt, kt0, p.T, Vs, nullptr);
-    __syncthreads();
-    if (kt0 + kTile - 1 < wlo || kt0 > whi) continue;
-
-    f32x16 s[2], dp[2];
-    bool on[2];
+  for (int it = 0; it < ntiles; ++it) {
+    const int cur = it & 1;
+    const int kt0 = kfirst + it * kTile;
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       const int nb0 = kt0 + nb * 32;
-      on[nb] = !(nb0 + 31 < wlo || nb0 > whi);
+      if (nb0 + 31 < wlo || nb0 > whi) continue;  // block outside this wavefront's band
+      const bool full = nb0 + 31 <= qw && qw + 31 - nb0 < W && qw + 31 < p.T;
+      f32x16 s, dp;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[nb][r] = dp[nb][r] = 0.f;
-      if (on[nb]) {
+      for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const int off = (nb * 32 + l32) * kRow + 16 * kk + 8 * half;
-          s[nb] = mfma32(*reinterpret_cast<const bf16x8*>(&Ks[off]), qf[kk], s[nb]);
-          dp[nb] = mfma32(*reinterpret_cast<const bf16x8*>(&Vs[off]), df[kk], dp[nb]);
-        }
+      for (int kk = 0; kk < 4; ++kk) {
+        const int off = (nb * 32 + l32) * kRow + 16 * kk + 8 * half;
+        s = mfma32(*reinterpret_cast<const bf16x8*>(&Ks[cur][off]), qf[kk], s);
+        dp = mfma32(*reinterpret_cast<const bf16x8*>(&Vs[cur][off]), df[kk], dp);
       }
-    }
-    // dS = P (dP - Delta), masked to the band
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+      // dS = P (dP - Delta)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int n = kt0 + nb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        const bool ok = on[nb] && n <= m && m - n < W;
-        const float pr = ok ? fast_exp2(s[nb][r] * sl2 - lse2) : 0.f;
-        s[nb][r] = pr * (dp[nb][r] - delta);
+        float pr = fast_exp2(fmaf(s[r], sl2, -lse2));
+        if (!full) {
+          const int n = nb0 + 8 * (r >> 2) + 4 * half + (r & 3);
+          pr = (n <= m && m - n < W) ? pr : 0.f;
+        }
+        s[r] = pr * (dp[r] - delta);
       }
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int nb = ks >> 1;
-      if (!on[nb]) continue;
-      bf16x8 dsb;
+      for (int h2 = 0; h2 < 2; ++h2) {
+        bf16x8 dsb;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) dsb[e] = static_cast<__bf16>(s[nb][8 * (ks & 1) + e]);
+        for (int e = 0; e < 8; ++e) dsb[e] = static_cast<__bf16>(s[8 * h2 + e]);
 #pragma unroll
-      for (int dblk = 0; dblk < 2; ++dblk)
-        acc[dblk] = mfma32(tr_operand(Kt, dblk * 32 + l32, ks, half), dsb, acc[dblk]);
+        for (int dblk = 0; dblk < 2; ++dblk)
+          acc[dblk] = mfma32(tr_operand(Kt[cur], dblk * 32 + l32, 2 * nb + h2, half), dsb, acc[dblk]);
+      }
     }
+    if (it + 1 < ntiles) {
+      pair_store(pk, Ks[cur ^ 1], Kt[cur ^ 1]);
+      pair_store(pv, Vs[cur ^ 1], nullptr);
+      if (it + 2 < ntiles) {
+        pair_load(pk, kb, skt, kt0 + 2 * kTile, p.T);
+        pair_load(pv, vb, svt, kt0 + 2 * kTile, p.T);
+      }
+    }
+    __syncthreads();
   }
 
-  // long-range edges j = m - d
-  for (int t = 0; t < p.n_dil; ++t) {
-    const int j = mc - p.dil[t];
-    const int jj = j < 0 ? 0 : j;
-    float sp = 0.f, dpp = 0.f;
+  if constexpr (HAS_DIL) {
+    // long-range edges j = m - d
+    for (int t = 0; t < p.n_dil; ++t) {
+      const int j = mc - p.dil[t];
+      const int jj = j < 0 ? 0 : j;
+      float sp = 0.f, dpp = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int off = (16 * kk + 8 * half) * 2;
-      const bf16x8 kv = as_bf16x8(ld16(kb + jj * skt + off));
-      const bf16x8 vv = as_bf16x8(ld16(vb + jj * svt + off));
+      for (int kk = 0; kk < 4; ++kk) {
+        const int off = (16 * kk + 8 * half) * 2;
+        const bf16x8 kv = as_bf16x8(ld16(kb + jj * skt + off));
+        const bf16x8 vv = as_bf16x8(ld16(vb + jj * svt + off));
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        sp = fmaf(bf(qf[kk], e), bf(kv, e), sp);
-        dpp = fmaf(bf(df[kk], e), bf(vv, e), dpp);
+        for (int e = 0; e < 8; ++e) {
+          sp = fmaf(bf(qf[kk], e), bf(kv, e), sp);
+          dpp = fmaf(bf(df[kk], e), bf(vv, e), dpp);
+        }
       }
+      sp += xhalf(sp);
+      dpp += xhalf(dpp);
+      const float pr = j >= 0 ? fast_exp2(fmaf(sp, sl2, -lse2)) : 0.f;
+      const float ds = pr * (dpp - delta);
+      uint2 kr[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        kr[c] = *reinterpret_cast<const uint2*>(kb + jj * skt + acc_col(c >> 2, c & 3, half) * 2);
+#pragma unroll
+      for (int dblk = 0; dblk < 2; ++dblk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[dblk][r] = fmaf(ds, acc_elem(kr, dblk, r), acc[dblk][r]);
     }
-    sp += xhalf(sp);
-    dpp += xhalf(dpp);
-    const float pr = j >= 0 ? fast_exp2(sp * sl2 - lse2) : 0.f;
-    const float ds = pr * (dpp - delta);
-    uint2 kr[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c)
-      kr[c] = *reinterpret_cast<const uint2*>(kb + jj * skt + acc_col(c >> 2, c & 3, half) * 2);
-#pragma unroll
-    for (int dblk = 0; dblk < 2; ++dblk)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[dblk][r] = fmaf(ds, acc_elem(kr, dblk, r), acc[dblk][r]);
   }
 
   if (m >= p.T) return;
@@ -240,13 +275,13 @@ __global__ __launch_bounds__(kThreads) void band_bwd_dq_kernel(Params p) {
 }
 
 // ------------------------------------------------------------------ dk, dv
-template <bool GRAD_BF16>
+template <bool GRAD_BF16, bool HAS_DIL>
 __global__ __launch_bounds__(kThreads) void band_bwd_dkv_kernel(Params p) {
-  __shared__ __align__(16) __bf16 Qs[kTile * kRow];
-  __shared__ __align__(16) __bf16 Qt[kD * kTRow];
-  __shared__ __align__(16) __bf16 Ds[kTile * kRow];
-  __shared__ __align__(16) __bf16 Dt[kD * kTRow];
-  __shared__ float Ls[kTile], Dl[kTile];
+  __shared__ __align__(16) __bf16 Qs[2][kRM];
+  __shared__ __align__(16) __bf16 Qt[2][kTR];
+  __shared__ __align__(16) __bf16 Ds[2][kRM];
+  __shared__ __align__(16) __bf16 Dt[2][kTR];
+  __shared__ __align__(16) float Ls[2][kTile], Dl[2][kTile];
 
   const int nblk = (p.T + kRows - 1) / kRows;
   const int logical = xcd_logical_block(p.B * p.H * nblk);
@@ -267,6 +302,33 @@ __global__ __launch_bounds__(kThreads) void band_bwd_dkv_kernel(Params p) {
   const int64_t sqt = p.sq_t * 2, skt = p.sk_t * 2, svt = p.sv_t * 2, sdot = p.sdo_t * 2;
   const float* lseb = p.lse + (int64_t)bh * p.T;
   const float* delb = p.delta + (int64_t)bh * p.T;
+  const int W = p.W;
+
+  const int hi_key = k0 + kRows - 1 < p.T - 1 ? k0 + kRows - 1 : p.T - 1;
+  const int qhi = hi_key + W - 1 < p.T - 1 ? hi_key + W - 1 : p.T - 1;
+  const int mfirst = k0;  // a multiple of the tile height
+  const int ntiles = (qhi - mfirst) / kTile + 1;
+
+  PairRegs pq, pd;
+  float pl = 0.f, pdl = 0.f;
+  auto load_tile = [&](int mt0) {
+    pair_load(pq, qb, sqt, mt0, p.T);
+    pair_load(pd, dob, sdot, mt0, p.T);
+    if (tid < kTile) {
+      const int row = mt0 + tid < p.T ? mt0 + tid : p.T - 1;
+      pl = lseb[row] * kLog2e;
+      pdl = delb[row];
+    }
+  };
+  auto store_tile = [&](int buf) {
+    pair_store(pq, Qs[buf], Qt[buf]);
+    pair_store(pd, Ds[buf], Dt[buf]);
+    if (tid < kTile) {
+      Ls[buf][tid] = pl;
+      Dl[buf][tid] = pdl;
+    }
+  };
+  load_tile(mfirst);
 
   bf16x8 kf[4], vf[4];
 #pragma unroll
@@ -276,110 +338,112 @@ __global__ __launch_bounds__(kThreads) void band_bwd_dkv_kernel(Params p) {
     vf[kk] = as_bf16x8(ld16(vb + nc * svt + off));
   }
   const float sl2 = p.scale_log2;
-  const int W = p.W;
+
+  store_tile(0);
+  if (ntiles > 1) load_tile(mfirst + kTile);
+  __syncthreads();
 
   f32x16 dk[2], dv[2];
 #pragma unroll
   for (int r = 0; r < 16; ++r) dk[0][r] = dk[1][r] = dv[0][r] = dv[1][r] = 0.f;
-
-  const int hi_key = k0 + kRows - 1 < p.T - 1 ? k0 + kRows - 1 : p.T - 1;
-  const int qlo = k0;
-  const int qhi = hi_key + W - 1 < p.T - 1 ? hi_key + W - 1 : p.T - 1;
   const int wlo = kw, whi = kw + 31 + W - 1;  // this wavefront's query range
 
-  for (int mt0 = (qlo / kTile) * kTile; mt0 <= qhi; mt0 += kTile) {
-    __syncthreads();
-    stage_tile(qb, sqt, mt0, p.T, Qs, Qt);
-    stage_tile(dob, sdot, mt0, p.T, Ds, Dt);
-    if (tid < kTile) {
-      const int row = mt0 + tid < p.T ? mt0 + tid : p.T - 1;
-      Ls[tid] = lseb[row] * kLog2e;
-      Dl[tid] = delb[row];
-    }
-    __syncthreads();
-    if (mt0 + kTile - 1 < wlo || mt0 > whi) continue;
-
-    f32x16 s[2], dp[2];
-    bool on[2];
+  for (int it = 0; it < ntiles; ++it) {
+    const int cur = it & 1;
+    const int mt0 = mfirst + it * kTile;
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb) {
       const int mb0 = mt0 + mb * 32;
-      on[mb] = !(mb0 + 31 < wlo || mb0 > whi);
+      if (mb0 + 31 < wlo || mb0 > whi) continue;
+      // every (query, key) of the block inside the band
+      const bool full = kw + 31 <= mb0 && mb0 + 31 - kw < W && mb0 + 31 < p.T;
+      f32x16 s, dp;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) s[mb][r] = dp[mb][r] = 0.f;
-      if (on[mb]) {
+      for (int r = 0; r < 16; ++r) s[r] = dp[r] = 0.f;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const int off = (mb * 32 + l32) * kRow + 16 * kk + 8 * half;
-          s[mb] = mfma32(*reinterpret_cast<const bf16x8*>(&Qs[off]), kf[kk], s[mb]);
-          dp[mb] = mfma32(*reinterpret_cast<const bf16x8*>(&Ds[off]), vf[kk], dp[mb]);
+      for (int kk = 0; kk < 4; ++kk) {
+        const int off = (mb * 32 + l32) * kRow + 16 * kk + 8 * half;
+        s = mfma32(*reinterpret_cast<const bf16x8*>(&Qs[cur][off]), kf[kk], s);
+        dp = mfma32(*reinterpret_cast<const bf16x8*>(&Ds[cur][off]), vf[kk], dp);
+      }
+      // rows m = mb0 + 8 (r/4) + 4 half + r%4 of this lane's key column n
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const int mi0 = mb * 32 + 8 * g4 + 4 * half;
+        const float4 l4 = *reinterpret_cast<const float4*>(&Ls[cur][mi0]);
+        const float4 d4 = *reinterpret_cast<const float4*>(&Dl[cur][mi0]);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+        const float dl[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g4 + e;
+          float pr = fast_exp2(fmaf(s[r], sl2, -lv[e]));
+          if (!full) {
+            const int mm = mt0 + mi0 + e;
+            pr = (n <= mm && mm - n < W && mm < p.T) ? pr : 0.f;
+          }
+          s[r] = pr;
+          dp[r] = pr * (dp[r] - dl[e]);
+        }
+      }
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        bf16x8 pb, dsb;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pb[e] = static_cast<__bf16>(s[8 * h2 + e]);
+          dsb[e] = static_cast<__bf16>(dp[8 * h2 + e]);
+        }
+#pragma unroll
+        for (int dblk = 0; dblk < 2; ++dblk) {
+          dv[dblk] = mfma32(tr_operand(Dt[cur], dblk * 32 + l32, 2 * mb + h2, half), pb, dv[dblk]);
+          dk[dblk] = mfma32(tr_operand(Qt[cur], dblk * 32 + l32, 2 * mb + h2, half), dsb, dk[dblk]);
         }
       }
     }
-    // P and dS for rows m = mt0 + 32 mb + 8 (r/4) + 4 half + r%4, key n
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int mi = mb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-        const int mm = mt0 + mi;
-        const bool ok = on[mb] && n <= mm && mm - n < W && mm < p.T;
-        const float pr = ok ? fast_exp2(s[mb][r] * sl2 - Ls[mi]) : 0.f;
-        s[mb][r] = pr;
-        dp[mb][r] = pr * (dp[mb][r] - Dl[mi]);
-      }
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int mb = ks >> 1;
-      if (!on[mb]) continue;
-      bf16x8 pb, dsb;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        pb[e] = static_cast<__bf16>(s[mb][8 * (ks & 1) + e]);
-        dsb[e] = static_cast<__bf16>(dp[mb][8 * (ks & 1) + e]);
-      }
-#pragma unroll
-      for (int dblk = 0; dblk < 2; ++dblk) {
-        dv[dblk] = mfma32(tr_operand(Dt, dblk * 32 + l32, ks, half), pb, dv[dblk]);
-        dk[dblk] = mfma32(tr_operand(Qt, dblk * 32 + l32, ks, half), dsb, dk[dblk]);
-      }
+    if (it + 1 < ntiles) {
+      store_tile(cur ^ 1);
+      if (it + 2 < ntiles) load_tile(mt0 + 2 * kTile);
     }
+    __syncthreads();
   }
 
-  // long-range edges: queries i = n + d
-  for (int t = 0; t < p.n_dil; ++t) {
-    const int i = nc + p.dil[t];
-    const int ii = i < p.T ? i : p.T - 1;
-    float sp = 0.f, dpp = 0.f;
+  if constexpr (HAS_DIL) {
+    // long-range edges: queries i = n + d
+    for (int t = 0; t < p.n_dil; ++t) {
+      const int i = nc + p.dil[t];
+      const int ii = i < p.T ? i : p.T - 1;
+      float sp = 0.f, dpp = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int off = (16 * kk + 8 * half) * 2;
-      const bf16x8 qv = as_bf16x8(ld16(qb + ii * sqt + off));
-      const bf16x8 dv8 = as_bf16x8(ld16(dob + ii * sdot + off));
+      for (int kk = 0; kk < 4; ++kk) {
+        const int off = (16 * kk + 8 * half) * 2;
+        const bf16x8 qv = as_bf16x8(ld16(qb + ii * sqt + off));
+        const bf16x8 dv8 = as_bf16x8(ld16(dob + ii * sdot + off));
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        sp = fmaf(bf(qv, e), bf(kf[kk], e), sp);
-        dpp = fmaf(bf(dv8, e), bf(vf[kk], e), dpp);
+        for (int e = 0; e < 8; ++e) {
+          sp = fmaf(bf(qv, e), bf(kf[kk], e), sp);
+          dpp = fmaf(bf(dv8, e), bf(vf[kk], e), dpp);
+        }
       }
-    }
-    sp += xhalf(sp);
-    dpp += xhalf(dpp);
-    const float pr = i < p.T ? fast_exp2(sp * sl2 - lseb[ii] * kLog2e) : 0.f;
-    const float ds = pr * (dpp - delb[ii]);
-    uint2 qr[8], dr[8];
+      sp += xhalf(sp);
+      dpp += xhalf(dpp);
+      const float pr = i < p.T ? fast_exp2(fmaf(sp, sl2, -lseb[ii] * kLog2e)) : 0.f;
+      const float ds = pr * (dpp - delb[ii]);
+      uint2 qr[8], dr[8];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const int col = acc_col(c >> 2, c & 3, half) * 2;
-      qr[c] = *reinterpret_cast<const uint2*>(qb + ii * sqt + col);
-      dr[c] = *reinterpret_cast<const uint2*>(dob + ii * sdot + col);
-    }
-#pragma unroll
-    for (int dblk = 0; dblk < 2; ++dblk)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        dv[dblk][r] = fmaf(pr, acc_elem(dr, dblk, r), dv[dblk][r]);
-        dk[dblk][r] = fmaf(ds, acc_elem(qr, dblk, r), dk[dblk][r]);
+      for (int c = 0; c < 8; ++c) {
+        const int col = acc_col(c >> 2, c & 3, half) * 2;
+        qr[c] = *reinterpret_cast<const uint2*>(qb + ii * sqt + col);
+        dr[c] = *reinterpret_cast<const uint2*>(dob + ii * sdot + col);
       }
+#pragma unroll
+      for (int dblk = 0; dblk < 2; ++dblk)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          dv[dblk][r] = fmaf(pr, acc_elem(dr, dblk, r), dv[dblk][r]);
+          dk[dblk][r] = fmaf(ds, acc_elem(qr, dblk, r), dk[dblk][r]);
+        }
+    }
   }
 
   if (n >= p.T) return;
@@ -387,21 +451,22 @@ __global__ __launch_bounds__(kThreads) void band_bwd_dkv_kernel(Params p) {
   store_acc_row<GRAD_BF16>(p.dk, b * p.sdk_b + h * p.sdk_h + (int64_t)n * p.sdk_t, dk, p.scale, half);
 }
 
-template <bool GRAD_BF16>
+template <bool GRAD_BF16, bool HAS_DIL>
 hipError_t launch(const Params& p, hipStream_t s) {
   const int nblk = (p.T + kRows - 1) / kRows;
   const int grid = xcd_grid(p.B * p.H * nblk);
-  hipLaunchKernelGGL(band_bwd_dq_kernel<GRAD_BF16>, dim3(grid), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL((band_bwd_dq_kernel<GRAD_BF16, HAS_DIL>), dim3(grid), dim3(kThreads), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(band_bwd_dkv_kernel<GRAD_BF16>, dim3(grid), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL((band_bwd_dkv_kernel<GRAD_BF16, HAS_DIL>), dim3(grid), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_band_bwd(const Params& p, hipStream_t s) {
-  return p.grad_bf16 ? launch<true>(p, s) : launch<false>(p, s);
+  if (p.n_dil > 0) return p.grad_bf16 ? launch<true, true>(p, s) : launch<false, true>(p, s);
+  return p.grad_bf16 ? launch<true, false>(p, s) : launch<false, false>(p, s);
 }
 
 }  // namespace sa
