@@ -50,6 +50,19 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
 
 __device__ __forceinline__ float xhalf(float x) { return __shfl_xor(x, 32, 64); }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// acc + <a, b> over 8 bf16 pairs with v_dot2c_f32_bf16 (exact bf16 products,
+// fp32 accumulation).
+__device__ __forceinline__ float dot8_bf16(const bf16x8& a, const uint4& b, float acc) {
+  const uint4 ua = __builtin_bit_cast(uint4, a);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, ua.x), __builtin_bit_cast(bf16x2, b.x), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, ua.y), __builtin_bit_cast(bf16x2, b.y), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, ua.z), __builtin_bit_cast(bf16x2, b.z), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, ua.w), __builtin_bit_cast(bf16x2, b.w), acc, false);
+  return acc;
+}
+
 // Global -> register staging of one 64-key tile (K row-major, V as key
 // pairs for the transposed LDS copy), then register -> LDS.
 struct TileRegs {
@@ -97,7 +110,7 @@ __device__ __forceinline__ void tile_store(const TileRegs& t, __bf16* Ks, __bf16
 }
 
 template <bool HAS_DIL>
-__global__ __launch_bounds__(kThreads) void band_fwd_kernel(Params p) {
+__global__ __launch_bounds__(kThreads, 4) void band_fwd_kernel(Params p) {
   __shared__ __align__(16) __bf16 Ks[2][kBK * kKRow];
   __shared__ __align__(16) __bf16 Vt[2][kD * kVRow];
 
@@ -149,74 +162,66 @@ __global__ __launch_bounds__(kThreads) void band_fwd_kernel(Params p) {
   for (int it = 0; it < ntiles; ++it) {
     const int cur = it & 1;
     const int kt0 = kfirst + it * kBK;
-    if (!(kt0 + kBK - 1 < wlo || kt0 > whi)) {
-      const __bf16* ks = Ks[cur];
-      const __bf16* vt = Vt[cur];
-      f32x16 sacc[2];
-      bool on[2], full[2];
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const int nb0 = kt0 + nb * 32;
-        on[nb] = !(nb0 + 31 < wlo || nb0 > whi);
-        // every (query, key) of the 32 x 32 block inside the band
-        full[nb] = nb0 + 31 <= qw && qw + 31 - nb0 < W && qw + 31 < p.T;
+    for (int nb = 0; nb < 2; ++nb) {
+      const int nb0 = kt0 + nb * 32;
+      if (nb0 + 31 < wlo || nb0 > whi) continue;  // block outside this wavefront's band
+      // every (query, key) of the 32 x 32 block inside the band
+      const bool full = nb0 + 31 <= qw && qw + 31 - nb0 < W && qw + 31 < p.T;
+      f32x16 sacc;
+      {
+        const __bf16* krow = &Ks[cur][(nb * 32 + l32) * kKRow + 8 * half];
+        sacc = mfma32(*reinterpret_cast<const bf16x8*>(krow), qf[0], f32x16{});
 #pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[nb][r] = 0.f;
-        if (on[nb]) {
-#pragma unroll
-          for (int kk = 0; kk < 4; ++kk) {
-            const bf16x8 a =
-                *reinterpret_cast<const bf16x8*>(&ks[(nb * 32 + l32) * kKRow + 16 * kk + 8 * half]);
-            sacc[nb] = mfma32(a, qf[kk], sacc[nb]);
-          }
-        }
+        for (int kk = 1; kk < 4; ++kk)
+          sacc = mfma32(*reinterpret_cast<const bf16x8*>(krow + 16 * kk), qf[kk], sacc);
       }
-      float tmax = -INFINITY;
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        if (!full[nb]) {
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int n = kt0 + nb * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-            const bool ok = on[nb] && n <= m && m - n < W;
-            sacc[nb][r] = ok ? sacc[nb][r] : -INFINITY;
-          }
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) tmax = fmaxf(tmax, sacc[nb][r]);
-      }
-      tmax = fmaxf(tmax, xhalf(tmax));
-      const float mnew = fmaxf(mrun, tmax);
-      const float mref = mnew == -INFINITY ? 0.f : mnew;
-      const float alpha = fast_exp2((mrun - mref) * sl2);
-      const float neg = -mref * sl2;
-      float psum = 0.f;
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
+      if (!full) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float pv = fast_exp2(fmaf(sacc[nb][r], sl2, neg));
-          sacc[nb][r] = pv;
-          psum += pv;
+          const int n = nb0 + 8 * (r >> 2) + 4 * half + (r & 3);
+          const bool ok = (n <= m) & (m - n < W);
+          sacc[r] = ok ? sacc[r] : -INFINITY;
         }
-      lrun = fmaf(lrun, alpha, psum);
-      mrun = mnew;
+      }
+      float tmax = sacc[0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, sacc[r]);
+      tmax = fmaxf(tmax, xhalf(tmax));
+      // Lazy rescale: the reference max moves only when a score exceeds it by
+      // more than 8 (log2 units), so exponents stay <= 8 and the accumulator
+      // is rescaled rarely.
+      const bool grow = tmax * sl2 > mrun * sl2 + 8.f;
+      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        const float mnew = grow ? tmax : mrun;
+        const float alpha = mrun == -INFINITY ? 0.f : fast_exp2((mrun - mnew) * sl2);
+        lrun *= alpha;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          oacc[0][r] *= alpha;
+          oacc[1][r] *= alpha;
+        }
+        mrun = mnew;
+      }
+      const float neg = mrun == -INFINITY ? 0.f : -mrun * sl2;  // no valid key yet: p = 0
+      float psum = 0.f;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        oacc[0][r] *= alpha;
-        oacc[1][r] *= alpha;
+        const float pv = fast_exp2(fmaf(sacc[r], sl2, neg));
+        sacc[r] = pv;
+        psum += pv;
       }
+      lrun += psum;
       // O^T += V^T P^T, 16 keys per step
 #pragma unroll
-      for (int ks4 = 0; ks4 < 4; ++ks4) {
-        const int nb = ks4 >> 1;
-        if (!on[nb]) continue;
+      for (int h2 = 0; h2 < 2; ++h2) {
         bf16x8 pb;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) pb[e] = static_cast<__bf16>(sacc[nb][8 * (ks4 & 1) + e]);
+        for (int e = 0; e < 8; ++e) pb[e] = static_cast<__bf16>(sacc[8 * h2 + e]);
+        const int ks4 = 2 * nb + h2;
 #pragma unroll
         for (int dblk = 0; dblk < 2; ++dblk) {
-          const __bf16* row = &vt[(dblk * 32 + l32) * kVRow + 16 * ks4 + 4 * half];
+          const __bf16* row = &Vt[cur][(dblk * 32 + l32) * kVRow + 16 * ks4 + 4 * half];
           const uint2 x0 = *reinterpret_cast<const uint2*>(row);
           const uint2 x1 = *reinterpret_cast<const uint2*>(row + 8);
           oacc[dblk] = mfma32(as_bf16x8(make_uint4(x0.x, x0.y, x1.x, x1.y)), pb, oacc[dblk]);
@@ -232,11 +237,6 @@ __global__ __launch_bounds__(kThreads) void band_fwd_kernel(Params p) {
 
   // ---- long-range edges j = m - d: row gathers in the accumulator layout
   if constexpr (HAS_DIL) {
-    float qv[32];  // q[m][16*kk + 8*half + e] in fp32
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qv[8 * kk + e] = static_cast<float>(qf[kk][e]);
     for (int t0 = 0; t0 < p.n_dil; t0 += kG) {
       uint4 kr[kG][4];
       uint2 vr[kG][8];
@@ -258,11 +258,7 @@ __global__ __launch_bounds__(kThreads) void band_fwd_kernel(Params p) {
       for (int g = 0; g < kG; ++g) {
         float part = 0.f;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-          const bf16x8 kv = as_bf16x8(kr[g][kk]);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) part = fmaf(qv[8 * kk + e], static_cast<float>(kv[e]), part);
-        }
+        for (int kk = 0; kk < 4; ++kk) part = dot8_bf16(qf[kk], kr[g][kk], part);
         s[g] = part;
       }
       float tmax = -INFINITY;
@@ -272,10 +268,11 @@ __global__ __launch_bounds__(kThreads) void band_fwd_kernel(Params p) {
         s[g] = j[g] >= 0 ? s[g] : -INFINITY;
         tmax = fmaxf(tmax, s[g]);
       }
-      const float mnew = fmaxf(mrun, tmax);
-      const float mref = mnew == -INFINITY ? 0.f : mnew;
-      const float alpha = fast_exp2((mrun - mref) * sl2);
-      const float neg = -mref * sl2;
+      const bool grow = tmax * sl2 > mrun * sl2 + 8.f;
+      const float mnew = grow ? tmax : mrun;
+      const float alpha = grow ? (mrun == -INFINITY ? 0.f : fast_exp2((mrun - mnew) * sl2)) : 1.f;
+      mrun = mnew;
+      const float neg = mrun == -INFINITY ? 0.f : -mrun * sl2;
       float pg[kG], psum = 0.f;
 #pragma unroll
       for (int g = 0; g < kG; ++g) {
@@ -284,7 +281,6 @@ __global__ __launch_bounds__(kThreads) void band_fwd_kernel(Params p) {
       }
       // both halves see the same edge: count its weight once in the row sum
       lrun = fmaf(lrun, alpha, half == 0 ? psum : 0.f);
-      mrun = mnew;
 #pragma unroll
       for (int dblk = 0; dblk < 2; ++dblk)
 #pragma unroll

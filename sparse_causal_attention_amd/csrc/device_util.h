@@ -34,10 +34,19 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 template <int DT>
 struct Frag;
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
 template <>
 struct Frag<DT_F32> {
   static constexpr int EPL = 4;
   static constexpr int BYTES = 4;
+  // acc + <a, b> over the fragment's elements
+  __device__ __forceinline__ static float dot(const uint4& a, const uint4& b, float acc) {
+    acc = fmaf(__uint_as_float(a.x), __uint_as_float(b.x), acc);
+    acc = fmaf(__uint_as_float(a.y), __uint_as_float(b.y), acc);
+    acc = fmaf(__uint_as_float(a.z), __uint_as_float(b.z), acc);
+    return fmaf(__uint_as_float(a.w), __uint_as_float(b.w), acc);
+  }
   __device__ __forceinline__ static void unpack(const uint4& u, float* f) {
     f[0] = __uint_as_float(u.x);
     f[1] = __uint_as_float(u.y);
@@ -54,6 +63,17 @@ template <>
 struct Frag<DT_BF16> {
   static constexpr int EPL = 8;
   static constexpr int BYTES = 2;
+  // acc + <a, b> with v_dot2c_f32_bf16: exact bf16 products, fp32 accumulation
+  __device__ __forceinline__ static float dot(const uint4& a, const uint4& b, float acc) {
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.x),
+                                          __builtin_bit_cast(bf16x2_t, b.x), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.y),
+                                          __builtin_bit_cast(bf16x2_t, b.y), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.z),
+                                          __builtin_bit_cast(bf16x2_t, b.z), acc, false);
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.w),
+                                           __builtin_bit_cast(bf16x2_t, b.w), acc, false);
+  }
   __device__ __forceinline__ static void unpack(const uint4& u, float* f) {
     f[0] = bf16_lo(u.x); f[1] = bf16_hi(u.x);
     f[2] = bf16_lo(u.y); f[3] = bf16_hi(u.y);

@@ -63,11 +63,12 @@ __global__ __launch_bounds__(kThreads) void gather_bwd_q_kernel(Params p) {
   const char* vb = static_cast<const char*>(p.v) + (b * p.sv_b + h * p.sv_h) * EB + sub * 16;
   const int64_t skt = p.sk_t * EB, svt = p.sv_t * EB;
 
-  float dof[EPL], qf[EPL];
+  // dout and q fragments as stored (dot operands)
+  uint4 doraw, qraw = make_uint4(0u, 0u, 0u, 0u);
   {
     const char* dorow = static_cast<const char*>(p.dout) +
                         (b * p.sdo_b + h * p.sdo_h + i * p.sdo_t) * EB + sub * 16;
-    F::unpack(ld16(dorow), dof);
+    doraw = ld16(dorow);
   }
   // lse includes beta in coordinate mode; the scores below omit it
   const float lse2 =
@@ -79,9 +80,7 @@ __global__ __launch_bounds__(kThreads) void gather_bwd_q_kernel(Params p) {
   if constexpr (!COORD) {
     const char* qrow = static_cast<const char*>(p.q) + (b * p.sq_b + h * p.sq_h + i * p.sq_t) * EB +
                        sub * 16;
-    F::unpack(ld16(qrow), qf);
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) qf[e] *= p.scale_log2;
+    qraw = ld16(qrow);
   } else {
     const float* cqr = p.cq + ((int64_t)bh * p.T + i) * 3;
     cqi[0] = cqr[0]; cqi[1] = cqr[1]; cqi[2] = cqr[2];
@@ -123,25 +122,13 @@ __global__ __launch_bounds__(kThreads) void gather_bwd_q_kernel(Params p) {
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      float vf[EPL];
-      F::unpack(vraw[g], vf);
-      float part = 0.f;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) part = fmaf(dof[e], vf[e], part);
-      dp[g] = part;
-      if constexpr (!COORD) {
-        float kf[EPL];
-        F::unpack(kraw[g], kf);
-        float ps = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) ps = fmaf(qf[e], kf[e], ps);
-        s[g] = ps;
-      }
+      dp[g] = F::dot(doraw, vraw[g], 0.f);
+      if constexpr (!COORD) s[g] = F::dot(qraw, kraw[g], 0.f);
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       dp[g] = group_sum<LG>(dp[g]);
-      if constexpr (!COORD) s[g] = group_sum<LG>(s[g]);
+      if constexpr (!COORD) s[g] = group_sum<LG>(s[g]) * p.scale_log2;
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -237,11 +224,12 @@ __global__ __launch_bounds__(kThreads) void gather_bwd_kv_kernel(Params p) {
   const float* delb = p.delta + (int64_t)bh * p.T;
   const float bsub = COORD ? p.beta[h] : 0.f;  // lse includes beta in coordinate mode
 
-  float kf[EPL], vf[EPL];
+  // own k and v fragments as stored (dot operands)
+  uint4 kraw_j = make_uint4(0u, 0u, 0u, 0u), vraw_j;
   {
     const char* vrow = static_cast<const char*>(p.v) + (b * p.sv_b + h * p.sv_h + j * p.sv_t) * EB +
                        sub * 16;
-    F::unpack(ld16(vrow), vf);
+    vraw_j = ld16(vrow);
   }
   float ckj[3] = {0.f, 0.f, 0.f};
   float gl2 = 0.f, gam = 0.f;
@@ -249,9 +237,7 @@ __global__ __launch_bounds__(kThreads) void gather_bwd_kv_kernel(Params p) {
   if constexpr (!COORD) {
     const char* krow = static_cast<const char*>(p.k) + (b * p.sk_b + h * p.sk_h + j * p.sk_t) * EB +
                        sub * 16;
-    F::unpack(ld16(krow), kf);
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) kf[e] *= p.scale_log2;
+    kraw_j = ld16(krow);
   } else {
     const float* ckr = p.ck + ((int64_t)bh * p.T + j) * 3;
     ckj[0] = ckr[0]; ckj[1] = ckr[1]; ckj[2] = ckr[2];
@@ -289,25 +275,13 @@ __global__ __launch_bounds__(kThreads) void gather_bwd_kv_kernel(Params p) {
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      float dof[EPL];
-      F::unpack(doraw[g], dof);
-      float part = 0.f;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) part = fmaf(dof[e], vf[e], part);
-      dp[g] = part;
-      if constexpr (!COORD) {
-        float qf[EPL];
-        F::unpack(qraw[g], qf);
-        float ps = 0.f;
-#pragma unroll
-        for (int e = 0; e < EPL; ++e) ps = fmaf(qf[e], kf[e], ps);
-        s[g] = ps;
-      }
+      dp[g] = F::dot(doraw[g], vraw_j, 0.f);
+      if constexpr (!COORD) s[g] = F::dot(qraw[g], kraw_j, 0.f);
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       dp[g] = group_sum<LG>(dp[g]);
-      if constexpr (!COORD) s[g] = group_sum<LG>(s[g]);
+      if constexpr (!COORD) s[g] = group_sum<LG>(s[g]) * p.scale_log2;
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) {

@@ -58,16 +58,14 @@ __global__ __launch_bounds__(kThreads) void gather_fwd_kernel(Params p) {
   const char* vb = static_cast<const char*>(p.v) + (b * p.sv_b + h * p.sv_h) * EB + sub * 16;
   const int64_t skt = p.sk_t * EB, svt = p.sv_t * EB;
 
-  float qf[EPL];
+  uint4 qraw = make_uint4(0u, 0u, 0u, 0u);  // q fragment as stored (dot operand)
   float cqi[3] = {0.f, 0.f, 0.f};
   float gl2 = 0.f;  // gamma * log2(e)
   const float* ckb = nullptr;
   if constexpr (!COORD) {
     const char* qrow = static_cast<const char*>(p.q) + (b * p.sq_b + h * p.sq_h + i * p.sq_t) * EB +
                        sub * 16;
-    F::unpack(ld16(qrow), qf);
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) qf[e] *= p.scale_log2;
+    qraw = ld16(qrow);
   } else {
     const float* cqr = p.cq + ((int64_t)bh * p.T + i) * 3;
     cqi[0] = cqr[0]; cqi[1] = cqr[1]; cqi[2] = cqr[2];
@@ -100,16 +98,9 @@ __global__ __launch_bounds__(kThreads) void gather_fwd_kernel(Params p) {
     }
     if constexpr (!COORD) {
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        float kf[EPL];
-        F::unpack(kraw[g], kf);
-        float part = 0.f;
+      for (int g = 0; g < G; ++g) s[g] = F::dot(qraw, kraw[g], 0.f);
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) part = fmaf(qf[e], kf[e], part);
-        s[g] = part;
-      }
-#pragma unroll
-      for (int g = 0; g < G; ++g) s[g] = group_sum<LG>(s[g]);
+      for (int g = 0; g < G; ++g) s[g] = group_sum<LG>(s[g]) * p.scale_log2;
     }
     float mx = m;
 #pragma unroll
