@@ -77,7 +77,8 @@ void fill_common(sa::Params* p, const sa_graph* g, const sa_attn_desc* d) {
   p->D = (int32_t)d->D;
   p->W = (int32_t)g->W;
   p->n_dil = g->n_dil;
-  for (int t = 0; t < g->n_dil; ++t) p->dil[t] = (int32_t)g->dil[t];
+  for (int t = 0; t < SA_MAX_DILATED + 8; ++t)
+    p->dil[t] = t < g->n_dil ? (int32_t)g->dil[t] : sa::kUnreachable;
   p->scale = d->scale > 0.f ? d->scale : (float)(1.0 / sqrt((double)d->D));
   p->scale_log2 = p->scale * 1.4426950408889634f;
   p->grad_bf16 = d->grad_dtype == SA_BF16;

@@ -1,15 +1,18 @@
 // Band backward: gradients of the sliding-window part on the bf16 matrix
 // cores, with the long-range edges of the same rows gathered in the same
-// kernels.  Deterministic and atomic-free: one kernel owns each query row
-// (dq), another each key row (dk, dv).
+// kernel.  One launch, two kinds of workgroup: a dq workgroup owns 128 query
+// rows, a dk/dv workgroup owns 128 key rows, so every output row has exactly
+// one writer (deterministic, no atomics).  The two kinds of the same row
+// block are adjacent in the launch order and so run on the same XCD, where
+// they share the K, V, Q, dO rows in L2.
 //
-//  dq kernel, one query row per lane (as in the forward):
+//  dq role, one query row per lane (as in the forward):
 //    S^T = K Q^T,  dP^T = V dO^T   (K, V tiles row-major in LDS),
 //    P = exp(S - lse),  dS = P (dP - Delta),  Delta_i = <dout_i, o_i>,
 //    dq^T += K^T dS^T              (K^T tile in LDS; dS^T from registers).
-//    Delta is written to the workspace for the second kernel.
-//  dk/dv kernel, one key row per lane, over the reverse band (queries
-//  j .. j+W-1):
+//  dk/dv role, one key row per lane, over the reverse band (queries
+//  j .. j+W-1), computing the Delta of each staged query tile itself from
+//  its dO and o rows:
 //    S = Q K^T,  dP = dO V^T       (Q, dO tiles row-major in LDS),
 //    dv^T += dO^T P,  dk^T += Q^T dS   (Q^T, dO^T tiles in LDS).
 // Lane layouts are those of v_mfma_f32_32x32x16_bf16 described in the
@@ -125,19 +128,23 @@ __device__ __forceinline__ void store_acc_row(void* base, int64_t off_elems, con
 }
 
 // ------------------------------------------------------------------ dq
-template <bool GRAD_BF16, bool HAS_DIL>
-__global__ __launch_bounds__(kThreads) void band_bwd_dq_kernel(Params p) {
-  __shared__ __align__(16) __bf16 Ks[2][kRM];
-  __shared__ __align__(16) __bf16 Kt[2][kTR];
-  __shared__ __align__(16) __bf16 Vs[2][kRM];
+// LDS of the dq role, carved from the kernel's shared buffer
+struct DqSmem {
+  __bf16 Ks[2][kRM];
+  __bf16 Kt[2][kTR];
+  __bf16 Vs[2][kRM];
+};
 
-  const int nblk = (p.T + kRows - 1) / kRows;
-  const int logical = xcd_logical_block(p.B * p.H * nblk);
-  if (logical < 0) return;
+template <bool GRAD_BF16, bool HAS_DIL>
+__device__ __forceinline__ void dq_role(const Params& p, int logical, int nblk, DqSmem& sm) {
+  auto& Ks = sm.Ks;
+  auto& Kt = sm.Kt;
+  auto& Vs = sm.Vs;
   const int bh = logical / nblk;
   const int rb = nblk - 1 - (logical - bh * nblk);
   const int b = bh / p.H, h = bh - b * p.H;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, half = lane >> 5;
   const int q0 = rb * kRows, qw = q0 + wave * 32;
   const int m = qw + l32;
@@ -173,7 +180,6 @@ __global__ __launch_bounds__(kThreads) void band_bwd_dq_kernel(Params p) {
     for (int e = 0; e < 8; ++e) delta = fmaf(bf(df[kk], e), bf(of, e), delta);
   }
   delta += xhalf(delta);
-  if (half == 0 && m < p.T) p.delta[(int64_t)bh * p.T + m] = delta;
   const float lse2 = p.lse[(int64_t)bh * p.T + mc] * kLog2e;
   const float sl2 = p.scale_log2;
 
@@ -275,21 +281,29 @@ __global__ __launch_bounds__(kThreads) void band_bwd_dq_kernel(Params p) {
 }
 
 // ------------------------------------------------------------------ dk, dv
-template <bool GRAD_BF16, bool HAS_DIL>
-__global__ __launch_bounds__(kThreads) void band_bwd_dkv_kernel(Params p) {
-  __shared__ __align__(16) __bf16 Qs[2][kRM];
-  __shared__ __align__(16) __bf16 Qt[2][kTR];
-  __shared__ __align__(16) __bf16 Ds[2][kRM];
-  __shared__ __align__(16) __bf16 Dt[2][kTR];
-  __shared__ __align__(16) float Ls[2][kTile], Dl[2][kTile];
+// LDS of the dk/dv role
+struct DkvSmem {
+  __bf16 Qs[2][kRM];
+  __bf16 Qt[2][kTR];
+  __bf16 Ds[2][kRM];
+  __bf16 Dt[2][kTR];
+  float Ls[2][kTile];
+  float Dl[2][kTile];
+};
 
-  const int nblk = (p.T + kRows - 1) / kRows;
-  const int logical = xcd_logical_block(p.B * p.H * nblk);
-  if (logical < 0) return;
+template <bool GRAD_BF16, bool HAS_DIL>
+__device__ __forceinline__ void dkv_role(const Params& p, int logical, int nblk, DkvSmem& sm) {
+  auto& Qs = sm.Qs;
+  auto& Qt = sm.Qt;
+  auto& Ds = sm.Ds;
+  auto& Dt = sm.Dt;
+  auto& Ls = sm.Ls;
+  auto& Dl = sm.Dl;
   const int bh = logical / nblk;
   const int rb = logical - bh * nblk;  // early key blocks see the longest query ranges
   const int b = bh / p.H, h = bh - b * p.H;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, half = lane >> 5;
   const int k0 = rb * kRows, kw = k0 + wave * 32;
   const int n = kw + l32;
@@ -299,9 +313,10 @@ __global__ __launch_bounds__(kThreads) void band_bwd_dkv_kernel(Params p) {
   const char* kb = static_cast<const char*>(p.k) + (b * p.sk_b + h * p.sk_h) * 2;
   const char* vb = static_cast<const char*>(p.v) + (b * p.sv_b + h * p.sv_h) * 2;
   const char* dob = static_cast<const char*>(p.dout) + (b * p.sdo_b + h * p.sdo_h) * 2;
-  const int64_t sqt = p.sq_t * 2, skt = p.sk_t * 2, svt = p.sv_t * 2, sdot = p.sdo_t * 2;
+  const char* ob = static_cast<const char*>(p.o) + (b * p.so_b + h * p.so_h) * 2;
+  const int64_t sqt = p.sq_t * 2, skt = p.sk_t * 2, svt = p.sv_t * 2, sdot = p.sdo_t * 2,
+                sot = p.so_t * 2;
   const float* lseb = p.lse + (int64_t)bh * p.T;
-  const float* delb = p.delta + (int64_t)bh * p.T;
   const int W = p.W;
 
   const int hi_key = k0 + kRows - 1 < p.T - 1 ? k0 + kRows - 1 : p.T - 1;
@@ -309,24 +324,30 @@ __global__ __launch_bounds__(kThreads) void band_bwd_dkv_kernel(Params p) {
   const int mfirst = k0;  // a multiple of the tile height
   const int ntiles = (qhi - mfirst) / kTile + 1;
 
-  PairRegs pq, pd;
-  float pl = 0.f, pdl = 0.f;
+  PairRegs pq, pd, po;
+  float pl = 0.f;
   auto load_tile = [&](int mt0) {
     pair_load(pq, qb, sqt, mt0, p.T);
     pair_load(pd, dob, sdot, mt0, p.T);
+    pair_load(po, ob, sot, mt0, p.T);
     if (tid < kTile) {
       const int row = mt0 + tid < p.T ? mt0 + tid : p.T - 1;
       pl = lseb[row] * kLog2e;
-      pdl = delb[row];
     }
   };
   auto store_tile = [&](int buf) {
     pair_store(pq, Qs[buf], Qt[buf]);
     pair_store(pd, Ds[buf], Dt[buf]);
-    if (tid < kTile) {
-      Ls[buf][tid] = pl;
-      Dl[buf][tid] = pdl;
+    // Delta of the tile's two rows of this thread: 8-element partial dots of
+    // dout and o, summed over the 8 consecutive lanes holding those rows
+    const float da = group_sum<8>(Frag<DT_BF16>::dot(pd.a, po.a, 0.f));
+    const float db = group_sum<8>(Frag<DT_BF16>::dot(pd.b, po.b, 0.f));
+    if ((tid & 7) == 0) {
+      const int kp = tid >> 3;
+      Dl[buf][2 * kp] = da;
+      Dl[buf][2 * kp + 1] = db;
     }
+    if (tid < kTile) Ls[buf][tid] = pl;
   };
   load_tile(mfirst);
 
@@ -427,8 +448,16 @@ __global__ __launch_bounds__(kThreads) void band_bwd_dkv_kernel(Params p) {
       }
       sp += xhalf(sp);
       dpp += xhalf(dpp);
+      // Delta of query ii from its dout and o rows
+      float di = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int off = (16 * kk + 8 * half) * 2;
+        di = Frag<DT_BF16>::dot(ld16(dob + ii * sdot + off), ld16(ob + ii * sot + off), di);
+      }
+      di += xhalf(di);
       const float pr = i < p.T ? fast_exp2(fmaf(sp, sl2, -lseb[ii] * kLog2e)) : 0.f;
-      const float ds = pr * (dpp - delb[ii]);
+      const float ds = pr * (dpp - di);
       uint2 qr[8], dr[8];
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
@@ -451,14 +480,26 @@ __global__ __launch_bounds__(kThreads) void band_bwd_dkv_kernel(Params p) {
   store_acc_row<GRAD_BF16>(p.dk, b * p.sdk_b + h * p.sdk_h + (int64_t)n * p.sdk_t, dk, p.scale, half);
 }
 
+constexpr size_t kSmemBytes = sizeof(DkvSmem) > sizeof(DqSmem) ? sizeof(DkvSmem) : sizeof(DqSmem);
+
+template <bool GRAD_BF16, bool HAS_DIL>
+__global__ __launch_bounds__(kThreads, 2) void band_bwd_kernel(Params p) {
+  __shared__ __align__(16) unsigned char smem[kSmemBytes];
+  const int nblk = (p.T + kRows - 1) / kRows;
+  const int logical = xcd_logical_block(2 * p.B * p.H * nblk);
+  if (logical < 0) return;
+  // the dq and dk/dv workgroups of one row block are adjacent: same XCD
+  if ((logical & 1) == 0)
+    dq_role<GRAD_BF16, HAS_DIL>(p, logical >> 1, nblk, *reinterpret_cast<DqSmem*>(smem));
+  else
+    dkv_role<GRAD_BF16, HAS_DIL>(p, logical >> 1, nblk, *reinterpret_cast<DkvSmem*>(smem));
+}
+
 template <bool GRAD_BF16, bool HAS_DIL>
 hipError_t launch(const Params& p, hipStream_t s) {
   const int nblk = (p.T + kRows - 1) / kRows;
-  const int grid = xcd_grid(p.B * p.H * nblk);
-  hipLaunchKernelGGL((band_bwd_dq_kernel<GRAD_BF16, HAS_DIL>), dim3(grid), dim3(kThreads), 0, s, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((band_bwd_dkv_kernel<GRAD_BF16, HAS_DIL>), dim3(grid), dim3(kThreads), 0, s, p);
+  const int grid = xcd_grid(2 * p.B * p.H * nblk);
+  hipLaunchKernelGGL((band_bwd_kernel<GRAD_BF16, HAS_DIL>), dim3(grid), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 

@@ -36,12 +36,9 @@ struct Geo {
   static constexpr int RPB = RPW * kWaves;
 };
 
-__device__ __forceinline__ int distance_of(const Params& p, int t) {
-  return t < p.W ? t : p.dil[t - p.W];
-}
 
 // ------------------------------------------------------------------ pass 1
-template <int DT, int D, bool COORD, int G>
+template <int DT, int D, bool COORD, int G, bool OFF32>
 __global__ __launch_bounds__(kThreads) void gather_bwd_q_kernel(Params p) {
   using F = Frag<DT>;
   using Gm = Geo<DT, D>;
@@ -53,15 +50,22 @@ __global__ __launch_bounds__(kThreads) void gather_bwd_q_kernel(Params p) {
   if (logical < 0) return;
   const int bh = logical / nblk, rb = logical - bh * nblk;
   const int b = bh / p.H, h = bh - b * p.H;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int sub = lane % LG;
-  int i = rb * RPB + wave * RPW + lane / LG;
+  const int i0w = rb * RPB + wave * RPW;
+  int i = i0w + lane / LG;
   const bool row_ok = i < p.T;
   if (!row_ok) i = p.T - 1;
+  const int imax = i0w + RPW - 1 < p.T - 1 ? i0w + RPW - 1 : p.T - 1;
 
-  const char* kb = static_cast<const char*>(p.k) + (b * p.sk_b + h * p.sk_h) * EB + sub * 16;
-  const char* vb = static_cast<const char*>(p.v) + (b * p.sv_b + h * p.sv_h) * EB + sub * 16;
+  const char* khead = static_cast<const char*>(p.k) + (b * p.sk_b + h * p.sk_h) * EB;
+  const char* vhead = static_cast<const char*>(p.v) + (b * p.sv_b + h * p.sv_h) * EB;
   const int64_t skt = p.sk_t * EB, svt = p.sv_t * EB;
+  int64_t kl = (int64_t)i * skt + sub * 16, vl = (int64_t)i * svt + sub * 16;
+  uint32_t kl32 = (uint32_t)kl, vl32 = (uint32_t)vl;
+  asm volatile("" : "+v"(kl32), "+v"(vl32), "+v"(kl), "+v"(vl));  // keep addresses scalar-offset
+  const uint32_t sub16 = (uint32_t)sub * 16u;
 
   // dout and q fragments as stored (dot operands)
   uint4 doraw, qraw = make_uint4(0u, 0u, 0u, 0u);
@@ -99,20 +103,27 @@ __global__ __launch_bounds__(kThreads) void gather_bwd_q_kernel(Params p) {
   float cdx[3] = {0.f, 0.f, 0.f}, cx[3] = {0.f, 0.f, 0.f};
   float r2dx = 0.f, r2x = 0.f, psum = 0.f;
 
-  const int nd = p.W + p.n_dil;
-  for (int t0 = 0; t0 < nd; t0 += G) {
+  auto group = [&](const int (&dist)[G]) {
     int j[G];
     uint4 kraw[G], vraw[G];
     float s[G], dp[G], r2[G], dif[G][3];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const int t = t0 + g;
-      j[g] = (t < nd) ? i - distance_of(p, t) : -1;
-      const int jj = j[g] < 0 ? 0 : j[g];
-      if constexpr (!COORD) kraw[g] = ld16(kb + jj * skt);
-      vraw[g] = ld16(vb + jj * svt);
+      j[g] = i - dist[g];
+      const bool ok = j[g] >= 0;
+      if constexpr (OFF32) {
+        const uint32_t ko = ok ? kl32 - (uint32_t)dist[g] * (uint32_t)skt : sub16;
+        const uint32_t vo = ok ? vl32 - (uint32_t)dist[g] * (uint32_t)svt : sub16;
+        if constexpr (!COORD) kraw[g] = ld16(khead + ko);
+        vraw[g] = ld16(vhead + vo);
+      } else {
+        const int64_t ko = ok ? kl - (int64_t)dist[g] * skt : (int64_t)sub16;
+        const int64_t vo = ok ? vl - (int64_t)dist[g] * svt : (int64_t)sub16;
+        if constexpr (!COORD) kraw[g] = ld16(khead + ko);
+        vraw[g] = ld16(vhead + vo);
+      }
       if constexpr (COORD) {
-        const float* c = ckb + (int64_t)jj * 3;
+        const float* c = ckb + (int64_t)(ok ? j[g] : 0) * 3;
         dif[g][0] = cqi[0] - c[0];
         dif[g][1] = cqi[1] - c[1];
         dif[g][2] = cqi[2] - c[2];
@@ -154,6 +165,21 @@ __global__ __launch_bounds__(kThreads) void gather_bwd_q_kernel(Params p) {
         psum += pr;
       }
     }
+  };
+
+  const int wend = p.W < imax + 1 ? p.W : imax + 1;
+  for (int t0 = 0; t0 < wend; t0 += G) {
+    int dist[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) dist[g] = t0 + g < p.W ? t0 + g : kUnreachable;
+    group(dist);
+  }
+  for (int t0 = 0; t0 < p.n_dil; t0 += G) {
+    int dist[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) dist[g] = p.dil[t0 + g];
+    if (dist[0] > imax) break;
+    group(dist);
   }
   if (row_ok && sub == 0) p.delta[(int64_t)bh * p.T + i] = delta;
 
@@ -199,7 +225,7 @@ __global__ __launch_bounds__(kThreads) void gather_bwd_q_kernel(Params p) {
 }
 
 // ------------------------------------------------------------------ pass 2
-template <int DT, int D, bool COORD, int G>
+template <int DT, int D, bool COORD, int G, bool OFF32>
 __global__ __launch_bounds__(kThreads) void gather_bwd_kv_kernel(Params p) {
   using F = Frag<DT>;
   using Gm = Geo<DT, D>;
@@ -211,15 +237,21 @@ __global__ __launch_bounds__(kThreads) void gather_bwd_kv_kernel(Params p) {
   if (logical < 0) return;
   const int bh = logical / nblk, rb = logical - bh * nblk;
   const int b = bh / p.H, h = bh - b * p.H;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int sub = lane % LG;
-  int j = rb * RPB + wave * RPW + lane / LG;
+  const int j0w = rb * RPB + wave * RPW;  // first key row of this wavefront
+  int j = j0w + lane / LG;
   const bool row_ok = j < p.T;
   if (!row_ok) j = p.T - 1;
+  const int room = p.T - 1 - j0w;  // largest distance any key of the wave can use
 
-  const char* qb = static_cast<const char*>(p.q) + (b * p.sq_b + h * p.sq_h) * EB + sub * 16;
-  const char* dob = static_cast<const char*>(p.dout) + (b * p.sdo_b + h * p.sdo_h) * EB + sub * 16;
+  const char* qhead = static_cast<const char*>(p.q) + (b * p.sq_b + h * p.sq_h) * EB;
+  const char* dohead = static_cast<const char*>(p.dout) + (b * p.sdo_b + h * p.sdo_h) * EB;
   const int64_t sqt = p.sq_t * EB, sdot = p.sdo_t * EB;
+  int64_t ql = (int64_t)j * sqt + sub * 16, dl = (int64_t)j * sdot + sub * 16;
+  uint32_t ql32 = (uint32_t)ql, dl32 = (uint32_t)dl;
+  asm volatile("" : "+v"(ql32), "+v"(dl32), "+v"(ql), "+v"(dl));  // keep addresses scalar-offset
   const float* lseb = p.lse + (int64_t)bh * p.T;
   const float* delb = p.delta + (int64_t)bh * p.T;
   const float bsub = COORD ? p.beta[h] : 0.f;  // lse includes beta in coordinate mode
@@ -251,20 +283,29 @@ __global__ __launch_bounds__(kThreads) void gather_bwd_kv_kernel(Params p) {
   for (int e = 0; e < EPL; ++e) dk[e] = dv[e] = 0.f;
   float dc[3] = {0.f, 0.f, 0.f};
 
-  const int nd = p.W + p.n_dil;
-  for (int t0 = 0; t0 < nd; t0 += G) {
+  auto group = [&](const int (&dist)[G]) {
     int i[G];
     uint4 qraw[G], doraw[G];
     float s[G], dp[G], lse2[G], del[G], dif[G][3];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const int t = t0 + g;
-      i[g] = (t < nd) ? j + distance_of(p, t) : p.T;
-      const int ii = i[g] < p.T ? i[g] : p.T - 1;  // clamped address, masked below
-      if constexpr (!COORD) qraw[g] = ld16(qb + ii * sqt);
-      doraw[g] = ld16(dob + ii * sdot);
+      // test the distance against the room left (j + kUnreachable would overflow)
+      const bool ok = dist[g] <= p.T - 1 - j;
+      const int ii = ok ? j + dist[g] : j;  // own row as a harmless stand-in
+      if constexpr (OFF32) {
+        const uint32_t qo = ok ? ql32 + (uint32_t)dist[g] * (uint32_t)sqt : ql32;
+        const uint32_t doo = ok ? dl32 + (uint32_t)dist[g] * (uint32_t)sdot : dl32;
+        if constexpr (!COORD) qraw[g] = ld16(qhead + qo);
+        doraw[g] = ld16(dohead + doo);
+      } else {
+        const int64_t qo = ok ? ql + (int64_t)dist[g] * sqt : ql;
+        const int64_t doo = ok ? dl + (int64_t)dist[g] * sdot : dl;
+        if constexpr (!COORD) qraw[g] = ld16(qhead + qo);
+        doraw[g] = ld16(dohead + doo);
+      }
       lse2[g] = (lseb[ii] - bsub) * kLog2e;
       del[g] = delb[ii];
+      i[g] = ok ? ii : p.T;  // p.T marks an absent edge
       if constexpr (COORD) {
         const float* c = cqb + (int64_t)ii * 3;
         dif[g][0] = c[0] - ckj[0];
@@ -302,6 +343,21 @@ __global__ __launch_bounds__(kThreads) void gather_bwd_kv_kernel(Params p) {
         dc[2] = fmaf(ds, dif[g][2], dc[2]);
       }
     }
+  };
+
+  const int wend = p.W < room + 1 ? p.W : room + 1;
+  for (int t0 = 0; t0 < wend; t0 += G) {
+    int dist[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) dist[g] = t0 + g < p.W ? t0 + g : kUnreachable;
+    group(dist);
+  }
+  for (int t0 = 0; t0 < p.n_dil; t0 += G) {
+    int dist[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) dist[g] = p.dil[t0 + g];
+    if (dist[0] > room) break;
+    group(dist);
   }
 
   if (!row_ok) return;
@@ -357,20 +413,36 @@ __global__ __launch_bounds__(256) void coord_param_reduce_kernel(const float* pa
   }
 }
 
-template <int DT, int D, bool COORD>
-hipError_t launch_one(const Params& p, hipStream_t s) {
-  constexpr int RPB = Geo<DT, D>::RPB;
-  const int nblk = (p.T + RPB - 1) / RPB;
-  const int grid = xcd_grid(p.B * p.H * nblk);
-  hipLaunchKernelGGL((gather_bwd_q_kernel<DT, D, COORD, 4>), dim3(grid), dim3(kThreads), 0, s, p);
+// Whether every gathered byte offset within one (batch, head) slice fits in
+// 31 bits, so addresses can be a uniform base plus a 32-bit offset.
+inline bool fits_off32(const Params& p, int eb) {
+  const int64_t lim = (int64_t)1 << 31;
+  const int64_t strides[4] = {p.sk_t, p.sv_t, p.sq_t, p.sdo_t};
+  for (int64_t st : strides)
+    if (((int64_t)(p.T - 1) * st + p.D) * eb >= lim) return false;
+  return true;
+}
+
+template <int DT, int D, bool COORD, bool OFF32>
+hipError_t launch_both(const Params& p, hipStream_t s, int grid, int nblk) {
+  hipLaunchKernelGGL((gather_bwd_q_kernel<DT, D, COORD, 4, OFF32>), dim3(grid), dim3(kThreads), 0, s, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((gather_bwd_kv_kernel<DT, D, COORD, 4>), dim3(grid), dim3(kThreads), 0, s, p);
+  hipLaunchKernelGGL((gather_bwd_kv_kernel<DT, D, COORD, 4, OFF32>), dim3(grid), dim3(kThreads), 0, s, p);
   e = hipGetLastError();
   if (e != hipSuccess || !COORD) return e;
   hipLaunchKernelGGL(coord_param_reduce_kernel, dim3(p.H), dim3(256), 0, s, p.partials, p.B, p.H,
                      nblk, p.dgamma, p.dbeta);
   return hipGetLastError();
+}
+
+template <int DT, int D, bool COORD>
+hipError_t launch_one(const Params& p, hipStream_t s) {
+  constexpr int RPB = Geo<DT, D>::RPB;
+  const int nblk = (p.T + RPB - 1) / RPB;
+  const int grid = xcd_grid(p.B * p.H * nblk);
+  return fits_off32(p, Frag<DT>::BYTES) ? launch_both<DT, D, COORD, true>(p, s, grid, nblk)
+                                        : launch_both<DT, D, COORD, false>(p, s, grid, nblk);
 }
 
 template <int DT, bool COORD>

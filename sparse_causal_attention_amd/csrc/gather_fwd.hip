@@ -9,7 +9,8 @@
 // so the K or V rows one distance needs form one contiguous, fully coalesced
 // block of 64 x 16 bytes.  Scores are reduced across the lane group with DPP,
 // and the softmax over the row's neighbours runs online (running max, sum
-// and weighted value accumulator, rescaled once per group of G distances).
+// and weighted value accumulator; the accumulator is rescaled only when the
+// max grows by more than 2^8).
 // Work and traffic are proportional to the number of edges (page "Longer
 // Attention Span ...", abstract: work-optimal graph processing); no score
 // matrix and no gathered copy of K or V is ever formed.
@@ -31,12 +32,8 @@ struct Geo {
   static_assert(LG >= 1 && LG <= 32 && (LG & (LG - 1)) == 0, "row must span 1..32 lanes");
 };
 
-// Distance of slot t in the concatenated list [0, 1, ..., W-1, dil...].
-__device__ __forceinline__ int distance_of(const Params& p, int t) {
-  return t < p.W ? t : p.dil[t - p.W];
-}
 
-template <int DT, int D, bool COORD, int G>
+template <int DT, int D, bool COORD, int G, bool OFF32>
 __global__ __launch_bounds__(kThreads) void gather_fwd_kernel(Params p) {
   using F = Frag<DT>;
   using Gm = Geo<DT, D>;
@@ -48,15 +45,24 @@ __global__ __launch_bounds__(kThreads) void gather_fwd_kernel(Params p) {
   if (logical < 0) return;
   const int bh = logical / nblk, rb = logical - bh * nblk;
   const int b = bh / p.H, h = bh - b * p.H;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform
   const int sub = lane % LG;
-  int i = rb * RPB + wave * RPW + lane / LG;
+  const int i0w = rb * RPB + wave * RPW;  // first row of this wavefront
+  int i = i0w + lane / LG;
   const bool row_ok = i < p.T;
   if (!row_ok) i = p.T - 1;  // compute a valid row, store nothing
 
-  const char* kb = static_cast<const char*>(p.k) + (b * p.sk_b + h * p.sk_h) * EB + sub * 16;
-  const char* vb = static_cast<const char*>(p.v) + (b * p.sv_b + h * p.sv_h) * EB + sub * 16;
+  // uniform per-head bases; per-lane byte offsets of row i's fragment
+  const char* khead = static_cast<const char*>(p.k) + (b * p.sk_b + h * p.sk_h) * EB;
+  const char* vhead = static_cast<const char*>(p.v) + (b * p.sv_b + h * p.sv_h) * EB;
   const int64_t skt = p.sk_t * EB, svt = p.sv_t * EB;
+  int64_t kl = (int64_t)i * skt + sub * 16, vl = (int64_t)i * svt + sub * 16;
+  uint32_t kl32 = (uint32_t)kl, vl32 = (uint32_t)vl;
+  // opaque to the optimiser: keeps the per-distance address a scalar offset
+  // from this per-lane value instead of a re-derived 64-bit multiply
+  asm volatile("" : "+v"(kl32), "+v"(vl32), "+v"(kl), "+v"(vl));
+  const uint32_t sub16 = (uint32_t)sub * 16u;
 
   uint4 qraw = make_uint4(0u, 0u, 0u, 0u);  // q fragment as stored (dot operand)
   float cqi[3] = {0.f, 0.f, 0.f};
@@ -73,25 +79,35 @@ __global__ __launch_bounds__(kThreads) void gather_fwd_kernel(Params p) {
     ckb = p.ck + (int64_t)bh * p.T * 3;
   }
 
-  float m = -INFINITY, l = 0.f;
+  float m = -INFINITY, l = 0.f;  // running max (log2 units), row sum
   float acc[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
 
-  const int nd = p.W + p.n_dil;
-  for (int t0 = 0; t0 < nd; t0 += G) {
+  const int imax = i0w + RPW - 1 < p.T - 1 ? i0w + RPW - 1 : p.T - 1;
+  // One group of G distances (wave-uniform, ascending; kUnreachable past
+  // the end of the list): gather, score, online softmax, accumulate.
+  auto group = [&](const int (&dist)[G]) {
     int j[G];
     uint4 kraw[G], vraw[G];
     float s[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const int t = t0 + g;
-      j[g] = (t < nd) ? i - distance_of(p, t) : -1;
-      const int jj = j[g] < 0 ? 0 : j[g];  // clamped address, masked below
-      if constexpr (!COORD) kraw[g] = ld16(kb + jj * skt);
-      vraw[g] = ld16(vb + jj * svt);
+      j[g] = i - dist[g];
+      const bool ok = j[g] >= 0;
+      if constexpr (OFF32) {
+        const uint32_t ko = ok ? kl32 - (uint32_t)dist[g] * (uint32_t)skt : sub16;
+        const uint32_t vo = ok ? vl32 - (uint32_t)dist[g] * (uint32_t)svt : sub16;
+        if constexpr (!COORD) kraw[g] = ld16(khead + ko);
+        vraw[g] = ld16(vhead + vo);
+      } else {
+        const int64_t ko = ok ? kl - (int64_t)dist[g] * skt : (int64_t)sub16;
+        const int64_t vo = ok ? vl - (int64_t)dist[g] * svt : (int64_t)sub16;
+        if constexpr (!COORD) kraw[g] = ld16(khead + ko);
+        vraw[g] = ld16(vhead + vo);
+      }
       if constexpr (COORD) {
-        const float* c = ckb + (int64_t)jj * 3;
+        const float* c = ckb + (int64_t)(ok ? j[g] : 0) * 3;
         const float d0 = cqi[0] - c[0], d1 = cqi[1] - c[1], d2 = cqi[2] - c[2];
         s[g] = -gl2 * (d0 * d0 + d1 * d1 + d2 * d2);
       }
@@ -102,32 +118,50 @@ __global__ __launch_bounds__(kThreads) void gather_fwd_kernel(Params p) {
 #pragma unroll
       for (int g = 0; g < G; ++g) s[g] = group_sum<LG>(s[g]) * p.scale_log2;
     }
-    float mx = m;
+    float mx = -INFINITY;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       s[g] = j[g] >= 0 ? s[g] : -INFINITY;
       mx = fmaxf(mx, s[g]);
     }
-    const float mref = mx == -INFINITY ? 0.f : mx;
-    const float alpha = fast_exp2(m - mref);
-    float pg[G];
-    float psum = 0.f;
+    // Lazy rescale: the reference moves only when a score exceeds it by more
+    // than 8 (log2 units), so exponents stay <= 8 and rescaling is rare.
+    const bool grow = mx > m + 8.f;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float mnew = grow ? mx : m;
+      const float alpha = m == -INFINITY ? 0.f : fast_exp2(m - mnew);
+      l *= alpha;
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      pg[g] = fast_exp2(s[g] - mref);
-      psum += pg[g];
+      for (int e = 0; e < EPL; ++e) acc[e] *= alpha;
+      m = mnew;
     }
-    l = fmaf(l, alpha, psum);
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[e] *= alpha;
+    const float neg = m == -INFINITY ? 0.f : -m;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
+      const float pg = fast_exp2(s[g] + neg);
+      l += pg;
       float vf[EPL];
       F::unpack(vraw[g], vf);
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(pg[g], vf[e], acc[e]);
+      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(pg, vf[e], acc[e]);
     }
-    m = mx;
+  };
+
+  // the window: distances 0 .. W-1
+  const int wend = p.W < imax + 1 ? p.W : imax + 1;  // larger distances reach no row
+  for (int t0 = 0; t0 < wend; t0 += G) {
+    int dist[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) dist[g] = t0 + g < p.W ? t0 + g : kUnreachable;
+    group(dist);
+  }
+  // the long-range distances (ascending; the table is padded with kUnreachable)
+  for (int t0 = 0; t0 < p.n_dil; t0 += G) {
+    int dist[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) dist[g] = p.dil[t0 + g];
+    if (dist[0] > imax) break;  // no row of this wavefront reaches it, nor any later one
+    group(dist);
   }
 
   if (!row_ok) return;
@@ -143,12 +177,22 @@ __global__ __launch_bounds__(kThreads) void gather_fwd_kernel(Params p) {
   }
 }
 
+// Whether every gathered byte offset within one (batch, head) slice of k and
+// v fits in 31 bits, so addresses can be a uniform base plus a 32-bit offset.
+inline bool fits_off32(const Params& p, int eb) {
+  const int64_t lim = (int64_t)1 << 31;
+  return ((int64_t)(p.T - 1) * p.sk_t + p.D) * eb < lim && ((int64_t)(p.T - 1) * p.sv_t + p.D) * eb < lim;
+}
+
 template <int DT, int D, bool COORD>
 hipError_t launch_one(const Params& p, hipStream_t s) {
   constexpr int RPB = Geo<DT, D>::RPB;
   const int nblk = (p.T + RPB - 1) / RPB;
   const int grid = xcd_grid(p.B * p.H * nblk);
-  hipLaunchKernelGGL((gather_fwd_kernel<DT, D, COORD, 4>), dim3(grid), dim3(kThreads), 0, s, p);
+  if (fits_off32(p, Frag<DT>::BYTES))
+    hipLaunchKernelGGL((gather_fwd_kernel<DT, D, COORD, 4, true>), dim3(grid), dim3(kThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL((gather_fwd_kernel<DT, D, COORD, 4, false>), dim3(grid), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 

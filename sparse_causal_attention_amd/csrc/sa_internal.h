@@ -19,13 +19,17 @@ namespace sa {
 
 enum { DT_F32 = 0, DT_BF16 = 1 };  // same values as sa_dtype
 
+// Distance-table padding: larger than any row index, so a padded slot never
+// yields a key.  Kernels read the table in groups past n_dil.
+constexpr int32_t kUnreachable = 0x7fffffff;
+
 // Everything a kernel needs, passed by value as one kernel argument.  Row
 // addresses are base + b*s_b + h*s_h + t*s_t elements (D contiguous).
 struct Params {
   int32_t B, H, T, D;
   int32_t W;      // effective window
   int32_t n_dil;  // long-range distances
-  int32_t dil[SA_MAX_DILATED];
+  int32_t dil[SA_MAX_DILATED + 8];  // ascending, padded with kUnreachable
   float scale;       // dot-mode scale
   float scale_log2;  // scale * log2(e)
   int32_t grad_bf16; // dq/dk/dv stored as bf16 (else fp32)
