@@ -56,6 +56,19 @@ def _compile(src: str) -> str:
     return obj
 
 
+def source_digest() -> str:
+    """sha256 over every source and build flag that goes into libsa.so (used to
+    tell whether profiler counters were taken on the kernels as they are now)."""
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in sources() + headers():
+        h.update(os.path.relpath(f, ROOT).encode())
+        h.update(open(f, "rb").read())
+    h.update(" ".join(COMMON + DEVICE).encode())
+    return h.hexdigest()
+
+
 def stale() -> bool:
     if not os.path.exists(LIB):
         return True

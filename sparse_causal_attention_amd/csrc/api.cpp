@@ -92,8 +92,8 @@ void fill_common(sa::Params* p, const sa_graph* g, const sa_attn_desc* d) {
 hipStream_t as_stream(sa_stream s) { return reinterpret_cast<hipStream_t>(s); }
 
 const char* fwd_kernel_name(const sa_attn_desc* d, Path path) {
-  if (path == Path::Band) return "band_fwd_mfma_bf16";
-  return d->score == SA_SCORE_COORD ? "gather_fwd_coord" : "gather_fwd_dot";
+  if (path == Path::Band) return "band_fwd_kernel";
+  return d->score == SA_SCORE_COORD ? "gather_fwd_kernel(coord)" : "gather_fwd_kernel(dot)";
 }
 
 }  // namespace
@@ -222,10 +222,10 @@ extern "C" sa_status sa_describe_plan(const sa_graph* g, const sa_attn_desc* d, 
   if (which == 0) {
     txt = fwd_kernel_name(d, plan.path);
   } else if (plan.path == Path::Band) {
-    txt = "band_bwd_dq_mfma_bf16+band_bwd_dkdv_mfma_bf16";
+    txt = "band_bwd_kernel";
   } else {
-    txt = coord ? "gather_bwd_q_coord+gather_bwd_kv_coord+coord_param_reduce"
-                : "gather_bwd_q_dot+gather_bwd_kv_dot";
+    txt = coord ? "gather_bwd_q_kernel(coord)+gather_bwd_kv_kernel(coord)+coord_param_reduce_kernel"
+                : "gather_bwd_q_kernel(dot)+gather_bwd_kv_kernel(dot)";
   }
   snprintf(buf, cap, "%s", txt);
   return SA_OK;

@@ -133,4 +133,4 @@ def test_plan_selection():
     st, name = plan(g, desc(B=1, H=8, T=16384, D=64, dtype=1, algo=1), 1)
     assert st == 0 and name.startswith("gather_bwd")
     st, name = plan(g, desc(B=1, H=8, T=16384, D=64, dtype=1, score=1), 0)
-    assert st == 0 and name == "gather_fwd_coord"
+    assert st == 0 and name == "gather_fwd_kernel(coord)"
