@@ -22,7 +22,7 @@
 // per 32-key block are keys 8*(r/4) + 4*half + r%4.  The output is computed
 // transposed too, O^T = V^T P^T: P^T is the B operand, which lane l supplies
 // from its own score registers (keys in the order above), and V^T comes from
-// a transposed copy of the V tile in LDS.  Each lane therefore keeps the
+// the row-major V tile through the transposing LDS read.  Each lane keeps the
 // running max, sum and output accumulator of exactly one query row, and the
 // two lanes l, l+32 of a row combine with one cross-half exchange per tile.
 #include "device_util.h"
@@ -38,7 +38,6 @@ constexpr int kD = 64;
 constexpr int kBQ = 128;        // query rows per workgroup: 4 wavefronts x 32
 constexpr int kBK = 64;         // keys per LDS tile
 constexpr int kKRow = kD + 8;   // K tile row stride, bf16 elements (144 B)
-constexpr int kVRow = kBK + 4;  // V^T tile row stride, bf16 elements (136 B)
 constexpr int kThreads = 256;
 constexpr int kG = 2;           // long-range edges in flight per lane
 
@@ -63,8 +62,8 @@ __device__ __forceinline__ float dot8_bf16(const bf16x8& a, const uint4& b, floa
   return acc;
 }
 
-// Global -> register staging of one 64-key tile (K row-major, V as key
-// pairs for the transposed LDS copy), then register -> LDS.
+// Global -> register staging of one 64-key tile of K and V (4 threads per
+// row, 2 x 16 B each), then register -> LDS, both row-major.
 struct TileRegs {
   uint4 k0, k1, v0, v1;
 };
@@ -72,47 +71,36 @@ struct TileRegs {
 __device__ __forceinline__ void tile_load(TileRegs& t, const char* kbase, const char* vbase, int64_t skt,
                                           int64_t svt, int kt0, int T) {
   const int tid = threadIdx.x;
-  {  // K: 4 threads per row, 2 x 16 B each
-    const int r = tid >> 2, c = (tid & 3) * 2;
-    const int key = kt0 + r < T ? kt0 + r : T - 1;
-    t.k0 = ld16(kbase + key * skt + c * 16);
-    t.k1 = ld16(kbase + key * skt + (c + 1) * 16);
-  }
-  {  // V: key pair (2 kp, 2 kp + 1), 16-byte chunk c
-    const int kp = tid >> 3, c = tid & 7;
-    const int k0 = kt0 + 2 * kp < T ? kt0 + 2 * kp : T - 1;
-    const int k1 = kt0 + 2 * kp + 1 < T ? kt0 + 2 * kp + 1 : T - 1;
-    t.v0 = ld16(vbase + k0 * svt + c * 16);
-    t.v1 = ld16(vbase + k1 * svt + c * 16);
-  }
+  const int r = tid >> 2, c = (tid & 3) * 2;
+  const int key = kt0 + r < T ? kt0 + r : T - 1;
+  t.k0 = ld16(kbase + key * skt + c * 16);
+  t.k1 = ld16(kbase + key * skt + (c + 1) * 16);
+  t.v0 = ld16(vbase + key * svt + c * 16);
+  t.v1 = ld16(vbase + key * svt + (c + 1) * 16);
 }
 
-__device__ __forceinline__ void tile_store(const TileRegs& t, __bf16* Ks, __bf16* Vt) {
+__device__ __forceinline__ void tile_store(const TileRegs& t, __bf16* Ks, __bf16* Vs) {
   const int tid = threadIdx.x;
-  {
-    const int r = tid >> 2, c = (tid & 3) * 2;
-    *reinterpret_cast<uint4*>(&Ks[r * kKRow + c * 8]) = t.k0;
-    *reinterpret_cast<uint4*>(&Ks[r * kKRow + (c + 1) * 8]) = t.k1;
-  }
-  {
-    const int kp = tid >> 3, c = tid & 7;
-    const uint32_t a[4] = {t.v0.x, t.v0.y, t.v0.z, t.v0.w};
-    const uint32_t bb[4] = {t.v1.x, t.v1.y, t.v1.z, t.v1.w};
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      // elements 2w (low halves) and 2w + 1 (high halves) of the two keys
-      const uint32_t lo = (a[w] & 0xffffu) | (bb[w] << 16);
-      const uint32_t hi = (a[w] >> 16) | (bb[w] & 0xffff0000u);
-      *reinterpret_cast<uint32_t*>(&Vt[(c * 8 + 2 * w) * kVRow + 2 * kp]) = lo;
-      *reinterpret_cast<uint32_t*>(&Vt[(c * 8 + 2 * w + 1) * kVRow + 2 * kp]) = hi;
-    }
-  }
+  const int r = tid >> 2, c = (tid & 3) * 2;
+  *reinterpret_cast<uint4*>(&Ks[r * kKRow + c * 8]) = t.k0;
+  *reinterpret_cast<uint4*>(&Ks[r * kKRow + (c + 1) * 8]) = t.k1;
+  *reinterpret_cast<uint4*>(&Vs[r * kKRow + c * 8]) = t.v0;
+  *reinterpret_cast<uint4*>(&Vs[r * kKRow + (c + 1) * 8]) = t.v1;
+}
+
+// A operand V^T[d][key] for keys 16*ks + 4*half + {0..3} and + 8 + {0..3}
+// (the accumulator order of the score registers), d = d0 + l % 32, read from
+// the row-major V tile.
+__device__ __forceinline__ bf16x8 vt_operand(const __bf16* vs, int ks, int d0, int lane, int half) {
+  const uint2 x0 = lds_tr4(vs, kKRow, 16 * ks + 4 * half, d0, lane);
+  const uint2 x1 = lds_tr4(vs, kKRow, 16 * ks + 8 + 4 * half, d0, lane);
+  return as_bf16x8(make_uint4(x0.x, x0.y, x1.x, x1.y));
 }
 
 template <bool HAS_DIL>
 __global__ __launch_bounds__(kThreads, 4) void band_fwd_kernel(Params p) {
   __shared__ __align__(16) __bf16 Ks[2][kBK * kKRow];
-  __shared__ __align__(16) __bf16 Vt[2][kD * kVRow];
+  __shared__ __align__(16) __bf16 Vs[2][kBK * kKRow];
 
   const int nblk = (p.T + kBQ - 1) / kBQ;
   const int logical = xcd_logical_block(p.B * p.H * nblk);
@@ -120,7 +108,8 @@ __global__ __launch_bounds__(kThreads, 4) void band_fwd_kernel(Params p) {
   const int bh = logical / nblk;
   const int rb = nblk - 1 - (logical - bh * nblk);  // late (longest) query blocks first
   const int b = bh / p.H, h = bh - b * p.H;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, half = lane >> 5;
   const int q0 = rb * kBQ;
   const int qw = q0 + wave * 32;
@@ -146,7 +135,7 @@ __global__ __launch_bounds__(kThreads, 4) void band_fwd_kernel(Params p) {
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) qf[kk] = as_bf16x8(ld16(qbase + mc * sqt + (16 * kk + 8 * half) * 2));
 
-  tile_store(pre, Ks[0], Vt[0]);
+  tile_store(pre, Ks[0], Vs[0]);
   if (ntiles > 1) tile_load(pre, kbase, vbase, skt, svt, kfirst + kBK, p.T);
   __syncthreads();
 
@@ -220,16 +209,12 @@ __global__ __launch_bounds__(kThreads, 4) void band_fwd_kernel(Params p) {
         for (int e = 0; e < 8; ++e) pb[e] = static_cast<__bf16>(sacc[8 * h2 + e]);
         const int ks4 = 2 * nb + h2;
 #pragma unroll
-        for (int dblk = 0; dblk < 2; ++dblk) {
-          const __bf16* row = &Vt[cur][(dblk * 32 + l32) * kVRow + 16 * ks4 + 4 * half];
-          const uint2 x0 = *reinterpret_cast<const uint2*>(row);
-          const uint2 x1 = *reinterpret_cast<const uint2*>(row + 8);
-          oacc[dblk] = mfma32(as_bf16x8(make_uint4(x0.x, x0.y, x1.x, x1.y)), pb, oacc[dblk]);
-        }
+        for (int dblk = 0; dblk < 2; ++dblk)
+          oacc[dblk] = mfma32(vt_operand(Vs[cur], ks4, dblk * 32, lane, half), pb, oacc[dblk]);
       }
     }
     if (it + 1 < ntiles) {
-      tile_store(pre, Ks[cur ^ 1], Vt[cur ^ 1]);  // last read in iteration it - 1
+      tile_store(pre, Ks[cur ^ 1], Vs[cur ^ 1]);  // last read in iteration it - 1
       if (it + 2 < ntiles) tile_load(pre, kbase, vbase, skt, svt, kt0 + 2 * kBK, p.T);
     }
     __syncthreads();

@@ -9,12 +9,13 @@
 //  dq role, one query row per lane (as in the forward):
 //    S^T = K Q^T,  dP^T = V dO^T   (K, V tiles row-major in LDS),
 //    P = exp(S - lse),  dS = P (dP - Delta),  Delta_i = <dout_i, o_i>,
-//    dq^T += K^T dS^T              (K^T tile in LDS; dS^T from registers).
+//    dq^T += K^T dS^T              (K^T read transposed from the K tile).
 //  dk/dv role, one key row per lane, over the reverse band (queries
 //  j .. j+W-1), computing the Delta of each staged query tile itself from
 //  its dO and o rows:
 //    S = Q K^T,  dP = dO V^T       (Q, dO tiles row-major in LDS),
-//    dv^T += dO^T P,  dk^T += Q^T dS   (Q^T, dO^T tiles in LDS).
+//    dv^T += dO^T P,  dk^T += Q^T dS   (Q^T, dO^T read transposed from the
+//    Q, dO tiles with ds_read_b64_tr_b16).
 // Lane layouts are those of v_mfma_f32_32x32x16_bf16 described in the
 // forward band kernel; P and dS enter the second product as B operands
 // straight from the score registers, with the contraction index ordered as
@@ -41,10 +42,8 @@ constexpr int kD = 64;
 constexpr int kRows = 128;        // rows (queries or keys) owned per workgroup
 constexpr int kTile = 64;         // streamed rows per LDS tile
 constexpr int kRow = kD + 8;      // row-major tile stride, bf16 (144 B)
-constexpr int kTRow = kTile + 4;  // transposed tile stride, bf16 (136 B)
 constexpr int kThreads = 256;
 constexpr int kRM = kTile * kRow;  // elements of a row-major tile
-constexpr int kTR = kD * kTRow;    // elements of a transposed tile
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8, u); }
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
@@ -70,31 +69,19 @@ __device__ __forceinline__ void pair_load(PairRegs& r, const char* base, int64_t
   r.b = ld16(base + x1 * st + c * 16);
 }
 
-__device__ __forceinline__ void pair_store(const PairRegs& r, __bf16* rm, __bf16* tr) {
+__device__ __forceinline__ void pair_store(const PairRegs& r, __bf16* rm) {
   const int tid = threadIdx.x;
   const int kp = tid >> 3, c = tid & 7;
-  if (rm != nullptr) {
-    *reinterpret_cast<uint4*>(&rm[(2 * kp) * kRow + c * 8]) = r.a;
-    *reinterpret_cast<uint4*>(&rm[(2 * kp + 1) * kRow + c * 8]) = r.b;
-  }
-  if (tr != nullptr) {
-    const uint32_t a[4] = {r.a.x, r.a.y, r.a.z, r.a.w};
-    const uint32_t b[4] = {r.b.x, r.b.y, r.b.z, r.b.w};
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      *reinterpret_cast<uint32_t*>(&tr[(c * 8 + 2 * w) * kTRow + 2 * kp]) = (a[w] & 0xffffu) | (b[w] << 16);
-      *reinterpret_cast<uint32_t*>(&tr[(c * 8 + 2 * w + 1) * kTRow + 2 * kp]) =
-          (a[w] >> 16) | (b[w] & 0xffff0000u);
-    }
-  }
+  *reinterpret_cast<uint4*>(&rm[(2 * kp) * kRow + c * 8]) = r.a;
+  *reinterpret_cast<uint4*>(&rm[(2 * kp + 1) * kRow + c * 8]) = r.b;
 }
 
-// A operand from a transposed tile: row d, the 16-row step ks in the
-// accumulator order (rows 16*ks + 4*half + {0..3} and + 8 + {0..3}).
-__device__ __forceinline__ bf16x8 tr_operand(const __bf16* tr, int d, int ks, int half) {
-  const __bf16* row = &tr[d * kTRow + 16 * ks + 4 * half];
-  const uint2 x0 = *reinterpret_cast<const uint2*>(row);
-  const uint2 x1 = *reinterpret_cast<const uint2*>(row + 8);
+// A operand X^T[d][row] of a row-major [row][d] tile for the 16-row step ks
+// in the accumulator order (rows 16*ks + 4*half + {0..3} and + 8 + {0..3}),
+// d = d0 + l % 32, through the transposing LDS read.
+__device__ __forceinline__ bf16x8 tr_operand(const __bf16* rm, int ks, int d0, int lane, int half) {
+  const uint2 x0 = lds_tr4(rm, kRow, 16 * ks + 4 * half, d0, lane);
+  const uint2 x1 = lds_tr4(rm, kRow, 16 * ks + 8 + 4 * half, d0, lane);
   return as_bf16x8(make_uint4(x0.x, x0.y, x1.x, x1.y));
 }
 
@@ -131,14 +118,12 @@ __device__ __forceinline__ void store_acc_row(void* base, int64_t off_elems, con
 // LDS of the dq role, carved from the kernel's shared buffer
 struct DqSmem {
   __bf16 Ks[2][kRM];
-  __bf16 Kt[2][kTR];
   __bf16 Vs[2][kRM];
 };
 
 template <bool GRAD_BF16, bool HAS_DIL>
 __device__ __forceinline__ void dq_role(const Params& p, int logical, int nblk, DqSmem& sm) {
   auto& Ks = sm.Ks;
-  auto& Kt = sm.Kt;
   auto& Vs = sm.Vs;
   const int bh = logical / nblk;
   const int rb = nblk - 1 - (logical - bh * nblk);
@@ -183,8 +168,8 @@ __device__ __forceinline__ void dq_role(const Params& p, int logical, int nblk, 
   const float lse2 = p.lse[(int64_t)bh * p.T + mc] * kLog2e;
   const float sl2 = p.scale_log2;
 
-  pair_store(pk, Ks[0], Kt[0]);
-  pair_store(pv, Vs[0], nullptr);
+  pair_store(pk, Ks[0]);
+  pair_store(pv, Vs[0]);
   if (ntiles > 1) {
     pair_load(pk, kb, skt, kfirst + kTile, p.T);
     pair_load(pv, vb, svt, kfirst + kTile, p.T);
@@ -230,12 +215,12 @@ __device__ __forceinline__ void dq_role(const Params& p, int logical, int nblk, 
         for (int e = 0; e < 8; ++e) dsb[e] = static_cast<__bf16>(s[8 * h2 + e]);
 #pragma unroll
         for (int dblk = 0; dblk < 2; ++dblk)
-          acc[dblk] = mfma32(tr_operand(Kt[cur], dblk * 32 + l32, 2 * nb + h2, half), dsb, acc[dblk]);
+          acc[dblk] = mfma32(tr_operand(Ks[cur], 2 * nb + h2, dblk * 32, lane, half), dsb, acc[dblk]);
       }
     }
     if (it + 1 < ntiles) {
-      pair_store(pk, Ks[cur ^ 1], Kt[cur ^ 1]);
-      pair_store(pv, Vs[cur ^ 1], nullptr);
+      pair_store(pk, Ks[cur ^ 1]);
+      pair_store(pv, Vs[cur ^ 1]);
       if (it + 2 < ntiles) {
         pair_load(pk, kb, skt, kt0 + 2 * kTile, p.T);
         pair_load(pv, vb, svt, kt0 + 2 * kTile, p.T);
@@ -284,9 +269,7 @@ __device__ __forceinline__ void dq_role(const Params& p, int logical, int nblk, 
 // LDS of the dk/dv role
 struct DkvSmem {
   __bf16 Qs[2][kRM];
-  __bf16 Qt[2][kTR];
   __bf16 Ds[2][kRM];
-  __bf16 Dt[2][kTR];
   float Ls[2][kTile];
   float Dl[2][kTile];
 };
@@ -294,9 +277,7 @@ struct DkvSmem {
 template <bool GRAD_BF16, bool HAS_DIL>
 __device__ __forceinline__ void dkv_role(const Params& p, int logical, int nblk, DkvSmem& sm) {
   auto& Qs = sm.Qs;
-  auto& Qt = sm.Qt;
   auto& Ds = sm.Ds;
-  auto& Dt = sm.Dt;
   auto& Ls = sm.Ls;
   auto& Dl = sm.Dl;
   const int bh = logical / nblk;
@@ -336,8 +317,8 @@ __device__ __forceinline__ void dkv_role(const Params& p, int logical, int nblk,
     }
   };
   auto store_tile = [&](int buf) {
-    pair_store(pq, Qs[buf], Qt[buf]);
-    pair_store(pd, Ds[buf], Dt[buf]);
+    pair_store(pq, Qs[buf]);
+    pair_store(pd, Ds[buf]);
     // Delta of the tile's two rows of this thread: 8-element partial dots of
     // dout and o, summed over the 8 consecutive lanes holding those rows
     const float da = group_sum<8>(Frag<DT_BF16>::dot(pd.a, po.a, 0.f));
@@ -417,8 +398,8 @@ __device__ __forceinline__ void dkv_role(const Params& p, int logical, int nblk,
         }
 #pragma unroll
         for (int dblk = 0; dblk < 2; ++dblk) {
-          dv[dblk] = mfma32(tr_operand(Dt[cur], dblk * 32 + l32, 2 * mb + h2, half), pb, dv[dblk]);
-          dk[dblk] = mfma32(tr_operand(Qt[cur], dblk * 32 + l32, 2 * mb + h2, half), dsb, dk[dblk]);
+          dv[dblk] = mfma32(tr_operand(Ds[cur], 2 * mb + h2, dblk * 32, lane, half), pb, dv[dblk]);
+          dk[dblk] = mfma32(tr_operand(Qs[cur], 2 * mb + h2, dblk * 32, lane, half), dsb, dk[dblk]);
         }
       }
     }

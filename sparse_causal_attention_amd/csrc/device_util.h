@@ -134,6 +134,22 @@ __device__ __forceinline__ float group_sum(float x) {
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 
+// ---------------------------------------------------------------- transposing LDS read
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
+// i % 4 of the 64-bit reads of group lanes i/4, i/4 + 4, i/4 + 8, i/4 + 12.
+// Group lane s here reads 4 consecutive bf16 of row key0 + s/4 of a row-major
+// LDS tile, starting at column d0 + 16 * (group % 2) + 4 * (s % 4); lane l
+// therefore receives column d0 + l % 32 of rows key0 .. key0 + 3.
+__device__ __forceinline__ uint2 lds_tr4(const __bf16* tile, int row_stride, int key0, int d0, int lane) {
+  const int s = lane & 15, g = lane >> 4;
+  const __bf16* src = tile + (key0 + (s >> 2)) * row_stride + d0 + 16 * (g & 1) + 4 * (s & 3);
+  const v4i16_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)src);
+  return __builtin_bit_cast(uint2, r);
+}
+
 // ---------------------------------------------------------------- XCD-aware order
 // Workgroup b of a launch is dispatched to XCD (b mod 8).  Give each XCD a
 // contiguous run of the logical work order, so the (batch, head) slices one
