@@ -131,7 +131,7 @@ size_t workspace_bytes_for(const sa_attn_desc* d) {
   const int rpb = sa::gather_rows_per_block(d->dtype == SA_BF16 ? sa::DT_BF16 : sa::DT_F32,
                                             (int)d->D);
   const size_t nblk = (size_t)((d->T + rpb - 1) / rpb);
-  return align256(rows * sizeof(float)) + align256((size_t)d->B * d->H * nblk * 2 * sizeof(float));
+  return 2 * align256(rows * sizeof(float)) + align256((size_t)d->B * d->H * nblk * 2 * sizeof(float));
 }
 
 }  // namespace
@@ -196,8 +196,10 @@ extern "C" sa_status sa_bwd(const sa_graph* g, const sa_attn_desc* d, const void
   p.dcq = dcq; p.dck = dck; p.dgamma = dgamma; p.dbeta = dbeta;
   p.lse = const_cast<float*>(lse);
   char* ws = static_cast<char*>(workspace);
+  const size_t row_bytes = align256((size_t)d->B * d->H * d->T * sizeof(float));
   p.delta = reinterpret_cast<float*>(ws);
-  p.partials = reinterpret_cast<float*>(ws + align256((size_t)d->B * d->H * d->T * sizeof(float)));
+  p.lse2 = reinterpret_cast<float*>(ws + row_bytes);
+  p.partials = reinterpret_cast<float*>(ws + 2 * row_bytes);
   hipError_t e = plan.path == Path::Band
                      ? sa::launch_band_bwd(p, as_stream(stream))
                      : sa::launch_gather_bwd(p, d->dtype == SA_BF16 ? sa::DT_BF16 : sa::DT_F32,
@@ -222,7 +224,7 @@ extern "C" sa_status sa_describe_plan(const sa_graph* g, const sa_attn_desc* d, 
   if (which == 0) {
     txt = fwd_kernel_name(d, plan.path);
   } else if (plan.path == Path::Band) {
-    txt = "band_bwd_kernel";
+    txt = "band_bwd_prepass_kernel+band_bwd_kernel";
   } else {
     txt = coord ? "gather_bwd_q_kernel(coord)+gather_bwd_kv_kernel(coord)+coord_param_reduce_kernel"
                 : "gather_bwd_q_kernel(dot)+gather_bwd_kv_kernel(dot)";

@@ -37,7 +37,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kD = 64;
 constexpr int kBQ = 128;        // query rows per workgroup: 4 wavefronts x 32
 constexpr int kBK = 64;         // keys per LDS tile
-constexpr int kKRow = kD + 8;   // K tile row stride, bf16 elements (144 B)
 constexpr int kThreads = 256;
 constexpr int kG = 2;           // long-range edges in flight per lane
 
@@ -62,45 +61,19 @@ __device__ __forceinline__ float dot8_bf16(const bf16x8& a, const uint4& b, floa
   return acc;
 }
 
-// Global -> register staging of one 64-key tile of K and V (4 threads per
-// row, 2 x 16 B each), then register -> LDS, both row-major.
-struct TileRegs {
-  uint4 k0, k1, v0, v1;
-};
-
-__device__ __forceinline__ void tile_load(TileRegs& t, const char* kbase, const char* vbase, int64_t skt,
-                                          int64_t svt, int kt0, int T) {
-  const int tid = threadIdx.x;
-  const int r = tid >> 2, c = (tid & 3) * 2;
-  const int key = kt0 + r < T ? kt0 + r : T - 1;
-  t.k0 = ld16(kbase + key * skt + c * 16);
-  t.k1 = ld16(kbase + key * skt + (c + 1) * 16);
-  t.v0 = ld16(vbase + key * svt + c * 16);
-  t.v1 = ld16(vbase + key * svt + (c + 1) * 16);
-}
-
-__device__ __forceinline__ void tile_store(const TileRegs& t, __bf16* Ks, __bf16* Vs) {
-  const int tid = threadIdx.x;
-  const int r = tid >> 2, c = (tid & 3) * 2;
-  *reinterpret_cast<uint4*>(&Ks[r * kKRow + c * 8]) = t.k0;
-  *reinterpret_cast<uint4*>(&Ks[r * kKRow + (c + 1) * 8]) = t.k1;
-  *reinterpret_cast<uint4*>(&Vs[r * kKRow + c * 8]) = t.v0;
-  *reinterpret_cast<uint4*>(&Vs[r * kKRow + (c + 1) * 8]) = t.v1;
-}
-
 // A operand V^T[d][key] for keys 16*ks + 4*half + {0..3} and + 8 + {0..3}
 // (the accumulator order of the score registers), d = d0 + l % 32, read from
-// the row-major V tile.
-__device__ __forceinline__ bf16x8 vt_operand(const __bf16* vs, int ks, int d0, int lane, int half) {
-  const uint2 x0 = lds_tr4(vs, kKRow, 16 * ks + 4 * half, d0, lane);
-  const uint2 x1 = lds_tr4(vs, kKRow, 16 * ks + 8 + 4 * half, d0, lane);
+// the row-major V tile with the transposing LDS read.
+__device__ __forceinline__ bf16x8 vt_operand(const char* vs, int ks, int d0, int lane, int half) {
+  const uint2 x0 = tile_tr4(vs, 16 * ks + 4 * half, d0, lane);
+  const uint2 x1 = tile_tr4(vs, 16 * ks + 8 + 4 * half, d0, lane);
   return as_bf16x8(make_uint4(x0.x, x0.y, x1.x, x1.y));
 }
 
 template <bool HAS_DIL>
 __global__ __launch_bounds__(kThreads, 4) void band_fwd_kernel(Params p) {
-  __shared__ __align__(16) __bf16 Ks[2][kBK * kKRow];
-  __shared__ __align__(16) __bf16 Vs[2][kBK * kKRow];
+  __shared__ __align__(1024) char Ks[2][kTileBytes];  // [buffer] swizzled 64-key tiles
+  __shared__ __align__(1024) char Vs[2][kTileBytes];
 
   const int nblk = (p.T + kBQ - 1) / kBQ;
   const int logical = xcd_logical_block(p.B * p.H * nblk);
@@ -127,16 +100,15 @@ __global__ __launch_bounds__(kThreads, 4) void band_fwd_kernel(Params p) {
   const int kfirst = (lo / kBK) * kBK;
   const int ntiles = (hi - kfirst) / kBK + 1;
 
-  TileRegs pre;
-  tile_load(pre, kbase, vbase, skt, svt, kfirst, p.T);
+  tile_issue(kbase, skt, kfirst, p.T, Ks[0], wave, lane);
+  tile_issue(vbase, svt, kfirst, p.T, Vs[0], wave, lane);
 
   // Q^T as B operand: lane holds q[m][16*kk + 8*half + e]
   bf16x8 qf[4];
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) qf[kk] = as_bf16x8(ld16(qbase + mc * sqt + (16 * kk + 8 * half) * 2));
 
-  tile_store(pre, Ks[0], Vs[0]);
-  if (ntiles > 1) tile_load(pre, kbase, vbase, skt, svt, kfirst + kBK, p.T);
+  wait_vmem();
   __syncthreads();
 
   // running max (raw score units), row sum (this lane's keys), O^T accumulator
@@ -151,6 +123,10 @@ __global__ __launch_bounds__(kThreads, 4) void band_fwd_kernel(Params p) {
   for (int it = 0; it < ntiles; ++it) {
     const int cur = it & 1;
     const int kt0 = kfirst + it * kBK;
+    if (it + 1 < ntiles) {  // the other buffer was last read in iteration it - 1
+      tile_issue(kbase, skt, kt0 + kBK, p.T, Ks[cur ^ 1], wave, lane);
+      tile_issue(vbase, svt, kt0 + kBK, p.T, Vs[cur ^ 1], wave, lane);
+    }
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       const int nb0 = kt0 + nb * 32;
@@ -159,11 +135,11 @@ __global__ __launch_bounds__(kThreads, 4) void band_fwd_kernel(Params p) {
       const bool full = nb0 + 31 <= qw && qw + 31 - nb0 < W && qw + 31 < p.T;
       f32x16 sacc;
       {
-        const __bf16* krow = &Ks[cur][(nb * 32 + l32) * kKRow + 8 * half];
-        sacc = mfma32(*reinterpret_cast<const bf16x8*>(krow), qf[0], f32x16{});
+        const int kr = nb * 32 + l32;
+        sacc = mfma32(as_bf16x8(tile_ld16(Ks[cur], kr, half)), qf[0], f32x16{});
 #pragma unroll
         for (int kk = 1; kk < 4; ++kk)
-          sacc = mfma32(*reinterpret_cast<const bf16x8*>(krow + 16 * kk), qf[kk], sacc);
+          sacc = mfma32(as_bf16x8(tile_ld16(Ks[cur], kr, 2 * kk + half)), qf[kk], sacc);
       }
       if (!full) {
 #pragma unroll
@@ -213,10 +189,7 @@ __global__ __launch_bounds__(kThreads, 4) void band_fwd_kernel(Params p) {
           oacc[dblk] = mfma32(vt_operand(Vs[cur], ks4, dblk * 32, lane, half), pb, oacc[dblk]);
       }
     }
-    if (it + 1 < ntiles) {
-      tile_store(pre, Ks[cur ^ 1], Vs[cur ^ 1]);  // last read in iteration it - 1
-      if (it + 2 < ntiles) tile_load(pre, kbase, vbase, skt, svt, kt0 + 2 * kBK, p.T);
-    }
+    wait_vmem();  // this wavefront's share of the next tile has landed
     __syncthreads();
   }
 

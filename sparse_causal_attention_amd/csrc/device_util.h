@@ -150,6 +150,58 @@ __device__ __forceinline__ uint2 lds_tr4(const __bf16* tile, int row_stride, int
   return __builtin_bit_cast(uint2, r);
 }
 
+// ---------------------------------------------------------------- swizzled LDS tiles
+// A tile holds 64 rows of 64 bf16 (128 B per row, no padding).  Logical
+// 16-byte chunk c of row r sits at physical chunk c ^ f(r), f(r) = (r % 8) ^
+// (r / 8 % 2): 16 consecutive rows read at one logical chunk land in 16
+// distinct 16-byte bank groups, and the 4 consecutive rows of a transposing
+// read never collide either.  Tiles are filled by direct global -> LDS loads
+// (global_load_lds_dwordx4: lane L of an instruction writes bytes
+// [16 L, 16 L + 16) after the instruction's LDS base), so staging needs no
+// registers and no LDS store instructions.
+constexpr int kTileRows = 64;
+constexpr int kTileRowBytes = 128;
+constexpr int kTileBytes = kTileRows * kTileRowBytes;
+
+__device__ __forceinline__ int tile_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int tile_off(int r, int c) { return r * kTileRowBytes + ((c ^ tile_swz(r)) << 4); }
+
+// Issue the loads of rows [r0, r0 + 64) of a [T, 64] bf16 tensor (row stride
+// st bytes, rows past T clamped to T - 1) into `tile`.  Wavefront w of the
+// four loads rows 16 w .. 16 w + 15 with two instructions of 8 rows.
+__device__ __forceinline__ void tile_issue(const char* base, int64_t st, int r0, int T, char* tile, int wave,
+                                           int lane) {
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int row0 = wave * 16 + k * 8;  // first tile row written by this instruction
+    const int r = row0 + (lane >> 3);
+    const int c = (lane & 7) ^ tile_swz(r);  // logical chunk stored in this lane's slot
+    const int row = r0 + r < T ? r0 + r : T - 1;
+    __builtin_amdgcn_global_load_lds(static_cast<const void*>(base + row * st + c * 16),
+                                     (__attribute__((address_space(3))) void*)(tile + row0 * kTileRowBytes),
+                                     16, 0, 0);
+  }
+}
+
+// Wait for this wavefront's direct-to-LDS loads (and every other load).
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// 16-byte fragment: logical chunk c of tile row r.
+__device__ __forceinline__ uint4 tile_ld16(const char* tile, int r, int c) {
+  return *reinterpret_cast<const uint4*>(tile + tile_off(r, c));
+}
+
+// Transposing read from a swizzled tile (see lds_tr4): lane l receives
+// column d0 + l % 32 of rows key0 .. key0 + 3 (key0 a multiple of 4, d0 of 32).
+__device__ __forceinline__ uint2 tile_tr4(const char* tile, int key0, int d0, int lane) {
+  const int s = lane & 15, g = lane >> 4;
+  const int r = key0 + (s >> 2);
+  const int col = d0 + 16 * (g & 1) + 4 * (s & 3);
+  const char* src = tile + r * kTileRowBytes + (((col >> 3) ^ tile_swz(r)) << 4) + (col & 7) * 2;
+  const v4i16_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)src);
+  return __builtin_bit_cast(uint2, v);
+}
+
 // ---------------------------------------------------------------- XCD-aware order
 // Workgroup b of a launch is dispatched to XCD (b mod 8).  Give each XCD a
 // contiguous run of the logical work order, so the (batch, head) slices one

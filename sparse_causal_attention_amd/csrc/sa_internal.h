@@ -51,6 +51,7 @@ struct Params {
 
   float* lse;       // [B, H, T]
   float* delta;     // workspace [B, H, T]
+  float* lse2;      // workspace [B, H, T]: lse * log2(e) (band backward)
   float* partials;  // workspace [B, H, nblk_q, 2]
 };
 
