@@ -55,25 +55,36 @@ def edge_counts(w):
 
 
 def models(w, grad_bytes=4):
-    """Algorithmic bytes and flops per call for workload w (all heads)."""
+    """Algorithmic bytes and flops per call for workload w (all heads).
+
+    Two byte models: "compulsory" reads and writes every tensor once (the
+    floor); "gather" adds the K/V (forward) and K, V, Q, dO, LSE, Delta
+    (backward) rows fetched per long-range edge, with no credit for cache
+    reuse across queries.  Window edges are charged as compulsory: their rows
+    are contiguous and reused on chip."""
     E, Ed = edge_counts(w)
     rows = w.B * w.H * w.T
     eb = 2 if w.dtype_name == "bf16" else 4
     D = w.D
     if w.coord:
         # forward: c_q, c_k (12 B), v, o rows, lse; backward: + dout, dv, dcq, dck
-        fwd = rows * (12 + 12 + 2 * D * eb + 4) + w.B * w.H * Ed * (12 + D * eb)
-        bwd = rows * (12 + 12 + D * eb + D * eb + D * eb + 4 + D * grad_bytes + 12 + 12) + \
-            w.B * w.H * Ed * 2 * (12 + D * eb + 8)
+        fwd_c = rows * (12 + 12 + 2 * D * eb + 4)
+        fwd_e = Ed * (12 + D * eb)
+        bwd_c = rows * (12 + 12 + D * eb + D * eb + D * eb + 4 + D * grad_bytes + 12 + 12)
+        bwd_e = Ed * 2 * (12 + D * eb + 8)
         ffl = w.B * w.H * E * (2 * D + 11)
         bfl = w.B * w.H * E * (4 * D + 35)
     else:
-        fwd = rows * (4 * D * eb + 4) + w.B * w.H * Ed * 2 * D * eb
-        bwd = rows * (5 * D * eb + 4 + 3 * D * grad_bytes) + w.B * w.H * Ed * (4 * D * eb + 8)
+        fwd_c = rows * (4 * D * eb + 4)
+        fwd_e = Ed * 2 * D * eb
+        bwd_c = rows * (5 * D * eb + 4 + 3 * D * grad_bytes)
+        bwd_e = Ed * (4 * D * eb + 8)
         ffl = w.B * w.H * E * 4 * D
         bfl = w.B * w.H * E * 10 * D
-    return {"edges": w.B * w.H * E, "fwd_bytes": fwd, "bwd_bytes": bwd, "fwd_flops": ffl,
-            "bwd_flops": bfl}
+    bh = w.B * w.H
+    return {"edges": bh * E, "fwd_bytes": fwd_c + bh * fwd_e, "bwd_bytes": bwd_c + bh * bwd_e,
+            "fwd_bytes_compulsory": fwd_c, "bwd_bytes_compulsory": bwd_c,
+            "fwd_flops": ffl, "bwd_flops": bfl}
 
 
 # ------------------------------------------------------------------ timing
@@ -200,20 +211,28 @@ def measured_traffic(workload, kernel):
 
 
 def roofline_for(w, r, m):
-    """Roofline entry for the longer of the two calls (on the band path each
-    call is one kernel launch)."""
+    """Roofline entry for the longer of the two calls.  The fraction is taken
+    against the gather byte model; where that exceeds 1 (rows reused from
+    cache), against the compulsory bytes instead, and `model` says which."""
     use_bwd = r["bwd_ms"] > r["fwd_ms"]
     ms = r["bwd_ms"] if use_bwd else r["fwd_ms"]
-    byt = m["bwd_bytes"] if use_bwd else m["fwd_bytes"]
-    fl = m["bwd_flops"] if use_bwd else m["fwd_flops"]
-    kernel = r["plan_bwd"] if use_bwd else r["plan_fwd"]
+    call = "bwd" if use_bwd else "fwd"
+    byt_g = m[call + "_bytes"]
+    byt_c = m[call + "_bytes_compulsory"]
+    fl = m[call + "_flops"]
+    kernel = r["plan_" + call]
+    frac_g = byt_g / (ms * 1e6) / HBM_PEAK_GBS
+    frac_c = byt_c / (ms * 1e6) / HBM_PEAK_GBS
+    model = "gather" if frac_g <= 1.0 else "compulsory"
+    byt = byt_g if model == "gather" else byt_c
     achieved = byt / (ms * 1e6)
     return {
         "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w.name, kernel),
         "kernel": kernel,
-        "call": "sa_bwd" if use_bwd else "sa_fwd",
-        "avg_ms": round(ms, 5), "algorithmic_bytes": byt,
+        "call": "sa_" + call,
+        "avg_ms": round(ms, 5), "algorithmic_bytes": byt, "model": model,
+        "frac_gather_model": round(frac_g, 4), "frac_compulsory": round(frac_c, 4),
         "mfma_bf16_frac": round(fl / (ms * 1e9) / MFMA_BF16_PEAK_TFS, 4),
     }
 

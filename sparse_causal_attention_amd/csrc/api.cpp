@@ -7,6 +7,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "sa_internal.h"
 
 namespace {
@@ -198,6 +200,7 @@ extern "C" sa_status sa_bwd(const sa_graph* g, const sa_attn_desc* d, const void
   char* ws = static_cast<char*>(workspace);
   const size_t row_bytes = align256((size_t)d->B * d->H * d->T * sizeof(float));
   p.delta = reinterpret_cast<float*>(ws);
+  p.ndelta = p.delta;
   p.lse2 = reinterpret_cast<float*>(ws + row_bytes);
   p.partials = reinterpret_cast<float*>(ws + 2 * row_bytes);
   hipError_t e = plan.path == Path::Band
@@ -244,3 +247,18 @@ extern "C" const char* sa_status_str(sa_status s) {
   }
   return "unknown status";
 }
+
+namespace sa {
+int device_cu_count() {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<int> cached[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  const int slot = dev < kMaxDevices ? dev : kMaxDevices - 1;
+  int n = cached[slot].load(std::memory_order_relaxed);
+  if (n > 0) return n;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+  cached[slot].store(n, std::memory_order_relaxed);
+  return n;
+}
+}  // namespace sa

@@ -46,7 +46,6 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float xhalf(float x) { return __shfl_xor(x, 32, 64); }
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
@@ -64,16 +63,20 @@ __device__ __forceinline__ float dot8_bf16(const bf16x8& a, const uint4& b, floa
 // A operand V^T[d][key] for keys 16*ks + 4*half + {0..3} and + 8 + {0..3}
 // (the accumulator order of the score registers), d = d0 + l % 32, read from
 // the row-major V tile with the transposing LDS read.
-__device__ __forceinline__ bf16x8 vt_operand(const char* vs, int ks, int d0, int lane, int half) {
-  const uint2 x0 = tile_tr4(vs, 16 * ks + 4 * half, d0, lane);
-  const uint2 x1 = tile_tr4(vs, 16 * ks + 8 + 4 * half, d0, lane);
+__device__ __forceinline__ bf16x8 vt_operand(const char* vs, const TileLane& tl, int ks, int d0) {
+  const uint2 x0 = tile_tr4(vs, tl, 16 * ks, d0);
+  const uint2 x1 = tile_tr4(vs, tl, 16 * ks + 8, d0);
   return as_bf16x8(make_uint4(x0.x, x0.y, x1.x, x1.y));
 }
 
 template <bool HAS_DIL>
 __global__ __launch_bounds__(kThreads, 4) void band_fwd_kernel(Params p) {
-  __shared__ __align__(1024) char Ks[2][kTileBytes];  // [buffer] swizzled 64-key tiles
-  __shared__ __align__(1024) char Vs[2][kTileBytes];
+  // Two buffers of swizzled 64-key tiles, each its own LDS object: the loads
+  // into one buffer are then known not to alias the reads of the other, so
+  // no wait for the tile in flight is placed before the reads of the tile
+  // being computed.
+  __shared__ __align__(16) char K0[kTileBytes], V0[kTileBytes];
+  __shared__ __align__(16) char K1[kTileBytes], V1[kTileBytes];
 
   const int nblk = (p.T + kBQ - 1) / kBQ;
   const int logical = xcd_logical_block(p.B * p.H * nblk);
@@ -84,6 +87,7 @@ __global__ __launch_bounds__(kThreads, 4) void band_fwd_kernel(Params p) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, half = lane >> 5;
+  const TileLane tl = tile_lane(lane);
   const int q0 = rb * kBQ;
   const int qw = q0 + wave * 32;
   const int m = qw + l32;
@@ -100,8 +104,8 @@ __global__ __launch_bounds__(kThreads, 4) void band_fwd_kernel(Params p) {
   const int kfirst = (lo / kBK) * kBK;
   const int ntiles = (hi - kfirst) / kBK + 1;
 
-  tile_issue(kbase, skt, kfirst, p.T, Ks[0], wave, lane);
-  tile_issue(vbase, svt, kfirst, p.T, Vs[0], wave, lane);
+  tile_issue(kbase, skt, kfirst, p.T, K0, wave, lane);
+  tile_issue(vbase, svt, kfirst, p.T, V0, wave, lane);
 
   // Q^T as B operand: lane holds q[m][16*kk + 8*half + e]
   bf16x8 qf[4];
@@ -120,12 +124,70 @@ __global__ __launch_bounds__(kThreads, 4) void band_fwd_kernel(Params p) {
   const int wlo = qw - W + 1, whi = qw + 31;  // this wavefront's key range
   const float sl2 = p.scale_log2;             // > 0
 
-  for (int it = 0; it < ntiles; ++it) {
-    const int cur = it & 1;
+  // One 32 x 32 block of (key, query) pairs; the band mask is applied unless
+  // every pair of the block lies inside the band.
+  auto block = [&](const char* ks, const char* vs, int nb, int nb0, bool full) {
+    f32x16 sacc;
+    sacc = mfma32(as_bf16x8(tile_ld16(ks, tl, nb * 32, 0)), qf[0], f32x16{});
+#pragma unroll
+    for (int kk = 1; kk < 4; ++kk) sacc = mfma32(as_bf16x8(tile_ld16(ks, tl, nb * 32, kk)), qf[kk], sacc);
+    if (!full) {
+      // key n = nb0 + 8 (r/4) + 4 half + r%4 is in the window iff 0 <= m - n < W
+      const int d = m - nb0 - 4 * half;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const bool ok = (uint32_t)(d - (8 * (r >> 2) + (r & 3))) < (uint32_t)W;
+        sacc[r] = ok ? sacc[r] : -INFINITY;
+      }
+    }
+    float tmax = sacc[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, sacc[r]);
+    tmax = max_halves(tmax);
+    // Lazy rescale: the reference max moves only when a score exceeds it by
+    // more than 8 (log2 units), so exponents stay <= 8 and the accumulator
+    // is rescaled rarely.
+    const bool grow = tmax * sl2 > mrun * sl2 + 8.f;
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+      const float mnew = grow ? tmax : mrun;
+      const float alpha = mrun == -INFINITY ? 0.f : fast_exp2((mrun - mnew) * sl2);
+      lrun *= alpha;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        oacc[0][r] *= alpha;
+        oacc[1][r] *= alpha;
+      }
+      mrun = mnew;
+    }
+    const float neg = mrun == -INFINITY ? 0.f : -mrun * sl2;  // no valid key yet: p = 0
+    float psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const float pv = fast_exp2(fmaf(sacc[r], sl2, neg));
+      sacc[r] = pv;
+      psum += pv;
+    }
+    lrun += psum;
+    // O^T += V^T P^T, 16 keys per step
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      bf16x8 pb;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) pb[e] = static_cast<__bf16>(sacc[8 * h2 + e]);
+      const int ks4 = 2 * nb + h2;
+#pragma unroll
+      for (int dblk = 0; dblk < 2; ++dblk)
+        oacc[dblk] = mfma32(vt_operand(vs, tl, ks4, dblk * 32), pb, oacc[dblk]);
+    }
+  };
+
+  // Tile `it` from (ks, vs) while the next one streams into (kn, vn), the
+  // buffers last read in tile it - 1.
+  auto tile = [&](int it, const char* ks, const char* vs, char* kn, char* vn) {
     const int kt0 = kfirst + it * kBK;
-    if (it + 1 < ntiles) {  // the other buffer was last read in iteration it - 1
-      tile_issue(kbase, skt, kt0 + kBK, p.T, Ks[cur ^ 1], wave, lane);
-      tile_issue(vbase, svt, kt0 + kBK, p.T, Vs[cur ^ 1], wave, lane);
+    if (it + 1 < ntiles) {
+      tile_issue(kbase, skt, kt0 + kBK, p.T, kn, wave, lane);
+      tile_issue(vbase, svt, kt0 + kBK, p.T, vn, wave, lane);
     }
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
@@ -133,64 +195,15 @@ __global__ __launch_bounds__(kThreads, 4) void band_fwd_kernel(Params p) {
       if (nb0 + 31 < wlo || nb0 > whi) continue;  // block outside this wavefront's band
       // every (query, key) of the 32 x 32 block inside the band
       const bool full = nb0 + 31 <= qw && qw + 31 - nb0 < W && qw + 31 < p.T;
-      f32x16 sacc;
-      {
-        const int kr = nb * 32 + l32;
-        sacc = mfma32(as_bf16x8(tile_ld16(Ks[cur], kr, half)), qf[0], f32x16{});
-#pragma unroll
-        for (int kk = 1; kk < 4; ++kk)
-          sacc = mfma32(as_bf16x8(tile_ld16(Ks[cur], kr, 2 * kk + half)), qf[kk], sacc);
-      }
-      if (!full) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int n = nb0 + 8 * (r >> 2) + 4 * half + (r & 3);
-          const bool ok = (n <= m) & (m - n < W);
-          sacc[r] = ok ? sacc[r] : -INFINITY;
-        }
-      }
-      float tmax = sacc[0];
-#pragma unroll
-      for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, sacc[r]);
-      tmax = fmaxf(tmax, xhalf(tmax));
-      // Lazy rescale: the reference max moves only when a score exceeds it by
-      // more than 8 (log2 units), so exponents stay <= 8 and the accumulator
-      // is rescaled rarely.
-      const bool grow = tmax * sl2 > mrun * sl2 + 8.f;
-      if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-        const float mnew = grow ? tmax : mrun;
-        const float alpha = mrun == -INFINITY ? 0.f : fast_exp2((mrun - mnew) * sl2);
-        lrun *= alpha;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          oacc[0][r] *= alpha;
-          oacc[1][r] *= alpha;
-        }
-        mrun = mnew;
-      }
-      const float neg = mrun == -INFINITY ? 0.f : -mrun * sl2;  // no valid key yet: p = 0
-      float psum = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float pv = fast_exp2(fmaf(sacc[r], sl2, neg));
-        sacc[r] = pv;
-        psum += pv;
-      }
-      lrun += psum;
-      // O^T += V^T P^T, 16 keys per step
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        bf16x8 pb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pb[e] = static_cast<__bf16>(sacc[8 * h2 + e]);
-        const int ks4 = 2 * nb + h2;
-#pragma unroll
-        for (int dblk = 0; dblk < 2; ++dblk)
-          oacc[dblk] = mfma32(vt_operand(Vs[cur], ks4, dblk * 32, lane, half), pb, oacc[dblk]);
-      }
+      block(ks, vs, nb, nb0, full);
     }
     wait_vmem();  // this wavefront's share of the next tile has landed
     __syncthreads();
+  };
+
+  for (int it = 0; it < ntiles; it += 2) {
+    tile(it, K0, V0, K1, V1);
+    if (it + 1 < ntiles) tile(it + 1, K1, V1, K0, V0);
   }
 
   // ---- long-range edges j = m - d: row gathers in the accumulator layout
@@ -222,7 +235,7 @@ __global__ __launch_bounds__(kThreads, 4) void band_fwd_kernel(Params p) {
       float tmax = -INFINITY;
 #pragma unroll
       for (int g = 0; g < kG; ++g) {
-        s[g] = s[g] + xhalf(s[g]);
+        s[g] = sum_halves(s[g]);
         s[g] = j[g] >= 0 ? s[g] : -INFINITY;
         tmax = fmaxf(tmax, s[g]);
       }
@@ -257,7 +270,7 @@ __global__ __launch_bounds__(kThreads, 4) void band_fwd_kernel(Params p) {
   }
 
   // ---- finish: O = acc / l, lse = m + log l (natural log)
-  const float ltot = lrun + xhalf(lrun);
+  const float ltot = sum_halves(lrun);
   if (m >= p.T) return;
   const float inv = 1.f / ltot;
   char* orow = static_cast<char*>(p.o) + (b * p.so_b + h * p.so_h + (int64_t)m * p.so_t) * 2;

@@ -1,17 +1,15 @@
 // Band backward: gradients of the sliding-window part on the bf16 matrix
 // cores, with the long-range edges of the same rows gathered in the same
-// kernel.  A small prepass writes Delta_i = <dout_i, o_i> and lse_i * log2(e)
-// per row; then one launch with two kinds of workgroup: a dq workgroup owns
-// 128 query rows, a dk/dv workgroup owns 128 key rows, so every output row has
-// exactly one writer (deterministic, no atomics).  The two kinds of the same
-// row block are adjacent in the launch order and so run on the same XCD,
-// where they share the K, V, Q, dO rows in L2.
+// kernel.  A small prepass writes -Delta_i = -<dout_i, o_i> and
+// lse_i * log2(e) per row; then one persistent launch works through units of
+// two kinds: a dq unit owns 128 query rows, a dk/dv unit owns 128 key rows,
+// so every output row has exactly one writer (deterministic, no atomics).
 //
-//  dq role, one query row per lane (as in the forward):
+//  dq unit, one query row per lane (as in the forward):
 //    S^T = K Q^T,  dP^T = V dO^T   (K, V tiles row-major in LDS),
 //    P = exp(S - lse),  dS = P (dP - Delta),  Delta_i = <dout_i, o_i>,
 //    dq^T += K^T dS^T              (K^T read transposed from the K tile).
-//  dk/dv role, one key row per lane, over the reverse band (queries
+//  dk/dv unit, one key row per lane, over the reverse band (queries
 //  j .. j+W-1):
 //    S = Q K^T,  dP = dO V^T       (Q, dO tiles row-major in LDS),
 //    dv^T += dO^T P,  dk^T += Q^T dS   (Q^T, dO^T read transposed from the
@@ -19,14 +17,23 @@
 // Lane layouts are those of v_mfma_f32_32x32x16_bf16 described in the
 // forward band kernel; P and dS enter the second product as B operands
 // straight from the score registers, with the contraction index ordered as
-// the accumulator rows (8*(r/4) + 4*half + r%4).
+// the accumulator rows (8*(r/4) + 4*half + r%4).  The dP products start from
+// -Delta, so dP - Delta comes out of the matrix cores.
 //
+// Scheduling.  The grid is a fixed number of workgroups (two per compute
+// unit).  Workgroup i of XCD x takes the (dq, dk/dv) unit pairs i, i + G,
+// i + 2G, ... of that XCD's contiguous share of row blocks (G workgroups per
+// XCD), so workgroups running side by side work on neighbouring row blocks
+// and share K, V, Q, dO rows in the XCD's L2; a dq unit and a dk/dv unit of
+// the same row block together have nearly the same work at every position.
 // Streamed 64-row tiles are double-buffered in LDS and filled by direct
-// global -> LDS loads into swizzled rows: the loads of tile t+1 are in flight
-// while tile t is computed, one barrier per tile, no staging registers.
-// Within a tile the two 32-row blocks are processed one after the other to
-// keep the score registers at 32 per lane; blocks wholly inside the band skip
-// the mask.
+// global -> LDS loads; the stream runs on across units: while a unit's last
+// tile is computed, the first tile of the next unit is loaded, together with
+// the next unit's per-row operands (into registers), so a workgroup never
+// waits for a unit's start-up loads.  Each unit's tile count is padded to an
+// even number so that every unit starts in the same buffer.  Within a tile the
+// two 32-row blocks are processed one after the other; blocks wholly inside
+// the band skip the mask.
 //
 // Delta_i = <dout_i, o_i> equals sum_j P_ij dP_ij up to the rounding of o;
 // with the dot-product score the resulting gradient error is far inside the
@@ -48,15 +55,14 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) { return __builtin_b
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ float xhalf(float x) { return __shfl_xor(x, 32, 64); }
 __device__ __forceinline__ float bf(const bf16x8& v, int e) { return static_cast<float>(v[e]); }
 
 // A operand X^T[d][row] of a row-major tile for the 16-row step ks in the
 // accumulator order (rows 16*ks + 4*half + {0..3} and + 8 + {0..3}),
 // d = d0 + l % 32, through the transposing LDS read.
-__device__ __forceinline__ bf16x8 tr_operand(const char* tile, int ks, int d0, int lane, int half) {
-  const uint2 x0 = tile_tr4(tile, 16 * ks + 4 * half, d0, lane);
-  const uint2 x1 = tile_tr4(tile, 16 * ks + 8 + 4 * half, d0, lane);
+__device__ __forceinline__ bf16x8 tr_operand(const char* tile, const TileLane& tl, int ks, int d0) {
+  const uint2 x0 = tile_tr4(tile, tl, 16 * ks, d0);
+  const uint2 x1 = tile_tr4(tile, tl, 16 * ks + 8, d0);
   return as_bf16x8(make_uint4(x0.x, x0.y, x1.x, x1.y));
 }
 
@@ -90,7 +96,9 @@ __device__ __forceinline__ void store_acc_row(void* base, int64_t off_elems, con
 }
 
 // ------------------------------------------------------------------ prepass
-// Delta_i = <dout_i, o_i> and lse_i * log2(e) for every row; 8 lanes per row.
+// -Delta_i = -<dout_i, o_i> and lse_i * log2(e) for every row; 8 lanes per
+// row.  The negated Delta is the initial accumulator of the dP products, so
+// dP - Delta leaves the matrix cores ready for dS = P (dP - Delta).
 __global__ __launch_bounds__(kThreads) void band_bwd_prepass_kernel(Params p) {
   const int rows_per_block = kThreads / 8;
   const int64_t gr = (int64_t)blockIdx.x * rows_per_block + (threadIdx.x >> 3);
@@ -105,110 +113,217 @@ __global__ __launch_bounds__(kThreads) void band_bwd_prepass_kernel(Params p) {
   const uint4 o = ld16(static_cast<const char*>(p.o) + (b * p.so_b + h * p.so_h + t * p.so_t) * 2 + sub * 16);
   const float delta = group_sum<8>(Frag<DT_BF16>::dot(d, o, 0.f));
   if (ok && sub == 0) {
-    p.delta[r] = delta;
+    p.ndelta[r] = -delta;
     p.lse2[r] = p.lse[r] * kLog2e;
   }
 }
 
-// ------------------------------------------------------------------ dq role
-struct DqSmem {
-  char Ks[2][kTileBytes];
-  char Vs[2][kTileBytes];
+// ------------------------------------------------------------------ units
+struct Unit {
+  int role;  // 0: dq, 1: dk/dv, -1: no unit
+  int b, h, bh;
+  int r0;    // first owned row: query (dq) or key (dk/dv)
+  int s0;    // first streamed row: key (dq) or query (dk/dv); a multiple of kTile
+  int nt;    // streamed tiles
 };
 
+__device__ __forceinline__ Unit make_unit(const Params& p, int pair, int role, int nblk) {
+  Unit u;
+  u.role = role;
+  u.bh = pair / nblk;
+  const int rb = pair - u.bh * nblk;
+  u.b = u.bh / p.H;
+  u.h = u.bh - u.b * p.H;
+  u.r0 = rb * kRows;
+  const int last = u.r0 + kRows - 1 < p.T - 1 ? u.r0 + kRows - 1 : p.T - 1;
+  if (role == 0) {  // keys max(0, r0 - W + 1) .. last
+    const int lo = u.r0 - p.W + 1 > 0 ? u.r0 - p.W + 1 : 0;
+    u.s0 = (lo / kTile) * kTile;
+    u.nt = (last - u.s0) / kTile + 1;
+  } else {  // queries r0 .. min(T - 1, last + W - 1)
+    const int qhi = last + p.W - 1 < p.T - 1 ? last + p.W - 1 : p.T - 1;
+    u.s0 = u.r0;
+    u.nt = (qhi - u.s0) / kTile + 1;
+  }
+  return u;
+}
+
+// Per-row operands of a lane's own row, held in registers for the whole
+// unit: Q and dO rows (dq) or K and V rows (dk/dv), as MFMA B operands
+// (elements 16 kk + 8 half .. + 7), and for dq the row's -Delta and
+// lse * log2(e).
+struct RowOps {
+  bf16x8 x[4], y[4];
+  float nd, l2;
+};
+
+__device__ __forceinline__ const char* tensor_base(const void* t, int64_t sb, int64_t sh, const Unit& u) {
+  return static_cast<const char*>(t) + (u.b * sb + u.h * sh) * 2;
+}
+
+// Direct loads of a tile's 64 per-row floats (one wavefront, 4 B per lane).
+__device__ __forceinline__ void rows_issue(const float* src, int r0, int T, float* dst, int lane) {
+  const int row = r0 + lane < T ? r0 + lane : T - 1;
+  __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + row),
+                                   (__attribute__((address_space(3))) void*)dst, 4, 0, 0);
+}
+
+// Issue the loads of streamed tile j of unit u: K, V rows (dq) or Q, dO rows
+// plus their lse * log2(e) and -Delta (dk/dv).
+__device__ __forceinline__ void issue_tile(const Params& p, const Unit& u, int j, char* a, char* bt, float* la,
+                                           float* lb) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r0 = u.s0 + j * kTile;
+  if (u.role == 0) {
+    tile_issue(tensor_base(p.k, p.sk_b, p.sk_h, u), p.sk_t * 2, r0, p.T, a, wave, lane);
+    tile_issue(tensor_base(p.v, p.sv_b, p.sv_h, u), p.sv_t * 2, r0, p.T, bt, wave, lane);
+  } else {
+    tile_issue(tensor_base(p.q, p.sq_b, p.sq_h, u), p.sq_t * 2, r0, p.T, a, wave, lane);
+    tile_issue(tensor_base(p.dout, p.sdo_b, p.sdo_h, u), p.sdo_t * 2, r0, p.T, bt, wave, lane);
+    if (wave == 0) rows_issue(p.lse2 + (int64_t)u.bh * p.T, r0, p.T, la, lane);
+    if (wave == 1) rows_issue(p.ndelta + (int64_t)u.bh * p.T, r0, p.T, lb, lane);
+  }
+}
+
+// Tile buffers: (a, b, la, lb) of buffer 0 and of buffer 1, and the row
+// stage (sx, sy, snd, sl2): 128 rows of the next unit's per-row operands.
+// Each its own LDS object (see band_bwd_kernel).
+struct Bufs {
+  char *a0, *b0, *a1, *b1;
+  float *la0, *lb0, *la1, *lb1;
+  char *sx, *sy;
+  float *snd, *sl2;
+};
+
+// Issue the loads of unit u's per-row operands into the row stage: rows
+// r0 .. r0 + 127 of Q and dO (dq) or K and V (dk/dv), and for dq their
+// -Delta and lse * log2(e).
+__device__ __forceinline__ void issue_stage(const Params& p, const Unit& u, const Bufs& bf) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const char *xb, *yb;
+  int64_t xs, ys;
+  if (u.role == 0) {
+    xb = tensor_base(p.q, p.sq_b, p.sq_h, u), xs = p.sq_t * 2;
+    yb = tensor_base(p.dout, p.sdo_b, p.sdo_h, u), ys = p.sdo_t * 2;
+    if (wave == 2) {
+      rows_issue(p.ndelta + (int64_t)u.bh * p.T, u.r0, p.T, bf.snd, lane);
+      rows_issue(p.ndelta + (int64_t)u.bh * p.T, u.r0 + 64, p.T, bf.snd + 64, lane);
+    }
+    if (wave == 3) {
+      rows_issue(p.lse2 + (int64_t)u.bh * p.T, u.r0, p.T, bf.sl2, lane);
+      rows_issue(p.lse2 + (int64_t)u.bh * p.T, u.r0 + 64, p.T, bf.sl2 + 64, lane);
+    }
+  } else {
+    xb = tensor_base(p.k, p.sk_b, p.sk_h, u), xs = p.sk_t * 2;
+    yb = tensor_base(p.v, p.sv_b, p.sv_h, u), ys = p.sv_t * 2;
+  }
+  tile_issue(xb, xs, u.r0, p.T, bf.sx, wave, lane);
+  tile_issue(xb, xs, u.r0 + kTile, p.T, bf.sx + kTileBytes, wave, lane);
+  tile_issue(yb, ys, u.r0, p.T, bf.sy, wave, lane);
+  tile_issue(yb, ys, u.r0 + kTile, p.T, bf.sy + kTileBytes, wave, lane);
+}
+
+// This lane's per-row operands from the row stage (row 32 wave + l % 32).
+__device__ __forceinline__ void read_stage(const Unit& u, const Bufs& bf, RowOps& r) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const TileLane tl = tile_lane(lane);
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    r.x[kk] = as_bf16x8(tile_ld16(bf.sx, tl, wave * 32, kk));
+    r.y[kk] = as_bf16x8(tile_ld16(bf.sy, tl, wave * 32, kk));
+  }
+  if (u.role == 0) {
+    r.nd = bf.snd[wave * 32 + (lane & 31)];
+    r.l2 = bf.sl2[wave * 32 + (lane & 31)];
+  } else {
+    r.nd = r.l2 = 0.f;
+  }
+}
+
+// ------------------------------------------------------------------ dq unit
 template <bool GRAD_BF16, bool HAS_DIL>
-__device__ __forceinline__ void dq_role(const Params& p, int logical, int nblk, DqSmem& sm) {
-  const int bh = logical / nblk;
-  const int rb = nblk - 1 - (logical - bh * nblk);
-  const int b = bh / p.H, h = bh - b * p.H;
+__device__ __forceinline__ void dq_unit(const Params& p, const Unit& u, const RowOps& ops, const Unit& nxt,
+                                        const Bufs& bf) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, half = lane >> 5;
-  const int q0 = rb * kRows, qw = q0 + wave * 32;
+  const TileLane tl = tile_lane(lane);
+  const int qw = u.r0 + wave * 32;
   const int m = qw + l32;
   const int mc = m < p.T ? m : p.T - 1;
-
-  const char* qb = static_cast<const char*>(p.q) + (b * p.sq_b + h * p.sq_h) * 2;
-  const char* kb = static_cast<const char*>(p.k) + (b * p.sk_b + h * p.sk_h) * 2;
-  const char* vb = static_cast<const char*>(p.v) + (b * p.sv_b + h * p.sv_h) * 2;
-  const char* dob = static_cast<const char*>(p.dout) + (b * p.sdo_b + h * p.sdo_h) * 2;
-  const int64_t sqt = p.sq_t * 2, skt = p.sk_t * 2, svt = p.sv_t * 2, sdot = p.sdo_t * 2;
   const int W = p.W;
-
-  const int lo = q0 - W + 1 > 0 ? q0 - W + 1 : 0;
-  const int hi = q0 + kRows - 1 < p.T - 1 ? q0 + kRows - 1 : p.T - 1;
-  const int kfirst = (lo / kTile) * kTile;
-  const int ntiles = (hi - kfirst) / kTile + 1;
-
-  tile_issue(kb, skt, kfirst, p.T, sm.Ks[0], wave, lane);
-  tile_issue(vb, svt, kfirst, p.T, sm.Vs[0], wave, lane);
-
-  bf16x8 qf[4], df[4];
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    const int off = (16 * kk + 8 * half) * 2;
-    qf[kk] = as_bf16x8(ld16(qb + mc * sqt + off));
-    df[kk] = as_bf16x8(ld16(dob + mc * sdot + off));
-  }
-  const float delta = p.delta[(int64_t)bh * p.T + mc];
-  const float lse2 = p.lse2[(int64_t)bh * p.T + mc];
   const float sl2 = p.scale_log2;
+  const int ntp = (u.nt + 1) & ~1;
 
+  f32x16 dp_init;  // -Delta of this lane's query row
+#pragma unroll
+  for (int r = 0; r < 16; ++r) dp_init[r] = ops.nd;
   f32x16 acc[2];
 #pragma unroll
   for (int r = 0; r < 16; ++r) acc[0][r] = acc[1][r] = 0.f;
   const int wlo = qw - W + 1, whi = qw + 31;
-  wait_vmem();
-  __syncthreads();
 
-  for (int it = 0; it < ntiles; ++it) {
-    const int cur = it & 1;
-    const int kt0 = kfirst + it * kTile;
-    if (it + 1 < ntiles) {  // the other buffer was last read in iteration it - 1
-      tile_issue(kb, skt, kt0 + kTile, p.T, sm.Ks[cur ^ 1], wave, lane);
-      tile_issue(vb, svt, kt0 + kTile, p.T, sm.Vs[cur ^ 1], wave, lane);
+  auto tile = [&](int it, const char* ks, const char* vs, char* kn, char* vn, float* lan, float* lbn) {
+    if (it + 1 < u.nt) {
+      issue_tile(p, u, it + 1, kn, vn, lan, lbn);  // (kn, vn) were last read in tile it - 1
+    } else if (it + 1 == ntp && nxt.role >= 0) {
+      issue_tile(p, nxt, 0, kn, vn, lan, lbn);  // buffer 0: the next unit's first tile
+      issue_stage(p, nxt, bf);                   // read at the start of this unit
+
     }
-    const char* ks = sm.Ks[cur];
-    const char* vs = sm.Vs[cur];
+    if (it < u.nt) {
+      const int kt0 = u.s0 + it * kTile;
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      const int nb0 = kt0 + nb * 32;
-      if (nb0 + 31 < wlo || nb0 > whi) continue;  // block outside this wavefront's band
-      const bool full = nb0 + 31 <= qw && qw + 31 - nb0 < W && qw + 31 < p.T;
-      const int kr = nb * 32 + l32;
-      f32x16 s = mfma32(as_bf16x8(tile_ld16(ks, kr, half)), qf[0], f32x16{});
-      f32x16 dp = mfma32(as_bf16x8(tile_ld16(vs, kr, half)), df[0], f32x16{});
+      for (int nb = 0; nb < 2; ++nb) {
+        const int nb0 = kt0 + nb * 32;
+        if (nb0 + 31 < wlo || nb0 > whi) continue;  // block outside this wavefront's band
+        const bool full = nb0 + 31 <= qw && qw + 31 - nb0 < W && qw + 31 < p.T;
+        f32x16 s = mfma32(as_bf16x8(tile_ld16(ks, tl, nb * 32, 0)), ops.x[0], f32x16{});
+        f32x16 dp = mfma32(as_bf16x8(tile_ld16(vs, tl, nb * 32, 0)), ops.y[0], dp_init);
 #pragma unroll
-      for (int kk = 1; kk < 4; ++kk) {
-        s = mfma32(as_bf16x8(tile_ld16(ks, kr, 2 * kk + half)), qf[kk], s);
-        dp = mfma32(as_bf16x8(tile_ld16(vs, kr, 2 * kk + half)), df[kk], dp);
-      }
-      // dS = P (dP - Delta)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pr = fast_exp2(fmaf(s[r], sl2, -lse2));
-        if (!full) {
-          const int n = nb0 + 8 * (r >> 2) + 4 * half + (r & 3);
-          pr = ((n <= m) & (m - n < W)) ? pr : 0.f;
+        for (int kk = 1; kk < 4; ++kk) {
+          s = mfma32(as_bf16x8(tile_ld16(ks, tl, nb * 32, kk)), ops.x[kk], s);
+          dp = mfma32(as_bf16x8(tile_ld16(vs, tl, nb * 32, kk)), ops.y[kk], dp);
         }
-        s[r] = pr * (dp[r] - delta);
-      }
+        // dS = P (dP - Delta); dp already holds dP - Delta
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        bf16x8 dsb;
+        for (int r = 0; r < 16; ++r) s[r] = fast_exp2(fmaf(s[r], sl2, -ops.l2));
+        if (!full) {
+          // key n = nb0 + 8 (r/4) + 4 half + r%4 is in the window iff 0 <= m - n < W
+          const int d = m - nb0 - 4 * half;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) dsb[e] = static_cast<__bf16>(s[8 * h2 + e]);
+          for (int r = 0; r < 16; ++r)
+            s[r] = (uint32_t)(d - (8 * (r >> 2) + (r & 3))) < (uint32_t)W ? s[r] : 0.f;
+        }
 #pragma unroll
-        for (int dblk = 0; dblk < 2; ++dblk)
-          acc[dblk] = mfma32(tr_operand(ks, 2 * nb + h2, dblk * 32, lane, half), dsb, acc[dblk]);
+        for (int r = 0; r < 16; ++r) s[r] = s[r] * dp[r];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          bf16x8 dsb;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) dsb[e] = static_cast<__bf16>(s[8 * h2 + e]);
+#pragma unroll
+          for (int dblk = 0; dblk < 2; ++dblk)
+            acc[dblk] = mfma32(tr_operand(ks, tl, 2 * nb + h2, dblk * 32), dsb, acc[dblk]);
+        }
       }
     }
     wait_vmem();
     __syncthreads();
+  };
+  for (int it = 0; it < ntp; it += 2) {
+    tile(it, bf.a0, bf.b0, bf.a1, bf.b1, bf.la1, bf.lb1);
+    tile(it + 1, bf.a1, bf.b1, bf.a0, bf.b0, bf.la0, bf.lb0);
   }
 
   if constexpr (HAS_DIL) {
     // long-range edges j = m - d
+    const char* kb = tensor_base(p.k, p.sk_b, p.sk_h, u);
+    const char* vb = tensor_base(p.v, p.sv_b, p.sv_h, u);
+    const int64_t skt = p.sk_t * 2, svt = p.sv_t * 2;
     for (int t = 0; t < p.n_dil; ++t) {
       const int j = mc - p.dil[t];
       const int jj = j < 0 ? 0 : j;
@@ -216,13 +331,13 @@ __device__ __forceinline__ void dq_role(const Params& p, int logical, int nblk, 
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const int off = (16 * kk + 8 * half) * 2;
-        sp = Frag<DT_BF16>::dot(__builtin_bit_cast(uint4, qf[kk]), ld16(kb + jj * skt + off), sp);
-        dpp = Frag<DT_BF16>::dot(__builtin_bit_cast(uint4, df[kk]), ld16(vb + jj * svt + off), dpp);
+        sp = Frag<DT_BF16>::dot(__builtin_bit_cast(uint4, ops.x[kk]), ld16(kb + jj * skt + off), sp);
+        dpp = Frag<DT_BF16>::dot(__builtin_bit_cast(uint4, ops.y[kk]), ld16(vb + jj * svt + off), dpp);
       }
-      sp += xhalf(sp);
-      dpp += xhalf(dpp);
-      const float pr = j >= 0 ? fast_exp2(fmaf(sp, sl2, -lse2)) : 0.f;
-      const float ds = pr * (dpp - delta);
+      sp = sum_halves(sp);
+      dpp = sum_halves(dpp);
+      const float pr = j >= 0 ? fast_exp2(fmaf(sp, sl2, -ops.l2)) : 0.f;
+      const float ds = pr * (dpp + ops.nd);
       uint2 kr[8];
 #pragma unroll
       for (int c = 0; c < 8; ++c)
@@ -234,136 +349,109 @@ __device__ __forceinline__ void dq_role(const Params& p, int logical, int nblk, 
     }
   }
 
-  if (m >= p.T) return;
-  store_acc_row<GRAD_BF16>(p.dq, b * p.sdq_b + h * p.sdq_h + (int64_t)m * p.sdq_t, acc, p.scale, half);
+  if (m < p.T)
+    store_acc_row<GRAD_BF16>(p.dq, u.b * p.sdq_b + u.h * p.sdq_h + (int64_t)m * p.sdq_t, acc, p.scale, half);
 }
 
-// ------------------------------------------------------------------ dk/dv role
-struct DkvSmem {
-  char Qs[2][kTileBytes];
-  char Ds[2][kTileBytes];
-  float Ls[2][kTile];  // lse * log2(e) of the tile's query rows
-  float Dl[2][kTile];  // Delta of the tile's query rows
-};
-
-// Direct loads of the tile's 64 per-row floats (one wavefront, 4 B per lane).
-__device__ __forceinline__ void rows_issue(const float* src, int r0, int T, float* dst, int lane) {
-  const int row = r0 + lane < T ? r0 + lane : T - 1;
-  __builtin_amdgcn_global_load_lds(static_cast<const void*>(src + row),
-                                   (__attribute__((address_space(3))) void*)dst, 4, 0, 0);
-}
-
+// ------------------------------------------------------------------ dk/dv unit
 template <bool GRAD_BF16, bool HAS_DIL>
-__device__ __forceinline__ void dkv_role(const Params& p, int logical, int nblk, DkvSmem& sm) {
-  const int bh = logical / nblk;
-  const int rb = logical - bh * nblk;  // early key blocks see the longest query ranges
-  const int b = bh / p.H, h = bh - b * p.H;
+__device__ __forceinline__ void dkv_unit(const Params& p, const Unit& u, const RowOps& ops, const Unit& nxt,
+                                         const Bufs& bf) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, half = lane >> 5;
-  const int k0 = rb * kRows, kw = k0 + wave * 32;
+  const TileLane tl = tile_lane(lane);
+  const int kw = u.r0 + wave * 32;
   const int n = kw + l32;
   const int nc = n < p.T ? n : p.T - 1;
-
-  const char* qb = static_cast<const char*>(p.q) + (b * p.sq_b + h * p.sq_h) * 2;
-  const char* kb = static_cast<const char*>(p.k) + (b * p.sk_b + h * p.sk_h) * 2;
-  const char* vb = static_cast<const char*>(p.v) + (b * p.sv_b + h * p.sv_h) * 2;
-  const char* dob = static_cast<const char*>(p.dout) + (b * p.sdo_b + h * p.sdo_h) * 2;
-  const int64_t sqt = p.sq_t * 2, skt = p.sk_t * 2, svt = p.sv_t * 2, sdot = p.sdo_t * 2;
-  const float* lseb = p.lse2 + (int64_t)bh * p.T;
-  const float* delb = p.delta + (int64_t)bh * p.T;
   const int W = p.W;
-
-  const int hi_key = k0 + kRows - 1 < p.T - 1 ? k0 + kRows - 1 : p.T - 1;
-  const int qhi = hi_key + W - 1 < p.T - 1 ? hi_key + W - 1 : p.T - 1;
-  const int mfirst = k0;  // a multiple of the tile height
-  const int ntiles = (qhi - mfirst) / kTile + 1;
-
-  auto issue = [&](int mt0, int buf) {
-    tile_issue(qb, sqt, mt0, p.T, sm.Qs[buf], wave, lane);
-    tile_issue(dob, sdot, mt0, p.T, sm.Ds[buf], wave, lane);
-    if (wave == 0) rows_issue(lseb, mt0, p.T, sm.Ls[buf], lane);
-    if (wave == 1) rows_issue(delb, mt0, p.T, sm.Dl[buf], lane);
-  };
-  issue(mfirst, 0);
-
-  bf16x8 kf[4], vf[4];
-#pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    const int off = (16 * kk + 8 * half) * 2;
-    kf[kk] = as_bf16x8(ld16(kb + nc * skt + off));
-    vf[kk] = as_bf16x8(ld16(vb + nc * svt + off));
-  }
   const float sl2 = p.scale_log2;
+  const int ntp = (u.nt + 1) & ~1;
+  // query mm is in the reverse band of key n iff 0 <= mm - n < min(W, T - n)
+  const int wn = W < p.T - n ? W : (p.T - n > 0 ? p.T - n : 0);
 
   f32x16 dk[2], dv[2];
 #pragma unroll
   for (int r = 0; r < 16; ++r) dk[0][r] = dk[1][r] = dv[0][r] = dv[1][r] = 0.f;
   const int wlo = kw, whi = kw + 31 + W - 1;  // this wavefront's query range
-  wait_vmem();
-  __syncthreads();
 
-  for (int it = 0; it < ntiles; ++it) {
-    const int cur = it & 1;
-    const int mt0 = mfirst + it * kTile;
-    if (it + 1 < ntiles) issue(mt0 + kTile, cur ^ 1);  // last read in iteration it - 1
-    const char* qs = sm.Qs[cur];
-    const char* ds = sm.Ds[cur];
+  auto tile = [&](int it, const char* qs, const char* ds, const float* ls, const float* es, char* qn, char* dn,
+                  float* ln, float* en) {
+    if (it + 1 < u.nt) {
+      issue_tile(p, u, it + 1, qn, dn, ln, en);  // last read in tile it - 1
+    } else if (it + 1 == ntp && nxt.role >= 0) {
+      issue_tile(p, nxt, 0, qn, dn, ln, en);  // buffer 0: the next unit's first tile
+      issue_stage(p, nxt, bf);
+    }
+    if (it < u.nt) {
+      const int mt0 = u.s0 + it * kTile;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      const int mb0 = mt0 + mb * 32;
-      if (mb0 + 31 < wlo || mb0 > whi) continue;
-      // every (query, key) of the block inside the band
-      const bool full = kw + 31 <= mb0 && mb0 + 31 - kw < W && mb0 + 31 < p.T;
-      const int qr = mb * 32 + l32;
-      f32x16 s = mfma32(as_bf16x8(tile_ld16(qs, qr, half)), kf[0], f32x16{});
-      f32x16 dp = mfma32(as_bf16x8(tile_ld16(ds, qr, half)), vf[0], f32x16{});
+      for (int mb = 0; mb < 2; ++mb) {
+        const int mb0 = mt0 + mb * 32;
+        if (mb0 + 31 < wlo || mb0 > whi) continue;
+        // every (query, key) of the block inside the band
+        const bool full = kw + 31 <= mb0 && mb0 + 31 - kw < W && mb0 + 31 < p.T;
+        // dP starts from -Delta of the block's query rows (row 8 (r/4) + 4 half + r%4)
+        f32x16 dp_init;
 #pragma unroll
-      for (int kk = 1; kk < 4; ++kk) {
-        s = mfma32(as_bf16x8(tile_ld16(qs, qr, 2 * kk + half)), kf[kk], s);
-        dp = mfma32(as_bf16x8(tile_ld16(ds, qr, 2 * kk + half)), vf[kk], dp);
-      }
-      // rows m = mb0 + 8 (r/4) + 4 half + r%4 of this lane's key column n
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const float4 d4 = *reinterpret_cast<const float4*>(&es[mb * 32 + 8 * g4 + 4 * half]);
 #pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int mi0 = mb * 32 + 8 * g4 + 4 * half;
-        const float4 l4 = *reinterpret_cast<const float4*>(&sm.Ls[cur][mi0]);
-        const float4 d4 = *reinterpret_cast<const float4*>(&sm.Dl[cur][mi0]);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-        const float dl[4] = {d4.x, d4.y, d4.z, d4.w};
+          for (int e = 0; e < 4; ++e) dp_init[4 * g4 + e] = (&d4.x)[e];
+        }
+        f32x16 s = mfma32(as_bf16x8(tile_ld16(qs, tl, mb * 32, 0)), ops.x[0], f32x16{});
+        f32x16 dp = mfma32(as_bf16x8(tile_ld16(ds, tl, mb * 32, 0)), ops.y[0], dp_init);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g4 + e;
-          float pr = fast_exp2(fmaf(s[r], sl2, -lv[e]));
-          if (!full) {
-            const int mm = mt0 + mi0 + e;
-            pr = ((n <= mm) & (mm - n < W) & (mm < p.T)) ? pr : 0.f;
+        for (int kk = 1; kk < 4; ++kk) {
+          s = mfma32(as_bf16x8(tile_ld16(qs, tl, mb * 32, kk)), ops.x[kk], s);
+          dp = mfma32(as_bf16x8(tile_ld16(ds, tl, mb * 32, kk)), ops.y[kk], dp);
+        }
+        // rows mm = mb0 + 8 (r/4) + 4 half + r%4 of this lane's key column n
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const float4 l4 = *reinterpret_cast<const float4*>(&ls[mb * 32 + 8 * g4 + 4 * half]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s[4 * g4 + e] = fast_exp2(fmaf(s[4 * g4 + e], sl2, -(&l4.x)[e]));
+        }
+        if (!full) {
+          const int d = mb0 + 4 * half - n;
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            s[r] = (uint32_t)(d + 8 * (r >> 2) + (r & 3)) < (uint32_t)wn ? s[r] : 0.f;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) dp[r] = s[r] * dp[r];  // dS = P (dP - Delta)
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          bf16x8 pb, dsb;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            pb[e] = static_cast<__bf16>(s[8 * h2 + e]);
+            dsb[e] = static_cast<__bf16>(dp[8 * h2 + e]);
           }
-          s[r] = pr;
-          dp[r] = pr * (dp[r] - dl[e]);
-        }
-      }
 #pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        bf16x8 pb, dsb;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          pb[e] = static_cast<__bf16>(s[8 * h2 + e]);
-          dsb[e] = static_cast<__bf16>(dp[8 * h2 + e]);
-        }
-#pragma unroll
-        for (int dblk = 0; dblk < 2; ++dblk) {
-          dv[dblk] = mfma32(tr_operand(ds, 2 * mb + h2, dblk * 32, lane, half), pb, dv[dblk]);
-          dk[dblk] = mfma32(tr_operand(qs, 2 * mb + h2, dblk * 32, lane, half), dsb, dk[dblk]);
+          for (int dblk = 0; dblk < 2; ++dblk) {
+            dv[dblk] = mfma32(tr_operand(ds, tl, 2 * mb + h2, dblk * 32), pb, dv[dblk]);
+            dk[dblk] = mfma32(tr_operand(qs, tl, 2 * mb + h2, dblk * 32), dsb, dk[dblk]);
+          }
         }
       }
     }
     wait_vmem();
     __syncthreads();
+  };
+  for (int it = 0; it < ntp; it += 2) {
+    tile(it, bf.a0, bf.b0, bf.la0, bf.lb0, bf.a1, bf.b1, bf.la1, bf.lb1);
+    tile(it + 1, bf.a1, bf.b1, bf.la1, bf.lb1, bf.a0, bf.b0, bf.la0, bf.lb0);
   }
 
   if constexpr (HAS_DIL) {
     // long-range edges: queries i = n + d
+    const char* qb = tensor_base(p.q, p.sq_b, p.sq_h, u);
+    const char* dob = tensor_base(p.dout, p.sdo_b, p.sdo_h, u);
+    const int64_t sqt = p.sq_t * 2, sdot = p.sdo_t * 2;
+    const float* lseb = p.lse2 + (int64_t)u.bh * p.T;
+    const float* ndelb = p.ndelta + (int64_t)u.bh * p.T;
     for (int t = 0; t < p.n_dil; ++t) {
       const bool ok = p.dil[t] <= p.T - 1 - nc;
       const int ii = ok ? nc + p.dil[t] : nc;
@@ -371,13 +459,13 @@ __device__ __forceinline__ void dkv_role(const Params& p, int logical, int nblk,
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
         const int off = (16 * kk + 8 * half) * 2;
-        sp = Frag<DT_BF16>::dot(ld16(qb + ii * sqt + off), __builtin_bit_cast(uint4, kf[kk]), sp);
-        dpp = Frag<DT_BF16>::dot(ld16(dob + ii * sdot + off), __builtin_bit_cast(uint4, vf[kk]), dpp);
+        sp = Frag<DT_BF16>::dot(ld16(qb + ii * sqt + off), __builtin_bit_cast(uint4, ops.x[kk]), sp);
+        dpp = Frag<DT_BF16>::dot(ld16(dob + ii * sdot + off), __builtin_bit_cast(uint4, ops.y[kk]), dpp);
       }
-      sp += xhalf(sp);
-      dpp += xhalf(dpp);
+      sp = sum_halves(sp);
+      dpp = sum_halves(dpp);
       const float pr = ok ? fast_exp2(fmaf(sp, sl2, -lseb[ii])) : 0.f;
-      const float ds = pr * (dpp - delb[ii]);
+      const float ds = pr * (dpp + ndelb[ii]);
       uint2 qr[8], dr[8];
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
@@ -395,24 +483,63 @@ __device__ __forceinline__ void dkv_role(const Params& p, int logical, int nblk,
     }
   }
 
-  if (n >= p.T) return;
-  store_acc_row<GRAD_BF16>(p.dv, b * p.sdv_b + h * p.sdv_h + (int64_t)n * p.sdv_t, dv, 1.f, half);
-  store_acc_row<GRAD_BF16>(p.dk, b * p.sdk_b + h * p.sdk_h + (int64_t)n * p.sdk_t, dk, p.scale, half);
+  if (n < p.T) {
+    store_acc_row<GRAD_BF16>(p.dv, u.b * p.sdv_b + u.h * p.sdv_h + (int64_t)n * p.sdv_t, dv, 1.f, half);
+    store_acc_row<GRAD_BF16>(p.dk, u.b * p.sdk_b + u.h * p.sdk_h + (int64_t)n * p.sdk_t, dk, p.scale, half);
+  }
 }
 
-constexpr size_t kSmemBytes = sizeof(DkvSmem) > sizeof(DqSmem) ? sizeof(DkvSmem) : sizeof(DqSmem);
-
+// ------------------------------------------------------------------ kernel
 template <bool GRAD_BF16, bool HAS_DIL>
 __global__ __launch_bounds__(kThreads, 2) void band_bwd_kernel(Params p) {
-  __shared__ __align__(1024) unsigned char smem[kSmemBytes];
+  // Double-buffered tiles shared by the two unit kinds.  Each buffer is its
+  // own LDS object, so the direct loads into one are known not to alias the
+  // reads of the other: no wait for the tile in flight is placed before the
+  // reads of the tile being computed.
+  __shared__ __align__(16) char t0a[kTileBytes], t0b[kTileBytes];
+  __shared__ __align__(16) char t1a[kTileBytes], t1b[kTileBytes];
+  __shared__ __align__(16) float r0a[kTile], r0b[kTile], r1a[kTile], r1b[kTile];
+  __shared__ __align__(16) char stx[2 * kTileBytes], sty[2 * kTileBytes];
+  __shared__ __align__(16) float stnd[kRows], stl2[kRows];
+  const Bufs bf{t0a, t0b, t1a, t1b, r0a, r0b, r1a, r1b, stx, sty, stnd, stl2};
+
   const int nblk = (p.T + kRows - 1) / kRows;
-  const int logical = xcd_logical_block(2 * p.B * p.H * nblk);
-  if (logical < 0) return;
-  // the dq and dk/dv workgroups of one row block are adjacent: same XCD
-  if ((logical & 1) == 0)
-    dq_role<GRAD_BF16, HAS_DIL>(p, logical >> 1, nblk, *reinterpret_cast<DqSmem*>(smem));
-  else
-    dkv_role<GRAD_BF16, HAS_DIL>(p, logical >> 1, nblk, *reinterpret_cast<DkvSmem*>(smem));
+  const int npairs = p.B * p.H * nblk;
+  const int per_xcd = (npairs + kNumXcd - 1) / kNumXcd;  // pairs of row blocks per XCD
+  const int xcd = blockIdx.x % kNumXcd, g = blockIdx.x / kNumXcd;
+  const int wgs_per_xcd = gridDim.x / kNumXcd;
+  const int pbeg = xcd * per_xcd;
+  const int pend = pbeg + per_xcd < npairs ? pbeg + per_xcd : npairs;
+  // unit k of this workgroup: pair pbeg + g + (k / 2) G, dq unit then dk/dv unit
+  auto unit_at = [&](int k) {
+    const int pair = pbeg + g + (k >> 1) * wgs_per_xcd;
+    Unit u;
+    if (pair < pend) {
+      u = make_unit(p, pair, k & 1, nblk);
+    } else {
+      u.role = -1;
+      u.b = u.h = u.bh = u.r0 = u.s0 = u.nt = 0;
+    }
+    return u;
+  };
+
+  Unit cur = unit_at(0);
+  if (cur.role < 0) return;  // uniform over the workgroup
+  issue_tile(p, cur, 0, bf.a0, bf.b0, bf.la0, bf.lb0);
+  issue_stage(p, cur, bf);
+  wait_vmem();
+  __syncthreads();
+  for (int k = 0;; ++k) {
+    const Unit nxt = unit_at(k + 1);
+    RowOps ops;
+    read_stage(cur, bf, ops);  // the stage is refilled only in this unit's last tile
+    if (cur.role == 0)
+      dq_unit<GRAD_BF16, HAS_DIL>(p, cur, ops, nxt, bf);
+    else
+      dkv_unit<GRAD_BF16, HAS_DIL>(p, cur, ops, nxt, bf);
+    if (nxt.role < 0) break;
+    cur = nxt;
+  }
 }
 
 template <bool GRAD_BF16, bool HAS_DIL>
@@ -424,7 +551,14 @@ hipError_t launch(const Params& p, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nblk = (p.T + kRows - 1) / kRows;
-  const int grid = xcd_grid(2 * p.B * p.H * nblk);
+  const int64_t npairs = (int64_t)p.B * p.H * nblk;
+  // two resident workgroups per compute unit, a multiple of the XCD count,
+  // no more than one per pair
+  int grid = 2 * device_cu_count();
+  const int64_t cap = ((npairs + kNumXcd - 1) / kNumXcd) * kNumXcd;
+  if (grid > cap) grid = (int)cap;
+  grid = (grid / kNumXcd) * kNumXcd;
+  if (grid < kNumXcd) grid = kNumXcd;
   hipLaunchKernelGGL((band_bwd_kernel<GRAD_BF16, HAS_DIL>), dim3(grid), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }

@@ -18,23 +18,33 @@ constexpr int kNumXcd = 8;  // MI355X: 8 accelerator complex dies, 32 CUs each
 __device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 
-// fp32 -> bf16 bits, round to nearest even (NaN kept quiet).
-__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16, round to nearest even (v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+  const bf16x2_t v = {static_cast<__bf16>(lo), static_cast<__bf16>(hi)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// ---------------------------------------------------------------- lane halves
+// v_permlane32_swap exchanges the upper 32 lanes of its first operand with
+// the lower 32 lanes of its second.  Applied to two copies of x, the two
+// results hold, in every lane l, x[l] and x[l ^ 32] (in some order), so the
+// sum or max over the lane pair (l, l ^ 32) is one more VALU operation, with
+// no LDS round trip.
+__device__ __forceinline__ float sum_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 // ---------------------------------------------------------------- element traits
 // A row fragment is the 16 bytes one lane owns: 8 bf16 or 4 fp32 elements.
 template <int DT>
 struct Frag;
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 template <>
 struct Frag<DT_F32> {
@@ -138,66 +148,75 @@ __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_lo
 typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) v4i16_t lds_v4i16_t;
 
-// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
-// i % 4 of the 64-bit reads of group lanes i/4, i/4 + 4, i/4 + 8, i/4 + 12.
-// Group lane s here reads 4 consecutive bf16 of row key0 + s/4 of a row-major
-// LDS tile, starting at column d0 + 16 * (group % 2) + 4 * (s % 4); lane l
-// therefore receives column d0 + l % 32 of rows key0 .. key0 + 3.
-__device__ __forceinline__ uint2 lds_tr4(const __bf16* tile, int row_stride, int key0, int d0, int lane) {
-  const int s = lane & 15, g = lane >> 4;
-  const __bf16* src = tile + (key0 + (s >> 2)) * row_stride + d0 + 16 * (g & 1) + 4 * (s & 3);
-  const v4i16_t r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)src);
-  return __builtin_bit_cast(uint2, r);
-}
-
-// ---------------------------------------------------------------- swizzled LDS tiles
-// A tile holds 64 rows of 64 bf16 (128 B per row, no padding).  Logical
-// 16-byte chunk c of row r sits at physical chunk c ^ f(r), f(r) = (r % 8) ^
-// (r / 8 % 2): 16 consecutive rows read at one logical chunk land in 16
-// distinct 16-byte bank groups, and the 4 consecutive rows of a transposing
-// read never collide either.  Tiles are filled by direct global -> LDS loads
-// (global_load_lds_dwordx4: lane L of an instruction writes bytes
-// [16 L, 16 L + 16) after the instruction's LDS base), so staging needs no
-// registers and no LDS store instructions.
+// ---------------------------------------------------------------- padded LDS tiles
+// A tile holds 64 rows of 64 bf16 at a row pitch of 144 bytes (128 bytes of
+// data, 16 of padding).  With a 36-dword pitch, 16 consecutive rows read at
+// one 16-byte chunk cover all 64 banks once, and every read address is one
+// per-lane base plus a compile-time offset (a single address register per
+// access pattern, whatever the row block, chunk or buffer).
+//
+// Tiles are filled by direct global -> LDS loads (global_load_lds_dwordx4:
+// lane L of an instruction writes bytes [16 L, 16 L + 16) after the
+// instruction's LDS base).  The tile is one stream of 576 16-byte slots,
+// nine per row (eight data chunks and the padding slot), so nine full
+// instructions fill it; a padding slot reloads the row's last chunk, which
+// lies in the same cache line.
 constexpr int kTileRows = 64;
-constexpr int kTileRowBytes = 128;
-constexpr int kTileBytes = kTileRows * kTileRowBytes;
-
-__device__ __forceinline__ int tile_swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
-__device__ __forceinline__ int tile_off(int r, int c) { return r * kTileRowBytes + ((c ^ tile_swz(r)) << 4); }
+constexpr int kTilePitch = 144;
+constexpr int kTileBytes = kTileRows * kTilePitch;
+constexpr int kTileSlots = kTileBytes / 16;  // 576 = 9 instructions of 64 lanes
 
 // Issue the loads of rows [r0, r0 + 64) of a [T, 64] bf16 tensor (row stride
-// st bytes, rows past T clamped to T - 1) into `tile`.  Wavefront w of the
-// four loads rows 16 w .. 16 w + 15 with two instructions of 8 rows.
+// st bytes, rows past T clamped to T - 1) into `tile`.  Instruction i of the
+// nine is issued by wavefront i % 4 of the workgroup's four.
 __device__ __forceinline__ void tile_issue(const char* base, int64_t st, int r0, int T, char* tile, int wave,
                                            int lane) {
 #pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int row0 = wave * 16 + k * 8;  // first tile row written by this instruction
-    const int r = row0 + (lane >> 3);
-    const int c = (lane & 7) ^ tile_swz(r);  // logical chunk stored in this lane's slot
+  for (int k = 0; k < 3; ++k) {
+    const int i = wave + 4 * k;
+    if (i >= kTileSlots / 64) break;  // wave-uniform
+    const int q = 64 * i + lane;      // slot index in the tile
+    const int r = q / 9, w = q - 9 * (q / 9);
+    const int c = w < 8 ? w : 7;
     const int row = r0 + r < T ? r0 + r : T - 1;
     __builtin_amdgcn_global_load_lds(static_cast<const void*>(base + row * st + c * 16),
-                                     (__attribute__((address_space(3))) void*)(tile + row0 * kTileRowBytes),
-                                     16, 0, 0);
+                                     (__attribute__((address_space(3))) void*)(tile + 1024 * i), 16, 0, 0);
   }
 }
 
 // Wait for this wavefront's direct-to-LDS loads (and every other load).
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// 16-byte fragment: logical chunk c of tile row r.
-__device__ __forceinline__ uint4 tile_ld16(const char* tile, int r, int c) {
-  return *reinterpret_cast<const uint4*>(tile + tile_off(r, c));
+// Per-lane byte offsets of the two tile read patterns.  They are computed
+// once and hidden from re-association, so every read below is one register
+// (tile + lane offset) plus an immediate offset.
+struct TileLane {
+  int row;  // row-major reads: row l % 32, chunk l / 32
+  int tr;   // transposing reads (see tile_tr4)
+};
+__device__ __forceinline__ TileLane tile_lane(int lane) {
+  const int s = lane & 15, g = lane >> 4, half = lane >> 5;
+  TileLane t;
+  t.row = (lane & 31) * kTilePitch + half * 16;
+  t.tr = ((s >> 2) + 4 * half) * kTilePitch + (16 * (g & 1) + 4 * (s & 3)) * 2;
+  asm volatile("" : "+v"(t.row), "+v"(t.tr));
+  return t;
 }
 
-// Transposing read from a swizzled tile (see lds_tr4): lane l receives
-// column d0 + l % 32 of rows key0 .. key0 + 3 (key0 a multiple of 4, d0 of 32).
-__device__ __forceinline__ uint2 tile_tr4(const char* tile, int key0, int d0, int lane) {
-  const int s = lane & 15, g = lane >> 4;
-  const int r = key0 + (s >> 2);
-  const int col = d0 + 16 * (g & 1) + 4 * (s & 3);
-  const char* src = tile + r * kTileRowBytes + (((col >> 3) ^ tile_swz(r)) << 4) + (col & 7) * 2;
+// 16-byte fragment of row row0 + l % 32, chunk 2 kk + l / 32 (row0 a
+// multiple of 32): the A operand rows of a 32 x 32 x 16 MFMA step kk.
+__device__ __forceinline__ uint4 tile_ld16(const char* tile, const TileLane& tl, int row0, int kk) {
+  return *reinterpret_cast<const uint4*>(tile + tl.row + row0 * kTilePitch + kk * 32);
+}
+
+// Transposing read (ds_read_b64_tr_b16: within each group of 16 lanes, lane i
+// receives element i % 4 of the 64-bit reads of group lanes i/4, i/4 + 4,
+// i/4 + 8, i/4 + 12).  Group lane s reads 4 bf16 of row key0 + 4 half + s/4
+// at column d0 + 16 (group % 2) + 4 (s % 4), so lane l receives column
+// d0 + l % 32 of rows key0 + 4 half .. key0 + 4 half + 3 (key0 a multiple of
+// 8, d0 of 32).
+__device__ __forceinline__ uint2 tile_tr4(const char* tile, const TileLane& tl, int key0, int d0) {
+  const char* src = tile + tl.tr + key0 * kTilePitch + d0 * 2;
   const v4i16_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_t*)src);
   return __builtin_bit_cast(uint2, v);
 }

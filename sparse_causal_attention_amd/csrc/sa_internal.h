@@ -50,7 +50,8 @@ struct Params {
   float* dgamma; float* dbeta;
 
   float* lse;       // [B, H, T]
-  float* delta;     // workspace [B, H, T]
+  float* delta;     // workspace [B, H, T]: Delta (gather backward)
+  float* ndelta;    // workspace [B, H, T]: -Delta (band backward; same region)
   float* lse2;      // workspace [B, H, T]: lse * log2(e) (band backward)
   float* partials;  // workspace [B, H, nblk_q, 2]
 };
@@ -64,6 +65,8 @@ int gather_rows_per_block(int dtype, int D);
 hipError_t launch_band_fwd(const Params& p, hipStream_t s);
 hipError_t launch_band_bwd(const Params& p, hipStream_t s);
 int band_rows_per_block();
+// Compute units of the current device (queried once per device).
+int device_cu_count();
 bool band_supported(int dtype, int D, bool coord, int64_t W);
 
 }  // namespace sa

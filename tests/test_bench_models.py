@@ -1,0 +1,49 @@
+"""The bench's work models on the CPU: edge counts from the closed form, and
+the per-call byte and flop figures at the five workloads (edge set and
+algorithmic work as defined by the neighbour graph: window {i-W+1..i} plus
+the long-range distances, each tensor once plus the rows fetched per
+long-range edge)."""
+import bench
+from sparse_causal_attention_amd.inputs import WORKLOADS
+
+import oracle
+
+
+def test_edge_counts_match_set_union_on_small_graph():
+    # the oracle's per-row set union, summed, equals the bench's closed form
+    from types import SimpleNamespace
+    for T, W, offs in [(256, 8, (16, 32, 64, 128)), (100, 3, (1, 2, 4, 8, 16, 32, 64, 128)), (50, 64, ())]:
+        w = SimpleNamespace(T=T, window=W, offsets=offs)
+        total = sum(len(oracle.row(T, W, offs, i)) for i in range(T))
+        long_range = sum(1 for i in range(T) for d in sorted(set(offs)) if min(W, T) <= d < T and i - d >= 0)
+        assert bench.edge_counts(w) == (total, long_range)
+
+
+def test_models_at_the_workloads():
+    MB = 1e6
+    band = bench.models(WORKLOADS["band"])
+    assert band["edges"] == 8 * 4161664
+    assert round(band["fwd_bytes"] / MB, 1) == 67.6 and round(band["bwd_bytes"] / MB, 1) == 185.1
+    assert band["fwd_bytes"] == band["fwd_bytes_compulsory"]  # no long-range edges
+    assert round(band["fwd_flops"] / 1e9, 2) == 8.52 and round(band["bwd_flops"] / 1e9, 2) == 21.31
+    dil = bench.models(WORKLOADS["dilated"])
+    assert dil["edges"] == 32 * 245758
+    assert round(dil["fwd_bytes_compulsory"] / MB, 1) == 270.5
+    assert round(dil["bwd_bytes_compulsory"] / MB, 1) == 740.3
+    # 32 slices x 180,228 long-range edges x (K + V rows of 128 B)
+    assert dil["fwd_bytes"] - dil["fwd_bytes_compulsory"] == 32 * 180228 * 256
+    assert dil["bwd_bytes"] - dil["bwd_bytes_compulsory"] == 32 * 180228 * 520
+    ultra = bench.models(WORKLOADS["ultra"])
+    assert ultra["edges"] == 5570033760
+
+
+def test_roofline_switches_to_compulsory_above_one():
+    w = WORKLOADS["dilated"]
+    m = bench.models(w)
+    # a forward call fast enough that the gather model would exceed the peak
+    r = {"fwd_ms": 0.1, "bwd_ms": 0.0, "plan_fwd": "k", "plan_bwd": None}
+    e = bench.roofline_for(w, r, m)
+    assert e["model"] == "compulsory" and e["frac_gather_model"] > 1.0
+    assert abs(e["frac"] - m["fwd_bytes_compulsory"] / 0.1e6 / bench.HBM_PEAK_GBS) < 1e-4
+    r = {"fwd_ms": 1.0, "bwd_ms": 0.0, "plan_fwd": "k", "plan_bwd": None}
+    assert bench.roofline_for(w, r, m)["model"] == "gather"
