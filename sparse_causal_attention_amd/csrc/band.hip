@@ -88,6 +88,7 @@ __global__ __launch_bounds__(kThreads, 4) void band_fwd_kernel(Params p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, half = lane >> 5;
   const TileLane tl = tile_lane(lane);
+  const DmaLane dl = dma_lane(wave, lane);
   const int q0 = rb * kBQ;
   const int qw = q0 + wave * 32;
   const int m = qw + l32;
@@ -104,8 +105,8 @@ __global__ __launch_bounds__(kThreads, 4) void band_fwd_kernel(Params p) {
   const int kfirst = (lo / kBK) * kBK;
   const int ntiles = (hi - kfirst) / kBK + 1;
 
-  tile_issue(kbase, skt, kfirst, p.T, K0, wave, lane);
-  tile_issue(vbase, svt, kfirst, p.T, V0, wave, lane);
+  tile_issue(kbase, skt, kfirst, p.T, K0, wave, dl);
+  tile_issue(vbase, svt, kfirst, p.T, V0, wave, dl);
 
   // Q^T as B operand: lane holds q[m][16*kk + 8*half + e]
   bf16x8 qf[4];
@@ -186,8 +187,8 @@ __global__ __launch_bounds__(kThreads, 4) void band_fwd_kernel(Params p) {
   auto tile = [&](int it, const char* ks, const char* vs, char* kn, char* vn) {
     const int kt0 = kfirst + it * kBK;
     if (it + 1 < ntiles) {
-      tile_issue(kbase, skt, kt0 + kBK, p.T, kn, wave, lane);
-      tile_issue(vbase, svt, kt0 + kBK, p.T, vn, wave, lane);
+      tile_issue(kbase, skt, kt0 + kBK, p.T, kn, wave, dl);
+      tile_issue(vbase, svt, kt0 + kBK, p.T, vn, wave, dl);
     }
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {

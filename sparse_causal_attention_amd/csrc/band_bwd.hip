@@ -176,11 +176,11 @@ __device__ __forceinline__ void issue_tile(const Params& p, const Unit& u, int j
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r0 = u.s0 + j * kTile;
   if (u.role == 0) {
-    tile_issue(tensor_base(p.k, p.sk_b, p.sk_h, u), p.sk_t * 2, r0, p.T, a, wave, lane);
-    tile_issue(tensor_base(p.v, p.sv_b, p.sv_h, u), p.sv_t * 2, r0, p.T, bt, wave, lane);
+    tile_issue_clamped(tensor_base(p.k, p.sk_b, p.sk_h, u), p.sk_t * 2, r0, p.T, a, wave, lane);
+    tile_issue_clamped(tensor_base(p.v, p.sv_b, p.sv_h, u), p.sv_t * 2, r0, p.T, bt, wave, lane);
   } else {
-    tile_issue(tensor_base(p.q, p.sq_b, p.sq_h, u), p.sq_t * 2, r0, p.T, a, wave, lane);
-    tile_issue(tensor_base(p.dout, p.sdo_b, p.sdo_h, u), p.sdo_t * 2, r0, p.T, bt, wave, lane);
+    tile_issue_clamped(tensor_base(p.q, p.sq_b, p.sq_h, u), p.sq_t * 2, r0, p.T, a, wave, lane);
+    tile_issue_clamped(tensor_base(p.dout, p.sdo_b, p.sdo_h, u), p.sdo_t * 2, r0, p.T, bt, wave, lane);
     if (wave == 0) rows_issue(p.lse2 + (int64_t)u.bh * p.T, r0, p.T, la, lane);
     if (wave == 1) rows_issue(p.ndelta + (int64_t)u.bh * p.T, r0, p.T, lb, lane);
   }
@@ -219,10 +219,10 @@ __device__ __forceinline__ void issue_stage(const Params& p, const Unit& u, cons
     xb = tensor_base(p.k, p.sk_b, p.sk_h, u), xs = p.sk_t * 2;
     yb = tensor_base(p.v, p.sv_b, p.sv_h, u), ys = p.sv_t * 2;
   }
-  tile_issue(xb, xs, u.r0, p.T, bf.sx, wave, lane);
-  tile_issue(xb, xs, u.r0 + kTile, p.T, bf.sx + kTileBytes, wave, lane);
-  tile_issue(yb, ys, u.r0, p.T, bf.sy, wave, lane);
-  tile_issue(yb, ys, u.r0 + kTile, p.T, bf.sy + kTileBytes, wave, lane);
+  tile_issue_clamped(xb, xs, u.r0, p.T, bf.sx, wave, lane);
+  tile_issue_clamped(xb, xs, u.r0 + kTile, p.T, bf.sx + kTileBytes, wave, lane);
+  tile_issue_clamped(yb, ys, u.r0, p.T, bf.sy, wave, lane);
+  tile_issue_clamped(yb, ys, u.r0 + kTile, p.T, bf.sy + kTileBytes, wave, lane);
 }
 
 // This lane's per-row operands from the row stage (row 32 wave + l % 32).

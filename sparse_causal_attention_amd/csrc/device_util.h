@@ -166,11 +166,60 @@ constexpr int kTilePitch = 144;
 constexpr int kTileBytes = kTileRows * kTilePitch;
 constexpr int kTileSlots = kTileBytes / 16;  // 576 = 9 instructions of 64 lanes
 
+// Slot assignment of this lane in the (at most three) load instructions its
+// wavefront issues per tile: instruction k writes slots 64 (wave + 4 k) +
+// lane, i.e. tile row r[k], 16-byte chunk c16[k] / 16 (the padding slot of a
+// row reloads its last chunk).  Computed once; opaque to re-derivation.
+struct DmaLane {
+  int r[3];
+  int c16[3];
+};
+__device__ __forceinline__ DmaLane dma_lane(int wave, int lane) {
+  DmaLane d;
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    const int q = 64 * (wave + 4 * k) + lane;  // slot index in the tile
+    const int r = q / 9, w = q - 9 * (q / 9);
+    d.r[k] = r;
+    d.c16[k] = (w < 8 ? w : 7) * 16;
+  }
+  asm volatile("" : "+v"(d.r[0]), "+v"(d.r[1]), "+v"(d.r[2]), "+v"(d.c16[0]), "+v"(d.c16[1]), "+v"(d.c16[2]));
+  return d;
+}
+
 // Issue the loads of rows [r0, r0 + 64) of a [T, 64] bf16 tensor (row stride
 // st bytes, rows past T clamped to T - 1) into `tile`.  Instruction i of the
-// nine is issued by wavefront i % 4 of the workgroup's four.
+// nine is issued by wavefront i % 4 of the workgroup's four.  A tile that
+// lies wholly inside the tensor takes one uniform base and a 32-bit per-lane
+// offset per instruction, from the precomputed slots `dl`.
 __device__ __forceinline__ void tile_issue(const char* base, int64_t st, int r0, int T, char* tile, int wave,
-                                           int lane) {
+                                           const DmaLane& dl) {
+  if (r0 + kTileRows <= T && st < (1 << 24)) {
+    const char* b = base + r0 * st;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      const int i = wave + 4 * k;
+      if (i >= kTileSlots / 64) break;  // wave-uniform
+      const uint32_t off = (uint32_t)(dl.r[k] * (int)st + dl.c16[k]);
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(b + off),
+                                       (__attribute__((address_space(3))) void*)(tile + 1024 * i), 16, 0, 0);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+      const int i = wave + 4 * k;
+      if (i >= kTileSlots / 64) break;  // wave-uniform
+      const int row = r0 + dl.r[k] < T ? r0 + dl.r[k] : T - 1;
+      __builtin_amdgcn_global_load_lds(static_cast<const void*>(base + row * st + dl.c16[k]),
+                                       (__attribute__((address_space(3))) void*)(tile + 1024 * i), 16, 0, 0);
+    }
+  }
+}
+
+// The same loads with every row index clamped and the slots derived on the
+// spot (no registers held between calls; for register-bound kernels).
+__device__ __forceinline__ void tile_issue_clamped(const char* base, int64_t st, int r0, int T, char* tile,
+                                                   int wave, int lane) {
 #pragma unroll
   for (int k = 0; k < 3; ++k) {
     const int i = wave + 4 * k;
