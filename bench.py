@@ -193,19 +193,23 @@ TRAFFIC_RECORD = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def measured_traffic(workload, kernel):
-    """HBM bytes per launch of `kernel` on `workload` from the committed
-    rocprofv3 --pmc record (FETCH_SIZE and WRITE_SIZE in KiB per dispatch, each
-    scaled by what the same counter reads for a plain 1 GiB device copy), or
-    None when there is no record or the kernels changed since it was taken."""
+    """HBM bytes per call of `kernel` (a plan name; "a+b" for a call of two
+    launches) on `workload` from the committed rocprofv3 --pmc record
+    (FETCH_SIZE and WRITE_SIZE in KiB per dispatch, each scaled by what the same
+    counter reads for a plain 1 GiB device copy), or None when there is no
+    record or the kernels changed since it was taken."""
     try:
         rec = json.load(open(TRAFFIC_RECORD))
         from sparse_causal_attention_amd.build import source_digest
         if rec.get("source_sha256") != source_digest():
             return None
-        e = rec["kernels"][workload][kernel]
         cf = rec["copy"]["bytes"] / (rec["copy"]["fetch_kib"] * 1024.0)
         cw = rec["copy"]["bytes"] / (rec["copy"]["write_kib"] * 1024.0)
-        return int(round((e["fetch_kib"] * cf + e["write_kib"] * cw) * 1024.0))
+        total = 0.0
+        for name in kernel.split("+"):  # a call of several launches: their sum
+            e = rec["kernels"][workload][name]
+            total += (e["fetch_kib"] * cf + e["write_kib"] * cw) * 1024.0
+        return int(round(total))
     except (OSError, KeyError, ValueError, TypeError, ZeroDivisionError):
         return None
 
