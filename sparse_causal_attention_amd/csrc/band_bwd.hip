@@ -530,6 +530,7 @@ __global__ __launch_bounds__(kThreads, 2) void band_bwd_kernel(Params p) {
   wait_vmem();
   __syncthreads();
   for (int k = 0;; ++k) {
+    progress_priority(k, 4);  // a workgroup takes about four units
     const Unit nxt = unit_at(k + 1);
     RowOps ops;
     read_stage(cur, bf, ops);  // the stage is refilled only in this unit's last tile

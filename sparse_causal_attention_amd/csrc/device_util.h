@@ -270,6 +270,22 @@ __device__ __forceinline__ uint2 tile_tr4(const char* tile, const TileLane& tl, 
   return __builtin_bit_cast(uint2, v);
 }
 
+// ---------------------------------------------------------------- progress priority
+// The SIMDs issue from the oldest ready wavefront first, so among the
+// workgroups that share a compute unit the youngest falls behind and the unit
+// idles while it finishes alone.  Wavefronts lower their issue priority as
+// they progress (level 3 at the start, 0 near the end; wave-uniform `done` of
+// `total`), so the workgroup that is behind gets the issue slots.
+__device__ __forceinline__ void progress_priority(int done, int total) {
+  const int level = 3 - (4 * done) / (total > 0 ? total : 1);
+  switch (level < 0 ? 0 : level) {
+    case 3: __builtin_amdgcn_s_setprio(3); break;
+    case 2: __builtin_amdgcn_s_setprio(2); break;
+    case 1: __builtin_amdgcn_s_setprio(1); break;
+    default: __builtin_amdgcn_s_setprio(0); break;
+  }
+}
+
 // ---------------------------------------------------------------- XCD-aware order
 // Workgroup b of a launch is dispatched to XCD (b mod 8).  Give each XCD a
 // contiguous run of the logical work order, so the (batch, head) slices one
