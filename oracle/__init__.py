@@ -32,7 +32,7 @@ _SRC = os.path.join(_HERE, "oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
 F64, F32, BF16 = 0, 1, 2
-SCORE_DOT, SCORE_COORD = 0, 1
+SCORE_DOT, SCORE_COORD, SCORE_UNIFORM = 0, 1, 2
 
 _lib = None
 
@@ -145,7 +145,8 @@ def graph_csr(T: int, W: int, offsets, r0: int = 0, r1: int | None = None):
 def fwd(T, W, offsets, v, q=None, k=None, cq=None, ck=None, gamma=0.0, beta=0.0,
         scale=None, rows=None):
     """One (batch, head) slice.  Dot mode when q, k are given, coordinate mode
-    when cq, ck are.  Returns (O [n, D] float64, LSE [n] float64)."""
+    when cq, ck are, uniform mode (equal weights) when neither is.  Returns
+    (O [n, D] float64, LSE [n] float64)."""
     o = _offs(offsets)
     v, vdt = _as_input(v)
     D = v.shape[-1]
@@ -156,6 +157,9 @@ def fwd(T, W, offsets, v, q=None, k=None, cq=None, ck=None, gamma=0.0, beta=0.0,
         cq, cdt = _as_input(cq)
         ck, cdt2 = _as_input(ck)
         assert cdt == cdt2
+        q_ = k_ = None
+    elif q is None and k is None:
+        mode, dt, cdt = SCORE_UNIFORM, vdt, F64
         q_ = k_ = None
     else:
         mode, cdt = SCORE_DOT, F64
@@ -199,7 +203,8 @@ def dense_causal(q, k, v, scale=None):
 def bwd(T, W, offsets, v, dO, q=None, k=None, cq=None, ck=None, gamma=0.0, beta=0.0,
         scale=None):
     """One (batch, head) slice.  Returns a dict of float64 gradients:
-    dot mode {dq, dk, dv}; coordinate mode {dv, dcq, dck, dgamma, dbeta, l1}."""
+    dot mode {dq, dk, dv}; coordinate mode {dv, dcq, dck, dgamma, dbeta, l1};
+    uniform mode (neither q, k nor cq, ck given) {dv}."""
     o = _offs(offsets)
     v, vdt = _as_input(v)
     dO, ddt = _as_input(dO)
@@ -223,6 +228,10 @@ def bwd(T, W, offsets, v, dO, q=None, k=None, cq=None, ck=None, gamma=0.0, beta=
                               _ptr(v), cdt, _ptr(cq), _ptr(ck), float(gamma), float(beta), _ptr(dO),
                               None, None, _ptr(dV), _ptr(dcq), _ptr(dck), _ptr(g), _ptr(b), _ptr(l1))
         out.update(dcq=dcq, dck=dck, dgamma=float(g[0]), dbeta=float(b[0]), l1=float(l1[0]))
+    elif q is None and k is None:
+        rc = lib().oracle_bwd(T, D, W, _ptr(o), len(o), SCORE_UNIFORM, float(scale), vdt, None, None,
+                              _ptr(v), F64, None, None, 0.0, 0.0, _ptr(dO),
+                              None, None, _ptr(dV), None, None, None, None, None)
     else:
         q, dt = _as_input(q)
         k, _ = _as_input(k)
@@ -252,6 +261,8 @@ def fwd_bh(W, offsets, v, q=None, k=None, cq=None, ck=None, gamma=None, beta=Non
             if cq is not None:
                 O[b, h], L[b, h] = fwd(T, W, offsets, v[b, h], cq=cq[b, h], ck=ck[b, h],
                                        gamma=float(gamma[h]), beta=float(beta[h]), rows=rows)
+            elif q is None:
+                O[b, h], L[b, h] = fwd(T, W, offsets, v[b, h], rows=rows)
             else:
                 O[b, h], L[b, h] = fwd(T, W, offsets, v[b, h], q=q[b, h], k=k[b, h],
                                        scale=scale, rows=rows)
@@ -269,6 +280,8 @@ def bwd_bh(W, offsets, v, dO, q=None, k=None, cq=None, ck=None, gamma=None, beta
             if cq is not None:
                 r = bwd(T, W, offsets, v[b, h], dO[b, h], cq=cq[b, h], ck=ck[b, h],
                         gamma=float(gamma[h]), beta=float(beta[h]))
+            elif q is None:
+                r = bwd(T, W, offsets, v[b, h], dO[b, h])
             else:
                 r = bwd(T, W, offsets, v[b, h], dO[b, h], q=q[b, h], k=k[b, h], scale=scale)
             for key, val in r.items():

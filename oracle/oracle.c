@@ -104,6 +104,11 @@ int64_t oracle_graph_csr(int64_t T, int64_t W, const int64_t* offs, int32_t n_of
 static double score(int mode, int64_t D, double scale, int dtype, const void* q,
                     const void* k, int cdtype, const void* cq, const void* ck,
                     double gamma, double beta, int64_t i, int64_t j) {
+  /* Uniform mode: one score for every admissible neighbour, so each of the
+   * |N(i)| neighbours gets weight 1 / |N(i)| (SpatialLM-Mini news page, "What
+   * to check before adopting it in your project": the same graph with fixed
+   * weights). */
+  if (mode == ORACLE_SCORE_UNIFORM) return 0.0;
   if (mode == ORACLE_SCORE_DOT) {
     double acc = 0.0;
     for (int64_t d = 0; d < D; ++d) acc += rd(q, dtype, i * D + d) * rd(k, dtype, j * D + d);
@@ -122,6 +127,7 @@ static int bad_attn_args(int64_t T, int64_t D, int mode, const void* q, const vo
   if (D < 1 || !v) return 1;
   if (mode == ORACLE_SCORE_DOT) return !q || !k;
   if (mode == ORACLE_SCORE_COORD) return !cq || !ck;
+  if (mode == ORACLE_SCORE_UNIFORM) return 0;
   (void)T;
   return 1;
 }

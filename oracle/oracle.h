@@ -15,6 +15,10 @@
  *    listing: key j is kept for query i iff j <= i and i - j < w.
  *  - MiniGPT (Part 6), same section, the sentence after the chunked_swa
  *    listing: with w >= T the windowed op equals causal attention exactly.
+ *  - SpatialLM-Mini news page, "What to check before adopting it in your
+ *    project": the same sparse graph with fixed weights as the comparison
+ *    that isolates the coordinates; read here as equal weights over each
+ *    row's neighbour list (uniform score mode).
  *
  * Every floating-point result is computed in IEEE double, in the plain order
  * of the definition (ascending key index j), with no blocking, fusion or
@@ -30,7 +34,7 @@ extern "C" {
 #endif
 
 enum { ORACLE_F64 = 0, ORACLE_F32 = 1, ORACLE_BF16 = 2 };
-enum { ORACLE_SCORE_DOT = 0, ORACLE_SCORE_COORD = 1 };
+enum { ORACLE_SCORE_DOT = 0, ORACLE_SCORE_COORD = 1, ORACLE_SCORE_UNIFORM = 2 };
 
 /* Neighbour set N(i) of row i, ascending, no repeats.  out must hold
  * min(W, T) + n_offs entries.  Returns |N(i)|, or -1 on a bad argument. */
@@ -45,8 +49,9 @@ int64_t oracle_graph_csr(int64_t T, int64_t W, const int64_t* offs, int32_t n_of
                          int64_t cols_cap);
 
 /* Forward over one (batch, head) slice.  q, k, v are [T, D] row-major with
- * element type `dtype` (q and k unused in coordinate mode); cq, ck are [T, 3]
- * with element type `cdtype` (unused in dot mode).  rows lists the query rows
+ * element type `dtype` (q and k used in dot mode only); cq, ck are [T, 3]
+ * with element type `cdtype` (coordinate mode only; uniform mode reads v
+ * alone).  rows lists the query rows
  * to evaluate (NULL: all T rows in order).  O is [n_rows, D], LSE [n_rows]
  * (natural log).  Returns 0, or -1 on a bad argument. */
 int oracle_fwd(int64_t T, int64_t D, int64_t W, const int64_t* offs, int32_t n_offs,
@@ -57,7 +62,7 @@ int oracle_fwd(int64_t T, int64_t D, int64_t W, const int64_t* offs, int32_t n_o
 /* Backward over one (batch, head) slice for upstream gradient dO ([T, D],
  * element type `dtype`).  Recomputes the forward itself.  Writes dQ, dK, dV
  * ([T, D]) in dot mode; dV, dcq, dck ([T, 3]), *dgamma, *dbeta in coordinate
- * mode (pass NULL for outputs not wanted).  *l1 receives sum |dS_ij| *
+ * mode; dV alone in uniform mode (pass NULL for outputs not wanted).  *l1 receives sum |dS_ij| *
  * (1 + ||c_q,i - c_k,j||^2) over all edges (coordinate mode; a magnitude for
  * reduction tolerances).  Returns 0, or -1 on a bad argument, -2 on OOM. */
 int oracle_bwd(int64_t T, int64_t D, int64_t W, const int64_t* offs, int32_t n_offs,

@@ -415,3 +415,61 @@ def test_bwd_bf16_inputs_upcast_exactly():
     gw = oracle.bwd(T, W, offs, wide[2], wide[3], q=wide[0], k=wide[1])
     for key in ("dq", "dk", "dv"):
         assert np.array_equal(gb[key], gw[key])
+
+
+# ------------------------------------------------------------------ uniform score mode
+def neighbours_from_definition(T, W, offsets, i):
+    """N(i) straight from the definition: itself and the W - 1 predecessors,
+    plus i - d for every long-range distance d, never before row 0."""
+    return sorted({i - d for d in range(W) if i - d >= 0} | {i - d for d in offsets if 0 <= i - d})
+
+
+@pytest.mark.parametrize("T,W,offs", [(64, 4, (4, 8, 16, 32)), (97, 1, (1, 2, 4, 8, 16, 32, 64)),
+                                      (40, 8, ()), (33, 50, (3, 40))])
+def test_fwd_uniform_is_the_neighbour_mean(T, W, offs):
+    """Equal weights over each row's neighbour list: O_i is the arithmetic
+    mean of the neighbours' v rows and LSE_i = ln |N(i)|, |N(i)| from the
+    closed-form degree."""
+    rng = np.random.default_rng(T * 7 + W)
+    v = rng.standard_normal((T, 6))
+    O, L = oracle.fwd(T, W, offs, v)
+    for i in range(T):
+        nb = neighbours_from_definition(T, W, offs, i)
+        np.testing.assert_allclose(O[i], v[nb].mean(axis=0), rtol=0, atol=1e-13)
+        assert len(nb) == closed_form_degree(T, W, offs, i)
+        assert abs(L[i] - math.log(len(nb))) < 1e-14
+
+
+def test_bwd_uniform_is_the_reverse_graph_sum():
+    """dV_j = sum over the rows i that list j of dO_i / |N(i)|; nothing else
+    is returned (the mode has no score parameters)."""
+    T, W, offs = 77, 3, (4, 8, 16, 32, 64)
+    rng = np.random.default_rng(5)
+    v = rng.standard_normal((T, 5))
+    dO = rng.standard_normal((T, 5))
+    g = oracle.bwd(T, W, offs, v, dO)
+    assert sorted(g) == ["dv"]
+    nbs = [neighbours_from_definition(T, W, offs, i) for i in range(T)]
+    ref = np.zeros((T, 5))
+    for i, nb in enumerate(nbs):
+        for j in nb:
+            ref[j] += dO[i] / len(nb)
+    np.testing.assert_allclose(g["dv"], ref, rtol=0, atol=1e-13)
+    # the forward is linear in v: <dO, O(v + e)> - <dO, O(v)> = <dV, e> exactly
+    e = rng.standard_normal((T, 5))
+    O0, _ = oracle.fwd(T, W, offs, v)
+    O1, _ = oracle.fwd(T, W, offs, v + e)
+    assert abs(np.sum(dO * (O1 - O0)) - np.sum(g["dv"] * e)) < 1e-11
+
+
+def test_fwd_uniform_equals_dot_mode_with_zero_queries():
+    """With q = 0 every dot-product score is 0, so dot mode reduces to the
+    uniform mode on the same graph."""
+    T, W, offs = 50, 4, (8, 16)
+    rng = np.random.default_rng(9)
+    v = rng.standard_normal((T, 8))
+    k = rng.standard_normal((T, 8))
+    O_u, L_u = oracle.fwd(T, W, offs, v)
+    O_d, L_d = oracle.fwd(T, W, offs, v, q=np.zeros((T, 8)), k=k)
+    np.testing.assert_allclose(O_u, O_d, rtol=0, atol=1e-14)
+    np.testing.assert_allclose(L_u, L_d, rtol=0, atol=1e-14)
