@@ -35,7 +35,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workloads", default="band,dilated,coord,ultra")
+    ap.add_argument("--workloads", default="band,dilated,coord,uniform,ultra")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample length")
     ap.add_argument("--algo", default="auto")
@@ -66,7 +66,16 @@ def models(w, grad_bytes=4):
     rows = w.B * w.H * w.T
     eb = 2 if w.dtype_name == "bf16" else 4
     D = w.D
-    if w.coord:
+    if w.uniform:
+        # forward: v, o rows, lse; backward: dout, lse, dv; per long-range edge
+        # the v row (forward) or the dout row and lse (backward)
+        fwd_c = rows * (2 * D * eb + 4)
+        fwd_e = Ed * D * eb
+        bwd_c = rows * (D * eb + 4 + D * grad_bytes)
+        bwd_e = Ed * (D * eb + 4)
+        ffl = w.B * w.H * E * 2 * D
+        bfl = w.B * w.H * E * 2 * D
+    elif w.coord:
         # forward: c_q, c_k (12 B), v, o rows, lse; backward: + dout, dv, dcq, dck
         fwd_c = rows * (12 + 12 + 2 * D * eb + 4)
         fwd_e = Ed * (12 + D * eb)
@@ -88,6 +97,10 @@ def models(w, grad_bytes=4):
 
 
 # ------------------------------------------------------------------ timing
+def score_name(w):
+    return "coord" if w.coord else ("uniform" if w.uniform else "dot")
+
+
 def run_workload(w, steps, warmup, algo, with_backward=True):
     import torch
 
@@ -107,7 +120,7 @@ def run_workload(w, steps, warmup, algo, with_backward=True):
     lse = torch.empty((w.B, w.H, w.T), dtype=torch.float32, device=dev)
     fkw = dict(v=x["v"], cq=x.get("cq"), ck=x.get("ck"), gamma=x.get("gamma"), beta=x.get("beta"),
                o=o, lse=lse, algo=algo)
-    if not coord:
+    if not coord and not w.uniform:
         fkw.update(q=x["q"], k=x["k"])
     grads = None
     if bwd:
@@ -118,14 +131,14 @@ def run_workload(w, steps, warmup, algo, with_backward=True):
                          dck=torch.empty((w.B, w.H, w.T, 3), dtype=torch.float32, device=dev),
                          dgamma=torch.empty((w.H,), dtype=torch.float32, device=dev),
                          dbeta=torch.empty((w.H,), dtype=torch.float32, device=dev))
-        else:
+        elif not w.uniform:
             grads.update(dq=torch.empty(gshape, dtype=torch.float32, device=dev),
                          dk=torch.empty(gshape, dtype=torch.float32, device=dev))
         from sparse_causal_attention_amd import sa_bwd_workspace_size
         ws = torch.empty(sa_bwd_workspace_size(g, x["v"]), dtype=torch.uint8, device=dev)
         bkw = dict(v=x["v"], o=o, lse=lse, dout=x["do"], cq=x.get("cq"), ck=x.get("ck"),
                    gamma=x.get("gamma"), beta=x.get("beta"), workspace=ws, algo=algo, **grads)
-        if not coord:
+        if not coord and not w.uniform:
             bkw.update(q=x["q"], k=x["k"])
 
     fwd_call = sa_fwd_prepared(g, **fkw)
@@ -157,8 +170,8 @@ def run_workload(w, steps, warmup, algo, with_backward=True):
         "wall_s": wall, "ms_per_step": 1e3 * wall / steps,
         "fwd_ms": sum(f_ms) / len(f_ms), "bwd_ms": sum(b_ms) / len(b_ms),
         "fwd_ms_min": min(f_ms), "bwd_ms_min": min(b_ms),
-        "plan_fwd": sa_describe_plan(g, x["v"], coord=coord, algo=algo, which="fwd"),
-        "plan_bwd": sa_describe_plan(g, x["v"], coord=coord, algo=algo, which="bwd") if bwd else None,
+        "plan_fwd": sa_describe_plan(g, x["v"], score=score_name(w), algo=algo, which="fwd"),
+        "plan_bwd": sa_describe_plan(g, x["v"], score=score_name(w), algo=algo, which="bwd") if bwd else None,
         "inputs": {k: t for k, t in x.items()},
     }
     del o, lse, grads
@@ -174,7 +187,7 @@ def summarize(w, r, steps):
         "workload": w.name,
         "shape": {"B": w.B, "H": w.H, "T": w.T, "D": w.D, "window": w.window,
                   "offsets": list(w.offsets), "dtype": w.dtype_name,
-                  "score": "coord" if w.coord else "dot", "backward": w.backward},
+                  "score": score_name(w), "backward": w.backward},
         "tokens_per_s": tokens * steps / wall,
         "edges_per_s": m["edges"] * steps / wall,
         "ms_per_step": r["ms_per_step"],
@@ -255,7 +268,10 @@ def cpu_baseline(w, inputs, target_s):
     t0 = time.perf_counter()
     while True:  # whole passes over the (batch, head) slices until target_s
         b, h = slices[done % len(slices)]
-        if w.coord:
+        if w.uniform:
+            oracle.fwd(w.T, w.window, w.offsets, hv["v"][b, h])
+            oracle.bwd(w.T, w.window, w.offsets, hv["v"][b, h], hv["do"][b, h])
+        elif w.coord:
             oracle.fwd(w.T, w.window, w.offsets, hv["v"][b, h], cq=hv["cq"][b, h], ck=hv["ck"][b, h],
                        gamma=float(hv["gamma"][h]), beta=float(hv["beta"][h]))
             oracle.bwd(w.T, w.window, w.offsets, hv["v"][b, h], hv["do"][b, h], cq=hv["cq"][b, h],

@@ -69,11 +69,14 @@ typedef enum {
 typedef enum { SA_F32 = 0, SA_BF16 = 1 } sa_dtype;
 
 /* Score of edge (i, j):
- *  SA_SCORE_DOT:   s_ij = scale * <q_i, k_j>
- *  SA_SCORE_COORD: s_ij = -gamma_h * ||c_q,i - c_k,j||^2 + beta_h
+ *  SA_SCORE_DOT:     s_ij = scale * <q_i, k_j>
+ *  SA_SCORE_COORD:   s_ij = -gamma_h * ||c_q,i - c_k,j||^2 + beta_h
+ *  SA_SCORE_UNIFORM: s_ij = 0, i.e. every neighbour of row i has weight
+ *                    1 / |N(i)| (fixed weights, no score parameters)
  * (SpatialLM-Mini news page, "How tokens choose whom to listen to", and the
- * dot-product comparison asked for in "What to check before adopting it"). */
-typedef enum { SA_SCORE_DOT = 0, SA_SCORE_COORD = 1 } sa_score;
+ * comparisons on the same graph with a dot product or fixed weights asked for
+ * in "What to check before adopting it"). */
+typedef enum { SA_SCORE_DOT = 0, SA_SCORE_COORD = 1, SA_SCORE_UNIFORM = 2 } sa_score;
 
 /* Kernel family.  AUTO picks the LDS/MFMA band kernels for the window when
  * they apply (bf16, dot score, D = 64, W >= 16) and the gather kernels
@@ -143,7 +146,8 @@ typedef struct {
  *   m_i = max_{j in N(i)} s_ij,  l_i = sum_{j in N(i)} exp(s_ij - m_i),
  *   o_i = sum_{j in N(i)} exp(s_ij - m_i) v_j / l_i,   lse_i = m_i + ln l_i.
  * Dot mode reads q, k, v (cq, ck, gamma, beta ignored, may be NULL);
- * coordinate mode reads cq, ck, gamma, beta, v (q, k ignored).  Writes o in
+ * coordinate mode reads cq, ck, gamma, beta, v (q, k ignored); uniform mode
+ * reads v alone (o_i is the mean of v over N(i), lse_i = ln |N(i)|).  Writes o in
  * `dtype` (bf16 rounded to nearest even) and lse in fp32 (natural log).
  * Arithmetic is fp32 with fp32 accumulation; bf16 MFMA products for the band. */
 sa_status sa_fwd(const sa_graph* g, const sa_attn_desc* desc, const void* q, const void* k,
@@ -166,7 +170,8 @@ sa_status sa_bwd_workspace_size(const sa_graph* g, const sa_attn_desc* desc, siz
  * Every output element is written (not accumulated into).  Deterministic: no
  * atomics, fixed summation order, bitwise identical across runs.  Dot mode
  * writes dq, dk, dv (dcq, dck, dgamma, dbeta may be NULL); coordinate mode
- * writes dv, dcq, dck, dgamma, dbeta (dq, dk may be NULL).  The workspace
+ * writes dv, dcq, dck, dgamma, dbeta (dq, dk may be NULL); uniform mode
+ * writes dv alone (dv_j = sum over i with j in N(i) of dout_i / |N(i)|).  The workspace
  * (at least sa_bwd_workspace_size bytes, 256-byte aligned) is scratch owned
  * by the caller and must not be shared by concurrent calls. */
 sa_status sa_bwd(const sa_graph* g, const sa_attn_desc* desc, const void* q, const void* k,

@@ -12,6 +12,8 @@ must be built (``python -m sparse_causal_attention_amd.build``).
 
 Coordinate score (-gamma_h ||c_q - c_k||^2 + beta_h): pass ``cq``, ``ck``
 ([B, H, T, 3] fp32), ``gamma``, ``beta`` ([H] fp32) instead of ``q``, ``k``.
+Uniform score (every neighbour weighted 1 / |N(i)|): pass ``v`` alone; the
+backward then returns ``{"dv"}`` only.
 """
 from __future__ import annotations
 
@@ -21,7 +23,7 @@ import numpy as np
 
 from . import _abi
 from ._abi import (SA_ALGO_AUTO, SA_ALGO_BAND, SA_ALGO_GATHER, SA_BF16, SA_F32,
-                   SA_MAX_DILATED, SA_SCORE_COORD, SA_SCORE_DOT, SaError)
+                   SA_MAX_DILATED, SA_SCORE_COORD, SA_SCORE_DOT, SA_SCORE_UNIFORM, SaError)
 
 __all__ = ["sa_build_graph", "sa_fwd", "sa_bwd", "sa_fwd_prepared", "sa_bwd_prepared",
            "sa_bwd_workspace_size", "sa_describe_plan", "Graph", "SaError"]
@@ -150,9 +152,20 @@ def _coord_args(cq, ck, gamma, beta, B, H, T):
             raise ValueError("%s must be a contiguous float32 tensor of shape %s" % (name, shp))
 
 
+def _score_mode(q, k, cq):
+    """Coordinate mode when c_q is given, uniform when neither q, k nor c_q
+    is, dot otherwise."""
+    if cq is not None:
+        return SA_SCORE_COORD
+    if q is None and k is None:
+        return SA_SCORE_UNIFORM
+    return SA_SCORE_DOT
+
+
 def _fwd_args(graph, q, k, v, cq, ck, gamma, beta, scale, o, lse, algo, stream):
     torch = _torch()
-    coord = cq is not None
+    mode = _score_mode(q, k, cq)
+    coord = mode == SA_SCORE_COORD
     _require_gpu(q=q, k=k, v=v, cq=cq, ck=ck, gamma=gamma, beta=beta, o=o, lse=lse)
     B, H, T, D = v.shape
     if coord:
@@ -163,7 +176,7 @@ def _fwd_args(graph, q, k, v, cq, ck, gamma, beta, scale, o, lse, algo, stream):
         lse = torch.empty((B, H, T), dtype=torch.float32, device=v.device)
     if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, T) or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [B, H, T] tensor")
-    d = _make_desc(v, score=SA_SCORE_COORD if coord else SA_SCORE_DOT, algo=algo, scale=scale,
+    d = _make_desc(v, score=mode, algo=algo, scale=scale,
                    grad_dtype=SA_F32, q=None if coord else q, k=None if coord else k, v=v, o=o)
     args = (graph.handle, ctypes.byref(d), _ptr(None if coord else q), _ptr(None if coord else k),
             _ptr(v), _ptr(cq), _ptr(ck), _ptr(gamma), _ptr(beta), _ptr(o), _ptr(lse), _stream(stream))
@@ -211,7 +224,9 @@ def _dtype_code_of(dt) -> int:
 def _bwd_args(graph, q, k, v, o, lse, dout, cq, ck, gamma, beta, scale, grad_dtype, dq, dk, dv,
               dcq, dck, dgamma, dbeta, workspace, algo, stream):
     torch = _torch()
-    coord = cq is not None
+    mode = _score_mode(q, k, cq)
+    coord = mode == SA_SCORE_COORD
+    uniform = mode == SA_SCORE_UNIFORM
     _require_gpu(q=q, k=k, v=v, o=o, lse=lse, dout=dout, cq=cq, ck=ck, gamma=gamma, beta=beta)
     B, H, T, D = v.shape
     gdt = torch.float32 if grad_dtype is None else grad_dtype
@@ -223,6 +238,8 @@ def _bwd_args(graph, q, k, v, o, lse, dout, cq, ck, gamma, beta, scale, grad_dty
         dck = torch.empty((B, H, T, 3), dtype=torch.float32, device=dev) if dck is None else dck
         dgamma = torch.empty((H,), dtype=torch.float32, device=dev) if dgamma is None else dgamma
         dbeta = torch.empty((H,), dtype=torch.float32, device=dev) if dbeta is None else dbeta
+    elif uniform:
+        dq = dk = None
     else:
         dq = torch.empty((B, H, T, D), dtype=gdt, device=dev) if dq is None else dq
         dk = torch.empty((B, H, T, D), dtype=gdt, device=dev) if dk is None else dk
@@ -230,7 +247,7 @@ def _bwd_args(graph, q, k, v, o, lse, dout, cq, ck, gamma, beta, scale, grad_dty
     for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
         if t is not None and t.dtype != gdt:
             raise ValueError("%s must have the gradient dtype %s" % (name, gdt))
-    d = _make_desc(v, score=SA_SCORE_COORD if coord else SA_SCORE_DOT, algo=algo, scale=scale,
+    d = _make_desc(v, score=mode, algo=algo, scale=scale,
                    grad_dtype=gcode, q=None if coord else q, k=None if coord else k, v=v, o=o,
                    dout=dout, dq=None if coord else dq, dk=None if coord else dk, dv=dv)
     L = _abi.lib()
@@ -247,6 +264,8 @@ def _bwd_args(graph, q, k, v, o, lse, dout, cq, ck, gamma, beta, scale, grad_dty
             _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
     if coord:
         out = {"dv": dv, "dcq": dcq, "dck": dck, "dgamma": dgamma, "dbeta": dbeta}
+    elif uniform:
+        out = {"dv": dv}
     else:
         out = {"dq": dq, "dk": dk, "dv": dv}
     return args, (d, workspace, out)
@@ -256,7 +275,8 @@ def sa_bwd(graph: Graph, q=None, k=None, v=None, o=None, lse=None, dout=None, *,
            gamma=None, beta=None, scale=None, grad_dtype=None, dq=None, dk=None, dv=None,
            dcq=None, dck=None, dgamma=None, dbeta=None, workspace=None, algo="auto", stream=None):
     """Gradients of sum <dout, o>.  Dot mode returns {dq, dk, dv}; coordinate
-    mode {dv, dcq, dck, dgamma, dbeta}.  Gradients default to fp32."""
+    mode {dv, dcq, dck, dgamma, dbeta}; uniform mode {dv}.  Gradients default
+    to fp32."""
     args, (_d, _ws, out) = _bwd_args(graph, q, k, v, o, lse, dout, cq, ck, gamma, beta, scale,
                                      grad_dtype, dq, dk, dv, dcq, dck, dgamma, dbeta, workspace,
                                      algo, stream)
@@ -281,10 +301,12 @@ def sa_bwd_prepared(graph: Graph, q=None, k=None, v=None, o=None, lse=None, dout
     return call
 
 
-def sa_describe_plan(graph: Graph, v, *, coord=False, algo="auto", which="fwd") -> str:
-    """Names of the kernels sa_fwd ("fwd") or sa_bwd ("bwd") would launch."""
-    d = _make_desc(v, score=SA_SCORE_COORD if coord else SA_SCORE_DOT, algo=algo, scale=None,
-                   grad_dtype=SA_F32)
+def sa_describe_plan(graph: Graph, v, *, coord=False, algo="auto", which="fwd", score=None) -> str:
+    """Names of the kernels sa_fwd ("fwd") or sa_bwd ("bwd") would launch.
+    score: "dot", "coord" or "uniform" (default: "coord" if coord else "dot")."""
+    modes = {"dot": SA_SCORE_DOT, "coord": SA_SCORE_COORD, "uniform": SA_SCORE_UNIFORM}
+    mode = modes[score] if score is not None else (SA_SCORE_COORD if coord else SA_SCORE_DOT)
+    d = _make_desc(v, score=mode, algo=algo, scale=None, grad_dtype=SA_F32)
     buf = ctypes.create_string_buffer(256)
     _abi.check(_abi.lib().sa_describe_plan(graph.handle, ctypes.byref(d), 0 if which == "fwd" else 1,
                                            buf, 256), "sa_describe_plan")

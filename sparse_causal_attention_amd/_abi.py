@@ -14,7 +14,7 @@ LIB_PATH = os.path.join(_PKG, "libsa.so")
 
 SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_SHAPE_MISMATCH, SA_ERR_WORKSPACE, SA_ERR_HIP = range(6)
 SA_F32, SA_BF16 = 0, 1
-SA_SCORE_DOT, SA_SCORE_COORD = 0, 1
+SA_SCORE_DOT, SA_SCORE_COORD, SA_SCORE_UNIFORM = 0, 1, 2
 SA_ALGO_AUTO, SA_ALGO_GATHER, SA_ALGO_BAND = 0, 1, 2
 SA_MAX_DILATED = 64
 

@@ -43,7 +43,8 @@ sa_status check_common(const sa_graph* g, const sa_attn_desc* d, const void* q, 
   if (g == nullptr || d == nullptr) return SA_ERR_INVALID_ARG;
   if (d->B < 1 || d->H < 1 || d->T < 1 || d->D < 1) return SA_ERR_INVALID_ARG;
   if (bad_dtype(d->dtype) || bad_dtype(d->grad_dtype)) return SA_ERR_INVALID_ARG;
-  if (d->score != SA_SCORE_DOT && d->score != SA_SCORE_COORD) return SA_ERR_INVALID_ARG;
+  if (d->score != SA_SCORE_DOT && d->score != SA_SCORE_COORD && d->score != SA_SCORE_UNIFORM)
+    return SA_ERR_INVALID_ARG;
   if (d->algo != SA_ALGO_AUTO && d->algo != SA_ALGO_GATHER && d->algo != SA_ALGO_BAND)
     return SA_ERR_INVALID_ARG;
   if (d->T != g->T) return SA_ERR_SHAPE_MISMATCH;
@@ -51,21 +52,20 @@ sa_status check_common(const sa_graph* g, const sa_attn_desc* d, const void* q, 
   if (d->B * d->H > (int64_t)1 << 24) return SA_ERR_UNSUPPORTED;
   // blocks of the smallest row tile must be countable in int32
   if ((double)d->B * d->H * (double)d->T > 1.0e12) return SA_ERR_UNSUPPORTED;
-  const bool coord = d->score == SA_SCORE_COORD;
   const int es = esize(d->dtype);
   if (v == nullptr || !aligned_rows(v, d->stride_v, es) || !offsets_fit(d, d->stride_v))
     return SA_ERR_INVALID_ARG;
-  if (!coord) {
+  if (d->score == SA_SCORE_DOT) {
     if (q == nullptr || k == nullptr) return SA_ERR_INVALID_ARG;
     if (!aligned_rows(q, d->stride_q, es) || !aligned_rows(k, d->stride_k, es))
       return SA_ERR_INVALID_ARG;
     if (!offsets_fit(d, d->stride_q) || !offsets_fit(d, d->stride_k)) return SA_ERR_INVALID_ARG;
-  } else {
+    if (!(d->scale == d->scale)) return SA_ERR_INVALID_ARG;  // NaN scale
+  } else if (d->score == SA_SCORE_COORD) {
     if (cq == nullptr || ck == nullptr || gamma == nullptr || beta == nullptr)
       return SA_ERR_INVALID_ARG;
-  }
-  if (!coord && !(d->scale == d->scale)) return SA_ERR_INVALID_ARG;  // NaN scale
-  const bool band_ok = sa::band_supported(d->dtype, (int)d->D, coord, g->W);
+  }  // uniform mode reads v alone
+  const bool band_ok = sa::band_supported(d->dtype, (int)d->D, d->score, g->W);
   if (d->algo == SA_ALGO_BAND && !band_ok) return SA_ERR_UNSUPPORTED;
   plan->path = (d->algo != SA_ALGO_GATHER && band_ok) ? Path::Band : Path::Gather;
   return SA_OK;
@@ -95,7 +95,8 @@ hipStream_t as_stream(sa_stream s) { return reinterpret_cast<hipStream_t>(s); }
 
 const char* fwd_kernel_name(const sa_attn_desc* d, Path path) {
   if (path == Path::Band) return "band_fwd_kernel";
-  return d->score == SA_SCORE_COORD ? "gather_fwd_kernel(coord)" : "gather_fwd_kernel(dot)";
+  if (d->score == SA_SCORE_COORD) return "gather_fwd_kernel(coord)";
+  return d->score == SA_SCORE_UNIFORM ? "gather_fwd_kernel(uniform)" : "gather_fwd_kernel(dot)";
 }
 
 }  // namespace
@@ -120,7 +121,7 @@ extern "C" sa_status sa_fwd(const sa_graph* g, const sa_attn_desc* d, const void
   hipError_t e = plan.path == Path::Band
                      ? sa::launch_band_fwd(p, as_stream(stream))
                      : sa::launch_gather_fwd(p, d->dtype == SA_BF16 ? sa::DT_BF16 : sa::DT_F32,
-                                             d->score == SA_SCORE_COORD, as_stream(stream));
+                                             d->score, as_stream(stream));
   return e == hipSuccess ? SA_OK : SA_ERR_HIP;
 }
 
@@ -172,13 +173,13 @@ extern "C" sa_status sa_bwd(const sa_graph* g, const sa_attn_desc* d, const void
     return offsets_fit(d, s);
   };
   if (!grad_ok(dv, d->stride_dv)) return SA_ERR_INVALID_ARG;
-  if (!coord) {
+  if (d->score == SA_SCORE_DOT) {
     if (dq == nullptr || dk == nullptr) return SA_ERR_INVALID_ARG;
     if (!grad_ok(dq, d->stride_dq) || !grad_ok(dk, d->stride_dk)) return SA_ERR_INVALID_ARG;
-  } else {
+  } else if (coord) {
     if (dcq == nullptr || dck == nullptr || dgamma == nullptr || dbeta == nullptr)
       return SA_ERR_INVALID_ARG;
-  }
+  }  // uniform mode writes dv alone
   if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return SA_ERR_WORKSPACE;
   const size_t need = workspace_bytes_for(d);
@@ -206,7 +207,7 @@ extern "C" sa_status sa_bwd(const sa_graph* g, const sa_attn_desc* d, const void
   hipError_t e = plan.path == Path::Band
                      ? sa::launch_band_bwd(p, as_stream(stream))
                      : sa::launch_gather_bwd(p, d->dtype == SA_BF16 ? sa::DT_BF16 : sa::DT_F32,
-                                             coord, as_stream(stream));
+                                             d->score, as_stream(stream));
   return e == hipSuccess ? SA_OK : SA_ERR_HIP;
 }
 
@@ -230,7 +231,8 @@ extern "C" sa_status sa_describe_plan(const sa_graph* g, const sa_attn_desc* d, 
     txt = "band_bwd_prepass_kernel+band_bwd_kernel";
   } else {
     txt = coord ? "gather_bwd_q_kernel(coord)+gather_bwd_kv_kernel(coord)+coord_param_reduce_kernel"
-                : "gather_bwd_q_kernel(dot)+gather_bwd_kv_kernel(dot)";
+          : d->score == SA_SCORE_UNIFORM ? "gather_bwd_kv_kernel(uniform)"
+                                          : "gather_bwd_q_kernel(dot)+gather_bwd_kv_kernel(dot)";
   }
   snprintf(buf, cap, "%s", txt);
   return SA_OK;

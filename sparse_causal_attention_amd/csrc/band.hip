@@ -288,8 +288,8 @@ __global__ __launch_bounds__(kThreads, 4) void band_fwd_kernel(Params p) {
 
 }  // namespace
 
-bool band_supported(int dtype, int D, bool coord, int64_t W) {
-  return dtype == DT_BF16 && D == kD && !coord && W >= 16;
+bool band_supported(int dtype, int D, int score_mode, int64_t W) {
+  return dtype == DT_BF16 && D == kD && score_mode == SM_DOT && W >= 16;
 }
 
 int band_rows_per_block() { return kBQ; }

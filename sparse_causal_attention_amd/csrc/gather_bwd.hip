@@ -225,8 +225,10 @@ __global__ __launch_bounds__(kThreads) void gather_bwd_q_kernel(Params p) {
 }
 
 // ------------------------------------------------------------------ pass 2
-template <int DT, int D, bool COORD, int G, bool OFF32>
+template <int DT, int D, int SM, int G, bool OFF32>
 __global__ __launch_bounds__(kThreads) void gather_bwd_kv_kernel(Params p) {
+  constexpr bool COORD = SM == SM_COORD;
+  constexpr bool UNIFORM = SM == SM_UNIFORM;  // dv only: no score parameters
   using F = Frag<DT>;
   using Gm = Geo<DT, D>;
   constexpr int EPL = Gm::EPL, LG = Gm::LG, RPW = Gm::RPW, RPB = Gm::RPB;
@@ -253,7 +255,7 @@ __global__ __launch_bounds__(kThreads) void gather_bwd_kv_kernel(Params p) {
   uint32_t ql32 = (uint32_t)ql, dl32 = (uint32_t)dl;
   asm volatile("" : "+v"(ql32), "+v"(dl32), "+v"(ql), "+v"(dl));  // keep addresses scalar-offset
   const float* lseb = p.lse + (int64_t)bh * p.T;
-  const float* delb = p.delta + (int64_t)bh * p.T;
+  const float* delb = UNIFORM ? nullptr : p.delta + (int64_t)bh * p.T;
   const float bsub = COORD ? p.beta[h] : 0.f;  // lse includes beta in coordinate mode
 
   // own k and v fragments as stored (dot operands)
@@ -266,11 +268,11 @@ __global__ __launch_bounds__(kThreads) void gather_bwd_kv_kernel(Params p) {
   float ckj[3] = {0.f, 0.f, 0.f};
   float gl2 = 0.f, gam = 0.f;
   const float* cqb = nullptr;
-  if constexpr (!COORD) {
+  if constexpr (SM == SM_DOT) {
     const char* krow = static_cast<const char*>(p.k) + (b * p.sk_b + h * p.sk_h + j * p.sk_t) * EB +
                        sub * 16;
     kraw_j = ld16(krow);
-  } else {
+  } else if constexpr (COORD) {
     const float* ckr = p.ck + ((int64_t)bh * p.T + j) * 3;
     ckj[0] = ckr[0]; ckj[1] = ckr[1]; ckj[2] = ckr[2];
     gam = p.gamma[h];
@@ -295,16 +297,16 @@ __global__ __launch_bounds__(kThreads) void gather_bwd_kv_kernel(Params p) {
       if constexpr (OFF32) {
         const uint32_t qo = ok ? ql32 + (uint32_t)dist[g] * (uint32_t)sqt : ql32;
         const uint32_t doo = ok ? dl32 + (uint32_t)dist[g] * (uint32_t)sdot : dl32;
-        if constexpr (!COORD) qraw[g] = ld16(qhead + qo);
+        if constexpr (SM == SM_DOT) qraw[g] = ld16(qhead + qo);
         doraw[g] = ld16(dohead + doo);
       } else {
         const int64_t qo = ok ? ql + (int64_t)dist[g] * sqt : ql;
         const int64_t doo = ok ? dl + (int64_t)dist[g] * sdot : dl;
-        if constexpr (!COORD) qraw[g] = ld16(qhead + qo);
+        if constexpr (SM == SM_DOT) qraw[g] = ld16(qhead + qo);
         doraw[g] = ld16(dohead + doo);
       }
       lse2[g] = (lseb[ii] - bsub) * kLog2e;
-      del[g] = delb[ii];
+      if constexpr (!UNIFORM) del[g] = delb[ii];
       i[g] = ok ? ii : p.T;  // p.T marks an absent edge
       if constexpr (COORD) {
         const float* c = cqb + (int64_t)ii * 3;
@@ -312,27 +314,32 @@ __global__ __launch_bounds__(kThreads) void gather_bwd_kv_kernel(Params p) {
         dif[g][1] = c[1] - ckj[1];
         dif[g][2] = c[2] - ckj[2];
         s[g] = -gl2 * (dif[g][0] * dif[g][0] + dif[g][1] * dif[g][1] + dif[g][2] * dif[g][2]);
+      } else if constexpr (UNIFORM) {
+        s[g] = 0.f;
+      }
+    }
+    if constexpr (!UNIFORM) {
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        dp[g] = F::dot(doraw[g], vraw_j, 0.f);
+        if constexpr (SM == SM_DOT) s[g] = F::dot(qraw[g], kraw_j, 0.f);
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        dp[g] = group_sum<LG>(dp[g]);
+        if constexpr (SM == SM_DOT) s[g] = group_sum<LG>(s[g]) * p.scale_log2;
       }
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      dp[g] = F::dot(doraw[g], vraw_j, 0.f);
-      if constexpr (!COORD) s[g] = F::dot(qraw[g], kraw_j, 0.f);
-    }
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      dp[g] = group_sum<LG>(dp[g]);
-      if constexpr (!COORD) s[g] = group_sum<LG>(s[g]) * p.scale_log2;
-    }
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
       const float pr = i[g] < p.T ? fast_exp2(s[g] - lse2[g]) : 0.f;
-      const float ds = pr * (dp[g] - del[g]);
       float dof[EPL];
       F::unpack(doraw[g], dof);
 #pragma unroll
       for (int e = 0; e < EPL; ++e) dv[e] = fmaf(pr, dof[e], dv[e]);
-      if constexpr (!COORD) {
+      if constexpr (UNIFORM) continue;
+      const float ds = pr * (dp[g] - del[g]);
+      if constexpr (SM == SM_DOT) {
         float qf[EPL];
         F::unpack(qraw[g], qf);
 #pragma unroll
@@ -365,13 +372,13 @@ __global__ __launch_bounds__(kThreads) void gather_bwd_kv_kernel(Params p) {
   char* dvrow = static_cast<char*>(p.dv) + (b * p.sdv_b + h * p.sdv_h + j * p.sdv_t) * gb +
                 sub * EPL * gb;
   store_vals<EPL>(dvrow, dv, p.grad_bf16 != 0);
-  if constexpr (!COORD) {
+  if constexpr (SM == SM_DOT) {
 #pragma unroll
     for (int e = 0; e < EPL; ++e) dk[e] *= p.scale;
     char* dkrow = static_cast<char*>(p.dk) + (b * p.sdk_b + h * p.sdk_h + j * p.sdk_t) * gb +
                   sub * EPL * gb;
     store_vals<EPL>(dkrow, dk, p.grad_bf16 != 0);
-  } else {
+  } else if constexpr (COORD) {
     if (sub == 0) {
       float* o = p.dck + ((int64_t)bh * p.T + j) * 3;
       o[0] = 2.f * gam * dc[0];
@@ -423,44 +430,56 @@ inline bool fits_off32(const Params& p, int eb) {
   return true;
 }
 
-template <int DT, int D, bool COORD, bool OFF32>
-hipError_t launch_both(const Params& p, hipStream_t s, int grid, int nblk) {
-  hipLaunchKernelGGL((gather_bwd_q_kernel<DT, D, COORD, 4, OFF32>), dim3(grid), dim3(kThreads), 0, s, p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((gather_bwd_kv_kernel<DT, D, COORD, 4, OFF32>), dim3(grid), dim3(kThreads), 0, s, p);
-  e = hipGetLastError();
-  if (e != hipSuccess || !COORD) return e;
+template <int DT, int D, int SM, bool OFF32>
+hipError_t launch_passes(const Params& p, hipStream_t s, int grid, int nblk) {
+  if constexpr (SM != SM_UNIFORM) {  // the uniform mode has no query-side gradient
+    hipLaunchKernelGGL((gather_bwd_q_kernel<DT, D, SM == SM_COORD, 4, OFF32>), dim3(grid), dim3(kThreads), 0, s,
+                       p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((gather_bwd_kv_kernel<DT, D, SM, 4, OFF32>), dim3(grid), dim3(kThreads), 0, s, p);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess || SM != SM_COORD) return e;
   hipLaunchKernelGGL(coord_param_reduce_kernel, dim3(p.H), dim3(256), 0, s, p.partials, p.B, p.H,
                      nblk, p.dgamma, p.dbeta);
   return hipGetLastError();
 }
 
-template <int DT, int D, bool COORD>
+template <int DT, int D, int SM>
 hipError_t launch_one(const Params& p, hipStream_t s) {
   constexpr int RPB = Geo<DT, D>::RPB;
   const int nblk = (p.T + RPB - 1) / RPB;
   const int grid = xcd_grid(p.B * p.H * nblk);
-  return fits_off32(p, Frag<DT>::BYTES) ? launch_both<DT, D, COORD, true>(p, s, grid, nblk)
-                                        : launch_both<DT, D, COORD, false>(p, s, grid, nblk);
+  return fits_off32(p, Frag<DT>::BYTES) ? launch_passes<DT, D, SM, true>(p, s, grid, nblk)
+                                        : launch_passes<DT, D, SM, false>(p, s, grid, nblk);
 }
 
-template <int DT, bool COORD>
+template <int DT, int SM>
 hipError_t launch_d(const Params& p, hipStream_t s) {
   switch (p.D) {
-    case 16: return launch_one<DT, 16, COORD>(p, s);
-    case 32: return launch_one<DT, 32, COORD>(p, s);
-    case 64: return launch_one<DT, 64, COORD>(p, s);
-    case 128: return launch_one<DT, 128, COORD>(p, s);
+    case 16: return launch_one<DT, 16, SM>(p, s);
+    case 32: return launch_one<DT, 32, SM>(p, s);
+    case 64: return launch_one<DT, 64, SM>(p, s);
+    case 128: return launch_one<DT, 128, SM>(p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <int DT>
+hipError_t launch_mode(const Params& p, int score_mode, hipStream_t s) {
+  switch (score_mode) {
+    case SM_DOT: return launch_d<DT, SM_DOT>(p, s);
+    case SM_COORD: return launch_d<DT, SM_COORD>(p, s);
+    case SM_UNIFORM: return launch_d<DT, SM_UNIFORM>(p, s);
   }
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_gather_bwd(const Params& p, int dtype, bool coord, hipStream_t s) {
-  if (dtype == DT_BF16) return coord ? launch_d<DT_BF16, true>(p, s) : launch_d<DT_BF16, false>(p, s);
-  return coord ? launch_d<DT_F32, true>(p, s) : launch_d<DT_F32, false>(p, s);
+hipError_t launch_gather_bwd(const Params& p, int dtype, int score_mode, hipStream_t s) {
+  return dtype == DT_BF16 ? launch_mode<DT_BF16>(p, score_mode, s) : launch_mode<DT_F32>(p, score_mode, s);
 }
 
 }  // namespace sa

@@ -33,7 +33,7 @@ struct Geo {
 };
 
 
-template <int DT, int D, bool COORD, int G, bool OFF32>
+template <int DT, int D, int SM, int G, bool OFF32>
 __global__ __launch_bounds__(kThreads) void gather_fwd_kernel(Params p) {
   using F = Frag<DT>;
   using Gm = Geo<DT, D>;
@@ -68,11 +68,11 @@ __global__ __launch_bounds__(kThreads) void gather_fwd_kernel(Params p) {
   float cqi[3] = {0.f, 0.f, 0.f};
   float gl2 = 0.f;  // gamma * log2(e)
   const float* ckb = nullptr;
-  if constexpr (!COORD) {
+  if constexpr (SM == SM_DOT) {
     const char* qrow = static_cast<const char*>(p.q) + (b * p.sq_b + h * p.sq_h + i * p.sq_t) * EB +
                        sub * 16;
     qraw = ld16(qrow);
-  } else {
+  } else if constexpr (SM == SM_COORD) {
     const float* cqr = p.cq + ((int64_t)bh * p.T + i) * 3;
     cqi[0] = cqr[0]; cqi[1] = cqr[1]; cqi[2] = cqr[2];
     gl2 = p.gamma[h] * kLog2e;
@@ -98,21 +98,23 @@ __global__ __launch_bounds__(kThreads) void gather_fwd_kernel(Params p) {
       if constexpr (OFF32) {
         const uint32_t ko = ok ? kl32 - (uint32_t)dist[g] * (uint32_t)skt : sub16;
         const uint32_t vo = ok ? vl32 - (uint32_t)dist[g] * (uint32_t)svt : sub16;
-        if constexpr (!COORD) kraw[g] = ld16(khead + ko);
+        if constexpr (SM == SM_DOT) kraw[g] = ld16(khead + ko);
         vraw[g] = ld16(vhead + vo);
       } else {
         const int64_t ko = ok ? kl - (int64_t)dist[g] * skt : (int64_t)sub16;
         const int64_t vo = ok ? vl - (int64_t)dist[g] * svt : (int64_t)sub16;
-        if constexpr (!COORD) kraw[g] = ld16(khead + ko);
+        if constexpr (SM == SM_DOT) kraw[g] = ld16(khead + ko);
         vraw[g] = ld16(vhead + vo);
       }
-      if constexpr (COORD) {
+      if constexpr (SM == SM_COORD) {
         const float* c = ckb + (int64_t)(ok ? j[g] : 0) * 3;
         const float d0 = cqi[0] - c[0], d1 = cqi[1] - c[1], d2 = cqi[2] - c[2];
         s[g] = -gl2 * (d0 * d0 + d1 * d1 + d2 * d2);
+      } else if constexpr (SM == SM_UNIFORM) {
+        s[g] = 0.f;  // one weight for every neighbour
       }
     }
-    if constexpr (!COORD) {
+    if constexpr (SM == SM_DOT) {
 #pragma unroll
       for (int g = 0; g < G; ++g) s[g] = F::dot(qraw, kraw[g], 0.f);
 #pragma unroll
@@ -172,7 +174,7 @@ __global__ __launch_bounds__(kThreads) void gather_fwd_kernel(Params p) {
   st16(orow, F::pack(acc));
   if (sub == 0) {
     float lse = (m + fast_log2(l)) * kLn2;
-    if constexpr (COORD) lse += p.beta[h];
+    if constexpr (SM == SM_COORD) lse += p.beta[h];
     p.lse[(int64_t)bh * p.T + i] = lse;
   }
 }
@@ -184,25 +186,25 @@ inline bool fits_off32(const Params& p, int eb) {
   return ((int64_t)(p.T - 1) * p.sk_t + p.D) * eb < lim && ((int64_t)(p.T - 1) * p.sv_t + p.D) * eb < lim;
 }
 
-template <int DT, int D, bool COORD>
+template <int DT, int D, int SM>
 hipError_t launch_one(const Params& p, hipStream_t s) {
   constexpr int RPB = Geo<DT, D>::RPB;
   const int nblk = (p.T + RPB - 1) / RPB;
   const int grid = xcd_grid(p.B * p.H * nblk);
   if (fits_off32(p, Frag<DT>::BYTES))
-    hipLaunchKernelGGL((gather_fwd_kernel<DT, D, COORD, 4, true>), dim3(grid), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((gather_fwd_kernel<DT, D, SM, 4, true>), dim3(grid), dim3(kThreads), 0, s, p);
   else
-    hipLaunchKernelGGL((gather_fwd_kernel<DT, D, COORD, 4, false>), dim3(grid), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((gather_fwd_kernel<DT, D, SM, 4, false>), dim3(grid), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 
-template <int DT, bool COORD>
+template <int DT, int SM>
 hipError_t launch_d(const Params& p, hipStream_t s) {
   switch (p.D) {
-    case 16: return launch_one<DT, 16, COORD>(p, s);
-    case 32: return launch_one<DT, 32, COORD>(p, s);
-    case 64: return launch_one<DT, 64, COORD>(p, s);
-    case 128: return launch_one<DT, 128, COORD>(p, s);
+    case 16: return launch_one<DT, 16, SM>(p, s);
+    case 32: return launch_one<DT, 32, SM>(p, s);
+    case 64: return launch_one<DT, 64, SM>(p, s);
+    case 128: return launch_one<DT, 128, SM>(p, s);
   }
   return hipErrorInvalidValue;
 }
@@ -214,9 +216,18 @@ int gather_rows_per_block(int dtype, int D) {
   return (64 / (D / epl)) * kWaves;
 }
 
-hipError_t launch_gather_fwd(const Params& p, int dtype, bool coord, hipStream_t s) {
-  if (dtype == DT_BF16) return coord ? launch_d<DT_BF16, true>(p, s) : launch_d<DT_BF16, false>(p, s);
-  return coord ? launch_d<DT_F32, true>(p, s) : launch_d<DT_F32, false>(p, s);
+template <int DT>
+hipError_t launch_mode(const Params& p, int score_mode, hipStream_t s) {
+  switch (score_mode) {
+    case SM_DOT: return launch_d<DT, SM_DOT>(p, s);
+    case SM_COORD: return launch_d<DT, SM_COORD>(p, s);
+    case SM_UNIFORM: return launch_d<DT, SM_UNIFORM>(p, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gather_fwd(const Params& p, int dtype, int score_mode, hipStream_t s) {
+  return dtype == DT_BF16 ? launch_mode<DT_BF16>(p, score_mode, s) : launch_mode<DT_F32>(p, score_mode, s);
 }
 
 }  // namespace sa

@@ -18,6 +18,7 @@ struct sa_graph {
 namespace sa {
 
 enum { DT_F32 = 0, DT_BF16 = 1 };  // same values as sa_dtype
+enum { SM_DOT = 0, SM_COORD = 1, SM_UNIFORM = 2 };  // same values as sa_score
 
 // Distance-table padding: larger than any row index, so a padded slot never
 // yields a key.  Kernels read the table in groups past n_dil.
@@ -58,8 +59,8 @@ struct Params {
 
 // Launchers (defined in the .hip files).  Each validates nothing: the C ABI
 // layer has already checked every argument.  Return the launch status.
-hipError_t launch_gather_fwd(const Params& p, int dtype, bool coord, hipStream_t s);
-hipError_t launch_gather_bwd(const Params& p, int dtype, bool coord, hipStream_t s);
+hipError_t launch_gather_fwd(const Params& p, int dtype, int score_mode, hipStream_t s);
+hipError_t launch_gather_bwd(const Params& p, int dtype, int score_mode, hipStream_t s);
 int gather_rows_per_block(int dtype, int D);
 
 hipError_t launch_band_fwd(const Params& p, hipStream_t s);
@@ -67,6 +68,6 @@ hipError_t launch_band_bwd(const Params& p, hipStream_t s);
 int band_rows_per_block();
 // Compute units of the current device (queried once per device).
 int device_cu_count();
-bool band_supported(int dtype, int D, bool coord, int64_t W);
+bool band_supported(int dtype, int D, int score_mode, int64_t W);
 
 }  // namespace sa

@@ -38,6 +38,7 @@ class Workload:
     offsets: tuple = field(default_factory=tuple)
     coord: bool = False
     backward: bool = True
+    uniform: bool = False  # fixed equal weights (v alone)
 
     @property
     def dtype_name(self) -> str:
@@ -61,6 +62,9 @@ WORKLOADS = {
     "coord": Workload("coord", 4, 4, 8, 16384, 64, torch.bfloat16, 4, _pow2(0, 13), coord=True),
     # coordinate-distance score on the W = 256 band graph (secondary)
     "coord_band": Workload("coord_band", 4, 1, 8, 16384, 64, torch.bfloat16, 256, (), coord=True),
+    # the dilated graph with fixed equal weights (the same-graph comparison
+    # that isolates the scores)
+    "uniform": Workload("uniform", 6, 4, 8, 16384, 64, torch.bfloat16, 4, _pow2(0, 13), uniform=True),
     # ultra-long single head, forward only: window 64 + distances 2^6..2^25
     "ultra": Workload("ultra", 5, 1, 1, 2 ** 26, 64, torch.bfloat16, 64, _pow2(6, 25),
                       backward=False),
@@ -98,6 +102,8 @@ def make_inputs(w: Workload, device="cpu", backward: bool | None = None,
         out["ck"] = _randn((B, H, T, 3), seed_of(w, SEED_CK))
         out["gamma"] = _uniform((H,), 0.5, 2.0, seed_of(w, SEED_GAMMA))
         out["beta"] = _randn((H,), seed_of(w, SEED_BETA)) * 0.1
+    elif w.uniform:
+        pass  # v alone
     else:
         out["q"] = _randn(shp, seed_of(w, SEED_Q)).to(w.dtype)
         out["k"] = _randn(shp, seed_of(w, SEED_K)).to(w.dtype)

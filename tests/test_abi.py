@@ -134,3 +134,22 @@ def test_plan_selection():
     assert st == 0 and name.startswith("gather_bwd")
     st, name = plan(g, desc(B=1, H=8, T=16384, D=64, dtype=1, score=1), 0)
     assert st == 0 and name == "gather_fwd_kernel(coord)"
+
+
+def test_plan_uniform_mode():
+    """The uniform score reads v alone and runs on the gather kernels; its
+    backward is the key-side pass only; the band kernels do not apply."""
+    g = sa_build_graph(16384, 4, [2 ** k for k in range(14)])
+    st, name = plan(g, desc(B=4, H=8, T=16384, D=64, dtype=1, score=2), 0)
+    assert st == 0 and name == "gather_fwd_kernel(uniform)"
+    st, name = plan(g, desc(B=4, H=8, T=16384, D=64, dtype=1, score=2), 1)
+    assert st == 0 and name == "gather_bwd_kv_kernel(uniform)"
+    gb = sa_build_graph(16384, 256, ())
+    st, _ = plan(gb, desc(B=1, H=8, T=16384, D=64, dtype=1, score=2, algo=2), 0)
+    assert st == _abi.SA_ERR_UNSUPPORTED
+    # q, k, cq, ck, gamma, beta are not needed: only v must be given
+    assert fwd(g64_graph(), desc(score=2), q=None, k=None, v=None) == _abi.SA_ERR_INVALID_ARG
+
+
+def g64_graph():
+    return sa_build_graph(64, 4, [4, 8, 16, 32])

@@ -47,3 +47,15 @@ def test_roofline_switches_to_compulsory_above_one():
     assert abs(e["frac"] - m["fwd_bytes_compulsory"] / 0.1e6 / bench.HBM_PEAK_GBS) < 1e-4
     r = {"fwd_ms": 1.0, "bwd_ms": 0.0, "plan_fwd": "k", "plan_bwd": None}
     assert bench.roofline_for(w, r, m)["model"] == "gather"
+
+
+def test_models_uniform_mode():
+    """Fixed equal weights read v alone: the forward moves v, o, lse per row
+    and one v row per long-range edge; the backward dout, lse, dv per row and
+    the dout row and lse per long-range edge; 2D flops per edge each way."""
+    m = bench.models(WORKLOADS["uniform"])
+    rows = 4 * 8 * 16384
+    assert m["fwd_bytes_compulsory"] == rows * (2 * 128 + 4)
+    assert m["bwd_bytes_compulsory"] == rows * (128 + 4 + 256)
+    assert m["fwd_bytes"] - m["fwd_bytes_compulsory"] == 32 * 180228 * 128
+    assert m["fwd_flops"] == m["bwd_flops"] == 32 * 245758 * 2 * 64

@@ -47,11 +47,14 @@ def run_and_compare(w: Workload, algo="auto", backward=True, grad_dtype=None, **
     B, H, T, D = x["v"].shape
     g = sa_build_graph(T, w.window, w.offsets)
     xd = {k: v.to(DEV) for k, v in x.items()}
+    score = "coord" if w.coord else ("uniform" if w.uniform else "dot")
     _say("%s algo=%s shape=%s plan=%s" % (w.name, algo, (B, H, T, D),
-                                          sa_describe_plan(g, xd["v"], coord=w.coord, algo=algo)))
+                                          sa_describe_plan(g, xd["v"], score=score, algo=algo)))
     if w.coord:
         o, lse = sa_fwd(g, v=xd["v"], cq=xd["cq"], ck=xd["ck"], gamma=xd["gamma"], beta=xd["beta"],
                         algo=algo)
+    elif w.uniform:
+        o, lse = sa_fwd(g, v=xd["v"], algo=algo)
     else:
         o, lse = sa_fwd(g, xd["q"], xd["k"], xd["v"], algo=algo)
     torch.cuda.synchronize()
@@ -60,6 +63,8 @@ def run_and_compare(w: Workload, algo="auto", backward=True, grad_dtype=None, **
     if w.coord:
         O, L = oracle.fwd_bh(w.window, w.offsets, hv["v"], cq=hv["cq"], ck=hv["ck"], gamma=hv["gamma"],
                              beta=hv["beta"])
+    elif w.uniform:
+        O, L = oracle.fwd_bh(w.window, w.offsets, hv["v"])
     else:
         O, L = oracle.fwd_bh(w.window, w.offsets, hv["v"], q=hv["q"], k=hv["k"])
     errs = {"o": maxabs(o, O), "lse": maxabs(lse, L)}
@@ -76,6 +81,12 @@ def run_and_compare(w: Workload, algo="auto", backward=True, grad_dtype=None, **
                 err = np.abs(gr[key].double().cpu().numpy() - ref[key])
                 bound = np.maximum(tol, 1e-6 * ref["l1"])
                 errs[key] = float(np.max(err / bound)) * tol  # scaled so that <= tol passes
+        elif w.uniform:
+            gr = sa_bwd(g, v=xd["v"], o=o, lse=lse, dout=xd["do"], algo=algo, grad_dtype=grad_dtype)
+            ref = oracle.bwd_bh(w.window, w.offsets, hv["v"], hv["do"])
+            torch.cuda.synchronize()
+            assert sorted(gr) == ["dv"]
+            errs["dv"] = maxabs(gr["dv"], ref["dv"])
         else:
             gr = sa_bwd(g, xd["q"], xd["k"], xd["v"], o, lse, xd["do"], algo=algo, grad_dtype=grad_dtype)
             ref = oracle.bwd_bh(w.window, w.offsets, hv["v"], hv["do"], q=hv["q"], k=hv["k"])
@@ -177,6 +188,21 @@ RAGGED = [
 def test_ragged_shapes(B, H, T, D, dt, W, offs):
     w = Workload("ragged", 9, B, H, T, D, dt, W, offs)
     run_and_compare(w)
+
+
+@pytest.mark.parametrize("B,H,T,D,dt,W,offs", [
+    (2, 3, 300, 32, torch.float32, 3, (4, 8, 16, 32, 64, 128)),
+    (1, 2, 1000, 64, torch.bfloat16, 4, tuple(2 ** k for k in range(10))),
+    (1, 1, 129, 128, torch.bfloat16, 300, ()),
+    (3, 1, 1, 16, torch.float32, 1, ()),
+])
+def test_uniform_small(B, H, T, D, dt, W, offs):
+    w = Workload("uniform_small", 6, B, H, T, D, dt, W, offs, uniform=True)
+    run_and_compare(w)
+
+
+def test_uniform_full_size():
+    run_and_compare(WORKLOADS["uniform"])
 
 
 @pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
