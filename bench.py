@@ -35,7 +35,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workloads", default="band,dilated,coord,uniform,ultra")
+    ap.add_argument("--workloads", default="band,dilated,coord,uniform,decode_band,decode_dilated,ultra")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample length")
     ap.add_argument("--algo", default="auto")
@@ -66,6 +66,13 @@ def models(w, grad_bytes=4):
     rows = w.B * w.H * w.T
     eb = 2 if w.dtype_name == "bf16" else 4
     D = w.D
+    if w.decode:
+        # one token per (b, h) at row T - 1: its k and v rows per edge, q, o, lse
+        deg = min(w.T, w.window) + sum(1 for d in sorted(set(w.offsets)) if min(w.T, w.window) <= d <= w.T - 1)
+        bh = w.B * w.H
+        byt = bh * (deg * 2 * D * eb + 2 * D * eb + 4) + 4 * w.B
+        return {"edges": bh * deg, "fwd_bytes": byt, "bwd_bytes": 0, "fwd_bytes_compulsory": byt,
+                "bwd_bytes_compulsory": 0, "fwd_flops": bh * deg * 4 * D, "bwd_flops": 0}
     if w.uniform:
         # forward: v, o rows, lse; backward: dout, lse, dv; per long-range edge
         # the v row (forward) or the dout row and lse (backward)
@@ -178,9 +185,37 @@ def run_workload(w, steps, warmup, algo, with_backward=True):
     return res
 
 
+def run_decode(w, steps, warmup):
+    """Decode steps: sa_decode of B new tokens (every head) at row T - 1."""
+    import torch
+
+    from sparse_causal_attention_amd import sa_build_graph, sa_decode_prepared
+    from sparse_causal_attention_amd.inputs import make_decode_inputs
+
+    dev = "cuda"
+    x = make_decode_inputs(w, dev)
+    g = sa_build_graph(w.T, w.window, w.offsets)
+    call = sa_decode_prepared(g, x["q"], x["k"], x["v"])
+    for _ in range(warmup):
+        call()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for e in evs:
+        e[0].record()
+        call()
+        e[1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    f_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    return {"wall_s": wall, "ms_per_step": 1e3 * wall / steps, "fwd_ms": sum(f_ms) / len(f_ms), "bwd_ms": 0.0,
+            "fwd_ms_min": min(f_ms), "bwd_ms_min": 0.0, "plan_fwd": "decode_kernel(dot)", "plan_bwd": None,
+            "inputs": x}
+
+
 def summarize(w, r, steps):
     m = models(w)
-    tokens = w.B * w.T
+    tokens = w.B if w.decode else w.B * w.T  # a decode step makes one token per sequence
     fb = r["fwd_ms"] + r["bwd_ms"]
     wall = r["wall_s"]
     out = {
@@ -188,8 +223,9 @@ def summarize(w, r, steps):
         "shape": {"B": w.B, "H": w.H, "T": w.T, "D": w.D, "window": w.window,
                   "offsets": list(w.offsets), "dtype": w.dtype_name,
                   "score": score_name(w), "backward": w.backward},
-        "tokens_per_s": tokens * steps / wall,
-        "edges_per_s": m["edges"] * steps / wall,
+        # decode steps last microseconds: their rate comes from the kernel events
+        "tokens_per_s": tokens / (r["fwd_ms"] * 1e-3) if w.decode else tokens * steps / wall,
+        "edges_per_s": m["edges"] / (r["fwd_ms"] * 1e-3) if w.decode else m["edges"] * steps / wall,
         "ms_per_step": r["ms_per_step"],
         "fwd_ms": r["fwd_ms"], "bwd_ms": r["bwd_ms"],
         "fwd_GBs": m["fwd_bytes"] / (r["fwd_ms"] * 1e6),
@@ -328,8 +364,10 @@ def main():
         w = WORKLOADS[name]
         steps = args.steps if name != "ultra" else max(2, min(args.steps, 5))
         warm = args.warmup if name != "ultra" else min(args.warmup, 2)
+        if w.decode:
+            steps, warm = max(steps, 200), max(warm, 20)  # microsecond steps
         print("[bench] %s: %d warmup + %d timed steps" % (name, warm, steps), file=sys.stderr, flush=True)
-        r = run_workload(w, steps, warm, args.algo)
+        r = run_decode(w, steps, warm) if w.decode else run_workload(w, steps, warm, args.algo)
         s, m = summarize(w, r, steps)
         s["roofline"] = roofline_for(w, r, m)
         s["steps"] = steps

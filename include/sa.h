@@ -180,6 +180,25 @@ sa_status sa_bwd(const sa_graph* g, const sa_attn_desc* desc, const void* q, con
                  void* dk, void* dv, float* dcq, float* dck, float* dgamma, float* dbeta,
                  void* workspace, size_t workspace_bytes, sa_stream stream);
 
+/* Decode step with a key/value cache: for every (b, h), the one new token at
+ * row t_b = positions[b] of the cache attends to its neighbour list N(t_b)
+ * (the window t_b .. t_b - W + 1 and t_b - d for the long-range distances
+ * d <= t_b), with the forward's softmax and score; O(W + log T) row reads per
+ * token, independent of how long the cache is (SpatialLM-Mini news page,
+ * "What to check before adopting it in your project": the prototype had no
+ * KV cache).  desc->T is the cache capacity and must equal the graph's T;
+ * k and v (dot mode), v (uniform), or ck and v (coordinate) are the caches in
+ * [B, H, T, D] (ck: [B, H, T, 3] fp32) with rows 0 .. t_b filled.  The new
+ * token's query is q [B, H, D] (strides desc->stride_q[0..1]; stride_q[2]
+ * unused) or cq [B, H, 3] fp32 contiguous; o is [B, H, D] (stride_o[0..1])
+ * in `dtype`, lse [B, H] fp32 (natural log).  positions is a device array of
+ * B int32 (NULL: every sequence at row T - 1); a position outside [0, T)
+ * cannot be checked on the host and yields NaN in that sequence's o and lse.
+ * Same validation and status rules as sa_fwd. */
+sa_status sa_decode(const sa_graph* g, const sa_attn_desc* desc, const int32_t* positions,
+                    const void* q, const void* k, const void* v, const float* cq, const float* ck,
+                    const float* gamma, const float* beta, void* o, float* lse, sa_stream stream);
+
 /* Names the kernels sa_fwd (which = 0) or sa_bwd (which = 1) would launch for
  * this graph and descriptor, as a NUL-terminated string in buf[0..cap).
  * Validates like the call itself. */

@@ -25,7 +25,8 @@ from . import _abi
 from ._abi import (SA_ALGO_AUTO, SA_ALGO_BAND, SA_ALGO_GATHER, SA_BF16, SA_F32,
                    SA_MAX_DILATED, SA_SCORE_COORD, SA_SCORE_DOT, SA_SCORE_UNIFORM, SaError)
 
-__all__ = ["sa_build_graph", "sa_fwd", "sa_bwd", "sa_fwd_prepared", "sa_bwd_prepared",
+__all__ = ["sa_build_graph", "sa_fwd", "sa_bwd", "sa_decode", "sa_decode_prepared", "sa_fwd_prepared",
+           "sa_bwd_prepared",
            "sa_bwd_workspace_size", "sa_describe_plan", "Graph", "SaError"]
 
 _ALGOS = {"auto": SA_ALGO_AUTO, "gather": SA_ALGO_GATHER, "band": SA_ALGO_BAND}
@@ -298,6 +299,66 @@ def sa_bwd_prepared(graph: Graph, q=None, k=None, v=None, o=None, lse=None, dout
         return keep[2]
 
     call.keepalive = (keep, graph)
+    return call
+
+
+def _decode_args(graph, q, k, v, positions, cq, ck, gamma, beta, scale, o, lse, stream):
+    torch = _torch()
+    mode = _score_mode(q, k, cq)
+    _require_gpu(q=q, k=k, v=v, positions=positions, cq=cq, ck=ck, gamma=gamma, beta=beta, o=o, lse=lse)
+    B, H, T, D = v.shape
+    if mode == SA_SCORE_COORD:
+        for name, t, shp in (("cq", cq, (B, H, 3)), ("ck", ck, (B, H, T, 3)), ("gamma", gamma, (H,)),
+                             ("beta", beta, (H,))):
+            if t is None or t.dtype != torch.float32 or tuple(t.shape) != shp or not t.is_contiguous():
+                raise ValueError("%s must be a contiguous float32 tensor of shape %s" % (name, shp))
+    if positions is not None and (positions.dtype != torch.int32 or tuple(positions.shape) != (B,)
+                                  or not positions.is_contiguous()):
+        raise ValueError("positions must be a contiguous int32 [B] tensor")
+    if o is None:
+        o = torch.empty((B, H, D), dtype=v.dtype, device=v.device)
+    if lse is None:
+        lse = torch.empty((B, H), dtype=torch.float32, device=v.device)
+    if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H) or not lse.is_contiguous():
+        raise ValueError("lse must be a contiguous float32 [B, H] tensor")
+    d = _make_desc(v, score=mode, algo="auto", scale=scale, grad_dtype=SA_F32,
+                   k=k if mode == SA_SCORE_DOT else None, v=v)
+    for name, t in (("q", q if mode == SA_SCORE_DOT else None), ("o", o)):
+        if t is None:
+            continue
+        if t.dim() != 3 or tuple(t.shape) != (B, H, D) or t.stride(2) != 1:
+            raise ValueError("%s must be [B, H, D] with a contiguous last dimension" % name)
+        getattr(d, "stride_" + name)[:] = (int(t.stride(0)), int(t.stride(1)), 0)
+    args = (graph.handle, ctypes.byref(d), _ptr(positions), _ptr(q if mode == SA_SCORE_DOT else None),
+            _ptr(k if mode == SA_SCORE_DOT else None), _ptr(v), _ptr(cq), _ptr(ck), _ptr(gamma), _ptr(beta),
+            _ptr(o), _ptr(lse), _stream(stream))
+    return args, (d, o, lse)
+
+
+def sa_decode(graph: Graph, q=None, k=None, v=None, *, positions=None, cq=None, ck=None, gamma=None,
+              beta=None, scale=None, o=None, lse=None, stream=None):
+    """One new token per (batch, head) against the key/value caches.
+    q [B, H, D] (dot) or cq [B, H, 3] (coordinate) or neither (uniform);
+    k, v (or ck) caches [B, H, T, D] with T the graph's T; positions: int32
+    [B] GPU tensor with each sequence's row (None: T - 1).  Returns
+    (o [B, H, D], lse [B, H])."""
+    args, (_d, o, lse) = _decode_args(graph, q, k, v, positions, cq, ck, gamma, beta, scale, o, lse,
+                                      stream)
+    _abi.check(_abi.lib().sa_decode(*args), "sa_decode")
+    return o, lse
+
+
+def sa_decode_prepared(graph: Graph, q=None, k=None, v=None, *, positions=None, cq=None, ck=None,
+                       gamma=None, beta=None, scale=None, o=None, lse=None, stream=None):
+    """Like sa_fwd_prepared, for sa_decode."""
+    args, keep = _decode_args(graph, q, k, v, positions, cq, ck, gamma, beta, scale, o, lse, stream)
+    fn = _abi.lib().sa_decode
+
+    def call():
+        _abi.check(fn(*args), "sa_decode")
+        return keep[1], keep[2]
+
+    call.keepalive = (keep, graph, positions)
     return call
 
 

@@ -36,7 +36,7 @@ class SaAttnDesc(ctypes.Structure):
 
 EXPORTED = (
     "sa_build_graph", "sa_graph_info", "sa_graph_rows", "sa_graph_rows_reverse", "sa_graph_free",
-    "sa_fwd", "sa_bwd_workspace_size", "sa_bwd", "sa_describe_plan", "sa_status_str",
+    "sa_fwd", "sa_bwd_workspace_size", "sa_bwd", "sa_decode", "sa_describe_plan", "sa_status_str",
 )
 
 _lib = None
@@ -74,6 +74,8 @@ def lib():
     L.sa_bwd_workspace_size.argtypes = [vp, ctypes.POINTER(SaAttnDesc), ctypes.POINTER(ctypes.c_size_t)]
     L.sa_bwd.restype = i32
     L.sa_bwd.argtypes = [vp, ctypes.POINTER(SaAttnDesc)] + [vp] * 17 + [vp, ctypes.c_size_t, vp]
+    L.sa_decode.restype = i32
+    L.sa_decode.argtypes = [vp, ctypes.POINTER(SaAttnDesc)] + [vp] * 11
     L.sa_describe_plan.restype = i32
     L.sa_describe_plan.argtypes = [vp, ctypes.POINTER(SaAttnDesc), i32, ctypes.c_char_p, ctypes.c_size_t]
     L.sa_status_str.restype = ctypes.c_char_p

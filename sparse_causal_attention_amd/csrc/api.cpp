@@ -211,6 +211,47 @@ extern "C" sa_status sa_bwd(const sa_graph* g, const sa_attn_desc* d, const void
   return e == hipSuccess ? SA_OK : SA_ERR_HIP;
 }
 
+extern "C" sa_status sa_decode(const sa_graph* g, const sa_attn_desc* d, const int32_t* positions,
+                               const void* q, const void* k, const void* v, const float* cq,
+                               const float* ck, const float* gamma, const float* beta, void* o,
+                               float* lse, sa_stream stream) {
+  if (g == nullptr || d == nullptr) return SA_ERR_INVALID_ARG;
+  if (d->B < 1 || d->H < 1 || d->T < 1 || d->D < 1) return SA_ERR_INVALID_ARG;
+  if (bad_dtype(d->dtype)) return SA_ERR_INVALID_ARG;
+  if (d->score != SA_SCORE_DOT && d->score != SA_SCORE_COORD && d->score != SA_SCORE_UNIFORM)
+    return SA_ERR_INVALID_ARG;
+  if (d->T != g->T) return SA_ERR_SHAPE_MISMATCH;
+  if (d->D != 16 && d->D != 32 && d->D != 64 && d->D != 128) return SA_ERR_UNSUPPORTED;
+  if (d->B * d->H > ((int64_t)1 << 31) - 1) return SA_ERR_UNSUPPORTED;
+  const int es = esize(d->dtype);
+  const int64_t row_only[3] = {d->stride_q[0], d->stride_q[1], 0};
+  const int64_t o_row[3] = {d->stride_o[0], d->stride_o[1], 0};
+  if (v == nullptr || !aligned_rows(v, d->stride_v, es) || !offsets_fit(d, d->stride_v))
+    return SA_ERR_INVALID_ARG;
+  if (d->score == SA_SCORE_DOT) {
+    if (q == nullptr || k == nullptr) return SA_ERR_INVALID_ARG;
+    if (!aligned_rows(q, row_only, es) || !aligned_rows(k, d->stride_k, es)) return SA_ERR_INVALID_ARG;
+    if (!offsets_fit(d, row_only) || !offsets_fit(d, d->stride_k)) return SA_ERR_INVALID_ARG;
+    if (!(d->scale == d->scale)) return SA_ERR_INVALID_ARG;  // NaN scale
+  } else if (d->score == SA_SCORE_COORD) {
+    if (cq == nullptr || ck == nullptr || gamma == nullptr || beta == nullptr) return SA_ERR_INVALID_ARG;
+  }
+  if (o == nullptr || lse == nullptr) return SA_ERR_INVALID_ARG;
+  if (!aligned_rows(o, o_row, es) || !offsets_fit(d, o_row)) return SA_ERR_INVALID_ARG;
+  sa::Params p;
+  fill_common(&p, g, d);
+  p.q = q; SET_STRIDES(sq, d->stride_q);
+  p.k = k; SET_STRIDES(sk, d->stride_k);
+  p.v = v; SET_STRIDES(sv, d->stride_v);
+  p.o = o; SET_STRIDES(so, d->stride_o);
+  p.cq = cq; p.ck = ck; p.gamma = gamma; p.beta = beta;
+  p.lse = lse;
+  p.pos = positions;
+  const hipError_t e = sa::launch_decode(p, d->dtype == SA_BF16 ? sa::DT_BF16 : sa::DT_F32, d->score,
+                                         as_stream(stream));
+  return e == hipSuccess ? SA_OK : SA_ERR_HIP;
+}
+
 extern "C" sa_status sa_describe_plan(const sa_graph* g, const sa_attn_desc* d, int32_t which,
                                       char* buf, size_t cap) {
   if (buf == nullptr || cap == 0 || (which != 0 && which != 1)) return SA_ERR_INVALID_ARG;

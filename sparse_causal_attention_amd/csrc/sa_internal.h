@@ -55,6 +55,7 @@ struct Params {
   float* ndelta;    // workspace [B, H, T]: -Delta (band backward; same region)
   float* lse2;      // workspace [B, H, T]: lse * log2(e) (band backward)
   float* partials;  // workspace [B, H, nblk_q, 2]
+  const int32_t* pos;  // decode: row of each sequence's new token [B] (NULL: T - 1)
 };
 
 // Launchers (defined in the .hip files).  Each validates nothing: the C ABI
@@ -65,6 +66,7 @@ int gather_rows_per_block(int dtype, int D);
 
 hipError_t launch_band_fwd(const Params& p, hipStream_t s);
 hipError_t launch_band_bwd(const Params& p, hipStream_t s);
+hipError_t launch_decode(const Params& p, int dtype, int score_mode, hipStream_t s);
 int band_rows_per_block();
 // Compute units of the current device (queried once per device).
 int device_cu_count();

@@ -39,6 +39,7 @@ class Workload:
     coord: bool = False
     backward: bool = True
     uniform: bool = False  # fixed equal weights (v alone)
+    decode: bool = False   # one new token per sequence at row T - 1 of a T-row cache
 
     @property
     def dtype_name(self) -> str:
@@ -65,6 +66,12 @@ WORKLOADS = {
     # the dilated graph with fixed equal weights (the same-graph comparison
     # that isolates the scores)
     "uniform": Workload("uniform", 6, 4, 8, 16384, 64, torch.bfloat16, 4, _pow2(0, 13), uniform=True),
+    # decode steps: 64 sequences x 8 heads, one new token each at the end of a
+    # 16,384-row key/value cache, on the band graph and on the dilated graph
+    "decode_band": Workload("decode_band", 7, 64, 8, 16384, 64, torch.bfloat16, 256, (), backward=False,
+                            decode=True),
+    "decode_dilated": Workload("decode_dilated", 8, 64, 8, 16384, 64, torch.bfloat16, 4, _pow2(0, 13),
+                               backward=False, decode=True),
     # ultra-long single head, forward only: window 64 + distances 2^6..2^25
     "ultra": Workload("ultra", 5, 1, 1, 2 ** 26, 64, torch.bfloat16, 64, _pow2(6, 25),
                       backward=False),
@@ -105,12 +112,24 @@ def make_inputs(w: Workload, device="cpu", backward: bool | None = None,
     elif w.uniform:
         pass  # v alone
     else:
-        out["q"] = _randn(shp, seed_of(w, SEED_Q)).to(w.dtype)
+        out["q"] = _randn((B, H, D) if w.decode else shp, seed_of(w, SEED_Q)).to(w.dtype)
         out["k"] = _randn(shp, seed_of(w, SEED_K)).to(w.dtype)
     out["v"] = _randn(shp, seed_of(w, SEED_V)).to(w.dtype)
     if backward:
         out["do"] = _randn(shp, seed_of(w, SEED_DO)).to(w.dtype)
     return {k: t.to(device) for k, t in out.items()}
+
+
+def make_decode_inputs(w: Workload, device) -> dict:
+    """Decode inputs drawn on the device (the caches are too large to draw on
+    the host quickly): q [B, H, D], k and v caches [B, H, T, D], fp32 normal
+    draws from seeded device generators rounded to the workload dtype."""
+    out = {}
+    for name, t, shp in (("q", SEED_Q, (w.B, w.H, w.D)), ("k", SEED_K, (w.B, w.H, w.T, w.D)),
+                         ("v", SEED_V, (w.B, w.H, w.T, w.D))):
+        g = torch.Generator(device=device).manual_seed(seed_of(w, t))
+        out[name] = torch.randn(shp, generator=g, device=device, dtype=torch.float32).to(w.dtype)
+    return out
 
 
 def make_device_inputs_chunked(w: Workload, device, chunk_rows: int = 1 << 22) -> dict:

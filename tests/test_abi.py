@@ -153,3 +153,29 @@ def test_plan_uniform_mode():
 
 def g64_graph():
     return sa_build_graph(64, 4, [4, 8, 16, 32])
+
+
+def decode(g, d, positions=None, q=FAKE, k=FAKE, v=FAKE, cq=None, ck=None, gm=None, bt=None, o=FAKE, lse=FAKE):
+    return _abi.lib().sa_decode(g.handle, ctypes.byref(d) if d is not None else None, positions, q, k, v,
+                                cq, ck, gm, bt, o, lse, None)
+
+
+def test_decode_validation(g64):
+    E = _abi
+    assert _abi.lib().sa_decode(None, ctypes.byref(desc()), None, FAKE, FAKE, FAKE, None, None, None, None,
+                                FAKE, FAKE, None) == E.SA_ERR_INVALID_ARG
+    assert decode(g64, desc(T=65)) == E.SA_ERR_SHAPE_MISMATCH
+    assert decode(g64, desc(D=48)) == E.SA_ERR_UNSUPPORTED
+    assert decode(g64, desc(score=5)) == E.SA_ERR_INVALID_ARG
+    assert decode(g64, desc(), v=None) == E.SA_ERR_INVALID_ARG
+    assert decode(g64, desc(), q=None) == E.SA_ERR_INVALID_ARG
+    assert decode(g64, desc(), k=None) == E.SA_ERR_INVALID_ARG
+    assert decode(g64, desc(), o=None) == E.SA_ERR_INVALID_ARG
+    assert decode(g64, desc(), lse=None) == E.SA_ERR_INVALID_ARG
+    assert decode(g64, desc(), q=FAKE + 4) == E.SA_ERR_INVALID_ARG
+    d = desc()
+    d.stride_o[1] = 33  # 132-byte rows of o: not 16-byte aligned
+    assert decode(g64, d) == E.SA_ERR_INVALID_ARG
+    # coordinate mode needs cq, ck, gamma, beta; uniform mode needs v alone
+    assert decode(g64, desc(score=1), q=None, k=None, cq=FAKE, ck=FAKE, gm=FAKE) == E.SA_ERR_INVALID_ARG
+    assert decode(g64, desc(score=2), q=None, k=None, v=None) == E.SA_ERR_INVALID_ARG

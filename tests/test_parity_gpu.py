@@ -12,7 +12,7 @@ import pytest
 import torch
 
 import oracle
-from sparse_causal_attention_amd import sa_build_graph, sa_bwd, sa_describe_plan, sa_fwd
+from sparse_causal_attention_amd import sa_build_graph, sa_bwd, sa_decode, sa_describe_plan, sa_fwd
 from sparse_causal_attention_amd.inputs import (WORKLOADS, Workload, host_view, make_device_inputs_chunked,
                                                 make_inputs, sample_rows)
 
@@ -270,3 +270,106 @@ def test_outputs_stay_in_bounds():
     torch.cuda.synchronize()
     for buf in [ob, lb] + list(bufs.values()):
         assert bool((buf[:pad].float() == canary).all()) and bool((buf[-pad:].float() == canary).all())
+
+
+# ------------------------------------------------------------------ decode step
+def decode_reference(W, offs, pos, v, q=None, k=None, cq=None, ck=None, gamma=None, beta=None):
+    """Oracle forward of row pos[b] of each (b, h) slice, the new token's query
+    placed at that row."""
+    B, H, T, D = v.shape
+    O = np.empty((B, H, D))
+    L = np.empty((B, H))
+    for b in range(B):
+        t = int(pos[b])
+        for h in range(H):
+            if cq is not None:
+                cqf = np.zeros((T, 3))
+                cqf[t] = cq[b, h]
+                o, l_ = oracle.fwd(T, W, offs, v[b, h], cq=cqf, ck=ck[b, h], gamma=float(gamma[h]),
+                                   beta=float(beta[h]), rows=[t])
+            elif q is None:
+                o, l_ = oracle.fwd(T, W, offs, v[b, h], rows=[t])
+            else:
+                qf = np.zeros((T, D), dtype=q.dtype)
+                qf[t] = q[b, h]
+                o, l_ = oracle.fwd(T, W, offs, v[b, h], q=qf, k=k[b, h], rows=[t])
+            O[b, h], L[b, h] = o[0], l_[0]
+    return O, L
+
+
+@pytest.mark.parametrize("score,dt,D,W,offs", [
+    ("dot", torch.bfloat16, 64, 64, tuple(2 ** k for k in range(6, 12))),
+    ("dot", torch.float32, 32, 4, tuple(2 ** k for k in range(12))),
+    ("dot", torch.bfloat16, 128, 300, ()),
+    ("coord", torch.bfloat16, 64, 4, tuple(2 ** k for k in range(12))),
+    ("uniform", torch.float32, 16, 8, (16, 32, 64, 1024)),
+])
+def test_decode_matches_oracle_rows(score, dt, D, W, offs):
+    B, H, T = 6, 3, 3000
+    pos = np.array([0, 1, W - 1 if W > 1 else 2, 1500, 2047, T - 1], dtype=np.int32)[:B]
+    gen = torch.Generator().manual_seed(4242 + D)
+    v = torch.randn((B, H, T, D), generator=gen).to(dt)
+    g = sa_build_graph(T, W, offs)
+    posd = torch.from_numpy(pos).to(DEV)
+    kw = {}
+    if score == "dot":
+        q = torch.randn((B, H, D), generator=gen).to(dt)
+        k = torch.randn((B, H, T, D), generator=gen).to(dt)
+        o, lse = sa_decode(g, q.to(DEV), k.to(DEV), v.to(DEV), positions=posd)
+        kw = dict(q=host_view(q), k=host_view(k))
+    elif score == "coord":
+        cq = torch.randn((B, H, 3), generator=gen)
+        ck = torch.randn((B, H, T, 3), generator=gen)
+        gamma = torch.rand((H,), generator=gen) * 1.5 + 0.5
+        beta = torch.randn((H,), generator=gen) * 0.1
+        o, lse = sa_decode(g, v=v.to(DEV), positions=posd, cq=cq.to(DEV), ck=ck.to(DEV), gamma=gamma.to(DEV),
+                           beta=beta.to(DEV))
+        kw = dict(cq=cq.numpy().astype(np.float64), ck=ck.numpy().astype(np.float64), gamma=gamma.numpy(),
+                  beta=beta.numpy())
+    else:
+        o, lse = sa_decode(g, v=v.to(DEV), positions=posd)
+    torch.cuda.synchronize()
+    O, L = decode_reference(W, offs, pos, host_view(v), **kw)
+    tol = tol_of(dt)
+    eo, el = maxabs(o, O), maxabs(lse, L)
+    _say("decode %s %s D=%d W=%d errors o %.2e lse %.2e" % (score, dt, D, W, eo, el))
+    assert eo <= tol and el <= tol
+
+
+def test_decode_default_position_and_bad_positions():
+    """positions=None decodes row T - 1; a position outside [0, T) gives NaN
+    for that sequence only."""
+    B, H, T, D, W, offs = 3, 2, 500, 64, 16, (32, 64, 128, 256)
+    gen = torch.Generator().manual_seed(99)
+    q = torch.randn((B, H, D), generator=gen).to(torch.bfloat16)
+    k = torch.randn((B, H, T, D), generator=gen).to(torch.bfloat16)
+    v = torch.randn((B, H, T, D), generator=gen).to(torch.bfloat16)
+    g = sa_build_graph(T, W, offs)
+    o, lse = sa_decode(g, q.to(DEV), k.to(DEV), v.to(DEV))
+    O, L = decode_reference(W, offs, np.full(B, T - 1, dtype=np.int32), host_view(v), q=host_view(q),
+                            k=host_view(k))
+    assert maxabs(o, O) <= 2e-2 and maxabs(lse, L) <= 2e-2
+    pos = torch.tensor([-1, 7, T], dtype=torch.int32, device=DEV)
+    o2, lse2 = sa_decode(g, q.to(DEV), k.to(DEV), v.to(DEV), positions=pos)
+    torch.cuda.synchronize()
+    assert torch.isnan(o2[0]).all() and torch.isnan(lse2[0]).all()
+    assert torch.isnan(o2[2]).all() and torch.isnan(lse2[2]).all()
+    O7, L7 = decode_reference(W, offs, np.array([0, 7, 0], dtype=np.int32), host_view(v), q=host_view(q),
+                              k=host_view(k))
+    assert maxabs(o2[1], O7[1]) <= 2e-2 and maxabs(lse2[1], L7[1]) <= 2e-2
+
+
+def test_decode_full_size_sampled():
+    """64 sequences x 8 heads, a 16,384-row cache, window 256: every
+    (b, h) against the oracle at its row."""
+    B, H, T, D, W = 64, 8, 16384, 64, 256
+    gen = torch.Generator().manual_seed(7007)
+    q = torch.randn((B, H, D), generator=gen).to(torch.bfloat16)
+    k = torch.randn((B, H, T, D), generator=gen).to(torch.bfloat16)
+    v = torch.randn((B, H, T, D), generator=gen).to(torch.bfloat16)
+    pos = torch.randint(0, T, (B,), generator=gen, dtype=torch.int32)
+    g = sa_build_graph(T, W, ())
+    o, lse = sa_decode(g, q.to(DEV), k.to(DEV), v.to(DEV), positions=pos.to(DEV))
+    torch.cuda.synchronize()
+    O, L = decode_reference(W, (), pos.numpy(), host_view(v), q=host_view(q), k=host_view(k))
+    assert maxabs(o, O) <= 2e-2 and maxabs(lse, L) <= 2e-2
