@@ -139,6 +139,10 @@ typedef struct {
   float scale;         /* dot mode; <= 0 selects 1/sqrt(D).  Unused in coordinate mode. */
   int64_t stride_q[3], stride_k[3], stride_v[3], stride_o[3], stride_do[3]; /* (b, h, t) */
   int64_t stride_dq[3], stride_dk[3], stride_dv[3];                          /* (b, h, t) */
+  int64_t H_kv;        /* key/value heads; 0 selects H.  H must be a multiple of H_kv: query
+                          head h reads key/value head h / (H / H_kv), and k, v, dk, dv (and
+                          the decode caches) are [B, H_kv, T, D] with strides over (b, h_kv,
+                          t).  Coordinate mode needs H_kv = H (per-head coordinates). */
 } sa_attn_desc;
 
 /* Forward (SpatialLM-Mini news page, "How tokens choose whom to listen to";
@@ -163,6 +167,7 @@ sa_status sa_bwd_workspace_size(const sa_graph* g, const sa_attn_desc* desc, siz
  * lse:  dP_ij = <dout_i, v_j>,  Delta_i = <dout_i, o_i>,
  *       dS_ij = P_ij (dP_ij - Delta_i),  P_ij = exp(s_ij - lse_i),
  *   dot mode:   dq_i = scale sum_j dS_ij k_j,   dk_j = scale sum_i dS_ij q_i,
+ *   (with H_kv < H, dk and dv of a key/value head also sum over its query heads)
  *   both modes: dv_j = sum_i P_ij dout_i,
  *   coordinate: dcq_i = -2 gamma sum_j dS_ij (c_q,i - c_k,j),
  *               dck_j =  2 gamma sum_i dS_ij (c_q,i - c_k,j),

@@ -128,10 +128,17 @@ def _stream(stream):
 
 
 def _make_desc(ref, *, score, algo, scale, grad_dtype, q=None, k=None, v=None, o=None, dout=None,
-               dq=None, dk=None, dv=None) -> _abi.SaAttnDesc:
-    B, H, T, D = ref.shape
+               dq=None, dk=None, dv=None, heads=None) -> _abi.SaAttnDesc:
+    """ref: a [B, H_kv, T, D] key/value-side tensor; heads: the query heads H
+    (None: H_kv).  Query-side tensors are checked against [B, H, T, D],
+    key/value-side ones against [B, H_kv, T, D]."""
+    B, Hkv, T, D = ref.shape
+    H = Hkv if heads is None else int(heads)
+    if H % Hkv != 0:
+        raise ValueError("query heads (%d) must be a multiple of key/value heads (%d)" % (H, Hkv))
     d = _abi.SaAttnDesc()
     d.B, d.H, d.T, d.D = B, H, T, D
+    d.H_kv = Hkv
     d.dtype = _dtype_code(ref)
     d.grad_dtype = grad_dtype
     d.score = score
@@ -139,10 +146,19 @@ def _make_desc(ref, *, score, algo, scale, grad_dtype, q=None, k=None, v=None, o
     d.scale = 0.0 if scale is None else float(scale)
     for name, t in (("q", q), ("k", k), ("v", v), ("o", o), ("do", dout), ("dq", dq), ("dk", dk),
                     ("dv", dv)):
-        if t is not None and tuple(t.shape) != (B, H, T, D):
-            raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), (B, H, T, D)))
+        want = (B, Hkv if name in ("k", "v", "dk", "dv") else H, T, D)
+        if t is not None and tuple(t.shape) != want:
+            raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), want))
         getattr(d, "stride_" + name)[:] = _strides(t, name)
     return d
+
+
+def _query_heads(q, o, v):
+    """H: from q when given, else from o, else the key/value heads of v."""
+    for t in (q, o):
+        if t is not None:
+            return t.shape[1]
+    return v.shape[1]
 
 
 def _coord_args(cq, ck, gamma, beta, B, H, T):
@@ -168,16 +184,17 @@ def _fwd_args(graph, q, k, v, cq, ck, gamma, beta, scale, o, lse, algo, stream):
     mode = _score_mode(q, k, cq)
     coord = mode == SA_SCORE_COORD
     _require_gpu(q=q, k=k, v=v, cq=cq, ck=ck, gamma=gamma, beta=beta, o=o, lse=lse)
-    B, H, T, D = v.shape
+    B, _, T, D = v.shape
+    H = _query_heads(q, o, v)
     if coord:
         _coord_args(cq, ck, gamma, beta, B, H, T)
     if o is None:
-        o = torch.empty_like(v, memory_format=torch.contiguous_format)
+        o = torch.empty((B, H, T, D), dtype=v.dtype, device=v.device)
     if lse is None:
         lse = torch.empty((B, H, T), dtype=torch.float32, device=v.device)
     if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, T) or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [B, H, T] tensor")
-    d = _make_desc(v, score=mode, algo=algo, scale=scale,
+    d = _make_desc(v, score=mode, algo=algo, scale=scale, heads=H,
                    grad_dtype=SA_F32, q=None if coord else q, k=None if coord else k, v=v, o=o)
     args = (graph.handle, ctypes.byref(d), _ptr(None if coord else q), _ptr(None if coord else k),
             _ptr(v), _ptr(cq), _ptr(ck), _ptr(gamma), _ptr(beta), _ptr(o), _ptr(lse), _stream(stream))
@@ -208,8 +225,10 @@ def sa_fwd_prepared(graph: Graph, q=None, k=None, v=None, *, cq=None, ck=None, g
     return call
 
 
-def sa_bwd_workspace_size(graph: Graph, v, grad_dtype=None) -> int:
-    d = _make_desc(v, score=SA_SCORE_DOT, algo="auto", scale=None,
+def sa_bwd_workspace_size(graph: Graph, v, grad_dtype=None, heads=None) -> int:
+    """Workspace bytes of sa_bwd for key/value tensor v ([B, H_kv, T, D]) and
+    `heads` query heads (None: H_kv)."""
+    d = _make_desc(v, score=SA_SCORE_DOT, algo="auto", scale=None, heads=heads,
                    grad_dtype=SA_F32 if grad_dtype is None else _dtype_code_of(grad_dtype))
     n = ctypes.c_size_t()
     _abi.check(_abi.lib().sa_bwd_workspace_size(graph.handle, ctypes.byref(d), ctypes.byref(n)),
@@ -229,7 +248,8 @@ def _bwd_args(graph, q, k, v, o, lse, dout, cq, ck, gamma, beta, scale, grad_dty
     coord = mode == SA_SCORE_COORD
     uniform = mode == SA_SCORE_UNIFORM
     _require_gpu(q=q, k=k, v=v, o=o, lse=lse, dout=dout, cq=cq, ck=ck, gamma=gamma, beta=beta)
-    B, H, T, D = v.shape
+    B, Hkv, T, D = v.shape
+    H = _query_heads(q, o, v)
     gdt = torch.float32 if grad_dtype is None else grad_dtype
     gcode = _dtype_code_of(gdt)
     dev = v.device
@@ -243,12 +263,12 @@ def _bwd_args(graph, q, k, v, o, lse, dout, cq, ck, gamma, beta, scale, grad_dty
         dq = dk = None
     else:
         dq = torch.empty((B, H, T, D), dtype=gdt, device=dev) if dq is None else dq
-        dk = torch.empty((B, H, T, D), dtype=gdt, device=dev) if dk is None else dk
-    dv = torch.empty((B, H, T, D), dtype=gdt, device=dev) if dv is None else dv
+        dk = torch.empty((B, Hkv, T, D), dtype=gdt, device=dev) if dk is None else dk
+    dv = torch.empty((B, Hkv, T, D), dtype=gdt, device=dev) if dv is None else dv
     for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
         if t is not None and t.dtype != gdt:
             raise ValueError("%s must have the gradient dtype %s" % (name, gdt))
-    d = _make_desc(v, score=mode, algo=algo, scale=scale,
+    d = _make_desc(v, score=mode, algo=algo, scale=scale, heads=H,
                    grad_dtype=gcode, q=None if coord else q, k=None if coord else k, v=v, o=o,
                    dout=dout, dq=None if coord else dq, dk=None if coord else dk, dv=dv)
     L = _abi.lib()
@@ -306,7 +326,8 @@ def _decode_args(graph, q, k, v, positions, cq, ck, gamma, beta, scale, o, lse, 
     torch = _torch()
     mode = _score_mode(q, k, cq)
     _require_gpu(q=q, k=k, v=v, positions=positions, cq=cq, ck=ck, gamma=gamma, beta=beta, o=o, lse=lse)
-    B, H, T, D = v.shape
+    B, _, T, D = v.shape
+    H = q.shape[1] if q is not None else (o.shape[1] if o is not None else v.shape[1])
     if mode == SA_SCORE_COORD:
         for name, t, shp in (("cq", cq, (B, H, 3)), ("ck", ck, (B, H, T, 3)), ("gamma", gamma, (H,)),
                              ("beta", beta, (H,))):
@@ -321,7 +342,7 @@ def _decode_args(graph, q, k, v, positions, cq, ck, gamma, beta, scale, o, lse, 
         lse = torch.empty((B, H), dtype=torch.float32, device=v.device)
     if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H) or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [B, H] tensor")
-    d = _make_desc(v, score=mode, algo="auto", scale=scale, grad_dtype=SA_F32,
+    d = _make_desc(v, score=mode, algo="auto", scale=scale, grad_dtype=SA_F32, heads=H,
                    k=k if mode == SA_SCORE_DOT else None, v=v)
     for name, t in (("q", q if mode == SA_SCORE_DOT else None), ("o", o)):
         if t is None:
@@ -362,12 +383,12 @@ def sa_decode_prepared(graph: Graph, q=None, k=None, v=None, *, positions=None, 
     return call
 
 
-def sa_describe_plan(graph: Graph, v, *, coord=False, algo="auto", which="fwd", score=None) -> str:
+def sa_describe_plan(graph: Graph, v, *, coord=False, algo="auto", which="fwd", score=None, heads=None) -> str:
     """Names of the kernels sa_fwd ("fwd") or sa_bwd ("bwd") would launch.
     score: "dot", "coord" or "uniform" (default: "coord" if coord else "dot")."""
     modes = {"dot": SA_SCORE_DOT, "coord": SA_SCORE_COORD, "uniform": SA_SCORE_UNIFORM}
     mode = modes[score] if score is not None else (SA_SCORE_COORD if coord else SA_SCORE_DOT)
-    d = _make_desc(v, score=mode, algo=algo, scale=None, grad_dtype=SA_F32)
+    d = _make_desc(v, score=mode, algo=algo, scale=None, grad_dtype=SA_F32, heads=heads)
     buf = ctypes.create_string_buffer(256)
     _abi.check(_abi.lib().sa_describe_plan(graph.handle, ctypes.byref(d), 0 if which == "fwd" else 1,
                                            buf, 256), "sa_describe_plan")

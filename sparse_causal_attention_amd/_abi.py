@@ -31,6 +31,7 @@ class SaAttnDesc(ctypes.Structure):
         ("stride_q", i64 * 3), ("stride_k", i64 * 3), ("stride_v", i64 * 3),
         ("stride_o", i64 * 3), ("stride_do", i64 * 3),
         ("stride_dq", i64 * 3), ("stride_dk", i64 * 3), ("stride_dv", i64 * 3),
+        ("H_kv", i64),
     ]
 
 

@@ -14,6 +14,17 @@
 namespace {
 
 bool bad_dtype(int32_t dt) { return dt != SA_F32 && dt != SA_BF16; }
+
+// Key/value heads (0 selects H).
+int64_t kv_heads(const sa_attn_desc* d) { return d->H_kv > 0 ? d->H_kv : d->H; }
+
+// Grouped key/value heads: H a multiple of H_kv; per-head coordinates only.
+sa_status check_heads(const sa_attn_desc* d) {
+  const int64_t hkv = kv_heads(d);
+  if (d->H_kv < 0 || d->H % hkv != 0) return SA_ERR_INVALID_ARG;
+  if (hkv != d->H && d->score == SA_SCORE_COORD) return SA_ERR_UNSUPPORTED;
+  return SA_OK;
+}
 int esize(int32_t dt) { return dt == SA_BF16 ? 2 : 4; }
 
 // Row starts 16-byte aligned for 16-byte vector accesses.
@@ -50,6 +61,7 @@ sa_status check_common(const sa_graph* g, const sa_attn_desc* d, const void* q, 
   if (d->T != g->T) return SA_ERR_SHAPE_MISMATCH;
   if (d->D != 16 && d->D != 32 && d->D != 64 && d->D != 128) return SA_ERR_UNSUPPORTED;
   if (d->B * d->H > (int64_t)1 << 24) return SA_ERR_UNSUPPORTED;
+  if (const sa_status hs = check_heads(d); hs != SA_OK) return hs;
   // blocks of the smallest row tile must be countable in int32
   if ((double)d->B * d->H * (double)d->T > 1.0e12) return SA_ERR_UNSUPPORTED;
   const int es = esize(d->dtype);
@@ -78,6 +90,8 @@ void fill_common(sa::Params* p, const sa_graph* g, const sa_attn_desc* d) {
   p->T = (int32_t)d->T;
   p->D = (int32_t)d->D;
   p->W = (int32_t)g->W;
+  p->Hkv = (int32_t)kv_heads(d);
+  p->G = (int32_t)(d->H / p->Hkv);
   p->n_dil = g->n_dil;
   for (int t = 0; t < SA_MAX_DILATED + 8; ++t)
     p->dil[t] = t < g->n_dil ? (int32_t)g->dil[t] : sa::kUnreachable;
@@ -134,7 +148,8 @@ size_t workspace_bytes_for(const sa_attn_desc* d) {
   const int rpb = sa::gather_rows_per_block(d->dtype == SA_BF16 ? sa::DT_BF16 : sa::DT_F32,
                                             (int)d->D);
   const size_t nblk = (size_t)((d->T + rpb - 1) / rpb);
-  return 2 * align256(rows * sizeof(float)) + align256((size_t)d->B * d->H * nblk * 2 * sizeof(float));
+  const size_t partials = kv_heads(d) != d->H ? 2 * align256(rows * (size_t)d->D * sizeof(float)) : 0;
+  return 2 * align256(rows * sizeof(float)) + align256((size_t)d->B * d->H * nblk * 2 * sizeof(float)) + partials;
 }
 
 }  // namespace
@@ -146,6 +161,7 @@ extern "C" sa_status sa_bwd_workspace_size(const sa_graph* g, const sa_attn_desc
   if (bad_dtype(d->dtype)) return SA_ERR_INVALID_ARG;
   if (d->D != 16 && d->D != 32 && d->D != 64 && d->D != 128) return SA_ERR_UNSUPPORTED;
   if (d->T != g->T) return SA_ERR_SHAPE_MISMATCH;
+  if (const sa_status hs = check_heads(d); hs != SA_OK) return hs;
   *bytes = workspace_bytes_for(d);
   return SA_OK;
 }
@@ -204,6 +220,14 @@ extern "C" sa_status sa_bwd(const sa_graph* g, const sa_attn_desc* d, const void
   p.ndelta = p.delta;
   p.lse2 = reinterpret_cast<float*>(ws + row_bytes);
   p.partials = reinterpret_cast<float*>(ws + 2 * row_bytes);
+  if (p.G > 1) {  // per-query-head dk, dv partials of the band kernels
+    const int rpb = sa::gather_rows_per_block(d->dtype == SA_BF16 ? sa::DT_BF16 : sa::DT_F32, (int)d->D);
+    const size_t nblk = (size_t)((d->T + rpb - 1) / rpb);
+    char* pp = ws + 2 * row_bytes + align256((size_t)d->B * d->H * nblk * 2 * sizeof(float));
+    const size_t pbytes = align256((size_t)d->B * d->H * d->T * d->D * sizeof(float));
+    p.pdk = reinterpret_cast<float*>(pp);
+    p.pdv = reinterpret_cast<float*>(pp + pbytes);
+  }
   hipError_t e = plan.path == Path::Band
                      ? sa::launch_band_bwd(p, as_stream(stream))
                      : sa::launch_gather_bwd(p, d->dtype == SA_BF16 ? sa::DT_BF16 : sa::DT_F32,
@@ -223,6 +247,7 @@ extern "C" sa_status sa_decode(const sa_graph* g, const sa_attn_desc* d, const i
   if (d->T != g->T) return SA_ERR_SHAPE_MISMATCH;
   if (d->D != 16 && d->D != 32 && d->D != 64 && d->D != 128) return SA_ERR_UNSUPPORTED;
   if (d->B * d->H > ((int64_t)1 << 31) - 1) return SA_ERR_UNSUPPORTED;
+  if (const sa_status hs = check_heads(d); hs != SA_OK) return hs;
   const int es = esize(d->dtype);
   const int64_t row_only[3] = {d->stride_q[0], d->stride_q[1], 0};
   const int64_t o_row[3] = {d->stride_o[0], d->stride_o[1], 0};

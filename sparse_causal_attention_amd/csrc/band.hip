@@ -95,8 +95,9 @@ __global__ __launch_bounds__(kThreads, 4) void band_fwd_kernel(Params p) {
   const int mc = m < p.T ? m : p.T - 1;
 
   const char* qbase = static_cast<const char*>(p.q) + (b * p.sq_b + h * p.sq_h) * 2;
-  const char* kbase = static_cast<const char*>(p.k) + (b * p.sk_b + h * p.sk_h) * 2;
-  const char* vbase = static_cast<const char*>(p.v) + (b * p.sv_b + h * p.sv_h) * 2;
+  const int hk = h / p.G;  // key/value head shared by G query heads
+  const char* kbase = static_cast<const char*>(p.k) + (b * p.sk_b + hk * p.sk_h) * 2;
+  const char* vbase = static_cast<const char*>(p.v) + (b * p.sv_b + hk * p.sv_h) * 2;
   const int64_t sqt = p.sq_t * 2, skt = p.sk_t * 2, svt = p.sv_t * 2;
 
   const int W = p.W;

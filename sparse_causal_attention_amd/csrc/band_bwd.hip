@@ -122,6 +122,7 @@ __global__ __launch_bounds__(kThreads) void band_bwd_prepass_kernel(Params p) {
 struct Unit {
   int role;  // 0: dq, 1: dk/dv, -1: no unit
   int b, h, bh;
+  int hk;    // key/value head of query head h
   int r0;    // first owned row: query (dq) or key (dk/dv)
   int s0;    // first streamed row: key (dq) or query (dk/dv); a multiple of kTile
   int nt;    // streamed tiles
@@ -134,6 +135,7 @@ __device__ __forceinline__ Unit make_unit(const Params& p, int pair, int role, i
   const int rb = pair - u.bh * nblk;
   u.b = u.bh / p.H;
   u.h = u.bh - u.b * p.H;
+  u.hk = u.h / p.G;
   u.r0 = rb * kRows;
   const int last = u.r0 + kRows - 1 < p.T - 1 ? u.r0 + kRows - 1 : p.T - 1;
   if (role == 0) {  // keys max(0, r0 - W + 1) .. last
@@ -160,6 +162,10 @@ struct RowOps {
 __device__ __forceinline__ const char* tensor_base(const void* t, int64_t sb, int64_t sh, const Unit& u) {
   return static_cast<const char*>(t) + (u.b * sb + u.h * sh) * 2;
 }
+// K and V live on the unit's key/value head.
+__device__ __forceinline__ const char* tensor_base_kv(const void* t, int64_t sb, int64_t sh, const Unit& u) {
+  return static_cast<const char*>(t) + (u.b * sb + u.hk * sh) * 2;
+}
 
 // Direct loads of a tile's 64 per-row floats (one wavefront, 4 B per lane).
 __device__ __forceinline__ void rows_issue(const float* src, int r0, int T, float* dst, int lane) {
@@ -176,8 +182,8 @@ __device__ __forceinline__ void issue_tile(const Params& p, const Unit& u, int j
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r0 = u.s0 + j * kTile;
   if (u.role == 0) {
-    tile_issue_clamped(tensor_base(p.k, p.sk_b, p.sk_h, u), p.sk_t * 2, r0, p.T, a, wave, lane);
-    tile_issue_clamped(tensor_base(p.v, p.sv_b, p.sv_h, u), p.sv_t * 2, r0, p.T, bt, wave, lane);
+    tile_issue_clamped(tensor_base_kv(p.k, p.sk_b, p.sk_h, u), p.sk_t * 2, r0, p.T, a, wave, lane);
+    tile_issue_clamped(tensor_base_kv(p.v, p.sv_b, p.sv_h, u), p.sv_t * 2, r0, p.T, bt, wave, lane);
   } else {
     tile_issue_clamped(tensor_base(p.q, p.sq_b, p.sq_h, u), p.sq_t * 2, r0, p.T, a, wave, lane);
     tile_issue_clamped(tensor_base(p.dout, p.sdo_b, p.sdo_h, u), p.sdo_t * 2, r0, p.T, bt, wave, lane);
@@ -216,8 +222,8 @@ __device__ __forceinline__ void issue_stage(const Params& p, const Unit& u, cons
       rows_issue(p.lse2 + (int64_t)u.bh * p.T, u.r0 + 64, p.T, bf.sl2 + 64, lane);
     }
   } else {
-    xb = tensor_base(p.k, p.sk_b, p.sk_h, u), xs = p.sk_t * 2;
-    yb = tensor_base(p.v, p.sv_b, p.sv_h, u), ys = p.sv_t * 2;
+    xb = tensor_base_kv(p.k, p.sk_b, p.sk_h, u), xs = p.sk_t * 2;
+    yb = tensor_base_kv(p.v, p.sv_b, p.sv_h, u), ys = p.sv_t * 2;
   }
   tile_issue_clamped(xb, xs, u.r0, p.T, bf.sx, wave, lane);
   tile_issue_clamped(xb, xs, u.r0 + kTile, p.T, bf.sx + kTileBytes, wave, lane);
@@ -321,8 +327,8 @@ __device__ __forceinline__ void dq_unit(const Params& p, const Unit& u, const Ro
 
   if constexpr (HAS_DIL) {
     // long-range edges j = m - d
-    const char* kb = tensor_base(p.k, p.sk_b, p.sk_h, u);
-    const char* vb = tensor_base(p.v, p.sv_b, p.sv_h, u);
+    const char* kb = tensor_base_kv(p.k, p.sk_b, p.sk_h, u);
+    const char* vb = tensor_base_kv(p.v, p.sv_b, p.sv_h, u);
     const int64_t skt = p.sk_t * 2, svt = p.sv_t * 2;
     for (int t = 0; t < p.n_dil; ++t) {
       const int j = mc - p.dil[t];
@@ -484,8 +490,13 @@ __device__ __forceinline__ void dkv_unit(const Params& p, const Unit& u, const R
   }
 
   if (n < p.T) {
-    store_acc_row<GRAD_BF16>(p.dv, u.b * p.sdv_b + u.h * p.sdv_h + (int64_t)n * p.sdv_t, dv, 1.f, half);
-    store_acc_row<GRAD_BF16>(p.dk, u.b * p.sdk_b + u.h * p.sdk_h + (int64_t)n * p.sdk_t, dk, p.scale, half);
+    if (p.G == 1) {
+      store_acc_row<GRAD_BF16>(p.dv, u.b * p.sdv_b + u.h * p.sdv_h + (int64_t)n * p.sdv_t, dv, 1.f, half);
+      store_acc_row<GRAD_BF16>(p.dk, u.b * p.sdk_b + u.h * p.sdk_h + (int64_t)n * p.sdk_t, dk, p.scale, half);
+    } else {  // this query head's share; summed over the group by band_bwd_group_sum_kernel
+      store_acc_row<false>(p.pdv, ((int64_t)u.bh * p.T + n) * 64, dv, 1.f, half);
+      store_acc_row<false>(p.pdk, ((int64_t)u.bh * p.T + n) * 64, dk, p.scale, half);
+    }
   }
 }
 
@@ -518,7 +529,7 @@ __global__ __launch_bounds__(kThreads, 2) void band_bwd_kernel(Params p) {
       u = make_unit(p, pair, k & 1, nblk);
     } else {
       u.role = -1;
-      u.b = u.h = u.bh = u.r0 = u.s0 = u.nt = 0;
+      u.b = u.h = u.bh = u.hk = u.r0 = u.s0 = u.nt = 0;
     }
     return u;
   };
@@ -543,6 +554,33 @@ __global__ __launch_bounds__(kThreads, 2) void band_bwd_kernel(Params p) {
   }
 }
 
+// dk, dv of key/value head hk = the sum, in head order, of the partials of its
+// G query heads (one thread per 4 elements of a row).
+__global__ __launch_bounds__(kThreads) void band_bwd_group_sum_kernel(Params p) {
+  const int64_t rows = (int64_t)p.B * p.Hkv * p.T;
+  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  if (idx >= rows * 16) return;
+  const int c4 = (int)(idx % 16);
+  const int64_t r = idx / 16;
+  const int t = (int)(r % p.T);
+  const int64_t bk = r / p.T;
+  const int b = (int)(bk / p.Hkv), hk = (int)(bk % p.Hkv);
+  float4 sk = make_float4(0.f, 0.f, 0.f, 0.f), sv = sk;
+  for (int g = 0; g < p.G; ++g) {
+    const int64_t src = ((((int64_t)b * p.H + hk * p.G + g) * p.T + t) * 64) + c4 * 4;
+    const float4 a = *reinterpret_cast<const float4*>(p.pdk + src);
+    const float4 c = *reinterpret_cast<const float4*>(p.pdv + src);
+    sk.x += a.x; sk.y += a.y; sk.z += a.z; sk.w += a.w;
+    sv.x += c.x; sv.y += c.y; sv.z += c.z; sv.w += c.w;
+  }
+  const float fk[4] = {sk.x, sk.y, sk.z, sk.w}, fv[4] = {sv.x, sv.y, sv.z, sv.w};
+  const int gb = p.grad_bf16 ? 2 : 4;
+  char* dkrow = static_cast<char*>(p.dk) + (b * p.sdk_b + hk * p.sdk_h + (int64_t)t * p.sdk_t + c4 * 4) * gb;
+  char* dvrow = static_cast<char*>(p.dv) + (b * p.sdv_b + hk * p.sdv_h + (int64_t)t * p.sdv_t + c4 * 4) * gb;
+  store_vals<4>(dkrow, fk, p.grad_bf16 != 0);
+  store_vals<4>(dvrow, fv, p.grad_bf16 != 0);
+}
+
 template <bool GRAD_BF16, bool HAS_DIL>
 hipError_t launch(const Params& p, hipStream_t s) {
   const int64_t rows = (int64_t)p.B * p.H * p.T;
@@ -561,6 +599,11 @@ hipError_t launch(const Params& p, hipStream_t s) {
   grid = (grid / kNumXcd) * kNumXcd;
   if (grid < kNumXcd) grid = kNumXcd;
   hipLaunchKernelGGL((band_bwd_kernel<GRAD_BF16, HAS_DIL>), dim3(grid), dim3(kThreads), 0, s, p);
+  e = hipGetLastError();
+  if (e != hipSuccess || p.G == 1) return e;
+  const int64_t n4 = (int64_t)p.B * p.Hkv * p.T * 16;  // four elements per thread
+  hipLaunchKernelGGL(band_bwd_group_sum_kernel, dim3((unsigned)((n4 + kThreads - 1) / kThreads)), dim3(kThreads), 0,
+                     s, p);
   return hipGetLastError();
 }
 

@@ -47,8 +47,9 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Params p) {
   while (nd < p.n_dil && p.dil[nd] <= tt) ++nd;  // uniform, ascending distances
   const int E = wn + nd;
 
-  const char* khead = static_cast<const char*>(p.k) + (b * p.sk_b + h * p.sk_h) * EB + sub * 16;
-  const char* vhead = static_cast<const char*>(p.v) + (b * p.sv_b + h * p.sv_h) * EB + sub * 16;
+  const int hk = h / p.G;  // key/value head shared by G query heads
+  const char* khead = static_cast<const char*>(p.k) + (b * p.sk_b + hk * p.sk_h) * EB + sub * 16;
+  const char* vhead = static_cast<const char*>(p.v) + (b * p.sv_b + hk * p.sv_h) * EB + sub * 16;
   uint4 qraw = make_uint4(0u, 0u, 0u, 0u);
   float cqi[3] = {0.f, 0.f, 0.f};
   float gl2 = 0.f;

@@ -59,8 +59,9 @@ __global__ __launch_bounds__(kThreads) void gather_bwd_q_kernel(Params p) {
   if (!row_ok) i = p.T - 1;
   const int imax = i0w + RPW - 1 < p.T - 1 ? i0w + RPW - 1 : p.T - 1;
 
-  const char* khead = static_cast<const char*>(p.k) + (b * p.sk_b + h * p.sk_h) * EB;
-  const char* vhead = static_cast<const char*>(p.v) + (b * p.sv_b + h * p.sv_h) * EB;
+  const int hk = h / p.G;  // key/value head shared by G query heads
+  const char* khead = static_cast<const char*>(p.k) + (b * p.sk_b + hk * p.sk_h) * EB;
+  const char* vhead = static_cast<const char*>(p.v) + (b * p.sv_b + hk * p.sv_h) * EB;
   const int64_t skt = p.sk_t * EB, svt = p.sv_t * EB;
   int64_t kl = (int64_t)i * skt + sub * 16, vl = (int64_t)i * svt + sub * 16;
   uint32_t kl32 = (uint32_t)kl, vl32 = (uint32_t)vl;
@@ -234,11 +235,16 @@ __global__ __launch_bounds__(kThreads) void gather_bwd_kv_kernel(Params p) {
   constexpr int EPL = Gm::EPL, LG = Gm::LG, RPW = Gm::RPW, RPB = Gm::RPB;
   constexpr int EB = F::BYTES;
 
+  // one key row per lane group of key/value head hk; the query side runs
+  // over the G query heads hk G .. hk G + G - 1 that share it (G = 1 in
+  // coordinate mode, where bh then names both)
   const int nblk = (p.T + RPB - 1) / RPB;
-  const int logical = xcd_logical_block(p.B * p.H * nblk);
+  const int logical = xcd_logical_block(p.B * p.Hkv * nblk);
   if (logical < 0) return;
-  const int bh = logical / nblk, rb = logical - bh * nblk;
-  const int b = bh / p.H, h = bh - b * p.H;
+  const int bk = logical / nblk, rb = logical - bk * nblk;
+  const int b = bk / p.Hkv, hk = bk - b * p.Hkv;
+  const int h0 = hk * p.G;
+  const int bh = b * p.H + h0;  // first query head of the group
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int sub = lane % LG;
@@ -248,20 +254,20 @@ __global__ __launch_bounds__(kThreads) void gather_bwd_kv_kernel(Params p) {
   if (!row_ok) j = p.T - 1;
   const int room = p.T - 1 - j0w;  // largest distance any key of the wave can use
 
-  const char* qhead = static_cast<const char*>(p.q) + (b * p.sq_b + h * p.sq_h) * EB;
-  const char* dohead = static_cast<const char*>(p.dout) + (b * p.sdo_b + h * p.sdo_h) * EB;
+  const char* qhead = nullptr;   // set per query head below
+  const char* dohead = nullptr;
   const int64_t sqt = p.sq_t * EB, sdot = p.sdo_t * EB;
   int64_t ql = (int64_t)j * sqt + sub * 16, dl = (int64_t)j * sdot + sub * 16;
   uint32_t ql32 = (uint32_t)ql, dl32 = (uint32_t)dl;
   asm volatile("" : "+v"(ql32), "+v"(dl32), "+v"(ql), "+v"(dl));  // keep addresses scalar-offset
-  const float* lseb = p.lse + (int64_t)bh * p.T;
-  const float* delb = UNIFORM ? nullptr : p.delta + (int64_t)bh * p.T;
-  const float bsub = COORD ? p.beta[h] : 0.f;  // lse includes beta in coordinate mode
+  const float* lseb = nullptr;
+  const float* delb = nullptr;
+  const float bsub = COORD ? p.beta[h0] : 0.f;  // lse includes beta in coordinate mode
 
   // own k and v fragments as stored (dot operands)
   uint4 kraw_j = make_uint4(0u, 0u, 0u, 0u), vraw_j;
   {
-    const char* vrow = static_cast<const char*>(p.v) + (b * p.sv_b + h * p.sv_h + j * p.sv_t) * EB +
+    const char* vrow = static_cast<const char*>(p.v) + (b * p.sv_b + hk * p.sv_h + j * p.sv_t) * EB +
                        sub * 16;
     vraw_j = ld16(vrow);
   }
@@ -269,13 +275,13 @@ __global__ __launch_bounds__(kThreads) void gather_bwd_kv_kernel(Params p) {
   float gl2 = 0.f, gam = 0.f;
   const float* cqb = nullptr;
   if constexpr (SM == SM_DOT) {
-    const char* krow = static_cast<const char*>(p.k) + (b * p.sk_b + h * p.sk_h + j * p.sk_t) * EB +
+    const char* krow = static_cast<const char*>(p.k) + (b * p.sk_b + hk * p.sk_h + j * p.sk_t) * EB +
                        sub * 16;
     kraw_j = ld16(krow);
   } else if constexpr (COORD) {
     const float* ckr = p.ck + ((int64_t)bh * p.T + j) * 3;
     ckj[0] = ckr[0]; ckj[1] = ckr[1]; ckj[2] = ckr[2];
-    gam = p.gamma[h];
+    gam = p.gamma[h0];
     gl2 = gam * kLog2e;
     cqb = p.cq + (int64_t)bh * p.T * 3;
   }
@@ -353,29 +359,35 @@ __global__ __launch_bounds__(kThreads) void gather_bwd_kv_kernel(Params p) {
   };
 
   const int wend = p.W < room + 1 ? p.W : room + 1;
-  for (int t0 = 0; t0 < wend; t0 += G) {
-    int dist[G];
+  for (int hq = h0; hq < h0 + p.G; ++hq) {  // the query heads of this key/value head, in order
+    qhead = static_cast<const char*>(p.q) + (b * p.sq_b + hq * p.sq_h) * EB;
+    dohead = static_cast<const char*>(p.dout) + (b * p.sdo_b + hq * p.sdo_h) * EB;
+    lseb = p.lse + ((int64_t)b * p.H + hq) * p.T;
+    if constexpr (!UNIFORM) delb = p.delta + ((int64_t)b * p.H + hq) * p.T;
+    for (int t0 = 0; t0 < wend; t0 += G) {
+      int dist[G];
 #pragma unroll
-    for (int g = 0; g < G; ++g) dist[g] = t0 + g < p.W ? t0 + g : kUnreachable;
-    group(dist);
-  }
-  for (int t0 = 0; t0 < p.n_dil; t0 += G) {
-    int dist[G];
+      for (int g = 0; g < G; ++g) dist[g] = t0 + g < p.W ? t0 + g : kUnreachable;
+      group(dist);
+    }
+    for (int t0 = 0; t0 < p.n_dil; t0 += G) {
+      int dist[G];
 #pragma unroll
-    for (int g = 0; g < G; ++g) dist[g] = p.dil[t0 + g];
-    if (dist[0] > room) break;
-    group(dist);
+      for (int g = 0; g < G; ++g) dist[g] = p.dil[t0 + g];
+      if (dist[0] > room) break;
+      group(dist);
+    }
   }
 
   if (!row_ok) return;
   const int gb = p.grad_bf16 ? 2 : 4;
-  char* dvrow = static_cast<char*>(p.dv) + (b * p.sdv_b + h * p.sdv_h + j * p.sdv_t) * gb +
+  char* dvrow = static_cast<char*>(p.dv) + (b * p.sdv_b + hk * p.sdv_h + j * p.sdv_t) * gb +
                 sub * EPL * gb;
   store_vals<EPL>(dvrow, dv, p.grad_bf16 != 0);
   if constexpr (SM == SM_DOT) {
 #pragma unroll
     for (int e = 0; e < EPL; ++e) dk[e] *= p.scale;
-    char* dkrow = static_cast<char*>(p.dk) + (b * p.sdk_b + h * p.sdk_h + j * p.sdk_t) * gb +
+    char* dkrow = static_cast<char*>(p.dk) + (b * p.sdk_b + hk * p.sdk_h + j * p.sdk_t) * gb +
                   sub * EPL * gb;
     store_vals<EPL>(dkrow, dk, p.grad_bf16 != 0);
   } else if constexpr (COORD) {
@@ -438,7 +450,8 @@ hipError_t launch_passes(const Params& p, hipStream_t s, int grid, int nblk) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((gather_bwd_kv_kernel<DT, D, SM, 4, OFF32>), dim3(grid), dim3(kThreads), 0, s, p);
+  const int grid_kv = xcd_grid(p.B * p.Hkv * nblk);  // key rows of the key/value heads
+  hipLaunchKernelGGL((gather_bwd_kv_kernel<DT, D, SM, 4, OFF32>), dim3(grid_kv), dim3(kThreads), 0, s, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess || SM != SM_COORD) return e;
   hipLaunchKernelGGL(coord_param_reduce_kernel, dim3(p.H), dim3(256), 0, s, p.partials, p.B, p.H,

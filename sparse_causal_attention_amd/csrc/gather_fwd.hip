@@ -54,8 +54,9 @@ __global__ __launch_bounds__(kThreads) void gather_fwd_kernel(Params p) {
   if (!row_ok) i = p.T - 1;  // compute a valid row, store nothing
 
   // uniform per-head bases; per-lane byte offsets of row i's fragment
-  const char* khead = static_cast<const char*>(p.k) + (b * p.sk_b + h * p.sk_h) * EB;
-  const char* vhead = static_cast<const char*>(p.v) + (b * p.sv_b + h * p.sv_h) * EB;
+  const int hk = h / p.G;  // key/value head shared by G query heads
+  const char* khead = static_cast<const char*>(p.k) + (b * p.sk_b + hk * p.sk_h) * EB;
+  const char* vhead = static_cast<const char*>(p.v) + (b * p.sv_b + hk * p.sv_h) * EB;
   const int64_t skt = p.sk_t * EB, svt = p.sv_t * EB;
   int64_t kl = (int64_t)i * skt + sub * 16, vl = (int64_t)i * svt + sub * 16;
   uint32_t kl32 = (uint32_t)kl, vl32 = (uint32_t)vl;

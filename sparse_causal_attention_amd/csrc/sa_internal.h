@@ -29,6 +29,8 @@ constexpr int32_t kUnreachable = 0x7fffffff;
 struct Params {
   int32_t B, H, T, D;
   int32_t W;      // effective window
+  int32_t Hkv;    // key/value heads
+  int32_t G;      // query heads per key/value head (H / Hkv)
   int32_t n_dil;  // long-range distances
   int32_t dil[SA_MAX_DILATED + 8];  // ascending, padded with kUnreachable
   float scale;       // dot-mode scale
@@ -56,6 +58,8 @@ struct Params {
   float* lse2;      // workspace [B, H, T]: lse * log2(e) (band backward)
   float* partials;  // workspace [B, H, nblk_q, 2]
   const int32_t* pos;  // decode: row of each sequence's new token [B] (NULL: T - 1)
+  float* pdk;  // band backward with G > 1: per-query-head dk, dv partials,
+  float* pdv;  // contiguous fp32 [B, H, T, D] in the workspace
 };
 
 // Launchers (defined in the .hip files).  Each validates nothing: the C ABI

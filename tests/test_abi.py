@@ -179,3 +179,30 @@ def test_decode_validation(g64):
     # coordinate mode needs cq, ck, gamma, beta; uniform mode needs v alone
     assert decode(g64, desc(score=1), q=None, k=None, cq=FAKE, ck=FAKE, gm=FAKE) == E.SA_ERR_INVALID_ARG
     assert decode(g64, desc(score=2), q=None, k=None, v=None) == E.SA_ERR_INVALID_ARG
+
+
+def test_grouped_heads_validation(g64):
+    """H must be a multiple of H_kv; coordinate mode needs H_kv = H; the
+    workspace grows by the band kernels' per-head dk, dv partials."""
+    E = _abi
+    d = desc(H=4)
+    d.H_kv = 3
+    assert fwd(g64, d) == E.SA_ERR_INVALID_ARG
+    d.H_kv = -1
+    assert fwd(g64, d) == E.SA_ERR_INVALID_ARG
+    d = desc(H=4, score=1)
+    d.H_kv = 2
+    assert fwd(g64, d, q=None, k=None, cq=FAKE, ck=FAKE, gm=FAKE, bt=FAKE) == E.SA_ERR_UNSUPPORTED
+    need1, need2 = ctypes.c_size_t(), ctypes.c_size_t()
+    d = desc(H=4)
+    assert _abi.lib().sa_bwd_workspace_size(g64.handle, ctypes.byref(d), ctypes.byref(need1)) == 0
+    d.H_kv = 2
+    assert _abi.lib().sa_bwd_workspace_size(g64.handle, ctypes.byref(d), ctypes.byref(need2)) == 0
+    assert need2.value >= need1.value + 2 * 4 * 64 * 32 * 4
+    d.H_kv = 3
+    assert _abi.lib().sa_bwd_workspace_size(g64.handle, ctypes.byref(d),
+                                            ctypes.byref(need2)) == E.SA_ERR_INVALID_ARG
+    # H_kv = 0 means H (callers that zero-fill the descriptor)
+    d.H_kv = 0
+    assert _abi.lib().sa_bwd_workspace_size(g64.handle, ctypes.byref(d), ctypes.byref(need2)) == 0
+    assert need2.value == need1.value

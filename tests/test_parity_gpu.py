@@ -373,3 +373,84 @@ def test_decode_full_size_sampled():
     torch.cuda.synchronize()
     O, L = decode_reference(W, (), pos.numpy(), host_view(v), q=host_view(q), k=host_view(k))
     assert maxabs(o, O) <= 2e-2 and maxabs(lse, L) <= 2e-2
+
+
+# ------------------------------------------------------------------ grouped key/value heads
+def gqa_reference(W, offs, G, v, dO=None, q=None, k=None):
+    """Per query head h the oracle with k, v of head h // G; dk, dv of a
+    key/value head are the sums over its G query heads (the gradient of a sum
+    of per-head losses that share k and v)."""
+    B, Hkv, T, D = v.shape
+    H = Hkv * G
+    O = np.empty((B, H, T, D))
+    L = np.empty((B, H, T))
+    grads = {"dv": np.zeros((B, Hkv, T, D))}
+    if q is not None:
+        grads.update(dq=np.empty((B, H, T, D)), dk=np.zeros((B, Hkv, T, D)))
+    for b in range(B):
+        for h in range(H):
+            hk = h // G
+            kw = dict(q=q[b, h], k=k[b, hk]) if q is not None else {}
+            O[b, h], L[b, h] = oracle.fwd(T, W, offs, v[b, hk], **kw)
+            if dO is not None:
+                r = oracle.bwd(T, W, offs, v[b, hk], dO[b, h], **kw)
+                grads["dv"][b, hk] += r["dv"]
+                if q is not None:
+                    grads["dq"][b, h] = r["dq"]
+                    grads["dk"][b, hk] += r["dk"]
+    return O, L, grads
+
+
+@pytest.mark.parametrize("B,H,Hkv,T,D,dt,W,offs,score,algo", [
+    (1, 8, 2, 2048, 64, torch.bfloat16, 256, (), "dot", "auto"),             # band kernels
+    (1, 4, 1, 1500, 64, torch.bfloat16, 64, (128, 256, 512), "dot", "auto"),  # band + long range
+    (2, 6, 3, 700, 32, torch.float32, 4, tuple(2 ** k for k in range(10)), "dot", "auto"),  # gather
+    (1, 4, 2, 2048, 64, torch.bfloat16, 256, (), "dot", "gather"),
+    (2, 4, 1, 500, 64, torch.bfloat16, 4, (8, 16, 32, 64), "uniform", "auto"),
+])
+def test_grouped_kv_heads(B, H, Hkv, T, D, dt, W, offs, score, algo):
+    G = H // Hkv
+    gen = torch.Generator().manual_seed(31 * H + Hkv + T)
+    v = torch.randn((B, Hkv, T, D), generator=gen).to(dt)
+    do = torch.randn((B, H, T, D), generator=gen).to(dt)
+    g = sa_build_graph(T, W, offs)
+    _say("gqa B=%d H=%d Hkv=%d T=%d D=%d %s W=%d %s %s plan %s / %s" % (
+        B, H, Hkv, T, D, dt, W, score, algo,
+        sa_describe_plan(g, v.to(DEV), score=score, algo=algo, heads=H),
+        sa_describe_plan(g, v.to(DEV), score=score, algo=algo, heads=H, which="bwd")))
+    if score == "dot":
+        q = torch.randn((B, H, T, D), generator=gen).to(dt)
+        k = torch.randn((B, Hkv, T, D), generator=gen).to(dt)
+        o, lse = sa_fwd(g, q.to(DEV), k.to(DEV), v.to(DEV), algo=algo)
+        gr = sa_bwd(g, q.to(DEV), k.to(DEV), v.to(DEV), o, lse, do.to(DEV), algo=algo)
+        O, L, ref = gqa_reference(W, offs, G, host_view(v), host_view(do), q=host_view(q), k=host_view(k))
+    else:
+        o = torch.empty((B, H, T, D), dtype=dt, device=DEV)
+        o, lse = sa_fwd(g, v=v.to(DEV), o=o, algo=algo)
+        gr = sa_bwd(g, v=v.to(DEV), o=o, lse=lse, dout=do.to(DEV), algo=algo)
+        O, L, ref = gqa_reference(W, offs, G, host_view(v), host_view(do))
+    torch.cuda.synchronize()
+    tol = tol_of(dt)
+    errs = {"o": maxabs(o, O), "lse": maxabs(lse, L)}
+    for key in ref:
+        errs[key] = maxabs(gr[key], ref[key])
+    _say("gqa errors %s (tol %g)" % ({k_: "%.2e" % e for k_, e in errs.items()}, tol))
+    for key, e in errs.items():
+        assert e <= tol, (key, e)
+
+
+def test_decode_grouped_kv_heads():
+    B, H, Hkv, T, D, W, offs = 3, 8, 2, 2000, 64, 16, (32, 64, 128, 256, 512, 1024)
+    gen = torch.Generator().manual_seed(1234)
+    q = torch.randn((B, H, D), generator=gen).to(torch.bfloat16)
+    k = torch.randn((B, Hkv, T, D), generator=gen).to(torch.bfloat16)
+    v = torch.randn((B, Hkv, T, D), generator=gen).to(torch.bfloat16)
+    pos = np.array([5, 1999, 1024], dtype=np.int32)
+    g = sa_build_graph(T, W, offs)
+    o, lse = sa_decode(g, q.to(DEV), k.to(DEV), v.to(DEV), positions=torch.from_numpy(pos).to(DEV))
+    torch.cuda.synchronize()
+    G = H // Hkv
+    kk = np.repeat(host_view(k), G, axis=1)  # query head h reads key/value head h // G
+    vv = np.repeat(host_view(v), G, axis=1)
+    O, L = decode_reference(W, offs, pos, vv, q=host_view(q), k=kk)
+    assert maxabs(o, O) <= 2e-2 and maxabs(lse, L) <= 2e-2
