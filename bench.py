@@ -35,7 +35,8 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workloads", default="band,dilated,coord,uniform,decode_band,decode_dilated,ultra")
+    ap.add_argument("--workloads",
+                    default="band,dilated,coord,uniform,band_gqa,dilated_gqa,decode_band,decode_dilated,ultra")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample length")
     ap.add_argument("--algo", default="auto")
@@ -91,9 +92,11 @@ def models(w, grad_bytes=4):
         ffl = w.B * w.H * E * (2 * D + 11)
         bfl = w.B * w.H * E * (4 * D + 35)
     else:
-        fwd_c = rows * (4 * D * eb + 4)
+        # q, o, dO, dq, lse per query-head row; k, v, dk, dv per key/value-head row
+        kv_rows = w.B * w.kv_heads * w.T
+        fwd_c = rows * (2 * D * eb + 4) + kv_rows * 2 * D * eb
         fwd_e = Ed * 2 * D * eb
-        bwd_c = rows * (5 * D * eb + 4 + 3 * D * grad_bytes)
+        bwd_c = rows * (3 * D * eb + 4 + D * grad_bytes) + kv_rows * (2 * D * eb + 2 * D * grad_bytes)
         bwd_e = Ed * (4 * D * eb + 8)
         ffl = w.B * w.H * E * 4 * D
         bfl = w.B * w.H * E * 10 * D
@@ -123,7 +126,7 @@ def run_workload(w, steps, warmup, algo, with_backward=True):
     g = sa_build_graph(w.T, w.window, w.offsets)
     bwd = with_backward and w.backward
     coord = w.coord
-    o = torch.empty_like(x["v"])
+    o = torch.empty((w.B, w.H, w.T, w.D), dtype=x["v"].dtype, device=dev)
     lse = torch.empty((w.B, w.H, w.T), dtype=torch.float32, device=dev)
     fkw = dict(v=x["v"], cq=x.get("cq"), ck=x.get("ck"), gamma=x.get("gamma"), beta=x.get("beta"),
                o=o, lse=lse, algo=algo)
@@ -132,7 +135,8 @@ def run_workload(w, steps, warmup, algo, with_backward=True):
     grads = None
     if bwd:
         gshape = (w.B, w.H, w.T, w.D)
-        grads = {"dv": torch.empty(gshape, dtype=torch.float32, device=dev)}
+        kvshape = (w.B, w.kv_heads, w.T, w.D)
+        grads = {"dv": torch.empty(kvshape, dtype=torch.float32, device=dev)}
         if coord:
             grads.update(dcq=torch.empty((w.B, w.H, w.T, 3), dtype=torch.float32, device=dev),
                          dck=torch.empty((w.B, w.H, w.T, 3), dtype=torch.float32, device=dev),
@@ -140,9 +144,9 @@ def run_workload(w, steps, warmup, algo, with_backward=True):
                          dbeta=torch.empty((w.H,), dtype=torch.float32, device=dev))
         elif not w.uniform:
             grads.update(dq=torch.empty(gshape, dtype=torch.float32, device=dev),
-                         dk=torch.empty(gshape, dtype=torch.float32, device=dev))
+                         dk=torch.empty(kvshape, dtype=torch.float32, device=dev))
         from sparse_causal_attention_amd import sa_bwd_workspace_size
-        ws = torch.empty(sa_bwd_workspace_size(g, x["v"]), dtype=torch.uint8, device=dev)
+        ws = torch.empty(sa_bwd_workspace_size(g, x["v"], heads=w.H), dtype=torch.uint8, device=dev)
         bkw = dict(v=x["v"], o=o, lse=lse, dout=x["do"], cq=x.get("cq"), ck=x.get("ck"),
                    gamma=x.get("gamma"), beta=x.get("beta"), workspace=ws, algo=algo, **grads)
         if not coord and not w.uniform:
@@ -177,8 +181,9 @@ def run_workload(w, steps, warmup, algo, with_backward=True):
         "wall_s": wall, "ms_per_step": 1e3 * wall / steps,
         "fwd_ms": sum(f_ms) / len(f_ms), "bwd_ms": sum(b_ms) / len(b_ms),
         "fwd_ms_min": min(f_ms), "bwd_ms_min": min(b_ms),
-        "plan_fwd": sa_describe_plan(g, x["v"], score=score_name(w), algo=algo, which="fwd"),
-        "plan_bwd": sa_describe_plan(g, x["v"], score=score_name(w), algo=algo, which="bwd") if bwd else None,
+        "plan_fwd": sa_describe_plan(g, x["v"], score=score_name(w), algo=algo, which="fwd", heads=w.H),
+        "plan_bwd": sa_describe_plan(g, x["v"], score=score_name(w), algo=algo, which="bwd",
+                                     heads=w.H) if bwd else None,
         "inputs": {k: t for k, t in x.items()},
     }
     del o, lse, grads
@@ -220,7 +225,7 @@ def summarize(w, r, steps):
     wall = r["wall_s"]
     out = {
         "workload": w.name,
-        "shape": {"B": w.B, "H": w.H, "T": w.T, "D": w.D, "window": w.window,
+        "shape": {"B": w.B, "H": w.H, "H_kv": w.kv_heads, "T": w.T, "D": w.D, "window": w.window,
                   "offsets": list(w.offsets), "dtype": w.dtype_name,
                   "score": score_name(w), "backward": w.backward},
         # decode steps last microseconds: their rate comes from the kernel events

@@ -40,6 +40,11 @@ class Workload:
     backward: bool = True
     uniform: bool = False  # fixed equal weights (v alone)
     decode: bool = False   # one new token per sequence at row T - 1 of a T-row cache
+    Hkv: int = 0           # key/value heads (0: H)
+
+    @property
+    def kv_heads(self) -> int:
+        return self.Hkv if self.Hkv > 0 else self.H
 
     @property
     def dtype_name(self) -> str:
@@ -66,6 +71,10 @@ WORKLOADS = {
     # the dilated graph with fixed equal weights (the same-graph comparison
     # that isolates the scores)
     "uniform": Workload("uniform", 6, 4, 8, 16384, 64, torch.bfloat16, 4, _pow2(0, 13), uniform=True),
+    # grouped key/value heads: 8 query heads sharing 2 key/value heads, on the
+    # band graph and on the dilated graph
+    "band_gqa": Workload("band_gqa", 9, 1, 8, 16384, 64, torch.bfloat16, 256, (), Hkv=2),
+    "dilated_gqa": Workload("dilated_gqa", 10, 4, 8, 16384, 64, torch.bfloat16, 4, _pow2(0, 13), Hkv=2),
     # decode steps: 64 sequences x 8 heads, one new token each at the end of a
     # 16,384-row key/value cache, on the band graph and on the dilated graph
     "decode_band": Workload("decode_band", 7, 64, 8, 16384, 64, torch.bfloat16, 256, (), backward=False,
@@ -103,6 +112,7 @@ def make_inputs(w: Workload, device="cpu", backward: bool | None = None,
     D = w.D if D is None else D
     backward = w.backward if backward is None else backward
     shp = (B, H, T, D)
+    kv_shp = (B, w.kv_heads if H == w.H else H, T, D)  # shape overrides keep one head per query head
     out = {}
     if w.coord:
         out["cq"] = _randn((B, H, T, 3), seed_of(w, SEED_CQ))
@@ -113,8 +123,8 @@ def make_inputs(w: Workload, device="cpu", backward: bool | None = None,
         pass  # v alone
     else:
         out["q"] = _randn((B, H, D) if w.decode else shp, seed_of(w, SEED_Q)).to(w.dtype)
-        out["k"] = _randn(shp, seed_of(w, SEED_K)).to(w.dtype)
-    out["v"] = _randn(shp, seed_of(w, SEED_V)).to(w.dtype)
+        out["k"] = _randn(kv_shp, seed_of(w, SEED_K)).to(w.dtype)
+    out["v"] = _randn(kv_shp, seed_of(w, SEED_V)).to(w.dtype)
     if backward:
         out["do"] = _randn(shp, seed_of(w, SEED_DO)).to(w.dtype)
     return {k: t.to(device) for k, t in out.items()}

@@ -59,3 +59,15 @@ def test_models_uniform_mode():
     assert m["bwd_bytes_compulsory"] == rows * (128 + 4 + 256)
     assert m["fwd_bytes"] - m["fwd_bytes_compulsory"] == 32 * 180228 * 128
     assert m["fwd_flops"] == m["bwd_flops"] == 32 * 245758 * 2 * 64
+
+
+def test_models_grouped_heads():
+    """With 8 query heads on 2 key/value heads the k, v, dk, dv tensors shrink
+    by 4; per long-range edge the rows fetched stay the same."""
+    full, gqa = bench.models(WORKLOADS["band"]), bench.models(WORKLOADS["band_gqa"])
+    rows, kv_rows = 8 * 16384, 2 * 16384
+    assert gqa["fwd_bytes_compulsory"] == rows * (2 * 128 + 4) + kv_rows * 2 * 128
+    assert gqa["bwd_bytes_compulsory"] == rows * (3 * 128 + 4 + 256) + kv_rows * (2 * 128 + 2 * 256)
+    assert full["fwd_flops"] == gqa["fwd_flops"]
+    d, dg = bench.models(WORKLOADS["dilated"]), bench.models(WORKLOADS["dilated_gqa"])
+    assert d["fwd_bytes"] - d["fwd_bytes_compulsory"] == dg["fwd_bytes"] - dg["fwd_bytes_compulsory"]
