@@ -142,7 +142,10 @@ typedef struct {
   int64_t H_kv;        /* key/value heads; 0 selects H.  H must be a multiple of H_kv: query
                           head h reads key/value head h / (H / H_kv), and k, v, dk, dv (and
                           the decode caches) are [B, H_kv, T, D] with strides over (b, h_kv,
-                          t).  Coordinate mode needs H_kv = H (per-head coordinates). */
+                          t) -- grouped-query attention (MiniGPT Part 6, opening and closing
+                          paragraphs: the series' grouped key/value heads, which shrink the
+                          key/value cache).  Coordinate mode needs H_kv = H (per-head
+                          coordinates). */
 } sa_attn_desc;
 
 /* Forward (SpatialLM-Mini news page, "How tokens choose whom to listen to";
