@@ -69,6 +69,13 @@ def lib():
         L.oracle_bwd.argtypes = [i64, i64, i64, vp, i32, ctypes.c_int, dbl, ctypes.c_int,
                                  vp, vp, vp, ctypes.c_int, vp, vp, dbl, dbl, vp,
                                  vp, vp, vp, vp, vp, vp, vp, vp]
+        L.oracle_fwd_csr.restype = ctypes.c_int
+        L.oracle_fwd_csr.argtypes = [i64, i64, vp, vp, ctypes.c_int, dbl, ctypes.c_int,
+                                     vp, vp, vp, ctypes.c_int, vp, vp, dbl, dbl, vp, vp]
+        L.oracle_bwd_csr.restype = ctypes.c_int
+        L.oracle_bwd_csr.argtypes = [i64, i64, vp, vp, ctypes.c_int, dbl, ctypes.c_int,
+                                     vp, vp, vp, ctypes.c_int, vp, vp, dbl, dbl, vp,
+                                     vp, vp, vp, vp, vp, vp, vp, vp]
         L.oracle_dense_causal.restype = ctypes.c_int
         L.oracle_dense_causal.argtypes = [i64, i64, dbl, ctypes.c_int, vp, vp, vp, vp, vp]
         L.oracle_num_threads.restype = ctypes.c_int
@@ -290,3 +297,73 @@ def bwd_bh(W, offsets, v, dO, q=None, k=None, cq=None, ck=None, gamma=None, beta
                 else:
                     res.setdefault(key, np.empty((B, H) + val.shape))[b, h] = val
     return res
+
+
+# ---------------------------------------------------------------- explicit graphs
+def _csr(row_ptr, cols):
+    rp = np.ascontiguousarray(np.asarray(row_ptr, dtype=np.int64))
+    cl = np.ascontiguousarray(np.asarray(cols, dtype=np.int64))
+    return rp, cl
+
+
+def _mode_args(q, k, cq, ck, vdt):
+    """(mode, dtype of q/k or v, cdtype, q, k, cq, ck) as the C calls take them."""
+    if cq is not None:
+        cq, cdt = _as_input(cq)
+        ck, _ = _as_input(ck)
+        return SCORE_COORD, vdt, cdt, None, None, cq, ck
+    if q is None and k is None:
+        return SCORE_UNIFORM, vdt, F64, None, None, None, None
+    q, dt = _as_input(q)
+    k, dt2 = _as_input(k)
+    assert dt == dt2 == vdt, "q, k, v share one element type"
+    return SCORE_DOT, dt, F64, q, k, None, None
+
+
+def fwd_csr(row_ptr, cols, v, q=None, k=None, cq=None, ck=None, gamma=0.0, beta=0.0, scale=None):
+    """One (batch, head) slice over an explicit graph (row i: keys
+    cols[row_ptr[i]:row_ptr[i+1]], ascending, each <= i).  Modes as in fwd.
+    Returns (O [T, D], LSE [T]) float64."""
+    rp, cl = _csr(row_ptr, cols)
+    v, vdt = _as_input(v)
+    T, D = v.shape
+    _check_shapes(T, D, v=v, q=q, k=k, cq=cq, ck=ck)
+    mode, dt, cdt, q_, k_, cq_, ck_ = _mode_args(q, k, cq, ck, vdt)
+    scale = 1.0 / np.sqrt(D) if scale is None else scale
+    O = np.empty((T, D), dtype=np.float64)
+    L = np.empty(T, dtype=np.float64)
+    rc = lib().oracle_fwd_csr(T, D, _ptr(rp), _ptr(cl), mode, float(scale), dt, _ptr(q_), _ptr(k_), _ptr(v),
+                              cdt, _ptr(cq_), _ptr(ck_), float(gamma), float(beta), _ptr(O), _ptr(L))
+    if rc != 0:
+        raise ValueError("oracle_fwd_csr failed (%d)" % rc)
+    return O, L
+
+
+def bwd_csr(row_ptr, cols, v, dO, q=None, k=None, cq=None, ck=None, gamma=0.0, beta=0.0, scale=None):
+    """Backward over an explicit graph; returns the gradients of bwd."""
+    rp, cl = _csr(row_ptr, cols)
+    v, vdt = _as_input(v)
+    dO, ddt = _as_input(dO)
+    assert ddt == vdt, "dO shares the element type of v"
+    T, D = v.shape
+    _check_shapes(T, D, v=v, dO=dO, q=q, k=k, cq=cq, ck=ck)
+    mode, dt, cdt, q_, k_, cq_, ck_ = _mode_args(q, k, cq, ck, vdt)
+    scale = 1.0 / np.sqrt(D) if scale is None else scale
+    out = {"dv": np.empty((T, D))}
+    g, b, l1 = np.zeros(1), np.zeros(1), np.zeros(1)
+    dQ = dK = dcq = dck = None
+    if mode == SCORE_DOT:
+        dQ, dK = np.empty((T, D)), np.empty((T, D))
+        out.update(dq=dQ, dk=dK)
+    if mode == SCORE_COORD:
+        dcq, dck = np.empty((T, 3)), np.empty((T, 3))
+    rc = lib().oracle_bwd_csr(T, D, _ptr(rp), _ptr(cl), mode, float(scale), dt, _ptr(q_), _ptr(k_), _ptr(v),
+                              cdt, _ptr(cq_), _ptr(ck_), float(gamma), float(beta), _ptr(dO),
+                              _ptr(dQ), _ptr(dK), _ptr(out["dv"]), _ptr(dcq), _ptr(dck),
+                              _ptr(g) if mode == SCORE_COORD else None, _ptr(b) if mode == SCORE_COORD else None,
+                              _ptr(l1) if mode == SCORE_COORD else None)
+    if rc != 0:
+        raise ValueError("oracle_bwd_csr failed (%d)" % rc)
+    if mode == SCORE_COORD:
+        out.update(dcq=dcq, dck=dck, dgamma=float(g[0]), dbeta=float(b[0]), l1=float(l1[0]))
+    return out

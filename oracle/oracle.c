@@ -135,7 +135,27 @@ static int bad_attn_args(int64_t T, int64_t D, int mode, const void* q, const vo
 /* Softmax over the neighbour set only, then the weighted sum of values:
  *   m_i = max_j s_ij,  l_i = sum_j exp(s_ij - m_i),  LSE_i = m_i + ln l_i,
  *   P_ij = exp(s_ij - m_i) / l_i,  O_i = sum_j P_ij v_j.
- * (SpatialLM-Mini news page, "How tokens choose whom to listen to".) */
+ * (SpatialLM-Mini news page, "How tokens choose whom to listen to".)
+ * One row i with neighbour list nb[0 .. n); s is scratch of n doubles. */
+static void fwd_row(int64_t D, int score_mode, double scale, int dtype, const void* q,
+                    const void* k, const void* v, int cdtype, const void* cq, const void* ck,
+                    double gamma, double beta, int64_t i, const int64_t* nb, int64_t n,
+                    double* s, double* O_row, double* LSE_out) {
+  for (int64_t t = 0; t < n; ++t)
+    s[t] = score(score_mode, D, scale, dtype, q, k, cdtype, cq, ck, gamma, beta, i, nb[t]);
+  double m = -INFINITY;
+  for (int64_t t = 0; t < n; ++t)
+    if (s[t] > m) m = s[t];
+  double l = 0.0;
+  for (int64_t t = 0; t < n; ++t) l += exp(s[t] - m);
+  *LSE_out = m + log(l);
+  for (int64_t d = 0; d < D; ++d) O_row[d] = 0.0;
+  for (int64_t t = 0; t < n; ++t) {
+    const double p = exp(s[t] - m) / l;
+    for (int64_t d = 0; d < D; ++d) O_row[d] += p * rd(v, dtype, nb[t] * D + d);
+  }
+}
+
 int oracle_fwd(int64_t T, int64_t D, int64_t W, const int64_t* offs, int32_t n_offs,
                int score_mode, double scale, int dtype, const void* q, const void* k,
                const void* v, int cdtype, const void* cq, const void* ck, double gamma,
@@ -161,22 +181,53 @@ int oracle_fwd(int64_t T, int64_t D, int64_t W, const int64_t* offs, int32_t n_o
       for (int64_t r = 0; r < n_rows; ++r) {
         const int64_t i = rows ? rows[r] : r;
         const int64_t n = oracle_row(T, W, offs, n_offs, i, nb);
-        for (int64_t t = 0; t < n; ++t)
-          s[t] = score(score_mode, D, scale, dtype, q, k, cdtype, cq, ck, gamma, beta, i, nb[t]);
-        double m = -INFINITY;
-        for (int64_t t = 0; t < n; ++t)
-          if (s[t] > m) m = s[t];
-        double l = 0.0;
-        for (int64_t t = 0; t < n; ++t) l += exp(s[t] - m);
-        LSE[r] = m + log(l);
-        for (int64_t d = 0; d < D; ++d) O[r * D + d] = 0.0;
-        for (int64_t t = 0; t < n; ++t) {
-          const double p = exp(s[t] - m) / l;
-          for (int64_t d = 0; d < D; ++d) O[r * D + d] += p * rd(v, dtype, nb[t] * D + d);
-        }
+        fwd_row(D, score_mode, scale, dtype, q, k, v, cdtype, cq, ck, gamma, beta, i, nb, n, s,
+                O + r * D, LSE + r);
       }
     }
     free(nb);
+    free(s);
+  }
+  return failed ? -2 : 0;
+}
+
+/* An explicit graph: row i lists its keys cols[row_ptr[i] .. row_ptr[i+1]),
+ * strictly ascending, each 0 <= j <= i, at least one per row (a softmax over
+ * an empty list is undefined). */
+static int bad_csr(int64_t T, const int64_t* row_ptr, const int64_t* cols) {
+  if (T < 1 || !row_ptr || row_ptr[0] != 0) return 1;
+  for (int64_t i = 0; i < T; ++i) {
+    if (row_ptr[i + 1] <= row_ptr[i]) return 1;
+    for (int64_t e = row_ptr[i]; e < row_ptr[i + 1]; ++e) {
+      if (!cols || cols[e] < 0 || cols[e] > i) return 1;
+      if (e > row_ptr[i] && cols[e] <= cols[e - 1]) return 1;
+    }
+  }
+  return 0;
+}
+
+int oracle_fwd_csr(int64_t T, int64_t D, const int64_t* row_ptr, const int64_t* cols,
+                   int score_mode, double scale, int dtype, const void* q, const void* k,
+                   const void* v, int cdtype, const void* cq, const void* ck, double gamma,
+                   double beta, double* O, double* LSE) {
+  if (bad_csr(T, row_ptr, cols) || bad_attn_args(T, D, score_mode, q, k, v, cq, ck) || !O || !LSE)
+    return -1;
+  int64_t cap = 1;
+  for (int64_t i = 0; i < T; ++i)
+    if (row_ptr[i + 1] - row_ptr[i] > cap) cap = row_ptr[i + 1] - row_ptr[i];
+  int failed = 0;
+#pragma omp parallel
+  {
+    double* s = (double*)malloc(sizeof(double) * (size_t)cap);
+    if (!s) {
+#pragma omp atomic write
+      failed = 1;
+    } else {
+#pragma omp for schedule(dynamic, 64)
+      for (int64_t i = 0; i < T; ++i)
+        fwd_row(D, score_mode, scale, dtype, q, k, v, cdtype, cq, ck, gamma, beta, i,
+                cols + row_ptr[i], row_ptr[i + 1] - row_ptr[i], s, O + i * D, LSE + i);
+    }
     free(s);
   }
   return failed ? -2 : 0;
@@ -193,39 +244,25 @@ int oracle_fwd(int64_t T, int64_t D, int64_t W, const int64_t* offs, int32_t n_o
  *               dgamma = -sum_ij dS_ij ||c_q,i - c_k,j||^2,  dbeta = sum_ij dS_ij.
  * Sums over i for a fixed key j run over the transposed edge list, so every
  * output row has one writer. */
-int oracle_bwd(int64_t T, int64_t D, int64_t W, const int64_t* offs, int32_t n_offs,
-               int score_mode, double scale, int dtype, const void* q, const void* k,
-               const void* v, int cdtype, const void* cq, const void* ck, double gamma,
-               double beta, const void* dO, double* dQ, double* dK, double* dV,
-               double* dcq, double* dck, double* dgamma, double* dbeta, double* l1) {
-  if (bad_graph_args(T, W, offs, n_offs) ||
-      bad_attn_args(T, D, score_mode, q, k, v, cq, ck) || !dO)
+/* The backward over an explicit graph (row_ptr, cols as in oracle_fwd_csr);
+ * the distance-graph backward below builds its lists and calls this. */
+int oracle_bwd_csr(int64_t T, int64_t D, const int64_t* row_ptr, const int64_t* cols,
+                   int score_mode, double scale, int dtype, const void* q, const void* k,
+                   const void* v, int cdtype, const void* cq, const void* ck, double gamma,
+                   double beta, const void* dO, double* dQ, double* dK, double* dV,
+                   double* dcq, double* dck, double* dgamma, double* dbeta, double* l1) {
+  if (bad_csr(T, row_ptr, cols) || bad_attn_args(T, D, score_mode, q, k, v, cq, ck) || !dO)
     return -1;
   int rc = -2;
-  int64_t* row_ptr = (int64_t*)malloc(sizeof(int64_t) * (size_t)(T + 1));
+  const int64_t E = row_ptr[T];
   int64_t* col_cnt = (int64_t*)calloc((size_t)(T + 1), sizeof(int64_t));
-  int64_t* cols = NULL;
-  int64_t* tptr = NULL;
-  int64_t* tedge = NULL;
-  int64_t* erow = NULL;
-  double *P = NULL, *dS = NULL, *Delta = NULL;
-  if (!row_ptr || !col_cnt) goto done;
-
-  /* 1. the graph, row by row */
-  {
-    int64_t e = oracle_graph_csr(T, W, offs, n_offs, 0, T, row_ptr, NULL, 0);
-    int64_t E = -(e + 2);
-    if (E < 0) goto done;
-    cols = (int64_t*)malloc(sizeof(int64_t) * (size_t)(E > 0 ? E : 1));
-    erow = (int64_t*)malloc(sizeof(int64_t) * (size_t)(E > 0 ? E : 1));
-    P = (double*)malloc(sizeof(double) * (size_t)(E > 0 ? E : 1));
-    dS = (double*)malloc(sizeof(double) * (size_t)(E > 0 ? E : 1));
-    tedge = (int64_t*)malloc(sizeof(int64_t) * (size_t)(E > 0 ? E : 1));
-    Delta = (double*)malloc(sizeof(double) * (size_t)T);
-    tptr = (int64_t*)malloc(sizeof(int64_t) * (size_t)(T + 1));
-    if (!cols || !erow || !P || !dS || !tedge || !Delta || !tptr) goto done;
-    if (oracle_graph_csr(T, W, offs, n_offs, 0, T, row_ptr, cols, E) != E) goto done;
-  }
+  int64_t* tptr = (int64_t*)malloc(sizeof(int64_t) * (size_t)(T + 1));
+  int64_t* tedge = (int64_t*)malloc(sizeof(int64_t) * (size_t)E);
+  int64_t* erow = (int64_t*)malloc(sizeof(int64_t) * (size_t)E);
+  double* P = (double*)malloc(sizeof(double) * (size_t)E);
+  double* dS = (double*)malloc(sizeof(double) * (size_t)E);
+  double* Delta = (double*)malloc(sizeof(double) * (size_t)T);
+  if (!col_cnt || !tptr || !tedge || !erow || !P || !dS || !Delta) goto done;
 
   /* 2. per row: scores, softmax, dP, Delta, dS (stored per edge) */
 #pragma omp parallel for schedule(dynamic, 64)
@@ -330,15 +367,35 @@ int oracle_bwd(int64_t T, int64_t D, int64_t W, const int64_t* offs, int32_t n_o
   rc = 0;
 
 done:
-  free(row_ptr);
   free(col_cnt);
-  free(cols);
   free(erow);
   free(P);
   free(dS);
   free(tedge);
   free(tptr);
   free(Delta);
+  return rc;
+}
+
+int oracle_bwd(int64_t T, int64_t D, int64_t W, const int64_t* offs, int32_t n_offs,
+               int score_mode, double scale, int dtype, const void* q, const void* k,
+               const void* v, int cdtype, const void* cq, const void* ck, double gamma,
+               double beta, const void* dO, double* dQ, double* dK, double* dV,
+               double* dcq, double* dck, double* dgamma, double* dbeta, double* l1) {
+  if (bad_graph_args(T, W, offs, n_offs) ||
+      bad_attn_args(T, D, score_mode, q, k, v, cq, ck) || !dO)
+    return -1;
+  /* the graph, row by row, then the explicit-list backward */
+  int64_t* row_ptr = (int64_t*)malloc(sizeof(int64_t) * (size_t)(T + 1));
+  if (!row_ptr) return -2;
+  const int64_t E = -(oracle_graph_csr(T, W, offs, n_offs, 0, T, row_ptr, NULL, 0) + 2);
+  int64_t* cols = E >= 0 ? (int64_t*)malloc(sizeof(int64_t) * (size_t)(E > 0 ? E : 1)) : NULL;
+  int rc = -2;
+  if (cols && oracle_graph_csr(T, W, offs, n_offs, 0, T, row_ptr, cols, E) == E)
+    rc = oracle_bwd_csr(T, D, row_ptr, cols, score_mode, scale, dtype, q, k, v, cdtype, cq, ck,
+                        gamma, beta, dO, dQ, dK, dV, dcq, dck, dgamma, dbeta, l1);
+  free(row_ptr);
+  free(cols);
   return rc;
 }
 

@@ -71,6 +71,21 @@ int oracle_bwd(int64_t T, int64_t D, int64_t W, const int64_t* offs, int32_t n_o
                double beta, const void* dO, double* dQ, double* dK, double* dV,
                double* dcq, double* dck, double* dgamma, double* dbeta, double* l1);
 
+/* The same forward and backward over an explicit graph: row i lists its keys
+ * cols[row_ptr[i] .. row_ptr[i+1]) strictly ascending, each 0 <= j <= i, at
+ * least one per row (row_ptr has T + 1 entries starting at 0).  All T rows
+ * are evaluated.  Returns 0, -1 on a bad argument (including a malformed
+ * list), -2 on OOM. */
+int oracle_fwd_csr(int64_t T, int64_t D, const int64_t* row_ptr, const int64_t* cols,
+                   int score_mode, double scale, int dtype, const void* q, const void* k,
+                   const void* v, int cdtype, const void* cq, const void* ck, double gamma,
+                   double beta, double* O, double* LSE);
+int oracle_bwd_csr(int64_t T, int64_t D, const int64_t* row_ptr, const int64_t* cols,
+                   int score_mode, double scale, int dtype, const void* q, const void* k,
+                   const void* v, int cdtype, const void* cq, const void* ck, double gamma,
+                   double beta, const void* dO, double* dQ, double* dK, double* dV,
+                   double* dcq, double* dck, double* dgamma, double* dbeta, double* l1);
+
 /* Dense causal attention (every j <= i), ascending j, dot mode only: the
  * plain definition the windowed op must reproduce exactly when W >= T. */
 int oracle_dense_causal(int64_t T, int64_t D, double scale, int dtype, const void* q,

@@ -473,3 +473,90 @@ def test_fwd_uniform_equals_dot_mode_with_zero_queries():
     O_d, L_d = oracle.fwd(T, W, offs, v, q=np.zeros((T, 8)), k=k)
     np.testing.assert_allclose(O_u, O_d, rtol=0, atol=1e-14)
     np.testing.assert_allclose(L_u, L_d, rtol=0, atol=1e-14)
+
+
+# ------------------------------------------------------------------ explicit (CSR) graphs
+def random_causal_csr(T, max_deg, seed):
+    """Row i: itself plus up to max_deg - 1 distinct earlier keys, ascending."""
+    rng = np.random.default_rng(seed)
+    rp, cols = [0], []
+    for i in range(T):
+        others = rng.choice(i, size=min(i, int(rng.integers(0, max_deg))), replace=False) if i else []
+        row = sorted(set(int(j) for j in others) | {i})
+        cols += row
+        rp.append(len(cols))
+    return np.array(rp), np.array(cols)
+
+
+def csr_mask(T, rp, cols):
+    m = np.zeros((T, T), dtype=bool)
+    for i in range(T):
+        m[i, cols[rp[i]:rp[i + 1]]] = True
+    return m
+
+
+@pytest.mark.parametrize("T,deg,seed", [(60, 5, 1), (97, 12, 2), (33, 40, 3)])
+def test_fwd_csr_matches_torch_sdpa_masked(T, deg, seed):
+    """Any causal neighbour list: torch fp64 scaled_dot_product_attention with
+    the graph as a boolean mask."""
+    rp, cols = random_causal_csr(T, deg, seed)
+    rng = np.random.default_rng(seed + 10)
+    D = 8
+    q, k, v = (rng.standard_normal((T, D)) for _ in range(3))
+    O, L = oracle.fwd_csr(rp, cols, v, q=q, k=k)
+    mask = torch.from_numpy(csr_mask(T, rp, cols))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None], torch.from_numpy(k)[None], torch.from_numpy(v)[None], attn_mask=mask[None])
+    np.testing.assert_allclose(O, ref[0].numpy(), rtol=0, atol=1e-12)
+    s = (q @ k.T) / math.sqrt(D)
+    s[~mask.numpy()] = -np.inf
+    np.testing.assert_allclose(L, np.log(np.exp(s - s.max(1, keepdims=True)).sum(1)) + s.max(1), rtol=0,
+                               atol=1e-12)
+
+
+def test_bwd_csr_matches_torch_autograd():
+    T, D = 70, 6
+    rp, cols = random_causal_csr(T, 9, 4)
+    rng = np.random.default_rng(14)
+    q, k, v, dO = (rng.standard_normal((T, D)) for _ in range(4))
+    g = oracle.bwd_csr(rp, cols, v, dO, q=q, k=k)
+    mask = torch.from_numpy(csr_mask(T, rp, cols))
+    tq, tk, tv = (torch.tensor(a, requires_grad=True) for a in (q, k, v))
+    o = torch.nn.functional.scaled_dot_product_attention(tq[None], tk[None], tv[None], attn_mask=mask[None])
+    (o[0] * torch.from_numpy(dO)).sum().backward()
+    for name, t in (("dq", tq), ("dk", tk), ("dv", tv)):
+        np.testing.assert_allclose(g[name], t.grad.numpy(), rtol=0, atol=1e-11)
+    # uniform mode on the same lists: dV_j = sum over the rows i listing j of dO_i / |N(i)|
+    gu = oracle.bwd_csr(rp, cols, v, dO)
+    ref = np.zeros((T, D))
+    for i in range(T):
+        row = cols[rp[i]:rp[i + 1]]
+        ref[row] += dO[i] / len(row)
+    np.testing.assert_allclose(gu["dv"], ref, rtol=0, atol=1e-13)
+
+
+def test_csr_of_the_distance_graph_reproduces_it():
+    T, W, offs = 80, 3, (4, 8, 16, 32, 64)
+    rp, cols = oracle.graph_csr(T, W, offs)
+    rng = np.random.default_rng(21)
+    q, k, v, dO = (rng.standard_normal((T, 8)) for _ in range(4))
+    O1, L1 = oracle.fwd_csr(rp, cols, v, q=q, k=k)
+    O2, L2 = oracle.fwd(T, W, offs, v, q=q, k=k)
+    np.testing.assert_array_equal(O1, O2)
+    np.testing.assert_array_equal(L1, L2)
+    g1, g2 = oracle.bwd_csr(rp, cols, v, dO, q=q, k=k), oracle.bwd(T, W, offs, v, dO, q=q, k=k)
+    for key in ("dq", "dk", "dv"):
+        np.testing.assert_array_equal(g1[key], g2[key])
+
+
+@pytest.mark.parametrize("rp,cols", [
+    ([0, 1, 2], [0, 2]),        # key after the query
+    ([0, 1, 3], [0, 1, 0]),     # not ascending
+    ([0, 1, 3], [0, 1, 1]),     # repeated key
+    ([0, 1, 1], [0]),           # empty row
+    ([1, 2, 3], [0, 1, 1]),     # row_ptr not starting at 0
+])
+def test_csr_rejects_malformed_lists(rp, cols):
+    v = np.zeros((2, 4))
+    with pytest.raises(ValueError):
+        oracle.fwd_csr(rp, cols, v)
