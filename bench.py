@@ -46,11 +46,27 @@ def parse():
 
 
 # ------------------------------------------------------------------ byte and flop models
+_LISTS = {}
+
+
+def random_lists(w):
+    """The seeded lists of a random-list workload (drawn once per process)."""
+    if w.name not in _LISTS:
+        from sparse_causal_attention_amd.inputs import workload_lists
+        _LISTS[w.name] = workload_lists(w)
+    return _LISTS[w.name]
+
+
 def edge_counts(w):
-    """(total edges per (b, h), long-range edges per (b, h))."""
+    """(total edges per (b, h), edges outside the window per (b, h)).  For
+    random lists every edge past the row's `window` nearest keys counts as a
+    long-range (gathered) edge."""
     T, Wc = w.T, min(w.window, w.T)
-    dil = sorted({d for d in w.offsets if Wc <= d < T})
     band = Wc * (Wc + 1) // 2 + Wc * (T - Wc)
+    if w.graph == "random":
+        E = int(random_lists(w)[0][-1])
+        return E, E - band
+    dil = sorted({d for d in w.offsets if Wc <= d < T})
     long_range = sum(T - d for d in dil)
     return band + long_range, long_range
 
@@ -62,8 +78,11 @@ def models(w, grad_bytes=4):
     floor); "gather" adds the K/V (forward) and K, V, Q, dO, LSE, Delta
     (backward) rows fetched per long-range edge, with no credit for cache
     reuse across queries.  Window edges are charged as compulsory: their rows
-    are contiguous and reused on chip."""
+    are contiguous and reused on chip.  Explicit lists add their int32 arrays
+    once per call (row pointers and keys; the backward reads the reverse lists
+    too): they are shared by every (batch, head) and stay in cache."""
     E, Ed = edge_counts(w)
+    lists = 4 * (w.T + 1) + 4 * E if w.graph != "distance" else 0
     rows = w.B * w.H * w.T
     eb = 2 if w.dtype_name == "bf16" else 4
     D = w.D
@@ -101,6 +120,8 @@ def models(w, grad_bytes=4):
         ffl = w.B * w.H * E * 4 * D
         bfl = w.B * w.H * E * 10 * D
     bh = w.B * w.H
+    fwd_c += lists
+    bwd_c += 2 * lists
     return {"edges": bh * E, "fwd_bytes": fwd_c + bh * fwd_e, "bwd_bytes": bwd_c + bh * bwd_e,
             "fwd_bytes_compulsory": fwd_c, "bwd_bytes_compulsory": bwd_c,
             "fwd_flops": ffl, "bwd_flops": bfl}
@@ -111,11 +132,22 @@ def score_name(w):
     return "coord" if w.coord else ("uniform" if w.uniform else "dot")
 
 
+def make_graph(w):
+    """The workload's graph: the window + distances descriptor, the same graph
+    as explicit lists (the library's own row export), or random lists."""
+    from sparse_causal_attention_amd import sa_build_graph, sa_build_graph_csr
+
+    if w.graph == "distance":
+        return sa_build_graph(w.T, w.window, w.offsets)
+    if w.graph == "lists":
+        return sa_build_graph_csr(w.T, *sa_build_graph(w.T, w.window, w.offsets).rows())
+    return sa_build_graph_csr(w.T, *random_lists(w))
+
+
 def run_workload(w, steps, warmup, algo, with_backward=True):
     import torch
 
-    from sparse_causal_attention_amd import (sa_build_graph, sa_bwd_prepared, sa_describe_plan,
-                                             sa_fwd_prepared)
+    from sparse_causal_attention_amd import sa_bwd_prepared, sa_describe_plan, sa_fwd_prepared
     from sparse_causal_attention_amd.inputs import make_device_inputs_chunked, make_inputs
 
     dev = "cuda"
@@ -123,7 +155,7 @@ def run_workload(w, steps, warmup, algo, with_backward=True):
         x = make_device_inputs_chunked(w, dev)
     else:
         x = {k: t.to(dev) for k, t in make_inputs(w, backward=with_backward and w.backward).items()}
-    g = sa_build_graph(w.T, w.window, w.offsets)
+    g = make_graph(w)
     bwd = with_backward and w.backward
     coord = w.coord
     o = torch.empty((w.B, w.H, w.T, w.D), dtype=x["v"].dtype, device=dev)
@@ -226,7 +258,7 @@ def summarize(w, r, steps):
     out = {
         "workload": w.name,
         "shape": {"B": w.B, "H": w.H, "H_kv": w.kv_heads, "T": w.T, "D": w.D, "window": w.window,
-                  "offsets": list(w.offsets), "dtype": w.dtype_name,
+                  "offsets": list(w.offsets), "graph": w.graph, "dtype": w.dtype_name,
                   "score": score_name(w), "backward": w.backward},
         # decode steps last microseconds: their rate comes from the kernel events
         "tokens_per_s": tokens / (r["fwd_ms"] * 1e-3) if w.decode else tokens * steps / wall,
@@ -305,11 +337,19 @@ def cpu_baseline(w, inputs, target_s):
 
     hv = {k: host_view(t) for k, t in inputs.items()}
     slices = [(b, h) for b in range(w.B) for h in range(w.H)]
+    lists = None
+    if w.graph == "lists":
+        lists = oracle.graph_csr(w.T, w.window, w.offsets)
+    elif w.graph == "random":
+        lists = random_lists(w)
     done = 0
     t0 = time.perf_counter()
     while True:  # whole passes over the (batch, head) slices until target_s
         b, h = slices[done % len(slices)]
-        if w.uniform:
+        if lists is not None:  # dot score over explicit lists
+            oracle.fwd_csr(*lists, hv["v"][b, h], q=hv["q"][b, h], k=hv["k"][b, h])
+            oracle.bwd_csr(*lists, hv["v"][b, h], hv["do"][b, h], q=hv["q"][b, h], k=hv["k"][b, h])
+        elif w.uniform:
             oracle.fwd(w.T, w.window, w.offsets, hv["v"][b, h])
             oracle.bwd(w.T, w.window, w.offsets, hv["v"][b, h], hv["do"][b, h])
         elif w.coord:

@@ -39,13 +39,16 @@
  *  - Coordinates c_q, c_k (and their gradients) are [B, H, T, 3] fp32,
  *    contiguous.  gamma, beta (and dgamma, dbeta) are [H] fp32.
  *  - Every pointer passed to sa_fwd / sa_bwd is a device pointer owned by the
- *    caller.  The library never allocates, frees or retains device memory.
+ *    caller.  The library never allocates or frees device memory; the one
+ *    device region it refers to beyond a call is the buffer an explicit-list
+ *    graph was uploaded into (sa_graph_upload), which stays the caller's.
  *  - Calls are asynchronous on the given stream (a hipStream_t; NULL is the
  *    null stream).  SA_OK means the work was validated and enqueued.
  *  - All validation happens before any HIP call, and nothing is written when
  *    validation fails.  No entry point aborts, throws or prints.
- *  - The library does not touch the GPU when it is loaded; sa_build_graph,
- *    sa_graph_* and the validation paths run on hosts without a GPU.
+ *  - The library does not touch the GPU when it is loaded; sa_build_graph*,
+ *    sa_graph_* (except sa_graph_upload) and the validation paths run on hosts
+ *    without a GPU.
  */
 #ifndef SPARSE_CAUSAL_ATTENTION_SA_H
 #define SPARSE_CAUSAL_ATTENTION_SA_H
@@ -79,14 +82,21 @@ typedef enum { SA_F32 = 0, SA_BF16 = 1 } sa_dtype;
 typedef enum { SA_SCORE_DOT = 0, SA_SCORE_COORD = 1, SA_SCORE_UNIFORM = 2 } sa_score;
 
 /* Kernel family.  AUTO picks the LDS/MFMA band kernels for the window when
- * they apply (bf16, dot score, D = 64, W >= 16) and the gather kernels
- * otherwise.  GATHER forces the gather kernels for every edge; BAND requests
- * the band kernels and fails with SA_ERR_UNSUPPORTED where they do not apply. */
+ * they apply (bf16, dot score, D = 64, W >= 16, a distance graph) and the
+ * gather kernels otherwise (the indexed ones for an explicit-list graph).
+ * GATHER forces the gather kernels for every edge; BAND requests the band
+ * kernels and fails with SA_ERR_UNSUPPORTED where they do not apply. */
 typedef enum { SA_ALGO_AUTO = 0, SA_ALGO_GATHER = 1, SA_ALGO_BAND = 2 } sa_algo;
 
 #define SA_MAX_DILATED 64 /* distinct long-range distances kept by a graph */
 
-typedef struct sa_graph sa_graph; /* opaque, host memory, immutable once built */
+typedef struct sa_graph sa_graph; /* opaque, host memory; its edges are fixed once built */
+
+/* The two graph representations. */
+typedef enum {
+  SA_GRAPH_DISTANCE = 0, /* window + long-range distances (sa_build_graph) */
+  SA_GRAPH_CSR = 1       /* explicit per-row key lists (sa_build_graph_csr) */
+} sa_graph_type;
 typedef void* sa_stream;          /* hipStream_t */
 
 /* ------------------------------------------------------------------ graph */
@@ -105,10 +115,47 @@ typedef void* sa_stream;          /* hipStream_t */
 sa_status sa_build_graph(int64_t T, int64_t window, const int64_t* offsets, int32_t n_offsets,
                          sa_graph** out);
 
+/* Builds a graph from explicit per-row key lists (compressed sparse rows, host
+ * memory, read during the call only): row i attends to the keys
+ * cols[row_ptr[i] .. row_ptr[i+1]), which must be strictly ascending, within
+ * 0 .. i (causal), and at least one per row; row_ptr has T + 1 entries with
+ * row_ptr[0] = 0.  This is the general graph view of "Longer Attention Span:
+ * Increasing Transformer Context Length with Sparse Graph Processing
+ * Techniques" (abstract: tokens as nodes, the attention mask as the edges,
+ * work proportional to the edges); the SpatialLM-Mini graph is the special
+ * case sa_build_graph describes without lists.  A list breaking a rule is
+ * SA_ERR_INVALID_ARG; T or E = row_ptr[T] of 2^31 or more is
+ * SA_ERR_UNSUPPORTED.  The builder also forms the reverse lists the backward
+ * walks (sa_graph_rows_reverse).  The same graph serves every (batch, head).
+ * Before sa_fwd, sa_bwd or sa_decode can use it, its lists must be uploaded
+ * (sa_graph_upload).  Integer only, bit-exact. */
+sa_status sa_build_graph_csr(int64_t T, const int64_t* row_ptr, const int64_t* cols, sa_graph** out);
+
+/* *kind receives the graph's sa_graph_type. */
+sa_status sa_graph_kind(const sa_graph* g, int32_t* kind);
+
+/* Device bytes an explicit-list graph's lists occupy once uploaded:
+ * 2 * (align256(4 (T + 1)) + align256(4 E)) -- forward and reverse lists, int32.
+ * 0 for a distance graph. */
+sa_status sa_graph_device_bytes(const sa_graph* g, size_t* bytes);
+
+/* Copies an explicit-list graph's forward and reverse lists into device_buf
+ * (device memory the caller owns: at least sa_graph_device_bytes bytes,
+ * 256-byte aligned, on the device the graph will be used on), on `stream`, and
+ * returns when the copy has completed.  From then on sa_fwd, sa_bwd and
+ * sa_decode read the lists there: the caller keeps the buffer allocated and
+ * unmodified while the graph is used and frees it after the last call that
+ * uses it has finished.  Uploading again (e.g. to a new buffer) replaces the
+ * reference; do not do so while calls on the graph are in flight.  A distance
+ * graph has nothing to upload: the call does nothing and returns SA_OK.  Bad
+ * buffer or size: SA_ERR_INVALID_ARG; a failed copy: SA_ERR_HIP. */
+sa_status sa_graph_upload(sa_graph* g, void* device_buf, size_t bytes, sa_stream stream);
+
 /* Normalised descriptor: T, the effective window min(W, T), the kept
  * long-range distances ascending (dil may be NULL; else SA_MAX_DILATED
  * entries of room) and the edge count per (batch, head)
  *   E = W'(W'+1)/2 + W'(T-W') + sum_{d in Dil} (T - d),  W' = min(W, T).
+ * For an explicit-list graph: T, window 0, no distances and E = row_ptr[T].
  * Any output pointer may be NULL. */
 sa_status sa_graph_info(const sa_graph* g, int64_t* T, int64_t* window, int32_t* n_dil,
                         int64_t* dil, int64_t* n_edges);
@@ -156,7 +203,9 @@ typedef struct {
  * coordinate mode reads cq, ck, gamma, beta, v (q, k ignored); uniform mode
  * reads v alone (o_i is the mean of v over N(i), lse_i = ln |N(i)|).  Writes o in
  * `dtype` (bf16 rounded to nearest even) and lse in fp32 (natural log).
- * Arithmetic is fp32 with fp32 accumulation; bf16 MFMA products for the band. */
+ * Arithmetic is fp32 with fp32 accumulation; bf16 MFMA products for the band.
+ * With an explicit-list graph N(i) is row i's list, and a graph that has not
+ * been uploaded is SA_ERR_INVALID_ARG (likewise for sa_bwd and sa_decode). */
 sa_status sa_fwd(const sa_graph* g, const sa_attn_desc* desc, const void* q, const void* k,
                  const void* v, const float* cq, const float* ck, const float* gamma,
                  const float* beta, void* o, float* lse, sa_stream stream);
@@ -191,7 +240,8 @@ sa_status sa_bwd(const sa_graph* g, const sa_attn_desc* desc, const void* q, con
 /* Decode step with a key/value cache: for every (b, h), the one new token at
  * row t_b = positions[b] of the cache attends to its neighbour list N(t_b)
  * (the window t_b .. t_b - W + 1 and t_b - d for the long-range distances
- * d <= t_b), with the forward's softmax and score; O(W + log T) row reads per
+ * d <= t_b; or row t_b of explicit lists), with the forward's softmax and
+ * score; O(W + log T) row reads per
  * token, independent of how long the cache is (SpatialLM-Mini news page,
  * "What to check before adopting it in your project": the prototype had no
  * KV cache).  desc->T is the cache capacity and must equal the graph's T;

@@ -10,6 +10,10 @@ must be built (``python -m sparse_causal_attention_amd.build``).
     o, lse = sa_fwd(g, q, k, v)                 # [B, H, T, D], [B, H, T]
     grads = sa_bwd(g, q, k, v, o, lse, dout)    # {"dq", "dk", "dv"}
 
+Any other causal graph is given as explicit per-row key lists:
+``sa_build_graph_csr(T, row_ptr, cols)``.  Its lists are copied into a
+device buffer (held by the Graph) on first use, or by ``Graph.upload``.
+
 Coordinate score (-gamma_h ||c_q - c_k||^2 + beta_h): pass ``cq``, ``ck``
 ([B, H, T, 3] fp32), ``gamma``, ``beta`` ([H] fp32) instead of ``q``, ``k``.
 Uniform score (every neighbour weighted 1 / |N(i)|): pass ``v`` alone; the
@@ -22,10 +26,11 @@ import ctypes
 import numpy as np
 
 from . import _abi
-from ._abi import (SA_ALGO_AUTO, SA_ALGO_BAND, SA_ALGO_GATHER, SA_BF16, SA_F32,
-                   SA_MAX_DILATED, SA_SCORE_COORD, SA_SCORE_DOT, SA_SCORE_UNIFORM, SaError)
+from ._abi import (SA_ALGO_AUTO, SA_ALGO_BAND, SA_ALGO_GATHER, SA_BF16, SA_F32, SA_GRAPH_CSR,
+                   SA_GRAPH_DISTANCE, SA_MAX_DILATED, SA_SCORE_COORD, SA_SCORE_DOT, SA_SCORE_UNIFORM,
+                   SaError)
 
-__all__ = ["sa_build_graph", "sa_fwd", "sa_bwd", "sa_decode", "sa_decode_prepared", "sa_fwd_prepared",
+__all__ = ["sa_build_graph", "sa_build_graph_csr", "sa_fwd", "sa_bwd", "sa_decode", "sa_decode_prepared", "sa_fwd_prepared",
            "sa_bwd_prepared",
            "sa_bwd_workspace_size", "sa_describe_plan", "Graph", "SaError"]
 
@@ -33,10 +38,12 @@ _ALGOS = {"auto": SA_ALGO_AUTO, "gather": SA_ALGO_GATHER, "band": SA_ALGO_BAND}
 
 
 class Graph:
-    """Owns an ``sa_graph`` handle (host memory)."""
+    """Owns an ``sa_graph`` handle (host memory) and, for explicit lists, the
+    device buffer they were uploaded into."""
 
     def __init__(self, handle: int):
         self._h = ctypes.c_void_p(handle)
+        self._dev = None  # device copy of explicit lists (torch uint8 tensor)
         L = _abi.lib()
         T, W, nd, ne = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int32(), ctypes.c_int64()
         dil = (ctypes.c_int64 * SA_MAX_DILATED)()
@@ -44,10 +51,41 @@ class Graph:
                                    dil, ctypes.byref(ne)), "sa_graph_info")
         self.T, self.window, self.n_edges = T.value, W.value, ne.value
         self.dilations = tuple(dil[t] for t in range(nd.value))
+        kind = ctypes.c_int32()
+        _abi.check(L.sa_graph_kind(self._h, ctypes.byref(kind)), "sa_graph_kind")
+        self.kind = kind.value
 
     @property
     def handle(self):
         return self._h
+
+    @property
+    def is_csr(self) -> bool:
+        return self.kind == SA_GRAPH_CSR
+
+    def device_bytes(self) -> int:
+        n = ctypes.c_size_t()
+        _abi.check(_abi.lib().sa_graph_device_bytes(self._h, ctypes.byref(n)), "sa_graph_device_bytes")
+        return n.value
+
+    def upload(self, device, stream=None):
+        """Copies explicit lists into a device buffer this Graph keeps (no-op for
+        distance graphs or when already on `device`)."""
+        if not self.is_csr:
+            return self
+        torch = _torch()
+        device = torch.device(device)
+        if self._dev is not None and self._dev.device == device:
+            return self
+        n = self.device_bytes()
+        buf = torch.empty(n + 256, dtype=torch.uint8, device=device)
+        off = (-buf.data_ptr()) % 256  # the library wants 256-byte alignment
+        view = buf[off:off + n]
+        with torch.cuda.device(device):
+            _abi.check(_abi.lib().sa_graph_upload(self._h, ctypes.c_void_p(view.data_ptr()), n,
+                                                  _stream(stream)), "sa_graph_upload")
+        self._dev = buf
+        return self
 
     def _rows(self, fn, r0, r1):
         L = _abi.lib()
@@ -75,6 +113,8 @@ class Graph:
             self._h = None
 
     def __repr__(self):
+        if self.is_csr:
+            return "Graph(T=%d, explicit lists, edges/head=%d)" % (self.T, self.n_edges)
         return "Graph(T=%d, window=%d, dilations=%s, edges/head=%d)" % (
             self.T, self.window, list(self.dilations), self.n_edges)
 
@@ -85,6 +125,22 @@ def sa_build_graph(T: int, window: int, offsets=()) -> Graph:
     h = ctypes.c_void_p()
     _abi.check(L.sa_build_graph(int(T), int(window), offs.ctypes.data if len(offs) else None,
                                 len(offs), ctypes.byref(h)), "sa_build_graph")
+    return Graph(h.value)
+
+
+def sa_build_graph_csr(T: int, row_ptr, cols) -> Graph:
+    """Graph from explicit lists: row i attends to cols[row_ptr[i]:row_ptr[i+1]]
+    (strictly ascending, each <= i, at least one per row)."""
+    L = _abi.lib()
+    rp = np.ascontiguousarray(np.asarray(row_ptr, dtype=np.int64).reshape(-1))
+    cl = np.ascontiguousarray(np.asarray(cols, dtype=np.int64).reshape(-1))
+    if len(rp) != int(T) + 1:
+        raise ValueError("row_ptr must have T + 1 entries")
+    if len(cl) < int(rp[-1]):
+        raise ValueError("cols has fewer than row_ptr[T] entries")
+    h = ctypes.c_void_p()
+    _abi.check(L.sa_build_graph_csr(int(T), rp.ctypes.data, cl.ctypes.data if len(cl) else None,
+                                    ctypes.byref(h)), "sa_build_graph_csr")
     return Graph(h.value)
 
 
@@ -196,6 +252,7 @@ def _fwd_args(graph, q, k, v, cq, ck, gamma, beta, scale, o, lse, algo, stream):
         raise ValueError("lse must be a contiguous float32 [B, H, T] tensor")
     d = _make_desc(v, score=mode, algo=algo, scale=scale, heads=H,
                    grad_dtype=SA_F32, q=None if coord else q, k=None if coord else k, v=v, o=o)
+    graph.upload(v.device, stream)
     args = (graph.handle, ctypes.byref(d), _ptr(None if coord else q), _ptr(None if coord else k),
             _ptr(v), _ptr(cq), _ptr(ck), _ptr(gamma), _ptr(beta), _ptr(o), _ptr(lse), _stream(stream))
     return args, (d, o, lse)
@@ -277,6 +334,7 @@ def _bwd_args(graph, q, k, v, o, lse, dout, cq, ck, gamma, beta, scale, grad_dty
                "sa_bwd_workspace_size")
     if workspace is None:
         workspace = torch.empty(max(n.value, 256), dtype=torch.uint8, device=dev)
+    graph.upload(dev, stream)
     args = (graph.handle, ctypes.byref(d), _ptr(None if coord else q), _ptr(None if coord else k),
             _ptr(v), _ptr(cq), _ptr(ck), _ptr(gamma), _ptr(beta), _ptr(o), _ptr(lse), _ptr(dout),
             _ptr(None if coord else dq), _ptr(None if coord else dk), _ptr(dv),
@@ -350,6 +408,7 @@ def _decode_args(graph, q, k, v, positions, cq, ck, gamma, beta, scale, o, lse, 
         if t.dim() != 3 or tuple(t.shape) != (B, H, D) or t.stride(2) != 1:
             raise ValueError("%s must be [B, H, D] with a contiguous last dimension" % name)
         getattr(d, "stride_" + name)[:] = (int(t.stride(0)), int(t.stride(1)), 0)
+    graph.upload(v.device, stream)
     args = (graph.handle, ctypes.byref(d), _ptr(positions), _ptr(q if mode == SA_SCORE_DOT else None),
             _ptr(k if mode == SA_SCORE_DOT else None), _ptr(v), _ptr(cq), _ptr(ck), _ptr(gamma), _ptr(beta),
             _ptr(o), _ptr(lse), _stream(stream))

@@ -16,6 +16,7 @@ SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_SHAPE_MISMATCH, SA_ERR_WOR
 SA_F32, SA_BF16 = 0, 1
 SA_SCORE_DOT, SA_SCORE_COORD, SA_SCORE_UNIFORM = 0, 1, 2
 SA_ALGO_AUTO, SA_ALGO_GATHER, SA_ALGO_BAND = 0, 1, 2
+SA_GRAPH_DISTANCE, SA_GRAPH_CSR = 0, 1
 SA_MAX_DILATED = 64
 
 i64 = ctypes.c_int64
@@ -36,7 +37,8 @@ class SaAttnDesc(ctypes.Structure):
 
 
 EXPORTED = (
-    "sa_build_graph", "sa_graph_info", "sa_graph_rows", "sa_graph_rows_reverse", "sa_graph_free",
+    "sa_build_graph", "sa_build_graph_csr", "sa_graph_kind", "sa_graph_device_bytes", "sa_graph_upload",
+    "sa_graph_info", "sa_graph_rows", "sa_graph_rows_reverse", "sa_graph_free",
     "sa_fwd", "sa_bwd_workspace_size", "sa_bwd", "sa_decode", "sa_describe_plan", "sa_status_str",
 )
 
@@ -61,6 +63,14 @@ def lib():
     L = ctypes.CDLL(LIB_PATH)
     L.sa_build_graph.restype = i32
     L.sa_build_graph.argtypes = [i64, i64, vp, i32, ctypes.POINTER(vp)]
+    L.sa_build_graph_csr.restype = i32
+    L.sa_build_graph_csr.argtypes = [i64, vp, vp, ctypes.POINTER(vp)]
+    L.sa_graph_kind.restype = i32
+    L.sa_graph_kind.argtypes = [vp, ctypes.POINTER(i32)]
+    L.sa_graph_device_bytes.restype = i32
+    L.sa_graph_device_bytes.argtypes = [vp, ctypes.POINTER(ctypes.c_size_t)]
+    L.sa_graph_upload.restype = i32
+    L.sa_graph_upload.argtypes = [vp, vp, ctypes.c_size_t, vp]
     L.sa_graph_info.restype = i32
     L.sa_graph_info.argtypes = [vp, vp, vp, vp, vp, vp]
     L.sa_graph_rows.restype = i32

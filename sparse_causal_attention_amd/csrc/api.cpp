@@ -42,7 +42,7 @@ bool offsets_fit(const sa_attn_desc* d, const int64_t st[3]) {
   return last < 9.0e18;
 }
 
-enum class Path { Gather, Band };
+enum class Path { Gather, Band, Csr };
 
 struct Plan {
   Path path;
@@ -77,11 +77,15 @@ sa_status check_common(const sa_graph* g, const sa_attn_desc* d, const void* q, 
     if (cq == nullptr || ck == nullptr || gamma == nullptr || beta == nullptr)
       return SA_ERR_INVALID_ARG;
   }  // uniform mode reads v alone
-  const bool band_ok = sa::band_supported(d->dtype, (int)d->D, d->score, g->W);
+  const bool csr = g->kind == SA_GRAPH_CSR;
+  const bool band_ok = !csr && sa::band_supported(d->dtype, (int)d->D, d->score, g->W);
   if (d->algo == SA_ALGO_BAND && !band_ok) return SA_ERR_UNSUPPORTED;
-  plan->path = (d->algo != SA_ALGO_GATHER && band_ok) ? Path::Band : Path::Gather;
+  plan->path = csr ? Path::Csr : (d->algo != SA_ALGO_GATHER && band_ok) ? Path::Band : Path::Gather;
   return SA_OK;
 }
+
+// An explicit-list graph is usable once its lists are in device memory.
+bool lists_ready(const sa_graph* g) { return g->kind != SA_GRAPH_CSR || g->d_rp != nullptr; }
 
 void fill_common(sa::Params* p, const sa_graph* g, const sa_attn_desc* d) {
   memset(p, 0, sizeof(*p));
@@ -98,6 +102,12 @@ void fill_common(sa::Params* p, const sa_graph* g, const sa_attn_desc* d) {
   p->scale = d->scale > 0.f ? d->scale : (float)(1.0 / sqrt((double)d->D));
   p->scale_log2 = p->scale * 1.4426950408889634f;
   p->grad_bf16 = d->grad_dtype == SA_BF16;
+  if (g->kind == SA_GRAPH_CSR) {
+    p->rp = g->d_rp;
+    p->cols = g->d_cols;
+    p->rrp = g->d_rrp;
+    p->rcols = g->d_rcols;
+  }
 }
 
 #define SET_STRIDES(prefix, arr) \
@@ -109,8 +119,24 @@ hipStream_t as_stream(sa_stream s) { return reinterpret_cast<hipStream_t>(s); }
 
 const char* fwd_kernel_name(const sa_attn_desc* d, Path path) {
   if (path == Path::Band) return "band_fwd_kernel";
+  if (path == Path::Csr) {
+    if (d->score == SA_SCORE_COORD) return "csr_fwd_kernel(coord)";
+    return d->score == SA_SCORE_UNIFORM ? "csr_fwd_kernel(uniform)" : "csr_fwd_kernel(dot)";
+  }
   if (d->score == SA_SCORE_COORD) return "gather_fwd_kernel(coord)";
   return d->score == SA_SCORE_UNIFORM ? "gather_fwd_kernel(uniform)" : "gather_fwd_kernel(dot)";
+}
+
+const char* bwd_kernel_names(const sa_attn_desc* d, Path path) {
+  const bool coord = d->score == SA_SCORE_COORD, uniform = d->score == SA_SCORE_UNIFORM;
+  if (path == Path::Band) return "band_bwd_prepass_kernel+band_bwd_kernel";
+  if (path == Path::Csr)
+    return coord ? "csr_bwd_q_kernel(coord)+csr_bwd_kv_kernel(coord)+coord_param_reduce_kernel"
+           : uniform ? "csr_bwd_kv_kernel(uniform)"
+                     : "csr_bwd_q_kernel(dot)+csr_bwd_kv_kernel(dot)";
+  return coord ? "gather_bwd_q_kernel(coord)+gather_bwd_kv_kernel(coord)+coord_param_reduce_kernel"
+         : uniform ? "gather_bwd_kv_kernel(uniform)"
+                   : "gather_bwd_q_kernel(dot)+gather_bwd_kv_kernel(dot)";
 }
 
 }  // namespace
@@ -121,7 +147,7 @@ extern "C" sa_status sa_fwd(const sa_graph* g, const sa_attn_desc* d, const void
   Plan plan;
   sa_status st = check_common(g, d, q, k, v, cq, ck, gamma, beta, &plan);
   if (st != SA_OK) return st;
-  if (o == nullptr || lse == nullptr) return SA_ERR_INVALID_ARG;
+  if (o == nullptr || lse == nullptr || !lists_ready(g)) return SA_ERR_INVALID_ARG;
   if (!aligned_rows(o, d->stride_o, esize(d->dtype)) || !offsets_fit(d, d->stride_o))
     return SA_ERR_INVALID_ARG;
   sa::Params p;
@@ -132,10 +158,10 @@ extern "C" sa_status sa_fwd(const sa_graph* g, const sa_attn_desc* d, const void
   p.o = o; SET_STRIDES(so, d->stride_o);
   p.cq = cq; p.ck = ck; p.gamma = gamma; p.beta = beta;
   p.lse = lse;
-  hipError_t e = plan.path == Path::Band
-                     ? sa::launch_band_fwd(p, as_stream(stream))
-                     : sa::launch_gather_fwd(p, d->dtype == SA_BF16 ? sa::DT_BF16 : sa::DT_F32,
-                                             d->score, as_stream(stream));
+  const int dt = d->dtype == SA_BF16 ? sa::DT_BF16 : sa::DT_F32;
+  hipError_t e = plan.path == Path::Band  ? sa::launch_band_fwd(p, as_stream(stream))
+                 : plan.path == Path::Csr ? sa::launch_csr_fwd(p, dt, d->score, as_stream(stream))
+                                          : sa::launch_gather_fwd(p, dt, d->score, as_stream(stream));
   return e == hipSuccess ? SA_OK : SA_ERR_HIP;
 }
 
@@ -177,7 +203,8 @@ extern "C" sa_status sa_bwd(const sa_graph* g, const sa_attn_desc* d, const void
   if (st != SA_OK) return st;
   const bool coord = d->score == SA_SCORE_COORD;
   const int es = esize(d->dtype), gs = esize(d->grad_dtype);
-  if (o == nullptr || lse == nullptr || dout == nullptr || dv == nullptr) return SA_ERR_INVALID_ARG;
+  if (o == nullptr || lse == nullptr || dout == nullptr || dv == nullptr || !lists_ready(g))
+    return SA_ERR_INVALID_ARG;
   if (!aligned_rows(o, d->stride_o, es) || !aligned_rows(dout, d->stride_do, es))
     return SA_ERR_INVALID_ARG;
   if (!offsets_fit(d, d->stride_o) || !offsets_fit(d, d->stride_do)) return SA_ERR_INVALID_ARG;
@@ -228,10 +255,10 @@ extern "C" sa_status sa_bwd(const sa_graph* g, const sa_attn_desc* d, const void
     p.pdk = reinterpret_cast<float*>(pp);
     p.pdv = reinterpret_cast<float*>(pp + pbytes);
   }
-  hipError_t e = plan.path == Path::Band
-                     ? sa::launch_band_bwd(p, as_stream(stream))
-                     : sa::launch_gather_bwd(p, d->dtype == SA_BF16 ? sa::DT_BF16 : sa::DT_F32,
-                                             d->score, as_stream(stream));
+  const int dt = d->dtype == SA_BF16 ? sa::DT_BF16 : sa::DT_F32;
+  hipError_t e = plan.path == Path::Band  ? sa::launch_band_bwd(p, as_stream(stream))
+                 : plan.path == Path::Csr ? sa::launch_csr_bwd(p, dt, d->score, as_stream(stream))
+                                          : sa::launch_gather_bwd(p, dt, d->score, as_stream(stream));
   return e == hipSuccess ? SA_OK : SA_ERR_HIP;
 }
 
@@ -261,7 +288,7 @@ extern "C" sa_status sa_decode(const sa_graph* g, const sa_attn_desc* d, const i
   } else if (d->score == SA_SCORE_COORD) {
     if (cq == nullptr || ck == nullptr || gamma == nullptr || beta == nullptr) return SA_ERR_INVALID_ARG;
   }
-  if (o == nullptr || lse == nullptr) return SA_ERR_INVALID_ARG;
+  if (o == nullptr || lse == nullptr || !lists_ready(g)) return SA_ERR_INVALID_ARG;
   if (!aligned_rows(o, o_row, es) || !offsets_fit(d, o_row)) return SA_ERR_INVALID_ARG;
   sa::Params p;
   fill_common(&p, g, d);
@@ -289,18 +316,7 @@ extern "C" sa_status sa_describe_plan(const sa_graph* g, const sa_attn_desc* d, 
   for (int c = 0; c < 3; ++c) tmp.stride_q[c] = tmp.stride_k[c] = tmp.stride_v[c] = 0;
   sa_status st = check_common(g, &tmp, dummy, dummy, dummy, dummy, dummy, dummy, dummy, &plan);
   if (st != SA_OK) return st;
-  const bool coord = d->score == SA_SCORE_COORD;
-  const char* txt;
-  if (which == 0) {
-    txt = fwd_kernel_name(d, plan.path);
-  } else if (plan.path == Path::Band) {
-    txt = "band_bwd_prepass_kernel+band_bwd_kernel";
-  } else {
-    txt = coord ? "gather_bwd_q_kernel(coord)+gather_bwd_kv_kernel(coord)+coord_param_reduce_kernel"
-          : d->score == SA_SCORE_UNIFORM ? "gather_bwd_kv_kernel(uniform)"
-                                          : "gather_bwd_q_kernel(dot)+gather_bwd_kv_kernel(dot)";
-  }
-  snprintf(buf, cap, "%s", txt);
+  snprintf(buf, cap, "%s", which == 0 ? fwd_kernel_name(d, plan.path) : bwd_kernel_names(d, plan.path));
   return SA_OK;
 }
 

@@ -7,6 +7,9 @@
 // the SpatialLM-Mini news page had no KV cache and did not measure
 // generation: "What to check before adopting it in your project").
 //
+// On an explicit-list graph the new token's edges are the keys its row of
+// the lists names.
+//
 // One workgroup per (batch, head).  Its lane groups (16 bytes of a row per
 // lane, so a group holds one key row) take the row's edges round robin, each
 // keeping its own online softmax state (running max, sum, weighted value
@@ -21,7 +24,7 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 
-template <int DT, int D, int SM>
+template <int DT, int D, int SM, bool CSR>
 __global__ __launch_bounds__(kThreads) void decode_kernel(Params p) {
   using F = Frag<DT>;
   constexpr int EPL = F::EPL;            // elements per lane
@@ -41,11 +44,18 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Params p) {
   const int t = p.pos != nullptr ? p.pos[b] : p.T - 1;  // row of the new token
   const bool valid = t >= 0 && t < p.T;
   const int tt = valid ? t : 0;
-  // edges: the window t, t-1, ..., t-W'+1, then t-d for the distances d <= t
+  // edges: the window t, t-1, ..., t-W'+1, then t-d for the distances d <= t;
+  // or the row's list
   const int wn = p.W < tt + 1 ? p.W : tt + 1;
-  int nd = 0;
-  while (nd < p.n_dil && p.dil[nd] <= tt) ++nd;  // uniform, ascending distances
-  const int E = wn + nd;
+  int E, beg = 0;
+  if constexpr (CSR) {
+    beg = p.rp[tt];
+    E = p.rp[tt + 1] - beg;
+  } else {
+    int nd = 0;
+    while (nd < p.n_dil && p.dil[nd] <= tt) ++nd;  // uniform, ascending distances
+    E = wn + nd;
+  }
 
   const int hk = h / p.G;  // key/value head shared by G query heads
   const char* khead = static_cast<const char*>(p.k) + (b * p.sk_b + hk * p.sk_h) * EB + sub * 16;
@@ -79,8 +89,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Params p) {
     for (int u = 0; u < kU; ++u) {
       const int e = e0 + u * NG;
       ok[u] = e < E;
-      const int d = !ok[u] ? 0 : (e < wn ? e : p.dil[e - wn]);
-      jj[u] = tt - d;  // >= 0 by construction; row tt stands in for absent edges
+      if constexpr (CSR) {
+        jj[u] = ok[u] ? p.cols[beg + e] : tt;
+      } else {
+        const int d = !ok[u] ? 0 : (e < wn ? e : p.dil[e - wn]);
+        jj[u] = tt - d;  // >= 0 by construction; row tt stands in for absent edges
+      }
       vraw[u] = ld16(vhead + (int64_t)jj[u] * p.sv_t * EB);
       if constexpr (SM == SM_DOT) kraw[u] = ld16(khead + (int64_t)jj[u] * p.sk_t * EB);
     }
@@ -149,33 +163,38 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(Params p) {
   }
 }
 
-template <int DT, int SM>
+template <int DT, int SM, bool CSR>
 hipError_t launch_d(const Params& p, hipStream_t s) {
   const dim3 grid((unsigned)(p.B * p.H)), block(kThreads);
   switch (p.D) {
-    case 16: hipLaunchKernelGGL((decode_kernel<DT, 16, SM>), grid, block, 0, s, p); break;
-    case 32: hipLaunchKernelGGL((decode_kernel<DT, 32, SM>), grid, block, 0, s, p); break;
-    case 64: hipLaunchKernelGGL((decode_kernel<DT, 64, SM>), grid, block, 0, s, p); break;
-    case 128: hipLaunchKernelGGL((decode_kernel<DT, 128, SM>), grid, block, 0, s, p); break;
+    case 16: hipLaunchKernelGGL((decode_kernel<DT, 16, SM, CSR>), grid, block, 0, s, p); break;
+    case 32: hipLaunchKernelGGL((decode_kernel<DT, 32, SM, CSR>), grid, block, 0, s, p); break;
+    case 64: hipLaunchKernelGGL((decode_kernel<DT, 64, SM, CSR>), grid, block, 0, s, p); break;
+    case 128: hipLaunchKernelGGL((decode_kernel<DT, 128, SM, CSR>), grid, block, 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <int DT>
+template <int DT, bool CSR>
 hipError_t launch_mode(const Params& p, int score_mode, hipStream_t s) {
   switch (score_mode) {
-    case SM_DOT: return launch_d<DT, SM_DOT>(p, s);
-    case SM_COORD: return launch_d<DT, SM_COORD>(p, s);
-    case SM_UNIFORM: return launch_d<DT, SM_UNIFORM>(p, s);
+    case SM_DOT: return launch_d<DT, SM_DOT, CSR>(p, s);
+    case SM_COORD: return launch_d<DT, SM_COORD, CSR>(p, s);
+    case SM_UNIFORM: return launch_d<DT, SM_UNIFORM, CSR>(p, s);
   }
   return hipErrorInvalidValue;
+}
+
+template <int DT>
+hipError_t launch_graph(const Params& p, int score_mode, hipStream_t s) {
+  return p.rp != nullptr ? launch_mode<DT, true>(p, score_mode, s) : launch_mode<DT, false>(p, score_mode, s);
 }
 
 }  // namespace
 
 hipError_t launch_decode(const Params& p, int dtype, int score_mode, hipStream_t s) {
-  return dtype == DT_BF16 ? launch_mode<DT_BF16>(p, score_mode, s) : launch_mode<DT_F32>(p, score_mode, s);
+  return dtype == DT_BF16 ? launch_graph<DT_BF16>(p, score_mode, s) : launch_graph<DT_F32>(p, score_mode, s);
 }
 
 }  // namespace sa

@@ -454,9 +454,7 @@ hipError_t launch_passes(const Params& p, hipStream_t s, int grid, int nblk) {
   hipLaunchKernelGGL((gather_bwd_kv_kernel<DT, D, SM, 4, OFF32>), dim3(grid_kv), dim3(kThreads), 0, s, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess || SM != SM_COORD) return e;
-  hipLaunchKernelGGL(coord_param_reduce_kernel, dim3(p.H), dim3(256), 0, s, p.partials, p.B, p.H,
-                     nblk, p.dgamma, p.dbeta);
-  return hipGetLastError();
+  return launch_coord_param_reduce(p, nblk, s);
 }
 
 template <int DT, int D, int SM>
@@ -490,6 +488,12 @@ hipError_t launch_mode(const Params& p, int score_mode, hipStream_t s) {
 }
 
 }  // namespace
+
+hipError_t launch_coord_param_reduce(const Params& p, int nblk, hipStream_t s) {
+  hipLaunchKernelGGL(coord_param_reduce_kernel, dim3(p.H), dim3(256), 0, s, p.partials, p.B, p.H,
+                     nblk, p.dgamma, p.dbeta);
+  return hipGetLastError();
+}
 
 hipError_t launch_gather_bwd(const Params& p, int dtype, int score_mode, hipStream_t s) {
   return dtype == DT_BF16 ? launch_mode<DT_BF16>(p, score_mode, s) : launch_mode<DT_F32>(p, score_mode, s);

@@ -1,4 +1,5 @@
-// Neighbour-graph construction and CSR export (host only, integer only).
+// Neighbour-graph construction and CSR export (host, integer only), and the
+// upload of explicit lists into caller-owned device memory.
 //
 // The graph of the SpatialLM-Mini news page ("How tokens choose whom to
 // listen to") is translation invariant: row i's keys are i - delta for a
@@ -6,6 +7,13 @@
 // descriptor {T, W' = min(W, T), sorted distinct long-range distances in
 // [W', T)} and never materialised for the kernels; CSR rows are produced on
 // request only (tests, users who want the explicit lists).
+//
+// Any other causal graph (the general view of "Longer Attention Span ...",
+// abstract: the mask as the edge set of a graph over the tokens) is given as
+// explicit per-row lists.  The builder checks them, forms the reverse lists
+// (for each key, the queries that list it) by a counting pass, and keeps
+// both as int32 CSR on the host until sa_graph_upload copies them to device
+// memory the caller provides.
 #include <algorithm>
 #include <new>
 #include <vector>
@@ -29,6 +37,7 @@ sa_status normalise(int64_t T, int64_t window, const int64_t* offsets, int32_t n
   std::sort(keep.begin(), keep.end());
   keep.erase(std::unique(keep.begin(), keep.end()), keep.end());
   if (keep.size() > SA_MAX_DILATED) return SA_ERR_UNSUPPORTED;
+  g->kind = SA_GRAPH_DISTANCE;
   g->T = T;
   g->W = w;
   g->n_dil = static_cast<int32_t>(keep.size());
@@ -51,6 +60,97 @@ extern "C" sa_status sa_build_graph(int64_t T, int64_t window, const int64_t* of
   sa_graph* g = new (std::nothrow) sa_graph(tmp);
   if (g == nullptr) return SA_ERR_INVALID_ARG;
   *out = g;
+  return SA_OK;
+}
+
+extern "C" sa_status sa_build_graph_csr(int64_t T, const int64_t* row_ptr, const int64_t* cols,
+                                        sa_graph** out) {
+  if (out == nullptr || row_ptr == nullptr || T < 1) return SA_ERR_INVALID_ARG;
+  if (T > INT32_MAX) return SA_ERR_UNSUPPORTED;
+  if (row_ptr[0] != 0) return SA_ERR_INVALID_ARG;
+  for (int64_t i = 0; i < T; ++i)
+    if (row_ptr[i + 1] <= row_ptr[i]) return SA_ERR_INVALID_ARG;  // every row lists a key
+  const int64_t E = row_ptr[T];
+  if (E > INT32_MAX) return SA_ERR_UNSUPPORTED;
+  if (cols == nullptr) return SA_ERR_INVALID_ARG;
+  for (int64_t i = 0; i < T; ++i)
+    for (int64_t e = row_ptr[i]; e < row_ptr[i + 1]; ++e) {
+      if (cols[e] < 0 || cols[e] > i) return SA_ERR_INVALID_ARG;       // causal
+      if (e > row_ptr[i] && cols[e] <= cols[e - 1]) return SA_ERR_INVALID_ARG;  // ascending, distinct
+    }
+  sa_graph* g = new (std::nothrow) sa_graph();
+  if (g == nullptr) return SA_ERR_INVALID_ARG;
+  try {
+    g->kind = SA_GRAPH_CSR;
+    g->T = T;
+    g->W = 0;
+    g->n_dil = 0;
+    g->n_edges = E;
+    g->rp.assign(row_ptr, row_ptr + T + 1);
+    g->cols.assign(cols, cols + E);
+    // reverse lists: count per key, prefix sum, then fill walking rows in
+    // ascending order, so each key's queries come out ascending
+    g->rrp.assign(static_cast<size_t>(T) + 1, 0);
+    for (int64_t e = 0; e < E; ++e) ++g->rrp[static_cast<size_t>(cols[e]) + 1];
+    for (int64_t j = 0; j < T; ++j) g->rrp[j + 1] += g->rrp[j];
+    g->rcols.resize(static_cast<size_t>(E));
+    std::vector<int32_t> fill(g->rrp.begin(), g->rrp.end() - 1);
+    for (int64_t i = 0; i < T; ++i)
+      for (int64_t e = row_ptr[i]; e < row_ptr[i + 1]; ++e) g->rcols[fill[cols[e]]++] = (int32_t)i;
+  } catch (const std::bad_alloc&) {
+    delete g;
+    return SA_ERR_INVALID_ARG;
+  }
+  *out = g;
+  return SA_OK;
+}
+
+extern "C" sa_status sa_graph_kind(const sa_graph* g, int32_t* kind) {
+  if (g == nullptr || kind == nullptr) return SA_ERR_INVALID_ARG;
+  *kind = g->kind;
+  return SA_OK;
+}
+
+namespace {
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+// device layout of the lists: rp [T+1], cols [E], rrp [T+1], rcols [E], int32,
+// each segment 256-byte aligned
+size_t ptr_bytes(const sa_graph* g) { return align256(sizeof(int32_t) * (size_t)(g->T + 1)); }
+size_t col_bytes(const sa_graph* g) { return align256(sizeof(int32_t) * (size_t)g->n_edges); }
+}  // namespace
+
+extern "C" sa_status sa_graph_device_bytes(const sa_graph* g, size_t* bytes) {
+  if (g == nullptr || bytes == nullptr) return SA_ERR_INVALID_ARG;
+  *bytes = g->kind == SA_GRAPH_CSR ? 2 * (ptr_bytes(g) + col_bytes(g)) : 0;
+  return SA_OK;
+}
+
+extern "C" sa_status sa_graph_upload(sa_graph* g, void* device_buf, size_t bytes, sa_stream stream) {
+  if (g == nullptr) return SA_ERR_INVALID_ARG;
+  if (g->kind != SA_GRAPH_CSR) return SA_OK;  // nothing lives on the device
+  const size_t pb = ptr_bytes(g), cb = col_bytes(g);
+  if (device_buf == nullptr || (reinterpret_cast<uintptr_t>(device_buf) & 255u) != 0 ||
+      bytes < 2 * (pb + cb))
+    return SA_ERR_INVALID_ARG;
+  char* base = static_cast<char*>(device_buf);
+  int32_t* d_rp = reinterpret_cast<int32_t*>(base);
+  int32_t* d_cols = reinterpret_cast<int32_t*>(base + pb);
+  int32_t* d_rrp = reinterpret_cast<int32_t*>(base + pb + cb);
+  int32_t* d_rcols = reinterpret_cast<int32_t*>(base + 2 * pb + cb);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const size_t np = sizeof(int32_t) * (size_t)(g->T + 1), nc = sizeof(int32_t) * (size_t)g->n_edges;
+  // host sources are pageable and owned by the graph: copy, then wait, so
+  // the lists are in place and the host vectors free to go when this returns
+  if (hipMemcpyAsync(d_rp, g->rp.data(), np, hipMemcpyHostToDevice, s) != hipSuccess ||
+      hipMemcpyAsync(d_cols, g->cols.data(), nc, hipMemcpyHostToDevice, s) != hipSuccess ||
+      hipMemcpyAsync(d_rrp, g->rrp.data(), np, hipMemcpyHostToDevice, s) != hipSuccess ||
+      hipMemcpyAsync(d_rcols, g->rcols.data(), nc, hipMemcpyHostToDevice, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return SA_ERR_HIP;
+  g->d_rp = d_rp;
+  g->d_cols = d_cols;
+  g->d_rrp = d_rrp;
+  g->d_rcols = d_rcols;
   return SA_OK;
 }
 
@@ -85,11 +185,25 @@ static int64_t rev_degree(const sa_graph* g, int64_t j) {
   return n;
 }
 
+// Rows [r0, r1) of explicit lists (ptr, idx), as int64 CSR.
+static sa_status export_lists(const std::vector<int32_t>& ptr, const std::vector<int32_t>& idx, int64_t r0,
+                              int64_t r1, int64_t* row_ptr, int64_t* cols, int64_t cols_cap) {
+  row_ptr[0] = 0;
+  for (int64_t r = r0; r < r1; ++r) row_ptr[r - r0 + 1] = row_ptr[r - r0] + (ptr[r + 1] - ptr[r]);
+  const int64_t need = row_ptr[r1 - r0];
+  if (need > cols_cap || (need > 0 && cols == nullptr)) return SA_ERR_INVALID_ARG;
+  for (int64_t e = 0; e < need; ++e) cols[e] = idx[ptr[r0] + e];
+  return SA_OK;
+}
+
 template <bool REVERSE>
 static sa_status export_rows(const sa_graph* g, int64_t r0, int64_t r1, int64_t* row_ptr,
                              int64_t* cols, int64_t cols_cap) {
   if (g == nullptr || row_ptr == nullptr || r0 < 0 || r1 < r0 || r1 > g->T || cols_cap < 0)
     return SA_ERR_INVALID_ARG;
+  if (g->kind == SA_GRAPH_CSR)
+    return REVERSE ? export_lists(g->rrp, g->rcols, r0, r1, row_ptr, cols, cols_cap)
+                   : export_lists(g->rp, g->cols, r0, r1, row_ptr, cols, cols_cap);
   row_ptr[0] = 0;
   for (int64_t r = r0; r < r1; ++r)
     row_ptr[r - r0 + 1] = row_ptr[r - r0] + (REVERSE ? rev_degree(g, r) : row_degree(g, r));

@@ -4,15 +4,27 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <vector>
+
 #include "../../include/sa.h"
 
-// Normalised translation-invariant graph (see graph.cpp).
+// A neighbour graph (see graph.cpp): either the normalised
+// translation-invariant descriptor, or explicit per-row lists.
 struct sa_graph {
+  int32_t kind;                 // SA_GRAPH_DISTANCE or SA_GRAPH_CSR
   int64_t T;                    // sequence length
-  int64_t W;                    // effective window, min(W, T)
+  int64_t W;                    // effective window, min(W, T) (distance graphs; 0 for lists)
   int32_t n_dil;                // kept long-range distances
   int64_t dil[SA_MAX_DILATED];  // ascending, W <= d < T
   int64_t n_edges;              // per (batch, head)
+  // explicit lists (kind == SA_GRAPH_CSR), host copies: forward rows i -> keys
+  // ascending, reverse rows j -> queries ascending; int32 since T, E < 2^31
+  std::vector<int32_t> rp, cols, rrp, rcols;
+  // the same four arrays in caller-owned device memory once uploaded
+  const int32_t* d_rp = nullptr;
+  const int32_t* d_cols = nullptr;
+  const int32_t* d_rrp = nullptr;
+  const int32_t* d_rcols = nullptr;
 };
 
 namespace sa {
@@ -60,6 +72,10 @@ struct Params {
   const int32_t* pos;  // decode: row of each sequence's new token [B] (NULL: T - 1)
   float* pdk;  // band backward with G > 1: per-query-head dk, dv partials,
   float* pdv;  // contiguous fp32 [B, H, T, D] in the workspace
+  // explicit neighbour lists (device): row i's keys cols[rp[i] .. rp[i+1]),
+  // key j's queries rcols[rrp[j] .. rrp[j+1]), both ascending
+  const int32_t* rp; const int32_t* cols;
+  const int32_t* rrp; const int32_t* rcols;
 };
 
 // Launchers (defined in the .hip files).  Each validates nothing: the C ABI
@@ -71,6 +87,12 @@ int gather_rows_per_block(int dtype, int D);
 hipError_t launch_band_fwd(const Params& p, hipStream_t s);
 hipError_t launch_band_bwd(const Params& p, hipStream_t s);
 hipError_t launch_decode(const Params& p, int dtype, int score_mode, hipStream_t s);
+// explicit-list graphs: forward, and backward (query pass, key pass over the
+// reverse lists, coordinate-parameter reduction)
+hipError_t launch_csr_fwd(const Params& p, int dtype, int score_mode, hipStream_t s);
+hipError_t launch_csr_bwd(const Params& p, int dtype, int score_mode, hipStream_t s);
+// dgamma, dbeta from the per-block partials of a query pass of nblk blocks
+hipError_t launch_coord_param_reduce(const Params& p, int nblk, hipStream_t s);
 int band_rows_per_block();
 // Compute units of the current device (queried once per device).
 int device_cu_count();

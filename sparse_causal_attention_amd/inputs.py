@@ -14,7 +14,15 @@ the very long single-GPU sequences of the sparse-graph-processing abstract
 bf16 (round-to-nearest-even) where the workload is bf16.
 
 Seed of tensor t of workload c: 1000 * c + t with t = 0 q, 1 k, 2 v, 3 dO,
-4 c_q, 5 c_k, 6 gamma, 7 beta, 8 sampled rows.
+4 c_q, 5 c_k, 6 gamma, 7 beta, 8 sampled rows, 9 random neighbour lists.
+
+Explicit-list workloads carry their graph as per-row key lists: either the
+window + distances graph written out row by row (`graph="lists"`, the same
+edges through the indexed kernels) or random causal lists (`graph="random"`:
+row i keeps its `window` nearest keys i-window+1 .. i plus `extra` distinct
+earlier keys drawn uniformly, the same degree as the dilated workload with no
+regular structure).  The pages name no particular mask, so this random
+pattern is a stand-in.
 """
 from __future__ import annotations
 
@@ -22,7 +30,7 @@ from dataclasses import dataclass, field
 
 import torch
 
-SEED_Q, SEED_K, SEED_V, SEED_DO, SEED_CQ, SEED_CK, SEED_GAMMA, SEED_BETA, SEED_ROWS = range(9)
+SEED_Q, SEED_K, SEED_V, SEED_DO, SEED_CQ, SEED_CK, SEED_GAMMA, SEED_BETA, SEED_ROWS, SEED_LISTS = range(10)
 
 
 @dataclass(frozen=True)
@@ -41,6 +49,8 @@ class Workload:
     uniform: bool = False  # fixed equal weights (v alone)
     decode: bool = False   # one new token per sequence at row T - 1 of a T-row cache
     Hkv: int = 0           # key/value heads (0: H)
+    graph: str = "distance"  # "distance", "lists" (same graph as lists) or "random" lists
+    extra: int = 0           # random lists: distinct earlier keys per row beyond the window
 
     @property
     def kv_heads(self) -> int:
@@ -81,6 +91,12 @@ WORKLOADS = {
                             decode=True),
     "decode_dilated": Workload("decode_dilated", 8, 64, 8, 16384, 64, torch.bfloat16, 4, _pow2(0, 13),
                                backward=False, decode=True),
+    # explicit per-row lists: the dilated graph written out, and random causal
+    # lists of the same degree (window 4 + 12 random earlier keys)
+    "csr_dilated": Workload("csr_dilated", 11, 4, 8, 16384, 64, torch.bfloat16, 4, _pow2(0, 13),
+                            graph="lists"),
+    "csr_random": Workload("csr_random", 12, 4, 8, 16384, 64, torch.bfloat16, 4, (), graph="random",
+                           extra=12),
     # ultra-long single head, forward only: window 64 + distances 2^6..2^25
     "ultra": Workload("ultra", 5, 1, 1, 2 ** 26, 64, torch.bfloat16, 64, _pow2(6, 25),
                       backward=False),
@@ -99,6 +115,40 @@ def _randn(shape, seed: int) -> torch.Tensor:
 def _uniform(shape, lo: float, hi: float, seed: int) -> torch.Tensor:
     g = torch.Generator().manual_seed(seed)
     return torch.rand(shape, generator=g, dtype=torch.float32) * (hi - lo) + lo
+
+
+def random_causal_lists(T: int, window: int, extra: int, seed: int):
+    """Seeded random causal lists (int64 numpy row_ptr [T+1], cols): row i
+    holds max(0, i-window+1) .. i and min(extra, i-window+1) distinct keys
+    drawn uniformly from 0 .. i-window, ascending."""
+    import numpy as np
+
+    rng = np.random.default_rng(seed)
+    rp = np.zeros(T + 1, dtype=np.int64)
+    rows = []
+    for i in range(T):
+        lo = max(0, i - window + 1)
+        pool = lo  # keys 0 .. lo-1 lie outside the window
+        n = min(extra, pool)
+        if n == 0:
+            far = np.empty(0, dtype=np.int64)
+        elif n * 4 >= pool:
+            far = np.sort(rng.permutation(pool)[:n])
+        else:
+            picked = set()
+            while len(picked) < n:
+                picked.update(int(x) for x in rng.integers(0, pool, size=n - len(picked)))
+            far = np.array(sorted(picked), dtype=np.int64)
+        row = np.concatenate([far, np.arange(lo, i + 1, dtype=np.int64)])
+        rows.append(row)
+        rp[i + 1] = rp[i] + len(row)
+    return rp, np.concatenate(rows)
+
+
+def workload_lists(w: Workload):
+    """The explicit lists of a random-list workload (row_ptr, cols)."""
+    assert w.graph == "random", w.name
+    return random_causal_lists(w.T, w.window, w.extra, seed_of(w, SEED_LISTS))
 
 
 def make_inputs(w: Workload, device="cpu", backward: bool | None = None,

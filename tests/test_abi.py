@@ -206,3 +206,43 @@ def test_grouped_heads_validation(g64):
     d.H_kv = 0
     assert _abi.lib().sa_bwd_workspace_size(g64.handle, ctypes.byref(d), ctypes.byref(need2)) == 0
     assert need2.value == need1.value
+
+
+def test_explicit_lists_need_an_upload_and_pick_indexed_kernels():
+    """An explicit-list graph: plans name the indexed kernels, the band kernels
+    are unsupported, and every compute call is refused until the lists are in
+    device memory.  sa_graph_upload rejects a bad buffer before touching the
+    GPU, and is a no-op for a distance graph."""
+    from sparse_causal_attention_amd import sa_build_graph_csr
+
+    E = _abi
+    L = _abi.lib()
+    T = 64
+    rp = [0]
+    cols = []
+    for i in range(T):
+        row = sorted({0, i // 2, i})
+        cols += row
+        rp.append(len(cols))
+    g = sa_build_graph_csr(T, rp, cols)
+    assert plan(g, desc(), 0) == (0, "csr_fwd_kernel(dot)")
+    assert plan(g, desc(score=1), 1) == (
+        0, "csr_bwd_q_kernel(coord)+csr_bwd_kv_kernel(coord)+coord_param_reduce_kernel")
+    assert plan(g, desc(score=2), 1) == (0, "csr_bwd_kv_kernel(uniform)")
+    assert plan(g, desc(dtype=1, D=64), 0) == (0, "csr_fwd_kernel(dot)")  # never the band kernels
+    assert plan(g, desc(dtype=1, D=64, algo=2), 0)[0] == E.SA_ERR_UNSUPPORTED
+    assert fwd(g, desc()) == E.SA_ERR_INVALID_ARG
+    assert bwd(g, desc()) == E.SA_ERR_INVALID_ARG
+    assert decode(g, desc()) == E.SA_ERR_INVALID_ARG
+    n = g.device_bytes()
+    assert n > 0
+    assert L.sa_graph_upload(g.handle, None, n, None) == E.SA_ERR_INVALID_ARG
+    assert L.sa_graph_upload(g.handle, FAKE + 16, n, None) == E.SA_ERR_INVALID_ARG  # not 256-byte aligned
+    assert L.sa_graph_upload(g.handle, FAKE, n - 1, None) == E.SA_ERR_INVALID_ARG
+    assert L.sa_graph_upload(None, FAKE, n, None) == E.SA_ERR_INVALID_ARG
+    d = g64_graph()
+    assert d.device_bytes() == 0 and not d.is_csr
+    assert L.sa_graph_upload(d.handle, None, 0, None) == E.SA_OK
+    kind = ctypes.c_int32(-1)
+    assert L.sa_graph_kind(g.handle, ctypes.byref(kind)) == E.SA_OK and kind.value == E.SA_GRAPH_CSR
+    assert L.sa_graph_kind(None, ctypes.byref(kind)) == E.SA_ERR_INVALID_ARG

@@ -12,9 +12,10 @@ import pytest
 import torch
 
 import oracle
-from sparse_causal_attention_amd import sa_build_graph, sa_bwd, sa_decode, sa_describe_plan, sa_fwd
+from sparse_causal_attention_amd import (sa_build_graph, sa_build_graph_csr, sa_bwd, sa_decode, sa_describe_plan,
+                                        sa_fwd)
 from sparse_causal_attention_amd.inputs import (WORKLOADS, Workload, host_view, make_device_inputs_chunked,
-                                                make_inputs, sample_rows)
+                                                make_inputs, random_causal_lists, sample_rows, workload_lists)
 
 pytestmark = pytest.mark.gpu
 
@@ -454,3 +455,218 @@ def test_decode_grouped_kv_heads():
     vv = np.repeat(host_view(v), G, axis=1)
     O, L = decode_reference(W, offs, pos, vv, q=host_view(q), k=kk)
     assert maxabs(o, O) <= 2e-2 and maxabs(lse, L) <= 2e-2
+
+
+# ------------------------------------------------------------------ explicit neighbour lists
+def csr_reference(rp, cols, G, v, dO=None, q=None, k=None, cq=None, ck=None, gamma=None, beta=None):
+    """Oracle per (b, h) over the lists; query head h reads key/value head
+    h // G, so dk, dv of a key/value head sum over its G query heads;
+    dgamma, dbeta, l1 are per head, summed over the batch."""
+    B, Hkv, T, D = v.shape
+    H = Hkv * G
+    O, L = np.empty((B, H, T, D)), np.empty((B, H, T))
+    grads = {}
+    for b in range(B):
+        for h in range(H):
+            hk = h // G
+            if cq is not None:
+                kw = dict(cq=cq[b, h], ck=ck[b, h], gamma=float(gamma[h]), beta=float(beta[h]))
+            elif q is not None:
+                kw = dict(q=q[b, h], k=k[b, hk])
+            else:
+                kw = {}
+            O[b, h], L[b, h] = oracle.fwd_csr(rp, cols, v[b, hk], **kw)
+            if dO is None:
+                continue
+            r = oracle.bwd_csr(rp, cols, v[b, hk], dO[b, h], **kw)
+            for key, val in r.items():
+                if key in ("dgamma", "dbeta", "l1"):
+                    grads.setdefault(key, np.zeros(H))[h] += val
+                elif key in ("dk", "dv"):
+                    grads.setdefault(key, np.zeros((B, Hkv, T, D)))[b, hk] += val
+                else:
+                    grads.setdefault(key, np.empty((B, H) + val.shape))[b, h] = val
+    return O, L, grads
+
+
+def run_csr(rp, cols, B, H, Hkv, D, dt, score, seed, grad_dtype=None):
+    T = len(rp) - 1
+    G = H // Hkv
+    gen = torch.Generator().manual_seed(seed)
+    x = {"v": torch.randn((B, Hkv, T, D), generator=gen).to(dt),
+         "do": torch.randn((B, H, T, D), generator=gen).to(dt)}
+    if score == "dot":
+        x["q"] = torch.randn((B, H, T, D), generator=gen).to(dt)
+        x["k"] = torch.randn((B, Hkv, T, D), generator=gen).to(dt)
+    elif score == "coord":
+        x["cq"] = torch.randn((B, H, T, 3), generator=gen)
+        x["ck"] = torch.randn((B, H, T, 3), generator=gen)
+        x["gamma"] = torch.rand((H,), generator=gen) * 1.5 + 0.5
+        x["beta"] = torch.randn((H,), generator=gen) * 0.1
+    g = sa_build_graph_csr(T, rp, cols)
+    xd = {k_: t.to(DEV) for k_, t in x.items()}
+    _say("csr B=%d H=%d Hkv=%d T=%d D=%d %s %s E=%d plan %s / %s" % (
+        B, H, Hkv, T, D, dt, score, rp[-1], sa_describe_plan(g, xd["v"], score=score, heads=H),
+        sa_describe_plan(g, xd["v"], score=score, heads=H, which="bwd")))
+    if score == "dot":
+        o, lse = sa_fwd(g, xd["q"], xd["k"], xd["v"])
+        gr = sa_bwd(g, xd["q"], xd["k"], xd["v"], o, lse, xd["do"], grad_dtype=grad_dtype)
+    elif score == "coord":
+        cw = dict(cq=xd["cq"], ck=xd["ck"], gamma=xd["gamma"], beta=xd["beta"])
+        o, lse = sa_fwd(g, v=xd["v"], **cw)
+        gr = sa_bwd(g, v=xd["v"], o=o, lse=lse, dout=xd["do"], grad_dtype=grad_dtype, **cw)
+    else:
+        o = torch.empty((B, H, T, D), dtype=dt, device=DEV)
+        o, lse = sa_fwd(g, v=xd["v"], o=o)
+        gr = sa_bwd(g, v=xd["v"], o=o, lse=lse, dout=xd["do"], grad_dtype=grad_dtype)
+    torch.cuda.synchronize()
+    hv = {k_: host_view(t) for k_, t in x.items()}
+    O, L, ref = csr_reference(rp, cols, G, hv["v"], hv["do"], q=hv.get("q"), k=hv.get("k"), cq=hv.get("cq"),
+                              ck=hv.get("ck"), gamma=hv.get("gamma"), beta=hv.get("beta"))
+    tol = tol_of(dt)
+    errs = {"o": maxabs(o, O), "lse": maxabs(lse, L)}
+    assert sorted(gr) == sorted(k_ for k_ in ref if k_ != "l1")
+    for key in gr:
+        if key in ("dgamma", "dbeta"):
+            err = np.abs(gr[key].double().cpu().numpy() - ref[key])
+            errs[key] = float(np.max(err / np.maximum(tol, 1e-6 * ref["l1"]))) * tol
+        else:
+            errs[key] = maxabs(gr[key], ref[key])
+    _say("csr errors %s (tol %g)" % ({k_: "%.2e" % e for k_, e in errs.items()}, tol))
+    gtol = tol if grad_dtype in (None, torch.float32) else max(tol, 5e-2)
+    for key, e in errs.items():
+        assert e <= (tol if key in ("o", "lse") else gtol), (key, e)
+    return g, xd, o, lse, gr
+
+
+def lists_of(kind, T, seed=0):
+    if kind == "random":
+        return random_causal_lists(T, 4, 12, seed)
+    if kind == "wide":       # long, very uneven rows: window 16 + up to 40 random keys
+        return random_causal_lists(T, 16, 40, seed)
+    if kind == "dense":      # every j <= i (dense causal attention)
+        return random_causal_lists(T, T, 0, seed)
+    if kind == "self":       # only the row itself
+        return random_causal_lists(T, 1, 0, seed)
+    if kind == "hub":        # rows {0, i}: key 0 has T queries, the others one
+        rp = np.concatenate([[0, 1], 1 + 2 * np.arange(1, T, dtype=np.int64)])
+        cols = np.concatenate([[0]] + [[0, i] for i in range(1, T)]).astype(np.int64)
+        return rp, cols
+    raise ValueError(kind)
+
+
+@pytest.mark.parametrize("kind,B,H,Hkv,T,D,dt,score", [
+    ("random", 2, 2, 2, 300, 32, torch.float32, "dot"),
+    ("random", 2, 2, 2, 300, 32, torch.float32, "coord"),
+    ("random", 2, 2, 2, 300, 32, torch.float32, "uniform"),
+    ("wide", 1, 4, 2, 777, 64, torch.bfloat16, "dot"),
+    ("wide", 1, 3, 3, 513, 64, torch.bfloat16, "coord"),
+    ("dense", 1, 2, 2, 257, 128, torch.float32, "dot"),
+    ("self", 2, 1, 1, 129, 16, torch.float32, "dot"),
+    ("hub", 1, 2, 1, 1000, 64, torch.bfloat16, "dot"),
+    ("hub", 1, 2, 2, 1000, 64, torch.bfloat16, "uniform"),
+])
+def test_explicit_lists_small(kind, B, H, Hkv, T, D, dt, score):
+    rp, cols = lists_of(kind, T, seed=T + D)
+    run_csr(rp, cols, B, H, Hkv, D, dt, score, seed=7 * T + D)
+
+
+def test_explicit_lists_self_only_is_identity():
+    """A graph where each row lists only itself: o = v exactly, lse = s_ii."""
+    T, D = 100, 32
+    rp, cols = lists_of("self", T)
+    g = sa_build_graph_csr(T, rp, cols)
+    v = torch.randn((1, 1, T, D), generator=torch.Generator().manual_seed(3), device="cpu").to(DEV)
+    o, lse = sa_fwd(g, v=v)
+    torch.cuda.synchronize()
+    assert torch.equal(o, v) and float(lse.abs().max()) == 0.0
+
+
+@pytest.mark.parametrize("name", ["csr_dilated", "csr_random"])
+def test_explicit_lists_full_size(name):
+    """The full-size list workloads (B=4, H=8, T=16384, D=64, bf16), every
+    output element against the oracle; the dilated graph as lists also
+    against the descriptor path on the same inputs."""
+    w = WORKLOADS[name]
+    if w.graph == "random":
+        rp, cols = workload_lists(w)
+    else:
+        rp, cols = oracle.graph_csr(w.T, w.window, w.offsets)
+    x = make_inputs(w, device="cpu")
+    gtest = run_csr_inputs(w, rp, cols, x)
+    if w.graph == "lists":
+        g, xd, o, lse, gr = gtest
+        gd = sa_build_graph(w.T, w.window, w.offsets)
+        o2, lse2 = sa_fwd(gd, xd["q"], xd["k"], xd["v"], algo="gather")
+        gr2 = sa_bwd(gd, xd["q"], xd["k"], xd["v"], o2, lse2, xd["do"], algo="gather")
+        torch.cuda.synchronize()
+        diffs = {"o": float((o.float() - o2.float()).abs().max()), "lse": float((lse - lse2).abs().max())}
+        diffs.update({k_: float((gr[k_] - gr2[k_]).abs().max()) for k_ in gr})
+        _say("lists vs descriptor path: %s" % {k_: "%.2e" % e for k_, e in diffs.items()})
+        assert all(e <= 2e-2 for e in diffs.values()), diffs
+
+
+def run_csr_inputs(w, rp, cols, x):
+    """run_csr on a workload's own seeded inputs (dot score)."""
+    B, H, T, D = x["q"].shape
+    g = sa_build_graph_csr(T, rp, cols)
+    xd = {k_: t.to(DEV) for k_, t in x.items()}
+    _say("%s full size B=%d H=%d T=%d E=%d" % (w.name, B, H, T, rp[-1]))
+    o, lse = sa_fwd(g, xd["q"], xd["k"], xd["v"])
+    gr = sa_bwd(g, xd["q"], xd["k"], xd["v"], o, lse, xd["do"])
+    torch.cuda.synchronize()
+    hv = {k_: host_view(t) for k_, t in x.items()}
+    O, L, ref = csr_reference(rp, cols, 1, hv["v"], hv["do"], q=hv["q"], k=hv["k"])
+    errs = {"o": maxabs(o, O), "lse": maxabs(lse, L)}
+    errs.update({k_: maxabs(gr[k_], ref[k_]) for k_ in ("dq", "dk", "dv")})
+    _say("%s errors %s" % (w.name, {k_: "%.2e" % e for k_, e in errs.items()}))
+    for key, e in errs.items():
+        assert e <= 2e-2, (key, e)
+    return g, xd, o, lse, gr
+
+
+@pytest.mark.parametrize("score", ["dot", "coord", "uniform"])
+def test_decode_explicit_lists(score):
+    """Decode on an explicit-list graph: the new token at row t attends to
+    row t's list; compared with the oracle's forward at that row."""
+    B, H, T, D = 4, 2, 1500, 64
+    rp, cols = random_causal_lists(T, 8, 24, 55)
+    g = sa_build_graph_csr(T, rp, cols)
+    pos = np.array([0, 3, 777, T - 1], dtype=np.int32)
+    gen = torch.Generator().manual_seed(808)
+    v = torch.randn((B, H, T, D), generator=gen).to(torch.bfloat16)
+    posd = torch.from_numpy(pos).to(DEV)
+    O, L = np.empty((B, H, D)), np.empty((B, H))
+    if score == "dot":
+        q = torch.randn((B, H, D), generator=gen).to(torch.bfloat16)
+        k = torch.randn((B, H, T, D), generator=gen).to(torch.bfloat16)
+        o, lse = sa_decode(g, q.to(DEV), k.to(DEV), v.to(DEV), positions=posd)
+    elif score == "coord":
+        cq = torch.randn((B, H, 3), generator=gen)
+        ck = torch.randn((B, H, T, 3), generator=gen)
+        gamma = torch.rand((H,), generator=gen) + 0.5
+        beta = torch.randn((H,), generator=gen) * 0.1
+        o, lse = sa_decode(g, v=v.to(DEV), positions=posd, cq=cq.to(DEV), ck=ck.to(DEV), gamma=gamma.to(DEV),
+                           beta=beta.to(DEV))
+    else:
+        o, lse = sa_decode(g, v=v.to(DEV), positions=posd)
+    torch.cuda.synchronize()
+    hvv = host_view(v)
+    for b in range(B):
+        t = int(pos[b])
+        for h in range(H):
+            if score == "dot":
+                qf = np.zeros((T, D), dtype=host_view(q).dtype)
+                qf[t] = host_view(q)[b, h]
+                kw = dict(q=qf, k=host_view(k)[b, h])
+            elif score == "coord":
+                cqf = np.zeros((T, 3))
+                cqf[t] = cq[b, h].double().numpy()
+                kw = dict(cq=cqf, ck=ck[b, h].double().numpy(), gamma=float(gamma[h]), beta=float(beta[h]))
+            else:
+                kw = {}
+            Of, Lf = oracle.fwd_csr(rp, cols, hvv[b, h], **kw)
+            O[b, h], L[b, h] = Of[t], Lf[t]
+    eo, el = maxabs(o, O), maxabs(lse, L)
+    _say("decode lists %s errors o %.2e lse %.2e" % (score, eo, el))
+    assert eo <= 2e-2 and el <= 2e-2
