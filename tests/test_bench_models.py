@@ -13,7 +13,7 @@ def test_edge_counts_match_set_union_on_small_graph():
     # the oracle's per-row set union, summed, equals the bench's closed form
     from types import SimpleNamespace
     for T, W, offs in [(256, 8, (16, 32, 64, 128)), (100, 3, (1, 2, 4, 8, 16, 32, 64, 128)), (50, 64, ())]:
-        w = SimpleNamespace(T=T, window=W, offsets=offs)
+        w = SimpleNamespace(T=T, window=W, offsets=offs, graph="distance")
         total = sum(len(oracle.row(T, W, offs, i)) for i in range(T))
         long_range = sum(1 for i in range(T) for d in sorted(set(offs)) if min(W, T) <= d < T and i - d >= 0)
         assert bench.edge_counts(w) == (total, long_range)
@@ -71,3 +71,22 @@ def test_models_grouped_heads():
     assert full["fwd_flops"] == gqa["fwd_flops"]
     d, dg = bench.models(WORKLOADS["dilated"]), bench.models(WORKLOADS["dilated_gqa"])
     assert d["fwd_bytes"] - d["fwd_bytes_compulsory"] == dg["fwd_bytes"] - dg["fwd_bytes_compulsory"]
+
+
+def test_models_explicit_lists():
+    """The dilated graph as lists has the dilated edge counts and bytes plus
+    the int32 lists (once forward, forward + reverse backward); random lists
+    count their own edges, every edge beyond the window being gathered."""
+    dil, lst = bench.models(WORKLOADS["dilated"]), bench.models(WORKLOADS["csr_dilated"])
+    w = WORKLOADS["csr_dilated"]
+    E = 245758
+    assert lst["edges"] == dil["edges"]
+    assert lst["fwd_bytes"] - dil["fwd_bytes"] == 4 * (w.T + 1) + 4 * E
+    assert lst["bwd_bytes"] - dil["bwd_bytes"] == 2 * (4 * (w.T + 1) + 4 * E)
+    r = WORKLOADS["csr_random"]
+    rp, cols = bench.random_lists(r)
+    total, far = bench.edge_counts(r)
+    assert total == len(cols) == rp[-1]
+    window = sum(min(i + 1, r.window) for i in range(r.T))
+    assert far == total - window
+    assert bench.models(r)["edges"] == r.B * r.H * total
