@@ -33,8 +33,8 @@ METRIC = "attention edges/s and tokens/s fwd+bwd at T=16384; % of HBM/MFMA roofl
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workloads",
                     default="band,dilated,coord,uniform,band_gqa,dilated_gqa,decode_band,decode_dilated,ultra")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -187,28 +187,29 @@ def run_workload(w, steps, warmup, algo, with_backward=True):
     fwd_call = sa_fwd_prepared(g, **fkw)
     bwd_call = sa_bwd_prepared(g, **bkw) if bwd else None
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record()
+    def step(start=None, mid=None):
+        if start is not None:
+            start.record()
         fwd_call()
-        if ev is not None:
-            ev[1].record()
+        if mid is not None:
+            mid.record()
         if bwd:
             bwd_call()
-            if ev is not None:
-                ev[2].record()
 
     for _ in range(warmup):
         step()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    # events on the kernels' stream: step s's forward runs from ev[2s] to
+    # ev[2s+1] and its backward from ev[2s+1] to ev[2s+2], the next step's start
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(steps):
-        step(evs[s])
+        step(ev[2 * s], ev[2 * s + 1])
+    ev[2 * steps].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    f_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    b_ms = [e[1].elapsed_time(e[2]) for e in evs] if bwd else [0.0]
+    f_ms = [ev[2 * s].elapsed_time(ev[2 * s + 1]) for s in range(steps)]
+    b_ms = [ev[2 * s + 1].elapsed_time(ev[2 * s + 2]) for s in range(steps)] if bwd else [0.0]
     res = {
         "wall_s": wall, "ms_per_step": 1e3 * wall / steps,
         "fwd_ms": sum(f_ms) / len(f_ms), "bwd_ms": sum(b_ms) / len(b_ms),

@@ -65,7 +65,9 @@ def source_digest() -> str:
     for f in sources() + headers():
         h.update(os.path.relpath(f, ROOT).encode())
         h.update(open(f, "rb").read())
-    h.update(" ".join(COMMON + DEVICE).encode())
+    # flags with the checkout location taken out, so the digest is the same
+    # wherever the repository sits
+    h.update(" ".join(COMMON + DEVICE).replace(ROOT, "<root>").encode())
     return h.hexdigest()
 
 

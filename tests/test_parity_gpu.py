@@ -670,3 +670,33 @@ def test_decode_explicit_lists(score):
     eo, el = maxabs(o, O), maxabs(lse, L)
     _say("decode lists %s errors o %.2e lse %.2e" % (score, eo, el))
     assert eo <= 2e-2 and el <= 2e-2
+
+
+def test_explicit_lists_edge_cases():
+    """T = 1 (one row listing itself); strided [B, T, H, D] storage; bf16
+    gradients; bitwise run-to-run determinism of every output."""
+    # T = 1
+    rp, cols = np.array([0, 1]), np.array([0])
+    run_csr(rp, cols, 2, 2, 2, 32, torch.float32, "dot", seed=1)
+    # strided storage and bf16 gradients
+    B, H, T, D = 2, 3, 400, 64
+    rp, cols = random_causal_lists(T, 6, 20, 77)
+    g = sa_build_graph_csr(T, rp, cols)
+    gen = torch.Generator().manual_seed(2024)
+    base = {k_: torch.randn((B, T, H, D), generator=gen).to(torch.bfloat16) for k_ in ("q", "k", "v", "do")}
+    xd = {k_: t.to(DEV).transpose(1, 2) for k_, t in base.items()}  # [B, H, T, D] views, t stride H*D
+    assert not xd["q"].is_contiguous()
+    o, lse = sa_fwd(g, xd["q"], xd["k"], xd["v"])
+    gr = sa_bwd(g, xd["q"], xd["k"], xd["v"], o, lse, xd["do"], grad_dtype=torch.bfloat16)
+    o2, lse2 = sa_fwd(g, xd["q"], xd["k"], xd["v"])
+    gr2 = sa_bwd(g, xd["q"], xd["k"], xd["v"], o2, lse2, xd["do"], grad_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(lse, lse2)
+    assert all(torch.equal(gr[k_], gr2[k_]) for k_ in gr)
+    hv = {k_: host_view(t.transpose(1, 2).contiguous()) for k_, t in base.items()}
+    O, L, ref = csr_reference(rp, cols, 1, hv["v"], hv["do"], q=hv["q"], k=hv["k"])
+    errs = {"o": maxabs(o, O), "lse": maxabs(lse, L)}
+    errs.update({k_: maxabs(gr[k_], ref[k_]) for k_ in ("dq", "dk", "dv")})
+    _say("csr strided / bf16 gradients errors %s" % {k_: "%.2e" % e for k_, e in errs.items()})
+    assert errs["o"] <= 2e-2 and errs["lse"] <= 2e-2
+    assert all(errs[k_] <= 5e-2 for k_ in ("dq", "dk", "dv")), errs
