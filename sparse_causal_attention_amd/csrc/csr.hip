@@ -159,11 +159,11 @@ __global__ __launch_bounds__(kThreads) void csr_fwd_kernel(Params p) {
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] *= inv_l;
   char* orow = static_cast<char*>(p.o) + (b * p.so_b + h * p.so_h + i * p.so_t) * EB + sub16;
-  st16(orow, F::pack(acc));
+  st16_stream(orow, F::pack(acc));
   if (sub == 0) {
     float lse = (m + fast_log2(l)) * kLn2;
     if constexpr (SM == SM_COORD) lse += p.beta[h];
-    p.lse[(int64_t)bh * p.T + i] = lse;
+    st_stream(p.lse + (int64_t)bh * p.T + i, lse);
   }
 }
 
@@ -291,7 +291,7 @@ __global__ __launch_bounds__(kThreads) void csr_bwd_q_kernel(Params p) {
     if (row_ok && sub == 0) {
       float* o = p.dcq + ((int64_t)bh * p.T + i) * 3;
 #pragma unroll
-      for (int c = 0; c < 3; ++c) o[c] = -2.f * gam * (cdx[c] - delta * cx[c]);
+      for (int c = 0; c < 3; ++c) st_stream(o + c, -2.f * gam * (cdx[c] - delta * cx[c]));
     }
     // dgamma_i = -sum_j dS_ij r2_ij,  dbeta_i = sum_j dS_ij = Delta_i (1 - sum_j P_ij);
     // one value per row, summed per block in a fixed order through LDS
@@ -439,9 +439,9 @@ __global__ __launch_bounds__(kThreads) void csr_bwd_kv_kernel(Params p) {
   } else if constexpr (COORD) {
     if (sub == 0) {
       float* o = p.dck + ((int64_t)bh * p.T + j) * 3;
-      o[0] = 2.f * gam * dc[0];
-      o[1] = 2.f * gam * dc[1];
-      o[2] = 2.f * gam * dc[2];
+      st_stream(o, 2.f * gam * dc[0]);
+      st_stream(o + 1, 2.f * gam * dc[1]);
+      st_stream(o + 2, 2.f * gam * dc[2]);
     }
   }
 }

@@ -101,21 +101,42 @@ __device__ __forceinline__ uint4 ld16(const char* p) {
 }
 __device__ __forceinline__ void st16(char* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
 
-// Store N fp32 values (N = 4 or 8) as fp32 or bf16 at p (aligned to the size).
+// Streaming stores (non-temporal hint) for output rows written once as whole
+// contiguous rows (a wavefront's store covers full cache lines): they pass
+// through the L2 without displacing the key/value rows that neighbouring
+// queries gather again.  Measured: up to a quarter faster on the gather
+// kernels.  Not for scattered partial-line stores (the band kernels' MFMA
+// accumulator layout writes 8 or 16 bytes per lane across 32 rows; there the
+// hint made stores several times dearer), and the same hint on the owner's
+// own-row loads did not help.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ void st16_stream(char* p, const uint4& v) {
+  const u32x4_t t = {v.x, v.y, v.z, v.w};
+  __builtin_nontemporal_store(t, reinterpret_cast<u32x4_t*>(p));
+}
+__device__ __forceinline__ void st_stream(float* p, float v) { __builtin_nontemporal_store(v, p); }
+__device__ __forceinline__ void st8_stream(char* p, const uint2& v) {
+  const u32x2_t t = {v.x, v.y};
+  __builtin_nontemporal_store(t, reinterpret_cast<u32x2_t*>(p));
+}
+
+// Store N fp32 values (N = 4 or 8) as fp32 or bf16 at p (aligned to the size),
+// streaming (each output row is written once).
 template <int N>
 __device__ __forceinline__ void store_vals(char* p, const float* f, bool as_bf16) {
   if (as_bf16) {
     if constexpr (N == 8) {
-      st16(p, make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
-                         pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])));
+      st16_stream(p, make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]),
+                                pack_bf16x2(f[4], f[5]), pack_bf16x2(f[6], f[7])));
     } else {
-      *reinterpret_cast<uint2*>(p) = make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]));
+      st8_stream(p, make_uint2(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3])));
     }
   } else {
 #pragma unroll
     for (int c = 0; c < N; c += 4)
-      st16(p + 4 * c, make_uint4(__float_as_uint(f[c]), __float_as_uint(f[c + 1]),
-                                 __float_as_uint(f[c + 2]), __float_as_uint(f[c + 3])));
+      st16_stream(p + 4 * c, make_uint4(__float_as_uint(f[c]), __float_as_uint(f[c + 1]),
+                                        __float_as_uint(f[c + 2]), __float_as_uint(f[c + 3])));
   }
 }
 

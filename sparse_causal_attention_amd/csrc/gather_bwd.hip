@@ -198,7 +198,7 @@ __global__ __launch_bounds__(kThreads) void gather_bwd_q_kernel(Params p) {
     if (row_ok && sub == 0) {
       float* o = p.dcq + ((int64_t)bh * p.T + i) * 3;
 #pragma unroll
-      for (int c = 0; c < 3; ++c) o[c] = -2.f * gam * (cdx[c] - delta * cx[c]);
+      for (int c = 0; c < 3; ++c) st_stream(o + c, -2.f * gam * (cdx[c] - delta * cx[c]));
     }
     // dgamma_i = -sum_j dS_ij r2_ij,  dbeta_i = sum_j dS_ij = Delta_i (1 - sum_j P_ij)
     const float gpart = -(r2dx - delta * r2x);
@@ -393,9 +393,9 @@ __global__ __launch_bounds__(kThreads) void gather_bwd_kv_kernel(Params p) {
   } else if constexpr (COORD) {
     if (sub == 0) {
       float* o = p.dck + ((int64_t)bh * p.T + j) * 3;
-      o[0] = 2.f * gam * dc[0];
-      o[1] = 2.f * gam * dc[1];
-      o[2] = 2.f * gam * dc[2];
+      st_stream(o, 2.f * gam * dc[0]);
+      st_stream(o + 1, 2.f * gam * dc[1]);
+      st_stream(o + 2, 2.f * gam * dc[2]);
     }
   }
 }

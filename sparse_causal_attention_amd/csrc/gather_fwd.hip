@@ -172,11 +172,11 @@ __global__ __launch_bounds__(kThreads) void gather_fwd_kernel(Params p) {
 #pragma unroll
   for (int e = 0; e < EPL; ++e) acc[e] *= inv_l;
   char* orow = static_cast<char*>(p.o) + (b * p.so_b + h * p.so_h + i * p.so_t) * EB + sub * 16;
-  st16(orow, F::pack(acc));
+  st16_stream(orow, F::pack(acc));
   if (sub == 0) {
     float lse = (m + fast_log2(l)) * kLn2;
     if constexpr (SM == SM_COORD) lse += p.beta[h];
-    p.lse[(int64_t)bh * p.T + i] = lse;
+    st_stream(p.lse + (int64_t)bh * p.T + i, lse);
   }
 }
 
