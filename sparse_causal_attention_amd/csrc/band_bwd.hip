@@ -95,6 +95,40 @@ __device__ __forceinline__ void store_acc_row(void* base, int64_t off_elems, con
     }
 }
 
+// Stores this wavefront's 32 accumulator rows (lane l owns row row0 + l % 32,
+// columns 32 dblk + 8 g + 4 half + e in acc[dblk][4 g + e]) as whole fp32
+// rows: each 32-column half is written to the wavefront's own LDS region (32
+// rows at a 144-byte pitch) and read back so that eight lanes hold one row's
+// 128 contiguous bytes, so the global stores cover whole cache lines.  Final
+// outputs stream past the L2 (STREAM); partials that another kernel sums next
+// stay cacheable.  Rows at or past T are not stored.
+template <bool STREAM>
+__device__ __forceinline__ void store_rows_f32(float* lds, char* gbase, int64_t row_bytes, int row0, int T,
+                                               const f32x16* acc, float mul) {
+  constexpr int kPitch = 36;  // floats per LDS row
+  const int lane = threadIdx.x & 63, l32 = lane & 31, half = lane >> 5;
+#pragma unroll
+  for (int dblk = 0; dblk < 2; ++dblk) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      *reinterpret_cast<float4*>(lds + l32 * kPitch + 8 * g + 4 * half) =
+          make_float4(acc[dblk][4 * g] * mul, acc[dblk][4 * g + 1] * mul, acc[dblk][4 * g + 2] * mul,
+                      acc[dblk][4 * g + 3] * mul);
+    __builtin_amdgcn_wave_barrier();  // the wavefront's LDS accesses stay in this order
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int rr = 8 * k + (lane >> 3), c = lane & 7;
+      const float4 v = *reinterpret_cast<const float4*>(lds + rr * kPitch + 4 * c);
+      if (row0 + rr < T) {
+        char* dst = gbase + (int64_t)(row0 + rr) * row_bytes + (dblk * 32 + 4 * c) * 4;
+        const uint4 w = make_uint4(__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w));
+        if constexpr (STREAM) st16_stream(dst, w); else st16(dst, w);
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
 // ------------------------------------------------------------------ prepass
 // -Delta_i = -<dout_i, o_i> and lse_i * log2(e) for every row; 8 lanes per
 // row.  The negated Delta is the initial accumulator of the dP products, so
@@ -200,6 +234,11 @@ struct Bufs {
   float *la0, *lb0, *la1, *lb1;
   char *sx, *sy;
   float *snd, *sl2;
+  // LDS region of wavefront w for store_rows_f32: tile buffer 1, idle from the
+  // end of a unit's last tile until the next unit issues its second tile
+  __device__ float* store_region(int w) const {
+    return reinterpret_cast<float*>((w < 2 ? a1 : b1) + (w & 1) * 32 * 36 * 4);
+  }
 };
 
 // Issue the loads of unit u's per-row operands into the row stage: rows
@@ -355,8 +394,13 @@ __device__ __forceinline__ void dq_unit(const Params& p, const Unit& u, const Ro
     }
   }
 
-  if (m < p.T)
-    store_acc_row<GRAD_BF16>(p.dq, u.b * p.sdq_b + u.h * p.sdq_h + (int64_t)m * p.sdq_t, acc, p.scale, half);
+  if constexpr (GRAD_BF16) {
+    if (m < p.T)
+      store_acc_row<GRAD_BF16>(p.dq, u.b * p.sdq_b + u.h * p.sdq_h + (int64_t)m * p.sdq_t, acc, p.scale, half);
+  } else {
+    store_rows_f32<true>(bf.store_region(wave), static_cast<char*>(p.dq) + (u.b * p.sdq_b + u.h * p.sdq_h) * 4,
+                   p.sdq_t * 4, qw, p.T, acc, p.scale);
+  }
 }
 
 // ------------------------------------------------------------------ dk/dv unit
@@ -489,14 +533,26 @@ __device__ __forceinline__ void dkv_unit(const Params& p, const Unit& u, const R
     }
   }
 
-  if (n < p.T) {
-    if (p.G == 1) {
-      store_acc_row<GRAD_BF16>(p.dv, u.b * p.sdv_b + u.h * p.sdv_h + (int64_t)n * p.sdv_t, dv, 1.f, half);
-      store_acc_row<GRAD_BF16>(p.dk, u.b * p.sdk_b + u.h * p.sdk_h + (int64_t)n * p.sdk_t, dk, p.scale, half);
-    } else {  // this query head's share; summed over the group by band_bwd_group_sum_kernel
-      store_acc_row<false>(p.pdv, ((int64_t)u.bh * p.T + n) * 64, dv, 1.f, half);
-      store_acc_row<false>(p.pdk, ((int64_t)u.bh * p.T + n) * 64, dk, p.scale, half);
+  if constexpr (GRAD_BF16) {
+    if (n < p.T) {
+      if (p.G == 1) {
+        store_acc_row<true>(p.dv, u.b * p.sdv_b + u.h * p.sdv_h + (int64_t)n * p.sdv_t, dv, 1.f, half);
+        store_acc_row<true>(p.dk, u.b * p.sdk_b + u.h * p.sdk_h + (int64_t)n * p.sdk_t, dk, p.scale, half);
+      } else {  // this query head's share; summed over the group by band_bwd_group_sum_kernel
+        store_acc_row<false>(p.pdv, ((int64_t)u.bh * p.T + n) * 64, dv, 1.f, half);
+        store_acc_row<false>(p.pdk, ((int64_t)u.bh * p.T + n) * 64, dk, p.scale, half);
+      }
     }
+  } else if (p.G > 1) {  // this query head's share; summed over the group by band_bwd_group_sum_kernel
+    float* lds = bf.store_region(wave);
+    store_rows_f32<false>(lds, reinterpret_cast<char*>(p.pdv + (int64_t)u.bh * p.T * 64), 64 * 4, kw, p.T, dv, 1.f);
+    store_rows_f32<false>(lds, reinterpret_cast<char*>(p.pdk + (int64_t)u.bh * p.T * 64), 64 * 4, kw, p.T, dk, p.scale);
+  } else {
+    float* lds = bf.store_region(wave);
+    store_rows_f32<true>(lds, static_cast<char*>(p.dv) + (u.b * p.sdv_b + u.h * p.sdv_h) * 4, p.sdv_t * 4, kw, p.T, dv,
+                   1.f);
+    store_rows_f32<true>(lds, static_cast<char*>(p.dk) + (u.b * p.sdk_b + u.h * p.sdk_h) * 4, p.sdk_t * 4, kw, p.T, dk,
+                   p.scale);
   }
 }
 
@@ -550,6 +606,7 @@ __global__ __launch_bounds__(kThreads, 2) void band_bwd_kernel(Params p) {
     else
       dkv_unit<GRAD_BF16, HAS_DIL>(p, cur, ops, nxt, bf);
     if (nxt.role < 0) break;
+    __syncthreads();  // the row stores' LDS regions are tile buffer 1, which the next unit refills
     cur = nxt;
   }
 }
