@@ -271,20 +271,31 @@ __global__ __launch_bounds__(kThreads, 4) void band_fwd_kernel(Params p) {
     }
   }
 
-  // ---- finish: O = acc / l, lse = m + log l (natural log)
+  // ---- finish: O = acc / l, lse = m + log l (natural log).  The rows go out
+  // whole: each wavefront writes its 32 bf16 rows into one of the (now idle)
+  // tile buffers at a 144-byte pitch, reads them back as 128 contiguous bytes
+  // per eight lanes, and stores whole cache lines with streaming stores
+  // (instead of 8-byte pieces scattered over 32 rows).
   const float ltot = sum_halves(lrun);
-  if (m >= p.T) return;
   const float inv = 1.f / ltot;
-  char* orow = static_cast<char*>(p.o) + (b * p.so_b + h * p.so_h + (int64_t)m * p.so_t) * 2;
+  char* stage = wave == 0 ? K0 : wave == 1 ? V0 : wave == 2 ? K1 : V1;  // every wavefront is past the last tile
 #pragma unroll
   for (int dblk = 0; dblk < 2; ++dblk)
 #pragma unroll
     for (int g4 = 0; g4 < 4; ++g4) {
       const uint2 w2 = make_uint2(pack_bf16x2(oacc[dblk][4 * g4] * inv, oacc[dblk][4 * g4 + 1] * inv),
                                   pack_bf16x2(oacc[dblk][4 * g4 + 2] * inv, oacc[dblk][4 * g4 + 3] * inv));
-      *reinterpret_cast<uint2*>(orow + (dblk * 32 + 8 * g4 + 4 * half) * 2) = w2;
+      *reinterpret_cast<uint2*>(stage + l32 * kTilePitch + (dblk * 32 + 8 * g4 + 4 * half) * 2) = w2;
     }
-  if (half == 0) p.lse[(int64_t)bh * p.T + m] = (mrun * sl2 + fast_log2(ltot)) * kLn2;
+  __builtin_amdgcn_wave_barrier();  // the wavefront's LDS accesses stay in this order
+  char* obase = static_cast<char*>(p.o) + (b * p.so_b + h * p.so_h) * 2;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int rr = 8 * k + (lane >> 3), c = lane & 7;
+    const uint4 v = *reinterpret_cast<const uint4*>(stage + rr * kTilePitch + c * 16);
+    if (qw + rr < p.T) st16_stream(obase + (int64_t)(qw + rr) * p.so_t * 2 + c * 16, v);
+  }
+  if (half == 0 && m < p.T) st_stream(p.lse + (int64_t)bh * p.T + m, (mrun * sl2 + fast_log2(ltot)) * kLn2);
 }
 
 }  // namespace
