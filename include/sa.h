@@ -43,7 +43,10 @@
  *    device region it refers to beyond a call is the buffer an explicit-list
  *    graph was uploaded into (sa_graph_upload), which stays the caller's.
  *  - Calls are asynchronous on the given stream (a hipStream_t; NULL is the
- *    null stream).  SA_OK means the work was validated and enqueued.
+ *    null stream).  SA_OK means the work was validated and enqueued.  sa_fwd,
+ *    sa_bwd and sa_decode only launch kernels (no allocation, memset or
+ *    synchronisation), so they can be captured in a HIP graph; upload an
+ *    explicit-list graph (sa_graph_upload) before capturing.
  *  - All validation happens before any HIP call, and nothing is written when
  *    validation fails.  No entry point aborts, throws or prints.
  *  - The library does not touch the GPU when it is loaded; sa_build_graph*,

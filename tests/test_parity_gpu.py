@@ -700,3 +700,49 @@ def test_explicit_lists_edge_cases():
     _say("csr strided / bf16 gradients errors %s" % {k_: "%.2e" % e for k_, e in errs.items()})
     assert errs["o"] <= 2e-2 and errs["lse"] <= 2e-2
     assert all(errs[k_] <= 5e-2 for k_ in ("dq", "dk", "dv")), errs
+
+
+@pytest.mark.parametrize("kind", ["band", "dilated", "lists"])
+def test_graph_capture_replays_match_eager(kind):
+    """sa_fwd + sa_bwd captured in a HIP graph (they allocate, clear and
+    synchronise nothing): several replays, with eager work and
+    synchronisation between them, each bitwise equal to the eager result."""
+    B, H, T, D = 1, 2, 1024, 64
+    if kind == "band":
+        g = sa_build_graph(T, 128, ())
+    elif kind == "dilated":
+        g = sa_build_graph(T, 4, tuple(2 ** k for k in range(10)))
+    else:
+        rp, cols = random_causal_lists(T, 4, 12, 99)
+        g = sa_build_graph_csr(T, rp, cols)
+    gen = torch.Generator().manual_seed(5150)
+    x = {k_: torch.randn((B, H, T, D), generator=gen).to(torch.bfloat16).to(DEV) for k_ in ("q", "k", "v", "do")}
+    s = torch.cuda.Stream()
+    o = torch.empty_like(x["q"])
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=DEV)
+    grads = {k_: torch.empty((B, H, T, D), dtype=torch.float32, device=DEV) for k_ in ("dq", "dk", "dv")}
+    with torch.cuda.stream(s):
+        sa_fwd(g, x["q"], x["k"], x["v"], o=o, lse=lse, stream=s)  # eager (uploads explicit lists)
+        sa_bwd(g, x["q"], x["k"], x["v"], o, lse, x["do"], stream=s, **grads)
+    torch.cuda.synchronize()
+    ref = {"o": o.clone(), "lse": lse.clone(), **{k_: t.clone() for k_, t in grads.items()}}
+    ws = torch.empty(max(sa_bwd_workspace_size_of(g, x["v"]), 256), dtype=torch.uint8, device=DEV)
+    cg = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(cg, stream=s):
+        sa_fwd(g, x["q"], x["k"], x["v"], o=o, lse=lse, stream=s)
+        sa_bwd(g, x["q"], x["k"], x["v"], o, lse, x["do"], workspace=ws, stream=s, **grads)
+    outs = {"o": o, "lse": lse, **grads}
+    for rep in range(4):
+        for t in outs.values():
+            t.fill_(float("nan"))  # eager work between replays
+        torch.cuda.synchronize()
+        cg.replay()
+        torch.cuda.synchronize()
+        for k_, t in outs.items():
+            assert torch.equal(t, ref[k_]), (kind, rep, k_)
+    _say("graph capture %s: %d replays equal to eager" % (kind, 4))
+
+
+def sa_bwd_workspace_size_of(g, v):
+    from sparse_causal_attention_amd import sa_bwd_workspace_size
+    return sa_bwd_workspace_size(g, v)
