@@ -75,6 +75,10 @@ class Graph:
             return self
         torch = _torch()
         device = torch.device(device)
+        if device.type != "cuda":
+            raise ValueError("explicit lists are uploaded to a GPU device, got %s" % device)
+        if device.index is None:
+            device = torch.device("cuda", torch.cuda.current_device())
         if self._dev is not None and self._dev.device == device:
             return self
         n = self.device_bytes()
