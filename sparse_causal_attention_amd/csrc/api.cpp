@@ -174,8 +174,7 @@ size_t workspace_bytes_for(const sa_attn_desc* d) {
   const int rpb = sa::gather_rows_per_block(d->dtype == SA_BF16 ? sa::DT_BF16 : sa::DT_F32,
                                             (int)d->D);
   const size_t nblk = (size_t)((d->T + rpb - 1) / rpb);
-  const size_t partials = kv_heads(d) != d->H ? 2 * align256(rows * (size_t)d->D * sizeof(float)) : 0;
-  return 2 * align256(rows * sizeof(float)) + align256((size_t)d->B * d->H * nblk * 2 * sizeof(float)) + partials;
+  return 2 * align256(rows * sizeof(float)) + align256((size_t)d->B * d->H * nblk * 2 * sizeof(float));
 }
 
 }  // namespace
@@ -247,14 +246,6 @@ extern "C" sa_status sa_bwd(const sa_graph* g, const sa_attn_desc* d, const void
   p.ndelta = p.delta;
   p.lse2 = reinterpret_cast<float*>(ws + row_bytes);
   p.partials = reinterpret_cast<float*>(ws + 2 * row_bytes);
-  if (p.G > 1) {  // per-query-head dk, dv partials of the band kernels
-    const int rpb = sa::gather_rows_per_block(d->dtype == SA_BF16 ? sa::DT_BF16 : sa::DT_F32, (int)d->D);
-    const size_t nblk = (size_t)((d->T + rpb - 1) / rpb);
-    char* pp = ws + 2 * row_bytes + align256((size_t)d->B * d->H * nblk * 2 * sizeof(float));
-    const size_t pbytes = align256((size_t)d->B * d->H * d->T * d->D * sizeof(float));
-    p.pdk = reinterpret_cast<float*>(pp);
-    p.pdv = reinterpret_cast<float*>(pp + pbytes);
-  }
   const int dt = d->dtype == SA_BF16 ? sa::DT_BF16 : sa::DT_F32;
   hipError_t e = plan.path == Path::Band  ? sa::launch_band_bwd(p, as_stream(stream))
                  : plan.path == Path::Csr ? sa::launch_csr_bwd(p, dt, d->score, as_stream(stream))

@@ -99,10 +99,8 @@ __device__ __forceinline__ void store_acc_row(void* base, int64_t off_elems, con
 // columns 32 dblk + 8 g + 4 half + e in acc[dblk][4 g + e]) as whole fp32
 // rows: each 32-column half is written to the wavefront's own LDS region (32
 // rows at a 144-byte pitch) and read back so that eight lanes hold one row's
-// 128 contiguous bytes, so the global stores cover whole cache lines.  Final
-// outputs stream past the L2 (STREAM); partials that another kernel sums next
-// stay cacheable.  Rows at or past T are not stored.
-template <bool STREAM>
+// 128 contiguous bytes, so the global stores cover whole cache lines and
+// stream past the L2.  Rows at or past T are not stored.
 __device__ __forceinline__ void store_rows_f32(float* lds, char* gbase, int64_t row_bytes, int row0, int T,
                                                const f32x16* acc, float mul) {
   constexpr int kPitch = 36;  // floats per LDS row
@@ -122,7 +120,7 @@ __device__ __forceinline__ void store_rows_f32(float* lds, char* gbase, int64_t 
       if (row0 + rr < T) {
         char* dst = gbase + (int64_t)(row0 + rr) * row_bytes + (dblk * 32 + 4 * c) * 4;
         const uint4 w = make_uint4(__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w));
-        if constexpr (STREAM) st16_stream(dst, w); else st16(dst, w);
+        st16_stream(dst, w);
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -157,9 +155,10 @@ struct Unit {
   int role;  // 0: dq, 1: dk/dv, -1: no unit
   int b, h, bh;
   int hk;    // key/value head of query head h
+  int ng;    // dk/dv: query heads h .. h + ng - 1 walked in turn (the G heads of hk)
   int r0;    // first owned row: query (dq) or key (dk/dv)
   int s0;    // first streamed row: key (dq) or query (dk/dv); a multiple of kTile
-  int nt;    // streamed tiles
+  int nt;    // streamed tiles (per query head)
 };
 
 __device__ __forceinline__ Unit make_unit(const Params& p, int pair, int role, int nblk) {
@@ -170,6 +169,7 @@ __device__ __forceinline__ Unit make_unit(const Params& p, int pair, int role, i
   u.b = u.bh / p.H;
   u.h = u.bh - u.b * p.H;
   u.hk = u.h / p.G;
+  u.ng = 1;
   u.r0 = rb * kRows;
   const int last = u.r0 + kRows - 1 < p.T - 1 ? u.r0 + kRows - 1 : p.T - 1;
   if (role == 0) {  // keys max(0, r0 - W + 1) .. last
@@ -398,13 +398,13 @@ __device__ __forceinline__ void dq_unit(const Params& p, const Unit& u, const Ro
     if (m < p.T)
       store_acc_row<GRAD_BF16>(p.dq, u.b * p.sdq_b + u.h * p.sdq_h + (int64_t)m * p.sdq_t, acc, p.scale, half);
   } else {
-    store_rows_f32<true>(bf.store_region(wave), static_cast<char*>(p.dq) + (u.b * p.sdq_b + u.h * p.sdq_h) * 4,
+    store_rows_f32(bf.store_region(wave), static_cast<char*>(p.dq) + (u.b * p.sdq_b + u.h * p.sdq_h) * 4,
                    p.sdq_t * 4, qw, p.T, acc, p.scale);
   }
 }
 
 // ------------------------------------------------------------------ dk/dv unit
-template <bool GRAD_BF16, bool HAS_DIL>
+template <bool GRAD_BF16, bool HAS_DIL, bool GROUPED>
 __device__ __forceinline__ void dkv_unit(const Params& p, const Unit& u, const RowOps& ops, const Unit& nxt,
                                          const Bufs& bf) {
   const int tid = threadIdx.x, lane = tid & 63;
@@ -425,10 +425,14 @@ __device__ __forceinline__ void dkv_unit(const Params& p, const Unit& u, const R
   for (int r = 0; r < 16; ++r) dk[0][r] = dk[1][r] = dv[0][r] = dv[1][r] = 0.f;
   const int wlo = kw, whi = kw + 31 + W - 1;  // this wavefront's query range
 
-  auto tile = [&](int it, const char* qs, const char* ds, const float* ls, const float* es, char* qn, char* dn,
-                  float* ln, float* en) {
+  // uh: the query head whose tiles are streamed (u itself unless the unit
+  // covers a group); more: a next head of the group follows, un
+  auto tile = [&](const Unit& uh, bool more, const Unit& un, int it, const char* qs, const char* ds, const float* ls,
+                  const float* es, char* qn, char* dn, float* ln, float* en) {
     if (it + 1 < u.nt) {
-      issue_tile(p, u, it + 1, qn, dn, ln, en);  // last read in tile it - 1
+      issue_tile(p, uh, it + 1, qn, dn, ln, en);  // last read in tile it - 1
+    } else if (more && it + 1 == ntp) {
+      issue_tile(p, un, 0, qn, dn, ln, en);  // buffer 0: the next query head's first tile
     } else if (it + 1 == ntp && nxt.role >= 0) {
       issue_tile(p, nxt, 0, qn, dn, ln, en);  // buffer 0: the next unit's first tile
       issue_stage(p, nxt, bf);
@@ -490,18 +494,20 @@ __device__ __forceinline__ void dkv_unit(const Params& p, const Unit& u, const R
     wait_vmem();
     __syncthreads();
   };
+  // one query head: its tiles, then its long-range edges
+  auto head = [&](const Unit& uh, bool more, const Unit& un) {
   for (int it = 0; it < ntp; it += 2) {
-    tile(it, bf.a0, bf.b0, bf.la0, bf.lb0, bf.a1, bf.b1, bf.la1, bf.lb1);
-    tile(it + 1, bf.a1, bf.b1, bf.la1, bf.lb1, bf.a0, bf.b0, bf.la0, bf.lb0);
+    tile(uh, more, un, it, bf.a0, bf.b0, bf.la0, bf.lb0, bf.a1, bf.b1, bf.la1, bf.lb1);
+    tile(uh, more, un, it + 1, bf.a1, bf.b1, bf.la1, bf.lb1, bf.a0, bf.b0, bf.la0, bf.lb0);
   }
 
   if constexpr (HAS_DIL) {
     // long-range edges: queries i = n + d
-    const char* qb = tensor_base(p.q, p.sq_b, p.sq_h, u);
-    const char* dob = tensor_base(p.dout, p.sdo_b, p.sdo_h, u);
+    const char* qb = tensor_base(p.q, p.sq_b, p.sq_h, uh);
+    const char* dob = tensor_base(p.dout, p.sdo_b, p.sdo_h, uh);
     const int64_t sqt = p.sq_t * 2, sdot = p.sdo_t * 2;
-    const float* lseb = p.lse2 + (int64_t)u.bh * p.T;
-    const float* ndelb = p.ndelta + (int64_t)u.bh * p.T;
+    const float* lseb = p.lse2 + (int64_t)uh.bh * p.T;
+    const float* ndelb = p.ndelta + (int64_t)uh.bh * p.T;
     for (int t = 0; t < p.n_dil; ++t) {
       const bool ok = p.dil[t] <= p.T - 1 - nc;
       const int ii = ok ? nc + p.dil[t] : nc;
@@ -532,32 +538,37 @@ __device__ __forceinline__ void dkv_unit(const Params& p, const Unit& u, const R
         }
     }
   }
+  };
+  if constexpr (GROUPED) {  // the G query heads of key/value head hk, in order
+    for (int gi = 0; gi < u.ng; ++gi) {
+      Unit uh = u, un = u;
+      uh.h += gi;
+      uh.bh += gi;
+      un.h = uh.h + 1;
+      un.bh = uh.bh + 1;
+      head(uh, gi + 1 < u.ng, un);
+    }
+  } else {
+    head(u, false, u);
+  }
 
+  // key/value head hk: the sums over every query head that reads it
   if constexpr (GRAD_BF16) {
     if (n < p.T) {
-      if (p.G == 1) {
-        store_acc_row<true>(p.dv, u.b * p.sdv_b + u.h * p.sdv_h + (int64_t)n * p.sdv_t, dv, 1.f, half);
-        store_acc_row<true>(p.dk, u.b * p.sdk_b + u.h * p.sdk_h + (int64_t)n * p.sdk_t, dk, p.scale, half);
-      } else {  // this query head's share; summed over the group by band_bwd_group_sum_kernel
-        store_acc_row<false>(p.pdv, ((int64_t)u.bh * p.T + n) * 64, dv, 1.f, half);
-        store_acc_row<false>(p.pdk, ((int64_t)u.bh * p.T + n) * 64, dk, p.scale, half);
-      }
+      store_acc_row<true>(p.dv, u.b * p.sdv_b + u.hk * p.sdv_h + (int64_t)n * p.sdv_t, dv, 1.f, half);
+      store_acc_row<true>(p.dk, u.b * p.sdk_b + u.hk * p.sdk_h + (int64_t)n * p.sdk_t, dk, p.scale, half);
     }
-  } else if (p.G > 1) {  // this query head's share; summed over the group by band_bwd_group_sum_kernel
-    float* lds = bf.store_region(wave);
-    store_rows_f32<false>(lds, reinterpret_cast<char*>(p.pdv + (int64_t)u.bh * p.T * 64), 64 * 4, kw, p.T, dv, 1.f);
-    store_rows_f32<false>(lds, reinterpret_cast<char*>(p.pdk + (int64_t)u.bh * p.T * 64), 64 * 4, kw, p.T, dk, p.scale);
   } else {
     float* lds = bf.store_region(wave);
-    store_rows_f32<true>(lds, static_cast<char*>(p.dv) + (u.b * p.sdv_b + u.h * p.sdv_h) * 4, p.sdv_t * 4, kw, p.T, dv,
-                   1.f);
-    store_rows_f32<true>(lds, static_cast<char*>(p.dk) + (u.b * p.sdk_b + u.h * p.sdk_h) * 4, p.sdk_t * 4, kw, p.T, dk,
-                   p.scale);
+    store_rows_f32(lds, static_cast<char*>(p.dv) + (u.b * p.sdv_b + u.hk * p.sdv_h) * 4, p.sdv_t * 4, kw, p.T,
+                         dv, 1.f);
+    store_rows_f32(lds, static_cast<char*>(p.dk) + (u.b * p.sdk_b + u.hk * p.sdk_h) * 4, p.sdk_t * 4, kw, p.T,
+                         dk, p.scale);
   }
 }
 
 // ------------------------------------------------------------------ kernel
-template <bool GRAD_BF16, bool HAS_DIL>
+template <bool GRAD_BF16, bool HAS_DIL, bool GROUPED>
 __global__ __launch_bounds__(kThreads, 2) void band_bwd_kernel(Params p) {
   // Double-buffered tiles shared by the two unit kinds.  Each buffer is its
   // own LDS object, so the direct loads into one are known not to alias the
@@ -571,22 +582,43 @@ __global__ __launch_bounds__(kThreads, 2) void band_bwd_kernel(Params p) {
   const Bufs bf{t0a, t0b, t1a, t1b, r0a, r0b, r1a, r1b, stx, sty, stnd, stl2};
 
   const int nblk = (p.T + kRows - 1) / kRows;
-  const int npairs = p.B * p.H * nblk;
-  const int per_xcd = (npairs + kNumXcd - 1) / kNumXcd;  // pairs of row blocks per XCD
   const int xcd = blockIdx.x % kNumXcd, g = blockIdx.x / kNumXcd;
   const int wgs_per_xcd = gridDim.x / kNumXcd;
-  const int pbeg = xcd * per_xcd;
-  const int pend = pbeg + per_xcd < npairs ? pbeg + per_xcd : npairs;
-  // unit k of this workgroup: pair pbeg + g + (k / 2) G, dq unit then dk/dv unit
+  Unit none;
+  none.role = -1;
+  none.b = none.h = none.bh = none.hk = none.ng = none.r0 = none.s0 = none.nt = 0;
+  // Without grouped heads: workgroup g of an XCD takes the (dq, dk/dv) unit
+  // pairs pbeg + g, pbeg + g + G, ... of that XCD's contiguous share of
+  // (head, row block) pairs.  With G query heads per key/value head, a dk/dv
+  // unit walks all G query heads (G times a dq unit's work): the first half
+  // of an XCD's workgroups take those, the second half the dq units, so both
+  // halves carry the same work.
+  constexpr bool grouped = GROUPED;  // p.G > 1
+  const int nitems = grouped ? p.B * p.Hkv * nblk : p.B * p.H * nblk;  // (b, hk, rb) or (b, h, rb)
+  const int per_xcd = (nitems + kNumXcd - 1) / kNumXcd;
+  const int ibeg = xcd * per_xcd;
+  const int iend = ibeg + per_xcd < nitems ? ibeg + per_xcd : nitems;
+  const int wh = wgs_per_xcd / 2, wd = wgs_per_xcd - wh;  // grouped: >= 1 each
+  const bool kv_wg = grouped && g < wh;
   auto unit_at = [&](int k) {
-    const int pair = pbeg + g + (k >> 1) * wgs_per_xcd;
-    Unit u;
-    if (pair < pend) {
-      u = make_unit(p, pair, k & 1, nblk);
-    } else {
-      u.role = -1;
-      u.b = u.h = u.bh = u.hk = u.r0 = u.s0 = u.nt = 0;
+    if (!grouped) {  // unit k: pair ibeg + g + (k / 2) wgs_per_xcd, dq unit then dk/dv unit
+      const int pair = ibeg + g + (k >> 1) * wgs_per_xcd;
+      return pair < iend ? make_unit(p, pair, k & 1, nblk) : none;
     }
+    int t, hq;
+    if (kv_wg) {
+      t = ibeg + g + k * wh;
+      hq = 0;
+    } else {
+      const int d = (g - wh) + k * wd;  // over this XCD's (item, query head of the group) pairs
+      t = ibeg + d / p.G;
+      hq = d - (d / p.G) * p.G;
+    }
+    if (t >= iend) return none;
+    const int bk = t / nblk, rb = t - bk * nblk;
+    const int b = bk / p.Hkv, hk = bk - b * p.Hkv;
+    Unit u = make_unit(p, (b * p.H + hk * p.G + hq) * nblk + rb, kv_wg ? 1 : 0, nblk);
+    if (kv_wg) u.ng = p.G;
     return u;
   };
 
@@ -597,45 +629,18 @@ __global__ __launch_bounds__(kThreads, 2) void band_bwd_kernel(Params p) {
   wait_vmem();
   __syncthreads();
   for (int k = 0;; ++k) {
-    progress_priority(k, 4);  // a workgroup takes about four units
+    progress_priority(kv_wg ? k * p.G : k, 4);  // about four units' work per workgroup
     const Unit nxt = unit_at(k + 1);
     RowOps ops;
     read_stage(cur, bf, ops);  // the stage is refilled only in this unit's last tile
     if (cur.role == 0)
       dq_unit<GRAD_BF16, HAS_DIL>(p, cur, ops, nxt, bf);
     else
-      dkv_unit<GRAD_BF16, HAS_DIL>(p, cur, ops, nxt, bf);
+      dkv_unit<GRAD_BF16, HAS_DIL, GROUPED>(p, cur, ops, nxt, bf);
     if (nxt.role < 0) break;
     __syncthreads();  // the row stores' LDS regions are tile buffer 1, which the next unit refills
     cur = nxt;
   }
-}
-
-// dk, dv of key/value head hk = the sum, in head order, of the partials of its
-// G query heads (one thread per 4 elements of a row).
-__global__ __launch_bounds__(kThreads) void band_bwd_group_sum_kernel(Params p) {
-  const int64_t rows = (int64_t)p.B * p.Hkv * p.T;
-  const int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-  if (idx >= rows * 16) return;
-  const int c4 = (int)(idx % 16);
-  const int64_t r = idx / 16;
-  const int t = (int)(r % p.T);
-  const int64_t bk = r / p.T;
-  const int b = (int)(bk / p.Hkv), hk = (int)(bk % p.Hkv);
-  float4 sk = make_float4(0.f, 0.f, 0.f, 0.f), sv = sk;
-  for (int g = 0; g < p.G; ++g) {
-    const int64_t src = ((((int64_t)b * p.H + hk * p.G + g) * p.T + t) * 64) + c4 * 4;
-    const float4 a = *reinterpret_cast<const float4*>(p.pdk + src);
-    const float4 c = *reinterpret_cast<const float4*>(p.pdv + src);
-    sk.x += a.x; sk.y += a.y; sk.z += a.z; sk.w += a.w;
-    sv.x += c.x; sv.y += c.y; sv.z += c.z; sv.w += c.w;
-  }
-  const float fk[4] = {sk.x, sk.y, sk.z, sk.w}, fv[4] = {sv.x, sv.y, sv.z, sv.w};
-  const int gb = p.grad_bf16 ? 2 : 4;
-  char* dkrow = static_cast<char*>(p.dk) + (b * p.sdk_b + hk * p.sdk_h + (int64_t)t * p.sdk_t + c4 * 4) * gb;
-  char* dvrow = static_cast<char*>(p.dv) + (b * p.sdv_b + hk * p.sdv_h + (int64_t)t * p.sdv_t + c4 * 4) * gb;
-  store_vals<4>(dkrow, fk, p.grad_bf16 != 0);
-  store_vals<4>(dvrow, fv, p.grad_bf16 != 0);
 }
 
 template <bool GRAD_BF16, bool HAS_DIL>
@@ -647,20 +652,20 @@ hipError_t launch(const Params& p, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int nblk = (p.T + kRows - 1) / kRows;
-  const int64_t npairs = (int64_t)p.B * p.H * nblk;
   // two resident workgroups per compute unit, a multiple of the XCD count,
-  // no more than one per pair
+  // no more than there are units to take; with grouped heads at least two per
+  // XCD (one for each kind of unit)
   int grid = 2 * device_cu_count();
-  const int64_t cap = ((npairs + kNumXcd - 1) / kNumXcd) * kNumXcd;
-  if (grid > cap) grid = (int)cap;
+  const int64_t per_xcd = p.G > 1 ? 2 * (((int64_t)p.B * p.Hkv * nblk + kNumXcd - 1) / kNumXcd)
+                                  : ((int64_t)p.B * p.H * nblk + kNumXcd - 1) / kNumXcd;
+  if (grid > per_xcd * kNumXcd) grid = (int)(per_xcd * kNumXcd);
   grid = (grid / kNumXcd) * kNumXcd;
-  if (grid < kNumXcd) grid = kNumXcd;
-  hipLaunchKernelGGL((band_bwd_kernel<GRAD_BF16, HAS_DIL>), dim3(grid), dim3(kThreads), 0, s, p);
-  e = hipGetLastError();
-  if (e != hipSuccess || p.G == 1) return e;
-  const int64_t n4 = (int64_t)p.B * p.Hkv * p.T * 16;  // four elements per thread
-  hipLaunchKernelGGL(band_bwd_group_sum_kernel, dim3((unsigned)((n4 + kThreads - 1) / kThreads)), dim3(kThreads), 0,
-                     s, p);
+  const int min_grid = p.G > 1 ? 2 * kNumXcd : kNumXcd;
+  if (grid < min_grid) grid = min_grid;
+  if (p.G > 1)
+    hipLaunchKernelGGL((band_bwd_kernel<GRAD_BF16, HAS_DIL, true>), dim3(grid), dim3(kThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL((band_bwd_kernel<GRAD_BF16, HAS_DIL, false>), dim3(grid), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 

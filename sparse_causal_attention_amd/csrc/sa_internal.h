@@ -70,8 +70,6 @@ struct Params {
   float* lse2;      // workspace [B, H, T]: lse * log2(e) (band backward)
   float* partials;  // workspace [B, H, nblk_q, 2]
   const int32_t* pos;  // decode: row of each sequence's new token [B] (NULL: T - 1)
-  float* pdk;  // band backward with G > 1: per-query-head dk, dv partials,
-  float* pdv;  // contiguous fp32 [B, H, T, D] in the workspace
   // explicit neighbour lists (device): row i's keys cols[rp[i] .. rp[i+1]),
   // key j's queries rcols[rrp[j] .. rrp[j+1]), both ascending
   const int32_t* rp; const int32_t* cols;
