@@ -69,7 +69,7 @@ __device__ __forceinline__ bf16x8 vt_operand(const char* vs, const TileLane& tl,
   return as_bf16x8(make_uint4(x0.x, x0.y, x1.x, x1.y));
 }
 
-template <bool HAS_DIL>
+template <bool HAS_DIL, int HW>
 __global__ __launch_bounds__(kThreads, 4) void band_fwd_kernel(Params p) {
   // Two buffers of swizzled 64-key tiles, each its own LDS object: the loads
   // into one buffer are then known not to alias the reads of the other, so
@@ -78,31 +78,40 @@ __global__ __launch_bounds__(kThreads, 4) void band_fwd_kernel(Params p) {
   __shared__ __align__(16) char K0[kTileBytes], V0[kTileBytes];
   __shared__ __align__(16) char K1[kTileBytes], V1[kTileBytes];
 
-  const int nblk = (p.T + kBQ - 1) / kBQ;
-  const int logical = xcd_logical_block(p.B * p.H * nblk);
+  // The four wavefronts take HW query heads of one key/value head (HW = 4
+  // or 2 when the grouping allows, else 1) times 4 / HW groups of 32 query
+  // rows: with grouped heads the wavefronts then share the key band and every
+  // K/V tile serves several heads.
+  constexpr int hw = HW;
+  constexpr int rows = kBQ / hw;  // query rows of the workgroup
+  const int nblk = (p.T + rows - 1) / rows;
+  const int ngrp = p.H / hw;  // head groups
+  const int logical = xcd_logical_block(p.B * ngrp * nblk);
   if (logical < 0) return;
-  const int bh = logical / nblk;
-  const int rb = nblk - 1 - (logical - bh * nblk);  // late (longest) query blocks first
-  const int b = bh / p.H, h = bh - b * p.H;
+  const int bg = logical / nblk;
+  const int rb = nblk - 1 - (logical - bg * nblk);  // late (longest) query blocks first
+  const int b = bg / ngrp;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int h = (bg - b * ngrp) * hw + wave % hw;  // this wavefront's query head
+  const int bh = b * p.H + h;
   const int l32 = lane & 31, half = lane >> 5;
   const TileLane tl = tile_lane(lane);
   const DmaLane dl = dma_lane(wave, lane);
-  const int q0 = rb * kBQ;
-  const int qw = q0 + wave * 32;
+  const int q0 = rb * rows;
+  const int qw = q0 + (wave / hw) * 32;
   const int m = qw + l32;
   const int mc = m < p.T ? m : p.T - 1;
 
   const char* qbase = static_cast<const char*>(p.q) + (b * p.sq_b + h * p.sq_h) * 2;
-  const int hk = h / p.G;  // key/value head shared by G query heads
+  const int hk = h / p.G;  // key/value head shared by G query heads (the same for every wavefront)
   const char* kbase = static_cast<const char*>(p.k) + (b * p.sk_b + hk * p.sk_h) * 2;
   const char* vbase = static_cast<const char*>(p.v) + (b * p.sv_b + hk * p.sv_h) * 2;
   const int64_t sqt = p.sq_t * 2, skt = p.sk_t * 2, svt = p.sv_t * 2;
 
   const int W = p.W;
   const int lo = q0 - W + 1 > 0 ? q0 - W + 1 : 0;
-  const int hi = q0 + kBQ - 1 < p.T - 1 ? q0 + kBQ - 1 : p.T - 1;
+  const int hi = q0 + rows - 1 < p.T - 1 ? q0 + rows - 1 : p.T - 1;
   const int kfirst = (lo / kBK) * kBK;
   const int ntiles = (hi - kfirst) / kBK + 1;
 
@@ -306,14 +315,23 @@ bool band_supported(int dtype, int D, int score_mode, int64_t W) {
 
 int band_rows_per_block() { return kBQ; }
 
-hipError_t launch_band_fwd(const Params& p, hipStream_t s) {
-  const int nblk = (p.T + kBQ - 1) / kBQ;
-  const int grid = xcd_grid(p.B * p.H * nblk);
+template <int HW>
+hipError_t launch_hw(const Params& p, hipStream_t s) {
+  const int rows = kBQ / HW;
+  const int nblk = (p.T + rows - 1) / rows;
+  const int grid = xcd_grid(p.B * (p.H / HW) * nblk);
   if (p.n_dil > 0)
-    hipLaunchKernelGGL(band_fwd_kernel<true>, dim3(grid), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((band_fwd_kernel<true, HW>), dim3(grid), dim3(kThreads), 0, s, p);
   else
-    hipLaunchKernelGGL(band_fwd_kernel<false>, dim3(grid), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((band_fwd_kernel<false, HW>), dim3(grid), dim3(kThreads), 0, s, p);
   return hipGetLastError();
+}
+
+hipError_t launch_band_fwd(const Params& p, hipStream_t s) {
+  // query heads per workgroup: as many of a key/value head's group as divide four
+  if (p.G % 4 == 0) return launch_hw<4>(p, s);
+  if (p.G % 2 == 0) return launch_hw<2>(p, s);
+  return launch_hw<1>(p, s);
 }
 
 }  // namespace sa
