@@ -115,8 +115,19 @@ __global__ __launch_bounds__(kThreads, 4) void band_fwd_kernel(Params p) {
   const int kfirst = (lo / kBK) * kBK;
   const int ntiles = (hi - kfirst) / kBK + 1;
 
-  tile_issue(kbase, skt, kfirst, p.T, K0, wave, dl);
-  tile_issue(vbase, svt, kfirst, p.T, V0, wave, dl);
+  // Tiles are taken in a rotated order: step `it` works on the tile whose
+  // absolute index is congruent to it modulo ntiles, so neighbouring query
+  // blocks (whose key ranges overlap) load the same tile at the same step and
+  // the first reads of K and V from HBM spread over the whole kernel instead
+  // of all falling into its first two steps.
+  const int a0 = kfirst / kBK;
+  const int rot = (ntiles - a0 % ntiles) % ntiles;
+  auto tile_key = [&](int it) {
+    const int r = it + rot;
+    return kfirst + (r < ntiles ? r : r - ntiles) * kBK;
+  };
+  tile_issue(kbase, skt, tile_key(0), p.T, K0, wave, dl);
+  tile_issue(vbase, svt, tile_key(0), p.T, V0, wave, dl);
 
   // Q^T as B operand: lane holds q[m][16*kk + 8*half + e]
   bf16x8 qf[4];
@@ -195,10 +206,11 @@ __global__ __launch_bounds__(kThreads, 4) void band_fwd_kernel(Params p) {
   // Tile `it` from (ks, vs) while the next one streams into (kn, vn), the
   // buffers last read in tile it - 1.
   auto tile = [&](int it, const char* ks, const char* vs, char* kn, char* vn) {
-    const int kt0 = kfirst + it * kBK;
+    const int kt0 = tile_key(it);
     if (it + 1 < ntiles) {
-      tile_issue(kbase, skt, kt0 + kBK, p.T, kn, wave, dl);
-      tile_issue(vbase, svt, kt0 + kBK, p.T, vn, wave, dl);
+      const int kt1 = tile_key(it + 1);
+      tile_issue(kbase, skt, kt1, p.T, kn, wave, dl);
+      tile_issue(vbase, svt, kt1, p.T, vn, wave, dl);
     }
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
