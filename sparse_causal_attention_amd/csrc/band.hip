@@ -206,6 +206,10 @@ __global__ __launch_bounds__(kThreads, 4) void band_fwd_kernel(Params p) {
   // Tile `it` from (ks, vs) while the next one streams into (kn, vn), the
   // buffers last read in tile it - 1.
   auto tile = [&](int it, const char* ks, const char* vs, char* kn, char* vn) {
+    // The SIMDs favour their oldest wavefront, so of the workgroups sharing a
+    // compute unit the last-started one would finish alone at low occupancy;
+    // lowering the priority with progress keeps them level.
+    progress_priority(it, ntiles);
     const int kt0 = tile_key(it);
     if (it + 1 < ntiles) {
       const int kt1 = tile_key(it + 1);
