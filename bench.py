@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 MFMA_BF16_PEAK_TFS = 2500.0  # dense bf16 MFMA
 METRIC = "attention edges/s and tokens/s fwd+bwd at T=16384; % of HBM/MFMA roofline"
+SAMPLE = 10                  # per-call HIP events on every SAMPLE-th timed step
 
 
 def parse():
@@ -198,20 +199,33 @@ def run_workload(w, steps, warmup, algo, with_backward=True):
 
     for _ in range(warmup):
         step()
-    # events on the kernels' stream: step s's forward runs from ev[2s] to
-    # ev[2s+1] and its backward from ev[2s+1] to ev[2s+2], the next step's start
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps + 1)]
+    # HIP events on the kernels' stream.  An event between two kernels holds
+    # the second back until the first has drained, so the per-call events are
+    # recorded on every SAMPLE-th step only (its forward runs from ev[s][0] to
+    # ev[s][1], its backward from ev[s][1] to ev[s][2]); the other steps run
+    # back to back, as they would in training, and the whole timed region is
+    # bracketed by its own pair of events.
+    sampled = list(range(0, steps, SAMPLE))
+    ev = {s: [torch.cuda.Event(enable_timing=True) for _ in range(3)] for s in sampled}
+    region = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    region[0].record()
     for s in range(steps):
-        step(ev[2 * s], ev[2 * s + 1])
-    ev[2 * steps].record()
+        e = ev.get(s)
+        if e is None:
+            step()
+        else:
+            step(e[0], e[1])
+            e[2].record()
+    region[1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    f_ms = [ev[2 * s].elapsed_time(ev[2 * s + 1]) for s in range(steps)]
-    b_ms = [ev[2 * s + 1].elapsed_time(ev[2 * s + 2]) for s in range(steps)] if bwd else [0.0]
+    f_ms = [ev[s][0].elapsed_time(ev[s][1]) for s in sampled]
+    b_ms = [ev[s][1].elapsed_time(ev[s][2]) for s in sampled] if bwd else [0.0]
     res = {
         "wall_s": wall, "ms_per_step": 1e3 * wall / steps,
+        "event_ms_per_step": region[0].elapsed_time(region[1]) / steps, "sampled_steps": len(sampled),
         "fwd_ms": sum(f_ms) / len(f_ms), "bwd_ms": sum(b_ms) / len(b_ms),
         "fwd_ms_min": min(f_ms), "bwd_ms_min": min(b_ms),
         "plan_fwd": sa_describe_plan(g, x["v"], score=score_name(w), algo=algo, which="fwd", heads=w.H),
@@ -273,6 +287,9 @@ def summarize(w, r, steps):
         "kernels": {"fwd": r["plan_fwd"], "bwd": r["plan_bwd"]},
         "event_ms_fwd_plus_bwd": fb,
     }
+    if "event_ms_per_step" in r:
+        out["event_ms_per_step"] = r["event_ms_per_step"]
+        out["per_call_events"] = "every %dth timed step (%d steps)" % (SAMPLE, r["sampled_steps"])
     return out, m
 
 
