@@ -37,7 +37,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workloads",
-                    default="band,dilated,coord,uniform,band_gqa,dilated_gqa,decode_band,decode_dilated,ultra")
+                    default="band,dilated,coord,uniform,band_gqa,dilated_gqa,csr_dilated,csr_random,decode_band,decode_dilated,ultra")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample length")
     ap.add_argument("--algo", default="auto")
