@@ -289,8 +289,8 @@ __device__ __forceinline__ void read_stage(const Unit& u, const Bufs& bf, RowOps
 }
 
 // ------------------------------------------------------------------ dq unit
-template <bool GRAD_BF16, bool HAS_DIL>
-__device__ __forceinline__ void dq_unit(const Params& p, const Unit& u, const RowOps& ops, const Unit& nxt,
+template <bool GRAD_BF16, bool HAS_DIL, class NextUnit>
+__device__ __forceinline__ void dq_unit(const Params& p, const Unit& u, const RowOps& ops, const NextUnit& next_unit,
                                         const Bufs& bf) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -314,9 +314,12 @@ __device__ __forceinline__ void dq_unit(const Params& p, const Unit& u, const Ro
   auto tile = [&](int it, const char* ks, const char* vs, char* kn, char* vn, float* lan, float* lbn) {
     if (it + 1 < u.nt) {
       issue_tile(p, u, it + 1, kn, vn, lan, lbn);  // (kn, vn) were last read in tile it - 1
-    } else if (it + 1 == ntp && nxt.role >= 0) {
-      issue_tile(p, nxt, 0, kn, vn, lan, lbn);  // buffer 0: the next unit's first tile
-      issue_stage(p, nxt, bf);                   // read at the start of this unit
+    } else if (it + 1 == ntp) {
+      const Unit nxt = next_unit();  // formed only here, so it holds no registers through the unit
+      if (nxt.role >= 0) {
+        issue_tile(p, nxt, 0, kn, vn, lan, lbn);  // buffer 0: the next unit's first tile
+        issue_stage(p, nxt, bf);                   // read at the start of this unit
+      }
 
     }
     if (it < u.nt) {
@@ -404,8 +407,8 @@ __device__ __forceinline__ void dq_unit(const Params& p, const Unit& u, const Ro
 }
 
 // ------------------------------------------------------------------ dk/dv unit
-template <bool GRAD_BF16, bool HAS_DIL, bool GROUPED>
-__device__ __forceinline__ void dkv_unit(const Params& p, const Unit& u, const RowOps& ops, const Unit& nxt,
+template <bool GRAD_BF16, bool HAS_DIL, bool GROUPED, class NextUnit>
+__device__ __forceinline__ void dkv_unit(const Params& p, const Unit& u, const RowOps& ops, const NextUnit& next_unit,
                                          const Bufs& bf) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -433,9 +436,12 @@ __device__ __forceinline__ void dkv_unit(const Params& p, const Unit& u, const R
       issue_tile(p, uh, it + 1, qn, dn, ln, en);  // last read in tile it - 1
     } else if (more && it + 1 == ntp) {
       issue_tile(p, un, 0, qn, dn, ln, en);  // buffer 0: the next query head's first tile
-    } else if (it + 1 == ntp && nxt.role >= 0) {
-      issue_tile(p, nxt, 0, qn, dn, ln, en);  // buffer 0: the next unit's first tile
-      issue_stage(p, nxt, bf);
+    } else if (it + 1 == ntp) {
+      const Unit nxt = next_unit();
+      if (nxt.role >= 0) {
+        issue_tile(p, nxt, 0, qn, dn, ln, en);  // buffer 0: the next unit's first tile
+        issue_stage(p, nxt, bf);
+      }
     }
     if (it < u.nt) {
       const int mt0 = u.s0 + it * kTile;
@@ -630,13 +636,14 @@ __global__ __launch_bounds__(kThreads, 2) void band_bwd_kernel(Params p) {
   __syncthreads();
   for (int k = 0;; ++k) {
     progress_priority(kv_wg ? k * p.G : k, 4);  // about four units' work per workgroup
-    const Unit nxt = unit_at(k + 1);
+    auto next_unit = [&]() { return unit_at(k + 1); };
     RowOps ops;
     read_stage(cur, bf, ops);  // the stage is refilled only in this unit's last tile
     if (cur.role == 0)
-      dq_unit<GRAD_BF16, HAS_DIL>(p, cur, ops, nxt, bf);
+      dq_unit<GRAD_BF16, HAS_DIL>(p, cur, ops, next_unit, bf);
     else
-      dkv_unit<GRAD_BF16, HAS_DIL, GROUPED>(p, cur, ops, nxt, bf);
+      dkv_unit<GRAD_BF16, HAS_DIL, GROUPED>(p, cur, ops, next_unit, bf);
+    const Unit nxt = unit_at(k + 1);
     if (nxt.role < 0) break;
     __syncthreads();  // the row stores' LDS regions are tile buffer 1, which the next unit refills
     cur = nxt;
