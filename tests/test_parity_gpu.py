@@ -405,6 +405,8 @@ def gqa_reference(W, offs, G, v, dO=None, q=None, k=None):
 @pytest.mark.parametrize("B,H,Hkv,T,D,dt,W,offs,score,algo", [
     (1, 8, 2, 2048, 64, torch.bfloat16, 256, (), "dot", "auto"),             # band kernels
     (1, 4, 1, 1500, 64, torch.bfloat16, 64, (128, 256, 512), "dot", "auto"),  # band + long range
+    (2, 6, 3, 1100, 64, torch.bfloat16, 128, (), "dot", "auto"),             # band, two heads per workgroup
+    (1, 6, 2, 900, 64, torch.bfloat16, 96, (256,), "dot", "auto"),           # band, groups of three
     (2, 6, 3, 700, 32, torch.float32, 4, tuple(2 ** k for k in range(10)), "dot", "auto"),  # gather
     (1, 4, 2, 2048, 64, torch.bfloat16, 256, (), "dot", "gather"),
     (2, 4, 1, 500, 64, torch.bfloat16, 4, (8, 16, 32, 64), "uniform", "auto"),
