@@ -445,7 +445,8 @@ inline bool fits_off32(const Params& p, int eb) {
 // Both passes take two distances per step: fewer rows in flight per lane
 // than the forward's four, but fewer registers and more resident wavefronts
 // (key side: 76 instead of 119 VGPRs), which measured 3 to 6 % faster on the
-// dilated workloads.
+// dilated workloads.  The fixed-weight key side, with no scores to compute,
+// keeps four (1 % faster there).
 constexpr int kBwdGroup = 2;
 
 template <int DT, int D, int SM, bool OFF32>
@@ -457,7 +458,8 @@ hipError_t launch_passes(const Params& p, hipStream_t s, int grid, int nblk) {
     if (e != hipSuccess) return e;
   }
   const int grid_kv = xcd_grid(p.B * p.Hkv * nblk);  // key rows of the key/value heads
-  hipLaunchKernelGGL((gather_bwd_kv_kernel<DT, D, SM, kBwdGroup, OFF32>), dim3(grid_kv), dim3(kThreads), 0, s, p);
+  constexpr int gkv = SM == SM_UNIFORM ? 4 : kBwdGroup;
+  hipLaunchKernelGGL((gather_bwd_kv_kernel<DT, D, SM, gkv, OFF32>), dim3(grid_kv), dim3(kThreads), 0, s, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess || SM != SM_COORD) return e;
   return launch_coord_param_reduce(p, nblk, s);
