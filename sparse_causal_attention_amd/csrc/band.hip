@@ -38,7 +38,7 @@ constexpr int kD = 64;
 constexpr int kBQ = 128;        // query rows per workgroup: 4 wavefronts x 32
 constexpr int kBK = 64;         // keys per LDS tile
 constexpr int kThreads = 256;
-constexpr int kG = 2;           // long-range edges in flight per lane
+constexpr int kG = 1;           // long-range edges per step (two measured 0.8 % slower on 2^26 rows)
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8, u); }
 
