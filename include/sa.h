@@ -85,10 +85,12 @@ typedef enum { SA_F32 = 0, SA_BF16 = 1 } sa_dtype;
 typedef enum { SA_SCORE_DOT = 0, SA_SCORE_COORD = 1, SA_SCORE_UNIFORM = 2 } sa_score;
 
 /* Kernel family.  AUTO picks the LDS/MFMA band kernels for the window when
- * they apply (bf16, dot score, D = 64, W >= 16, a distance graph) and the
- * gather kernels otherwise (the indexed ones for an explicit-list graph).
- * GATHER forces the gather kernels for every edge; BAND requests the band
- * kernels and fails with SA_ERR_UNSUPPORTED where they do not apply. */
+ * they apply (bf16, dot score, D = 64, W >= 16, a distance graph; for
+ * sa_bwd also: each (batch, head) slice of q, k, v and dout spans fewer
+ * than 2^31 bytes, i.e. (T - 1) * row stride + D elements) and the gather
+ * kernels otherwise (the indexed ones for an explicit-list graph).  GATHER
+ * forces the gather kernels for every edge; BAND requests the band kernels
+ * and fails with SA_ERR_UNSUPPORTED where they do not apply. */
 typedef enum { SA_ALGO_AUTO = 0, SA_ALGO_GATHER = 1, SA_ALGO_BAND = 2 } sa_algo;
 
 #define SA_MAX_DILATED 64 /* distinct long-range distances kept by a graph */

@@ -44,6 +44,15 @@ bool offsets_fit(const sa_attn_desc* d, const int64_t st[3]) {
 
 enum class Path { Gather, Band, Csr };
 
+// The band backward loads its tiles through buffer resources over one (batch,
+// head) slice of q, k, v and dout, with 32-bit offsets: each slice must span
+// fewer than 2^31 bytes, else the backward takes the gather kernels.
+bool band_bwd_slices_fit(const sa_attn_desc* d) {
+  const double es = d->dtype == SA_BF16 ? 2.0 : 4.0;
+  auto fits = [&](const int64_t st[3]) { return ((double)(d->T - 1) * st[2] + (double)d->D) * es < 2147483648.0; };
+  return fits(d->stride_q) && fits(d->stride_k) && fits(d->stride_v) && fits(d->stride_do);
+}
+
 struct Plan {
   Path path;
 };
@@ -200,6 +209,10 @@ extern "C" sa_status sa_bwd(const sa_graph* g, const sa_attn_desc* d, const void
   Plan plan;
   sa_status st = check_common(g, d, q, k, v, cq, ck, gamma, beta, &plan);
   if (st != SA_OK) return st;
+  if (plan.path == Path::Band && !band_bwd_slices_fit(d)) {
+    if (d->algo == SA_ALGO_BAND) return SA_ERR_UNSUPPORTED;
+    plan.path = Path::Gather;
+  }
   const bool coord = d->score == SA_SCORE_COORD;
   const int es = esize(d->dtype), gs = esize(d->grad_dtype);
   if (o == nullptr || lse == nullptr || dout == nullptr || dv == nullptr || !lists_ready(g))
@@ -307,6 +320,10 @@ extern "C" sa_status sa_describe_plan(const sa_graph* g, const sa_attn_desc* d, 
   for (int c = 0; c < 3; ++c) tmp.stride_q[c] = tmp.stride_k[c] = tmp.stride_v[c] = 0;
   sa_status st = check_common(g, &tmp, dummy, dummy, dummy, dummy, dummy, dummy, dummy, &plan);
   if (st != SA_OK) return st;
+  if (which == 1 && plan.path == Path::Band && !band_bwd_slices_fit(d)) {
+    if (d->algo == SA_ALGO_BAND) return SA_ERR_UNSUPPORTED;
+    plan.path = Path::Gather;
+  }
   snprintf(buf, cap, "%s", which == 0 ? fwd_kernel_name(d, plan.path) : bwd_kernel_names(d, plan.path));
   return SA_OK;
 }

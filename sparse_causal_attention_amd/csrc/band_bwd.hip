@@ -48,6 +48,9 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kRows = 128;  // rows (queries or keys) owned per workgroup
+// Word 3 of a raw buffer resource on gfx9-family GPUs (32-bit data format,
+// no swizzle): the streamed tiles are loaded with buffer_load ... lds.
+constexpr int kBufferWord3 = 0x00020000;
 constexpr int kTile = 64;   // streamed rows per LDS tile
 constexpr int kThreads = 256;
 
@@ -208,24 +211,6 @@ __device__ __forceinline__ void rows_issue(const float* src, int r0, int T, floa
                                    (__attribute__((address_space(3))) void*)dst, 4, 0, 0);
 }
 
-// Issue the loads of streamed tile j of unit u: K, V rows (dq) or Q, dO rows
-// plus their lse * log2(e) and -Delta (dk/dv).
-__device__ __forceinline__ void issue_tile(const Params& p, const Unit& u, int j, char* a, char* bt, float* la,
-                                           float* lb) {
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int r0 = u.s0 + j * kTile;
-  if (u.role == 0) {
-    tile_issue_clamped(tensor_base_kv(p.k, p.sk_b, p.sk_h, u), p.sk_t * 2, r0, p.T, a, wave, lane);
-    tile_issue_clamped(tensor_base_kv(p.v, p.sv_b, p.sv_h, u), p.sv_t * 2, r0, p.T, bt, wave, lane);
-  } else {
-    tile_issue_clamped(tensor_base(p.q, p.sq_b, p.sq_h, u), p.sq_t * 2, r0, p.T, a, wave, lane);
-    tile_issue_clamped(tensor_base(p.dout, p.sdo_b, p.sdo_h, u), p.sdo_t * 2, r0, p.T, bt, wave, lane);
-    if (wave == 0) rows_issue(p.lse2 + (int64_t)u.bh * p.T, r0, p.T, la, lane);
-    if (wave == 1) rows_issue(p.ndelta + (int64_t)u.bh * p.T, r0, p.T, lb, lane);
-  }
-}
-
 // Tile buffers: (a, b, la, lb) of buffer 0 and of buffer 1, and the row
 // stage (sx, sy, snd, sl2): 128 rows of the next unit's per-row operands.
 // Each its own LDS object (see band_bwd_kernel).
@@ -234,12 +219,55 @@ struct Bufs {
   float *la0, *lb0, *la1, *lb1;
   char *sx, *sy;
   float *snd, *sl2;
+  DmaLane dl;  // this lane's slots of the direct tile loads
   // LDS region of wavefront w for store_rows_f32: tile buffer 1, idle from the
   // end of a unit's last tile until the next unit issues its second tile
   __device__ float* store_region(int w) const {
     return reinterpret_cast<float*>((w < 2 ? a1 : b1) + (w & 1) * 32 * 36 * 4);
   }
 };
+
+// Rows [r0, r0 + 64) of a bf16 [T, 64] tensor (row stride st bytes, rows
+// past T clamped to T - 1) into `tile`, through a buffer resource over the
+// tensor's (batch, head) slice: the lane's offset is its clamped slot row
+// times st plus its 16-byte column, with no 64-bit address arithmetic (the
+// per-load cost of the global form was two dozen instructions).  The slice
+// must span fewer than 2^31 bytes; the host sends larger ones to the gather
+// kernels.
+__device__ __forceinline__ void tile_issue_buf(const char* base, int64_t st, int r0, int T, char* tile,
+                                               const DmaLane& dl) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), (short)0, (int)((int64_t)(T - 1) * st + 128),
+                                        kBufferWord3);
+#pragma unroll
+  for (int k = 0; k < 3; ++k) {
+    const int i = wave + 4 * k;
+    if (i >= kTileSlots / 64) break;  // wave-uniform
+    const int row = r0 + dl.r[k] < T ? r0 + dl.r[k] : T - 1;
+    const uint32_t off = (uint32_t)row * (uint32_t)st + (uint32_t)dl.c16[k];
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(tile + 1024 * i), 16,
+                                             off, 0, 0, 0);
+  }
+}
+
+// Issue the loads of streamed tile j of unit u: K, V rows (dq) or Q, dO rows
+// plus their lse * log2(e) and -Delta (dk/dv).
+__device__ __forceinline__ void issue_tile(const Params& p, const Unit& u, int j, char* a, char* bt, float* la,
+                                           float* lb, const Bufs& bf) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r0 = u.s0 + j * kTile;
+  if (u.role == 0) {
+    tile_issue_buf(tensor_base_kv(p.k, p.sk_b, p.sk_h, u), p.sk_t * 2, r0, p.T, a, bf.dl);
+    tile_issue_buf(tensor_base_kv(p.v, p.sv_b, p.sv_h, u), p.sv_t * 2, r0, p.T, bt, bf.dl);
+  } else {
+    tile_issue_buf(tensor_base(p.q, p.sq_b, p.sq_h, u), p.sq_t * 2, r0, p.T, a, bf.dl);
+    tile_issue_buf(tensor_base(p.dout, p.sdo_b, p.sdo_h, u), p.sdo_t * 2, r0, p.T, bt, bf.dl);
+    if (wave == 0) rows_issue(p.lse2 + (int64_t)u.bh * p.T, r0, p.T, la, lane);
+    if (wave == 1) rows_issue(p.ndelta + (int64_t)u.bh * p.T, r0, p.T, lb, lane);
+  }
+}
 
 // Issue the loads of unit u's per-row operands into the row stage: rows
 // r0 .. r0 + 127 of Q and dO (dq) or K and V (dk/dv), and for dq their
@@ -264,10 +292,10 @@ __device__ __forceinline__ void issue_stage(const Params& p, const Unit& u, cons
     xb = tensor_base_kv(p.k, p.sk_b, p.sk_h, u), xs = p.sk_t * 2;
     yb = tensor_base_kv(p.v, p.sv_b, p.sv_h, u), ys = p.sv_t * 2;
   }
-  tile_issue_clamped(xb, xs, u.r0, p.T, bf.sx, wave, lane);
-  tile_issue_clamped(xb, xs, u.r0 + kTile, p.T, bf.sx + kTileBytes, wave, lane);
-  tile_issue_clamped(yb, ys, u.r0, p.T, bf.sy, wave, lane);
-  tile_issue_clamped(yb, ys, u.r0 + kTile, p.T, bf.sy + kTileBytes, wave, lane);
+  tile_issue_buf(xb, xs, u.r0, p.T, bf.sx, bf.dl);
+  tile_issue_buf(xb, xs, u.r0 + kTile, p.T, bf.sx + kTileBytes, bf.dl);
+  tile_issue_buf(yb, ys, u.r0, p.T, bf.sy, bf.dl);
+  tile_issue_buf(yb, ys, u.r0 + kTile, p.T, bf.sy + kTileBytes, bf.dl);
 }
 
 // This lane's per-row operands from the row stage (row 32 wave + l % 32).
@@ -313,11 +341,11 @@ __device__ __forceinline__ void dq_unit(const Params& p, const Unit& u, const Ro
 
   auto tile = [&](int it, const char* ks, const char* vs, char* kn, char* vn, float* lan, float* lbn) {
     if (it + 1 < u.nt) {
-      issue_tile(p, u, it + 1, kn, vn, lan, lbn);  // (kn, vn) were last read in tile it - 1
+      issue_tile(p, u, it + 1, kn, vn, lan, lbn, bf);  // (kn, vn) were last read in tile it - 1
     } else if (it + 1 == ntp) {
       const Unit nxt = next_unit();  // formed only here, so it holds no registers through the unit
       if (nxt.role >= 0) {
-        issue_tile(p, nxt, 0, kn, vn, lan, lbn);  // buffer 0: the next unit's first tile
+        issue_tile(p, nxt, 0, kn, vn, lan, lbn, bf);  // buffer 0: the next unit's first tile
         issue_stage(p, nxt, bf);                   // read at the start of this unit
       }
 
@@ -433,13 +461,13 @@ __device__ __forceinline__ void dkv_unit(const Params& p, const Unit& u, const R
   auto tile = [&](const Unit& uh, bool more, const Unit& un, int it, const char* qs, const char* ds, const float* ls,
                   const float* es, char* qn, char* dn, float* ln, float* en) {
     if (it + 1 < u.nt) {
-      issue_tile(p, uh, it + 1, qn, dn, ln, en);  // last read in tile it - 1
+      issue_tile(p, uh, it + 1, qn, dn, ln, en, bf);  // last read in tile it - 1
     } else if (more && it + 1 == ntp) {
-      issue_tile(p, un, 0, qn, dn, ln, en);  // buffer 0: the next query head's first tile
+      issue_tile(p, un, 0, qn, dn, ln, en, bf);  // buffer 0: the next query head's first tile
     } else if (it + 1 == ntp) {
       const Unit nxt = next_unit();
       if (nxt.role >= 0) {
-        issue_tile(p, nxt, 0, qn, dn, ln, en);  // buffer 0: the next unit's first tile
+        issue_tile(p, nxt, 0, qn, dn, ln, en, bf);  // buffer 0: the next unit's first tile
         issue_stage(p, nxt, bf);
       }
     }
@@ -585,7 +613,8 @@ __global__ __launch_bounds__(kThreads, 2) void band_bwd_kernel(Params p) {
   __shared__ __align__(16) float r0a[kTile], r0b[kTile], r1a[kTile], r1b[kTile];
   __shared__ __align__(16) char stx[2 * kTileBytes], sty[2 * kTileBytes];
   __shared__ __align__(16) float stnd[kRows], stl2[kRows];
-  const Bufs bf{t0a, t0b, t1a, t1b, r0a, r0b, r1a, r1b, stx, sty, stnd, stl2};
+  const Bufs bf{t0a, t0b, t1a, t1b, r0a, r0b, r1a, r1b, stx, sty, stnd, stl2,
+                dma_lane(__builtin_amdgcn_readfirstlane(threadIdx.x >> 6), threadIdx.x & 63)};
 
   const int nblk = (p.T + kRows - 1) / kRows;
   const int xcd = blockIdx.x % kNumXcd, g = blockIdx.x / kNumXcd;
@@ -630,7 +659,7 @@ __global__ __launch_bounds__(kThreads, 2) void band_bwd_kernel(Params p) {
 
   Unit cur = unit_at(0);
   if (cur.role < 0) return;  // uniform over the workgroup
-  issue_tile(p, cur, 0, bf.a0, bf.b0, bf.la0, bf.lb0);
+  issue_tile(p, cur, 0, bf.a0, bf.b0, bf.la0, bf.lb0, bf);
   issue_stage(p, cur, bf);
   wait_vmem();
   __syncthreads();

@@ -136,6 +136,29 @@ def test_plan_selection():
     assert st == 0 and name == "gather_fwd_kernel(coord)"
 
 
+def test_plan_band_backward_slice_limit():
+    """The band backward loads its tiles with 32-bit offsets over one (batch,
+    head) slice: past 2^31 bytes per slice the backward takes the gather
+    kernels (BAND fails) while the forward stays on the band kernel."""
+    for T, band_bwd in ((1 << 23, True), (1 << 25, False)):
+        g = sa_build_graph(T, 256, ())
+        d = desc(B=1, H=1, T=T, D=64, dtype=1)
+        st, name = plan(g, d, 0)
+        assert st == 0 and name == "band_fwd_kernel"
+        st, name = plan(g, d, 1)
+        assert st == 0
+        assert name.startswith("band_bwd") == band_bwd, (T, name)
+        st, _ = plan(g, desc(B=1, H=1, T=T, D=64, dtype=1, algo=2), 1)
+        assert st == (0 if band_bwd else _abi.SA_ERR_UNSUPPORTED)
+    # a wide row stride counts: 2^21 rows at 2 KiB per row exceed 2^31 bytes
+    g = sa_build_graph(1 << 21, 256, ())
+    d = desc(B=1, H=16, T=1 << 21, D=64, dtype=1)
+    for name_ in ("q", "k", "v", "do"):
+        getattr(d, "stride_" + name_)[:] = (16 * (1 << 21) * 64, 64, 16 * 64)
+    st, name = plan(g, d, 1)
+    assert st == 0 and name.startswith("gather_bwd"), name
+
+
 def test_plan_uniform_mode():
     """The uniform score reads v alone and runs on the gather kernels; its
     backward is the key-side pass only; the band kernels do not apply."""
