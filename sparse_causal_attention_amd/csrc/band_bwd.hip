@@ -27,7 +27,7 @@
 // and share K, V, Q, dO rows in the XCD's L2; a dq unit and a dk/dv unit of
 // the same row block together have nearly the same work at every position.
 // Streamed 64-row tiles are double-buffered in LDS and filled by direct
-// global -> LDS loads; the stream runs on across units: while a unit's last
+// buffer -> LDS loads; the stream runs on across units: while a unit's last
 // tile is computed, the first tile of the next unit is loaded, together with
 // the next unit's per-row operands (into registers), so a workgroup never
 // waits for a unit's start-up loads.  Each unit's tile count is padded to an

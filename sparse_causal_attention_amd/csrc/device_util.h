@@ -237,23 +237,6 @@ __device__ __forceinline__ void tile_issue(const char* base, int64_t st, int r0,
   }
 }
 
-// The same loads with every row index clamped and the slots derived on the
-// spot (no registers held between calls; for register-bound kernels).
-__device__ __forceinline__ void tile_issue_clamped(const char* base, int64_t st, int r0, int T, char* tile,
-                                                   int wave, int lane) {
-#pragma unroll
-  for (int k = 0; k < 3; ++k) {
-    const int i = wave + 4 * k;
-    if (i >= kTileSlots / 64) break;  // wave-uniform
-    const int q = 64 * i + lane;      // slot index in the tile
-    const int r = q / 9, w = q - 9 * (q / 9);
-    const int c = w < 8 ? w : 7;
-    const int row = r0 + r < T ? r0 + r : T - 1;
-    __builtin_amdgcn_global_load_lds(static_cast<const void*>(base + row * st + c * 16),
-                                     (__attribute__((address_space(3))) void*)(tile + 1024 * i), 16, 0, 0);
-  }
-}
-
 // Wait for this wavefront's direct-to-LDS loads (and every other load).
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
