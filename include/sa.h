@@ -87,7 +87,8 @@ typedef enum { SA_SCORE_DOT = 0, SA_SCORE_COORD = 1, SA_SCORE_UNIFORM = 2 } sa_s
 /* Kernel family.  AUTO picks the LDS/MFMA band kernels for the window when
  * they apply (bf16, dot score, D = 64, W >= 16, a distance graph; for
  * sa_bwd also: each (batch, head) slice of q, k, v and dout spans fewer
- * than 2^31 bytes, i.e. (T - 1) * row stride + D elements) and the gather
+ * than 2^31 bytes, i.e. (T - 1) * row stride + D elements, and each of their
+ * strides is below 2^31 elements) and the gather
  * kernels otherwise (the indexed ones for an explicit-list graph).  GATHER
  * forces the gather kernels for every edge; BAND requests the band kernels
  * and fails with SA_ERR_UNSUPPORTED where they do not apply. */

@@ -45,11 +45,17 @@ bool offsets_fit(const sa_attn_desc* d, const int64_t st[3]) {
 enum class Path { Gather, Band, Csr };
 
 // The band backward loads its tiles through buffer resources over one (batch,
-// head) slice of q, k, v and dout, with 32-bit offsets: each slice must span
-// fewer than 2^31 bytes, else the backward takes the gather kernels.
+// head) slice of q, k, v and dout, with 32-bit offsets, and holds their
+// strides as 32-bit values: each slice must span fewer than 2^31 bytes and
+// each stride be below 2^31 elements, else the backward takes the gather
+// kernels.
 bool band_bwd_slices_fit(const sa_attn_desc* d) {
   const double es = d->dtype == SA_BF16 ? 2.0 : 4.0;
-  auto fits = [&](const int64_t st[3]) { return ((double)(d->T - 1) * st[2] + (double)d->D) * es < 2147483648.0; };
+  auto fits = [&](const int64_t st[3]) {
+    for (int c = 0; c < 3; ++c)
+      if (st[c] >= ((int64_t)1 << 31)) return false;
+    return ((double)(d->T - 1) * st[2] + (double)d->D) * es < 2147483648.0;
+  };
   return fits(d->stride_q) && fits(d->stride_k) && fits(d->stride_v) && fits(d->stride_do);
 }
 

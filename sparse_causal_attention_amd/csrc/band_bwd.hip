@@ -202,12 +202,14 @@ struct RowOps {
   float nd, l2;
 };
 
+// (Strides of q, k, v and dout fit 32 bits on the band backward's path, which
+// keeps them in one scalar register each instead of two.)
 __device__ __forceinline__ const char* tensor_base(const void* t, int64_t sb, int64_t sh, const Unit& u) {
-  return static_cast<const char*>(t) + (u.b * sb + u.h * sh) * 2;
+  return static_cast<const char*>(t) + ((int64_t)u.b * (int32_t)sb + (int64_t)u.h * (int32_t)sh) * 2;
 }
 // K and V live on the unit's key/value head.
 __device__ __forceinline__ const char* tensor_base_kv(const void* t, int64_t sb, int64_t sh, const Unit& u) {
-  return static_cast<const char*>(t) + (u.b * sb + u.hk * sh) * 2;
+  return static_cast<const char*>(t) + ((int64_t)u.b * (int32_t)sb + (int64_t)u.hk * (int32_t)sh) * 2;
 }
 
 // Direct loads of a tile's 64 per-row floats (one wavefront, 4 B per lane).
@@ -265,11 +267,11 @@ __device__ __forceinline__ void issue_tile(const Params& p, const Unit& u, int j
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r0 = u.s0 + j * kTile;
   if (u.role == 0) {
-    tile_issue_buf(tensor_base_kv(p.k, p.sk_b, p.sk_h, u), p.sk_t * 2, r0, p.T, a, bf.dl);
-    tile_issue_buf(tensor_base_kv(p.v, p.sv_b, p.sv_h, u), p.sv_t * 2, r0, p.T, bt, bf.dl);
+    tile_issue_buf(tensor_base_kv(p.k, p.sk_b, p.sk_h, u), (int32_t)p.sk_t * 2, r0, p.T, a, bf.dl);
+    tile_issue_buf(tensor_base_kv(p.v, p.sv_b, p.sv_h, u), (int32_t)p.sv_t * 2, r0, p.T, bt, bf.dl);
   } else {
-    tile_issue_buf(tensor_base(p.q, p.sq_b, p.sq_h, u), p.sq_t * 2, r0, p.T, a, bf.dl);
-    tile_issue_buf(tensor_base(p.dout, p.sdo_b, p.sdo_h, u), p.sdo_t * 2, r0, p.T, bt, bf.dl);
+    tile_issue_buf(tensor_base(p.q, p.sq_b, p.sq_h, u), (int32_t)p.sq_t * 2, r0, p.T, a, bf.dl);
+    tile_issue_buf(tensor_base(p.dout, p.sdo_b, p.sdo_h, u), (int32_t)p.sdo_t * 2, r0, p.T, bt, bf.dl);
     if (wave == 0) rows_issue(p.lse2 + (int64_t)u.bh * p.T, r0, p.T, la, lane);
     if (wave == 1) rows_issue(p.ndelta + (int64_t)u.bh * p.T, r0, p.T, lb, lane);
   }
@@ -284,8 +286,8 @@ __device__ __forceinline__ void issue_stage(const Params& p, const Unit& u, cons
   const char *xb, *yb;
   int64_t xs, ys;
   if (u.role == 0) {
-    xb = tensor_base(p.q, p.sq_b, p.sq_h, u), xs = p.sq_t * 2;
-    yb = tensor_base(p.dout, p.sdo_b, p.sdo_h, u), ys = p.sdo_t * 2;
+    xb = tensor_base(p.q, p.sq_b, p.sq_h, u), xs = (int32_t)p.sq_t * 2;
+    yb = tensor_base(p.dout, p.sdo_b, p.sdo_h, u), ys = (int32_t)p.sdo_t * 2;
     if (wave == 2) {
       rows_issue(p.ndelta + (int64_t)u.bh * p.T, u.r0, p.T, bf.snd, lane);
       rows_issue(p.ndelta + (int64_t)u.bh * p.T, u.r0 + 64, p.T, bf.snd + 64, lane);
@@ -295,8 +297,8 @@ __device__ __forceinline__ void issue_stage(const Params& p, const Unit& u, cons
       rows_issue(p.lse2 + (int64_t)u.bh * p.T, u.r0 + 64, p.T, bf.sl2 + 64, lane);
     }
   } else {
-    xb = tensor_base_kv(p.k, p.sk_b, p.sk_h, u), xs = p.sk_t * 2;
-    yb = tensor_base_kv(p.v, p.sv_b, p.sv_h, u), ys = p.sv_t * 2;
+    xb = tensor_base_kv(p.k, p.sk_b, p.sk_h, u), xs = (int32_t)p.sk_t * 2;
+    yb = tensor_base_kv(p.v, p.sv_b, p.sv_h, u), ys = (int32_t)p.sv_t * 2;
   }
   tile_issue_buf(xb, xs, u.r0, p.T, bf.sx, bf.dl);
   tile_issue_buf(xb, xs, u.r0 + kTile, p.T, bf.sx + kTileBytes, bf.dl);
@@ -405,7 +407,7 @@ __device__ __forceinline__ void dq_unit(const Params& p, const Unit& u, const Ro
     // long-range edges j = m - d
     const char* kb = tensor_base_kv(p.k, p.sk_b, p.sk_h, u);
     const char* vb = tensor_base_kv(p.v, p.sv_b, p.sv_h, u);
-    const int64_t skt = p.sk_t * 2, svt = p.sv_t * 2;
+    const int64_t skt = (int32_t)p.sk_t * 2, svt = (int32_t)p.sv_t * 2;
     for (int t = 0; t < p.n_dil; ++t) {
       const int j = mc - p.dil[t];
       const int jj = j < 0 ? 0 : j;
@@ -545,7 +547,7 @@ __device__ __forceinline__ void dkv_unit(const Params& p, const Unit& u, const R
     // long-range edges: queries i = n + d
     const char* qb = tensor_base(p.q, p.sq_b, p.sq_h, uh);
     const char* dob = tensor_base(p.dout, p.sdo_b, p.sdo_h, uh);
-    const int64_t sqt = p.sq_t * 2, sdot = p.sdo_t * 2;
+    const int64_t sqt = (int32_t)p.sq_t * 2, sdot = (int32_t)p.sdo_t * 2;
     const float* lseb = p.lse2 + (int64_t)uh.bh * p.T;
     const float* ndelb = p.ndelta + (int64_t)uh.bh * p.T;
     for (int t = 0; t < p.n_dil; ++t) {

@@ -157,6 +157,14 @@ def test_plan_band_backward_slice_limit():
         getattr(d, "stride_" + name_)[:] = (16 * (1 << 21) * 64, 64, 16 * 64)
     st, name = plan(g, d, 1)
     assert st == 0 and name.startswith("gather_bwd"), name
+    # so does a batch stride of 2^31 elements or more (the strides are held in 32 bits)
+    g = sa_build_graph(4096, 256, ())
+    d = desc(B=2, H=1, T=4096, D=64, dtype=1)
+    st, name = plan(g, d, 1)
+    assert st == 0 and name.startswith("band_bwd"), name
+    d.stride_k[0] = 1 << 31
+    st, name = plan(g, d, 1)
+    assert st == 0 and name.startswith("gather_bwd"), name
 
 
 def test_plan_uniform_mode():
