@@ -29,6 +29,8 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 MFMA_BF16_PEAK_TFS = 2500.0  # dense bf16 MFMA
 METRIC = "attention edges/s and tokens/s fwd+bwd at T=16384; % of HBM/MFMA roofline"
 SAMPLE = 10                  # per-call HIP events on every SAMPLE-th timed step
+COLD_REPS = 10               # cold-cache repetitions per call
+FLUSH_BYTES = 1 << 30        # written before each cold call: more than the L2s and the 256 MB MALL
 
 
 def parse():
@@ -41,6 +43,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample length")
     ap.add_argument("--algo", default="auto")
+    ap.add_argument("--no-cold", action="store_true",
+                    help="skip the cold-cache repetitions (profiled runs: keeps per-kernel averages warm)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (scales profiler byte counters)")
     return ap.parse_args()
@@ -145,7 +149,7 @@ def make_graph(w):
     return sa_build_graph_csr(w.T, *random_lists(w))
 
 
-def run_workload(w, steps, warmup, algo, with_backward=True):
+def run_workload(w, steps, warmup, algo, with_backward=True, no_cold=False):
     import torch
 
     from sparse_causal_attention_amd import sa_bwd_prepared, sa_describe_plan, sa_fwd_prepared
@@ -223,11 +227,13 @@ def run_workload(w, steps, warmup, algo, with_backward=True):
     wall = time.perf_counter() - t0
     f_ms = [ev[s][0].elapsed_time(ev[s][1]) for s in sampled]
     b_ms = [ev[s][1].elapsed_time(ev[s][2]) for s in sampled] if bwd else [0.0]
+    cold = None if no_cold else cold_cache(fwd_call, bwd_call, COLD_REPS if steps >= COLD_REPS else 1)
     res = {
         "wall_s": wall, "ms_per_step": 1e3 * wall / steps,
         "event_ms_per_step": region[0].elapsed_time(region[1]) / steps, "sampled_steps": len(sampled),
         "fwd_ms": sum(f_ms) / len(f_ms), "bwd_ms": sum(b_ms) / len(b_ms),
         "fwd_ms_min": min(f_ms), "bwd_ms_min": min(b_ms),
+        "fwd_ms_median": median(f_ms), "bwd_ms_median": median(b_ms), "cold": cold,
         "plan_fwd": sa_describe_plan(g, x["v"], score=score_name(w), algo=algo, which="fwd", heads=w.H),
         "plan_bwd": sa_describe_plan(g, x["v"], score=score_name(w), algo=algo, which="bwd",
                                      heads=w.H) if bwd else None,
@@ -237,7 +243,41 @@ def run_workload(w, steps, warmup, algo, with_backward=True):
     return res
 
 
-def run_decode(w, steps, warmup):
+def median(xs):
+    ys = sorted(xs)
+    n = len(ys)
+    return ys[n // 2] if n % 2 else 0.5 * (ys[n // 2 - 1] + ys[n // 2])
+
+
+def cold_cache(fwd_call, bwd_call, reps):
+    """Each call timed alone after FLUSH_BYTES of unrelated writes (a fill
+    kernel) have evicted the inputs from the L2s and the MALL: median and
+    minimum over `reps` repetitions.  The backward reads the o and lse of the
+    forward just before it, as in a training step."""
+    import torch
+
+    flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    f_ms, b_ms = [], []
+    for r in range(reps):
+        for call, out in ((fwd_call, f_ms), (bwd_call, b_ms)):
+            if call is None:
+                continue
+            flush.fill_(r & 0xFF)
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+            e[0].record()
+            call()
+            e[1].record()
+            torch.cuda.synchronize()
+            out.append(e[0].elapsed_time(e[1]))
+    del flush
+    res = {"reps": reps, "flush_bytes": FLUSH_BYTES,
+           "fwd_ms_median": median(f_ms), "fwd_ms_min": min(f_ms)}
+    if b_ms:
+        res.update(bwd_ms_median=median(b_ms), bwd_ms_min=min(b_ms))
+    return res
+
+
+def run_decode(w, steps, warmup, no_cold=False):
     """Decode steps: sa_decode of B new tokens (every head) at row T - 1."""
     import torch
 
@@ -260,9 +300,10 @@ def run_decode(w, steps, warmup):
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     f_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    cold = None if no_cold else cold_cache(call, None, COLD_REPS)
     return {"wall_s": wall, "ms_per_step": 1e3 * wall / steps, "fwd_ms": sum(f_ms) / len(f_ms), "bwd_ms": 0.0,
-            "fwd_ms_min": min(f_ms), "bwd_ms_min": 0.0, "plan_fwd": "decode_kernel(dot)", "plan_bwd": None,
-            "inputs": x}
+            "fwd_ms_min": min(f_ms), "bwd_ms_min": 0.0, "fwd_ms_median": median(f_ms), "bwd_ms_median": 0.0,
+            "cold": cold, "plan_fwd": "decode_kernel(dot)", "plan_bwd": None, "inputs": x}
 
 
 def summarize(w, r, steps):
@@ -287,6 +328,16 @@ def summarize(w, r, steps):
         "kernels": {"fwd": r["plan_fwd"], "bwd": r["plan_bwd"]},
         "event_ms_fwd_plus_bwd": fb,
     }
+    if "fwd_ms_median" in r:
+        out["warm_median_min_ms"] = {"fwd": [r["fwd_ms_median"], r["fwd_ms_min"]],
+                                     "bwd": [r["bwd_ms_median"], r["bwd_ms_min"]] if r["bwd_ms"] > 0 else None}
+    if r.get("cold") is not None:
+        c = r["cold"]
+        out["cold_cache"] = {"fwd_ms_median": c["fwd_ms_median"], "fwd_ms_min": c["fwd_ms_min"],
+                             "bwd_ms_median": c.get("bwd_ms_median"), "bwd_ms_min": c.get("bwd_ms_min"),
+                             "reps": c["reps"],
+                             "how": "each call alone after a %d MiB fill evicts the L2s and the MALL"
+                                    % (c["flush_bytes"] >> 20)}
     if "event_ms_per_step" in r:
         out["event_ms_per_step"] = r["event_ms_per_step"]
         out["per_call_events"] = "every %dth timed step (%d steps)" % (SAMPLE, r["sampled_steps"])
@@ -430,7 +481,8 @@ def main():
         if w.decode:
             steps, warm = max(steps, 200), max(warm, 20)  # microsecond steps
         print("[bench] %s: %d warmup + %d timed steps" % (name, warm, steps), file=sys.stderr, flush=True)
-        r = run_decode(w, steps, warm) if w.decode else run_workload(w, steps, warm, args.algo)
+        r = (run_decode(w, steps, warm, args.no_cold) if w.decode
+             else run_workload(w, steps, warm, args.algo, no_cold=args.no_cold))
         s, m = summarize(w, r, steps)
         s["roofline"] = roofline_for(w, r, m)
         s["steps"] = steps
