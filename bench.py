@@ -397,10 +397,21 @@ def roofline_for(w, r, m):
 
 
 # ------------------------------------------------------------------ CPU baseline (oracle)
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, inputs, target_s):
     """The fp64 oracle, as it stands, on a bounded sample of the same inputs:
-    whole (b, h) slices (forward + backward) until target_s seconds elapse.
-    Scaled to tokens/s of the full workload."""
+    whole (b, h) slices (forward + backward) until target_s seconds elapse on
+    every host thread, then one slice on a single thread.  Scaled to tokens/s
+    of the full workload."""
     import oracle
     from sparse_causal_attention_amd.inputs import host_view
 
@@ -411,10 +422,8 @@ def cpu_baseline(w, inputs, target_s):
         lists = oracle.graph_csr(w.T, w.window, w.offsets)
     elif w.graph == "random":
         lists = random_lists(w)
-    done = 0
-    t0 = time.perf_counter()
-    while True:  # whole passes over the (batch, head) slices until target_s
-        b, h = slices[done % len(slices)]
+
+    def one_slice(b, h):
         if lists is not None:  # dot score over explicit lists
             oracle.fwd_csr(*lists, hv["v"][b, h], q=hv["q"][b, h], k=hv["k"][b, h])
             oracle.bwd_csr(*lists, hv["v"][b, h], hv["do"][b, h], q=hv["q"][b, h], k=hv["k"][b, h])
@@ -430,17 +439,32 @@ def cpu_baseline(w, inputs, target_s):
             oracle.fwd(w.T, w.window, w.offsets, hv["v"][b, h], q=hv["q"][b, h], k=hv["k"][b, h])
             oracle.bwd(w.T, w.window, w.offsets, hv["v"][b, h], hv["do"][b, h], q=hv["q"][b, h],
                        k=hv["k"][b, h])
+
+    threads = oracle.num_threads()
+    done = 0
+    t0 = time.perf_counter()
+    while True:  # whole passes over the (batch, head) slices until target_s
+        one_slice(*slices[done % len(slices)])
         done += 1
         if time.perf_counter() - t0 >= target_s:
             break
     el = time.perf_counter() - t0
     frac = done / len(slices)
     tokens_per_s = w.B * w.T * frac / el
-    return {"value": tokens_per_s, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+    # one slice on one thread: how the oracle's rate scales with the host's cores
+    oracle.set_num_threads(1)
+    t1 = time.perf_counter()
+    one_slice(*slices[0])
+    el1 = time.perf_counter() - t1
+    oracle.set_num_threads(threads)
+    return {"value": tokens_per_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": "%d (batch, head) slices (%.2f passes over the %d slices of the %s workload), "
                       "forward + backward, fp64, %.1f s; tokens/s scaled by the slice fraction"
                       % (done, frac, len(slices), w.name, el),
-            "edges_per_s": edge_counts(w)[0] * done / el}
+            "edges_per_s": edge_counts(w)[0] * done / el,
+            "single_thread": {"value": w.B * w.T / len(slices) / el1, "unit": "tokens/s",
+                              "sample": "1 slice, %.1f s" % el1},
+            "cpu_model": cpu_model()}
 
 
 def copy_probe():

@@ -80,12 +80,19 @@ def lib():
         L.oracle_dense_causal.argtypes = [i64, i64, dbl, ctypes.c_int, vp, vp, vp, vp, vp]
         L.oracle_num_threads.restype = ctypes.c_int
         L.oracle_num_threads.argtypes = []
+        L.oracle_set_num_threads.restype = None
+        L.oracle_set_num_threads.argtypes = [ctypes.c_int]
         _lib = L
     return _lib
 
 
 def num_threads() -> int:
     return int(lib().oracle_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the OpenMP regions that follow (timing only)."""
+    lib().oracle_set_num_threads(int(n))
 
 
 # ---------------------------------------------------------------- marshalling

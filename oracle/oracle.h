@@ -94,6 +94,10 @@ int oracle_dense_causal(int64_t T, int64_t D, double scale, int dtype, const voi
 /* Number of OpenMP threads a parallel region here would use. */
 int oracle_num_threads(void);
 
+/* Threads for the parallel regions that follow (n >= 1; timing only, the
+ * results do not depend on it). */
+void oracle_set_num_threads(int n);
+
 #ifdef __cplusplus
 }
 #endif
