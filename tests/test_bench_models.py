@@ -90,3 +90,29 @@ def test_models_explicit_lists():
     window = sum(min(i + 1, r.window) for i in range(r.T))
     assert far == total - window
     assert bench.models(r)["edges"] == r.B * r.H * total
+
+
+def test_summary_carries_warm_and_cold_figures():
+    """The JSON detail reports warm medians and minima and the cold-cache
+    block beside the means; `value` stays on the warm wall-clock rate."""
+    w = WORKLOADS["band"]
+    r = {"wall_s": 0.02, "ms_per_step": 0.1, "fwd_ms": 0.025, "bwd_ms": 0.075,
+         "fwd_ms_min": 0.02, "bwd_ms_min": 0.07, "fwd_ms_median": 0.024, "bwd_ms_median": 0.074,
+         "cold": {"reps": 10, "flush_bytes": 1 << 30, "fwd_ms_median": 0.03, "fwd_ms_min": 0.029,
+                  "bwd_ms_median": 0.09, "bwd_ms_min": 0.088},
+         "plan_fwd": "band_fwd_kernel", "plan_bwd": "band_bwd_prepass_kernel+band_bwd_kernel"}
+    s, _ = bench.summarize(w, r, 200)
+    assert s["warm_median_min_ms"] == {"fwd": [0.024, 0.02], "bwd": [0.074, 0.07]}
+    c = s["cold_cache"]
+    assert (c["fwd_ms_median"], c["bwd_ms_min"], c["reps"]) == (0.03, 0.088, 10)
+    assert "1024 MiB" in c["how"]
+    assert abs(s["tokens_per_s"] - w.B * w.T * 200 / 0.02) < 1e-3
+    # a run without the cold leg (profiled runs) reports none
+    r["cold"] = None
+    s, _ = bench.summarize(w, r, 200)
+    assert "cold_cache" not in s
+
+
+def test_median():
+    assert bench.median([3.0, 1.0, 2.0]) == 2.0
+    assert bench.median([4.0, 1.0, 2.0, 3.0]) == 2.5
