@@ -137,10 +137,13 @@ sa_status sa_build_graph(int64_t T, int64_t window, const int64_t* offsets, int3
  * (sa_graph_upload).  Integer only, bit-exact. */
 sa_status sa_build_graph_csr(int64_t T, const int64_t* row_ptr, const int64_t* cols, sa_graph** out);
 
-/* *kind receives the graph's sa_graph_type. */
+/* *kind receives the graph's sa_graph_type (the window-and-distances graph of
+ * SpatialLM-Mini's "How tokens choose whom to listen to", or the general
+ * mask-as-edges lists of arXiv 2502.01659's abstract). */
 sa_status sa_graph_kind(const sa_graph* g, int32_t* kind);
 
-/* Device bytes an explicit-list graph's lists occupy once uploaded:
+/* Library plumbing (no source passage): device bytes an explicit-list
+ * graph's lists occupy once uploaded:
  * 2 * (align256(4 (T + 1)) + align256(4 E)) -- forward and reverse lists, int32.
  * 0 for a distance graph. */
 sa_status sa_graph_device_bytes(const sa_graph* g, size_t* bytes);
@@ -151,13 +154,21 @@ sa_status sa_graph_device_bytes(const sa_graph* g, size_t* bytes);
  * returns when the copy has completed.  From then on sa_fwd, sa_bwd and
  * sa_decode read the lists there: the caller keeps the buffer allocated and
  * unmodified while the graph is used and frees it after the last call that
- * uses it has finished.  Uploading again (e.g. to a new buffer) replaces the
- * reference; do not do so while calls on the graph are in flight.  A distance
- * graph has nothing to upload: the call does nothing and returns SA_OK.  Bad
- * buffer or size: SA_ERR_INVALID_ARG; a failed copy: SA_ERR_HIP. */
+ * uses it has finished (and after sa_graph_free).  A graph is uploaded once:
+ * its device lists are then fixed for its lifetime (the handle stays
+ * immutable and shareable across streams), and a second upload is
+ * SA_ERR_INVALID_ARG with nothing copied; to use the same lists on another
+ * device, build a second graph.  A distance graph has nothing to upload: the
+ * call does nothing and returns SA_OK.  Bad buffer or size:
+ * SA_ERR_INVALID_ARG; a failed copy: SA_ERR_HIP (the graph stays
+ * un-uploaded).  The fixed list is the SpatialLM-Mini news page's ("How
+ * tokens choose whom to listen to": each token's admissible list is set in
+ * advance); the upload itself is library plumbing with no source passage. */
 sa_status sa_graph_upload(sa_graph* g, void* device_buf, size_t bytes, sa_stream stream);
 
-/* Normalised descriptor: T, the effective window min(W, T), the kept
+/* Normalised descriptor (the window and distances of SpatialLM-Mini's "How
+ * tokens choose whom to listen to" and MiniGPT Part 6's window predicate,
+ * with the set reading: each edge once): T, the effective window min(W, T), the kept
  * long-range distances ascending (dil may be NULL; else SA_MAX_DILATED
  * entries of room) and the edge count per (batch, head)
  *   E = W'(W'+1)/2 + W'(T-W') + sum_{d in Dil} (T - d),  W' = min(W, T).
@@ -166,7 +177,10 @@ sa_status sa_graph_upload(sa_graph* g, void* device_buf, size_t bytes, sa_stream
 sa_status sa_graph_info(const sa_graph* g, int64_t* T, int64_t* window, int32_t* n_dil,
                         int64_t* dil, int64_t* n_edges);
 
-/* CSR rows [row_begin, row_end) of the graph: row_ptr receives
+/* The neighbour lists N(i) themselves (the per-token list of SpatialLM-Mini's
+ * "How tokens choose whom to listen to"; the mask-as-edges view of arXiv
+ * 2502.01659's abstract), exported for inspection and testing.
+ * CSR rows [row_begin, row_end) of the graph: row_ptr receives
  * row_end - row_begin + 1 offsets starting at 0, cols the key indices of each
  * row in ascending order.  cols_cap is the room in cols; too little room is
  * SA_ERR_INVALID_ARG with row_ptr filled (so row_ptr[last] is the size
@@ -175,10 +189,14 @@ sa_status sa_graph_rows(const sa_graph* g, int64_t row_begin, int64_t row_end, i
                         int64_t* cols, int64_t cols_cap);
 
 /* The reverse graph in the same format: row j lists, ascending, the queries
- * i with j in N(i) (i = j + delta, delta in {0..W-1} U Dil, i < T). */
+ * i with j in N(i) (i = j + delta, delta in {0..W-1} U Dil, i < T) -- the
+ * edges the key-side backward sums over (chain rule; no passage of the pages
+ * describes a backward). */
 sa_status sa_graph_rows_reverse(const sa_graph* g, int64_t row_begin, int64_t row_end,
                                 int64_t* row_ptr, int64_t* cols, int64_t cols_cap);
 
+/* Releases a handle (NULL is a no-op).  The caller's upload buffer, if any,
+ * is not touched.  Library plumbing: no source passage. */
 void sa_graph_free(sa_graph* g);
 
 /* ------------------------------------------------------------------ attention */
@@ -217,12 +235,20 @@ sa_status sa_fwd(const sa_graph* g, const sa_attn_desc* desc, const void* q, con
                  const float* beta, void* o, float* lse, sa_stream stream);
 
 /* Bytes of device workspace sa_bwd needs for this graph and descriptor
- * (per-row Delta_i plus per-block partial sums of the coordinate-mode
- * parameter gradients). */
+ * (per-row Delta_i and lse_i * log2(e), plus per-block partial sums of the
+ * coordinate-mode parameter gradients): 2 * align256(4 B H T) +
+ * align256(8 B H ceil(T / rows_per_block)).  The quantities are those of the
+ * chain rule through sa_fwd; the pages describe no backward, so no passage
+ * defines them.  Same validation as sa_bwd's shape checks. */
 sa_status sa_bwd_workspace_size(const sa_graph* g, const sa_attn_desc* desc, size_t* bytes);
 
 /* Backward of L = sum <dout, o> through sa_fwd, given the forward's o and
- * lse:  dP_ij = <dout_i, v_j>,  Delta_i = <dout_i, o_i>,
+ * lse.  The pages train these models end to end (SpatialLM-Mini news page,
+ * "What the comparison on 8 GB showed": training throughput; MiniGPT Part 6,
+ * "Memory against context length": forward plus backward memory) but print no
+ * backward formula: what follows is the chain rule through the forward's
+ * definition above, written out.
+ *       dP_ij = <dout_i, v_j>,  Delta_i = <dout_i, o_i>,
  *       dS_ij = P_ij (dP_ij - Delta_i),  P_ij = exp(s_ij - lse_i),
  *   dot mode:   dq_i = scale sum_j dS_ij k_j,   dk_j = scale sum_i dS_ij q_i,
  *   (with H_kv < H, dk and dv of a key/value head also sum over its query heads)
@@ -265,11 +291,12 @@ sa_status sa_decode(const sa_graph* g, const sa_attn_desc* desc, const int32_t* 
 
 /* Names the kernels sa_fwd (which = 0) or sa_bwd (which = 1) would launch for
  * this graph and descriptor, as a NUL-terminated string in buf[0..cap).
- * Validates like the call itself. */
+ * Validates like the call itself.  Library introspection: no source
+ * passage. */
 sa_status sa_describe_plan(const sa_graph* g, const sa_attn_desc* desc, int32_t which, char* buf,
                            size_t cap);
 
-/* Static description of a status code. */
+/* Static description of a status code (library plumbing: no source passage). */
 const char* sa_status_str(sa_status s);
 
 #ifdef __cplusplus

@@ -12,7 +12,15 @@ must be built (``python -m sparse_causal_attention_amd.build``).
 
 Any other causal graph is given as explicit per-row key lists:
 ``sa_build_graph_csr(T, row_ptr, cols)``.  Its lists are copied into a
-device buffer (held by the Graph) on first use, or by ``Graph.upload``.
+device buffer (held by the Graph for its whole life) on first use, or by
+``Graph.upload``; a graph is uploaded once, to one device.
+
+Streams: calls run on ``stream`` (default: torch's current stream).  When
+``stream`` is another stream, it first waits for the current stream's queued
+work (which produced the inputs), and every tensor the binding allocates
+(outputs, the backward's workspace) is allocated on ``stream`` itself, so the
+caching allocator never hands that memory to other work before the kernels
+on ``stream`` are done with it.
 
 Coordinate score (-gamma_h ||c_q - c_k||^2 + beta_h): pass ``cq``, ``ck``
 ([B, H, T, 3] fp32), ``gamma``, ``beta`` ([H] fp32) instead of ``q``, ``k``.
@@ -69,8 +77,10 @@ class Graph:
         return n.value
 
     def upload(self, device, stream=None):
-        """Copies explicit lists into a device buffer this Graph keeps (no-op for
-        distance graphs or when already on `device`)."""
+        """Copies explicit lists into a device buffer this Graph keeps until it
+        is freed (no-op for distance graphs or when already on `device`).  The
+        library fixes a graph's device lists at the first upload, so a graph
+        used on one device cannot move to another: build a second graph."""
         if not self.is_csr:
             return self
         torch = _torch()
@@ -79,8 +89,11 @@ class Graph:
             raise ValueError("explicit lists are uploaded to a GPU device, got %s" % device)
         if device.index is None:
             device = torch.device("cuda", torch.cuda.current_device())
-        if self._dev is not None and self._dev.device == device:
-            return self
+        if self._dev is not None:
+            if self._dev.device == device:
+                return self
+            raise ValueError("this graph's lists are on %s; build another graph for %s"
+                             % (self._dev.device, device))
         n = self.device_bytes()
         buf = torch.empty(n + 256, dtype=torch.uint8, device=device)
         off = (-buf.data_ptr()) % 256  # the library wants 256-byte alignment
@@ -88,8 +101,18 @@ class Graph:
         with torch.cuda.device(device):
             _abi.check(_abi.lib().sa_graph_upload(self._h, ctypes.c_void_p(view.data_ptr()), n,
                                                   _stream(stream)), "sa_graph_upload")
-        self._dev = buf
+        self._dev = buf  # kept for the Graph's lifetime: the library refers to it
         return self
+
+    def _used_on(self, stream):
+        """Marks the uploaded lists as read by kernels on `stream` (when that is
+        not the current stream), so that dropping the Graph while such kernels
+        run does not release the buffer to other work."""
+        if self._dev is None or stream is None:
+            return
+        torch = _torch()
+        if stream.cuda_stream != torch.cuda.current_stream(self._dev.device).cuda_stream:
+            self._dev.record_stream(stream)
 
     def _rows(self, fn, r0, r1):
         L = _abi.lib()
@@ -187,6 +210,37 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+class _on_stream:
+    """Context for marshalling a call that will run on `stream`: if that is not
+    torch's current stream, the launch stream first waits for the current
+    stream's queued work, and tensors allocated inside the context belong to
+    the launch stream (torch.cuda.stream), so the caching allocator reuses
+    their memory only after the launch stream's kernels.  A no-op for the
+    current stream (and so under graph capture, where the captured stream is
+    the current one)."""
+
+    def __init__(self, stream, device):
+        self.stream = stream
+        self.device = device
+        self._ctx = None
+
+    def __enter__(self):
+        torch = _torch()
+        if self.stream is None:
+            return self
+        cur = torch.cuda.current_stream(self.device)
+        if self.stream.cuda_stream != cur.cuda_stream:
+            self.stream.wait_stream(cur)
+            self._ctx = torch.cuda.stream(self.stream)
+            self._ctx.__enter__()
+        return self
+
+    def __exit__(self, *exc):
+        if self._ctx is not None:
+            self._ctx.__exit__(*exc)
+        return False
+
+
 def _make_desc(ref, *, score, algo, scale, grad_dtype, q=None, k=None, v=None, o=None, dout=None,
                dq=None, dk=None, dv=None, heads=None) -> _abi.SaAttnDesc:
     """ref: a [B, H_kv, T, D] key/value-side tensor; heads: the query heads H
@@ -248,15 +302,17 @@ def _fwd_args(graph, q, k, v, cq, ck, gamma, beta, scale, o, lse, algo, stream):
     H = _query_heads(q, o, v)
     if coord:
         _coord_args(cq, ck, gamma, beta, B, H, T)
-    if o is None:
-        o = torch.empty((B, H, T, D), dtype=v.dtype, device=v.device)
-    if lse is None:
-        lse = torch.empty((B, H, T), dtype=torch.float32, device=v.device)
+    with _on_stream(stream, v.device):
+        if o is None:
+            o = torch.empty((B, H, T, D), dtype=v.dtype, device=v.device)
+        if lse is None:
+            lse = torch.empty((B, H, T), dtype=torch.float32, device=v.device)
     if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H, T) or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [B, H, T] tensor")
     d = _make_desc(v, score=mode, algo=algo, scale=scale, heads=H,
                    grad_dtype=SA_F32, q=None if coord else q, k=None if coord else k, v=v, o=o)
     graph.upload(v.device, stream)
+    graph._used_on(stream)
     args = (graph.handle, ctypes.byref(d), _ptr(None if coord else q), _ptr(None if coord else k),
             _ptr(v), _ptr(cq), _ptr(ck), _ptr(gamma), _ptr(beta), _ptr(o), _ptr(lse), _stream(stream))
     return args, (d, o, lse)
@@ -274,7 +330,9 @@ def sa_fwd_prepared(graph: Graph, q=None, k=None, v=None, *, cq=None, ck=None, g
                     beta=None, scale=None, o=None, lse=None, algo="auto", stream=None):
     """Marshals the arguments of sa_fwd once and returns a zero-argument
     callable that enqueues the same call again (same tensors, same stream).
-    For tight loops where per-call Python marshalling would dominate."""
+    For tight loops where per-call Python marshalling would dominate.  The
+    callable adds no stream synchronisation of its own: with a stream other
+    than the current one, ordering against other streams is the caller's."""
     args, keep = _fwd_args(graph, q, k, v, cq, ck, gamma, beta, scale, o, lse, algo, stream)
     fn = _abi.lib().sa_fwd
 
@@ -316,16 +374,18 @@ def _bwd_args(graph, q, k, v, o, lse, dout, cq, ck, gamma, beta, scale, grad_dty
     dev = v.device
     if coord:
         _coord_args(cq, ck, gamma, beta, B, H, T)
-        dcq = torch.empty((B, H, T, 3), dtype=torch.float32, device=dev) if dcq is None else dcq
-        dck = torch.empty((B, H, T, 3), dtype=torch.float32, device=dev) if dck is None else dck
-        dgamma = torch.empty((H,), dtype=torch.float32, device=dev) if dgamma is None else dgamma
-        dbeta = torch.empty((H,), dtype=torch.float32, device=dev) if dbeta is None else dbeta
-    elif uniform:
-        dq = dk = None
-    else:
-        dq = torch.empty((B, H, T, D), dtype=gdt, device=dev) if dq is None else dq
-        dk = torch.empty((B, Hkv, T, D), dtype=gdt, device=dev) if dk is None else dk
-    dv = torch.empty((B, Hkv, T, D), dtype=gdt, device=dev) if dv is None else dv
+    with _on_stream(stream, dev):
+        if coord:
+            dcq = torch.empty((B, H, T, 3), dtype=torch.float32, device=dev) if dcq is None else dcq
+            dck = torch.empty((B, H, T, 3), dtype=torch.float32, device=dev) if dck is None else dck
+            dgamma = torch.empty((H,), dtype=torch.float32, device=dev) if dgamma is None else dgamma
+            dbeta = torch.empty((H,), dtype=torch.float32, device=dev) if dbeta is None else dbeta
+        elif uniform:
+            dq = dk = None
+        else:
+            dq = torch.empty((B, H, T, D), dtype=gdt, device=dev) if dq is None else dq
+            dk = torch.empty((B, Hkv, T, D), dtype=gdt, device=dev) if dk is None else dk
+        dv = torch.empty((B, Hkv, T, D), dtype=gdt, device=dev) if dv is None else dv
     for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
         if t is not None and t.dtype != gdt:
             raise ValueError("%s must have the gradient dtype %s" % (name, gdt))
@@ -337,8 +397,10 @@ def _bwd_args(graph, q, k, v, o, lse, dout, cq, ck, gamma, beta, scale, grad_dty
     _abi.check(L.sa_bwd_workspace_size(graph.handle, ctypes.byref(d), ctypes.byref(n)),
                "sa_bwd_workspace_size")
     if workspace is None:
-        workspace = torch.empty(max(n.value, 256), dtype=torch.uint8, device=dev)
+        with _on_stream(stream, dev):  # freed after the call, on the stream that used it
+            workspace = torch.empty(max(n.value, 256), dtype=torch.uint8, device=dev)
     graph.upload(dev, stream)
+    graph._used_on(stream)
     args = (graph.handle, ctypes.byref(d), _ptr(None if coord else q), _ptr(None if coord else k),
             _ptr(v), _ptr(cq), _ptr(ck), _ptr(gamma), _ptr(beta), _ptr(o), _ptr(lse), _ptr(dout),
             _ptr(None if coord else dq), _ptr(None if coord else dk), _ptr(dv),
@@ -398,10 +460,11 @@ def _decode_args(graph, q, k, v, positions, cq, ck, gamma, beta, scale, o, lse, 
     if positions is not None and (positions.dtype != torch.int32 or tuple(positions.shape) != (B,)
                                   or not positions.is_contiguous()):
         raise ValueError("positions must be a contiguous int32 [B] tensor")
-    if o is None:
-        o = torch.empty((B, H, D), dtype=v.dtype, device=v.device)
-    if lse is None:
-        lse = torch.empty((B, H), dtype=torch.float32, device=v.device)
+    with _on_stream(stream, v.device):
+        if o is None:
+            o = torch.empty((B, H, D), dtype=v.dtype, device=v.device)
+        if lse is None:
+            lse = torch.empty((B, H), dtype=torch.float32, device=v.device)
     if lse.dtype != torch.float32 or tuple(lse.shape) != (B, H) or not lse.is_contiguous():
         raise ValueError("lse must be a contiguous float32 [B, H] tensor")
     d = _make_desc(v, score=mode, algo="auto", scale=scale, grad_dtype=SA_F32, heads=H,
@@ -413,6 +476,7 @@ def _decode_args(graph, q, k, v, positions, cq, ck, gamma, beta, scale, o, lse, 
             raise ValueError("%s must be [B, H, D] with a contiguous last dimension" % name)
         getattr(d, "stride_" + name)[:] = (int(t.stride(0)), int(t.stride(1)), 0)
     graph.upload(v.device, stream)
+    graph._used_on(stream)
     args = (graph.handle, ctypes.byref(d), _ptr(positions), _ptr(q if mode == SA_SCORE_DOT else None),
             _ptr(k if mode == SA_SCORE_DOT else None), _ptr(v), _ptr(cq), _ptr(ck), _ptr(gamma), _ptr(beta),
             _ptr(o), _ptr(lse), _stream(stream))

@@ -42,6 +42,29 @@ bool offsets_fit(const sa_attn_desc* d, const int64_t st[3]) {
   return last < 9.0e18;
 }
 
+// Output rows must not overlap (a zero or too-small stride would let several
+// workgroups store the same row, in no fixed order).  Sufficient test: with
+// the dimensions of extent above 1 ordered by stride, each stride covers the
+// span of everything inside it, starting from the D contiguous elements of a
+// row.  Called after offsets_fit, so no product below overflows.
+bool rows_disjoint(int64_t n0, int64_t n1, int64_t n2, const int64_t st[3], int64_t D) {
+  int64_t n[3] = {n0, n1, n2}, s[3] = {st[0], st[1], st[2]};
+  for (int a = 0; a < 3; ++a)  // order by stride (three elements)
+    for (int b = a + 1; b < 3; ++b)
+      if (s[b] < s[a]) {
+        const int64_t tn = n[a], ts = s[a];
+        n[a] = n[b]; s[a] = s[b];
+        n[b] = tn; s[b] = ts;
+      }
+  int64_t span = D;
+  for (int a = 0; a < 3; ++a) {
+    if (n[a] <= 1) continue;
+    if (s[a] < span) return false;
+    span += s[a] * (n[a] - 1);
+  }
+  return true;
+}
+
 enum class Path { Gather, Band, Csr };
 
 // The band backward loads its tiles through buffer resources over one (batch,
@@ -77,8 +100,9 @@ sa_status check_common(const sa_graph* g, const sa_attn_desc* d, const void* q, 
   if (d->D != 16 && d->D != 32 && d->D != 64 && d->D != 128) return SA_ERR_UNSUPPORTED;
   if (d->B * d->H > (int64_t)1 << 24) return SA_ERR_UNSUPPORTED;
   if (const sa_status hs = check_heads(d); hs != SA_OK) return hs;
-  // blocks of the smallest row tile must be countable in int32
-  if ((double)d->B * d->H * (double)d->T > 1.0e12) return SA_ERR_UNSUPPORTED;
+  // workgroups of the smallest row tile (8 rows: fp32, D = 128), plus the
+  // XCD padding of the grid, must be countable in int32
+  if (d->B * d->H * ((d->T + 7) / 8) > ((int64_t)1 << 31) - 64) return SA_ERR_UNSUPPORTED;
   const int es = esize(d->dtype);
   if (v == nullptr || !aligned_rows(v, d->stride_v, es) || !offsets_fit(d, d->stride_v))
     return SA_ERR_INVALID_ARG;
@@ -163,7 +187,8 @@ extern "C" sa_status sa_fwd(const sa_graph* g, const sa_attn_desc* d, const void
   sa_status st = check_common(g, d, q, k, v, cq, ck, gamma, beta, &plan);
   if (st != SA_OK) return st;
   if (o == nullptr || lse == nullptr || !lists_ready(g)) return SA_ERR_INVALID_ARG;
-  if (!aligned_rows(o, d->stride_o, esize(d->dtype)) || !offsets_fit(d, d->stride_o))
+  if (!aligned_rows(o, d->stride_o, esize(d->dtype)) || !offsets_fit(d, d->stride_o) ||
+      !rows_disjoint(d->B, d->H, d->T, d->stride_o, d->D))
     return SA_ERR_INVALID_ARG;
   sa::Params p;
   fill_common(&p, g, d);
@@ -226,17 +251,18 @@ extern "C" sa_status sa_bwd(const sa_graph* g, const sa_attn_desc* d, const void
   if (!aligned_rows(o, d->stride_o, es) || !aligned_rows(dout, d->stride_do, es))
     return SA_ERR_INVALID_ARG;
   if (!offsets_fit(d, d->stride_o) || !offsets_fit(d, d->stride_do)) return SA_ERR_INVALID_ARG;
-  // gradient rows: 16-byte aligned starts, like the inputs
-  auto grad_ok = [&](const void* ptr, const int64_t s[3]) {
+  // gradient rows: 16-byte aligned starts, like the inputs, and disjoint
+  auto grad_ok = [&](const void* ptr, const int64_t s[3], int64_t heads) {
     if ((reinterpret_cast<uintptr_t>(ptr) & 15u) != 0) return false;
     for (int c = 0; c < 3; ++c)
       if (s[c] < 0 || (s[c] * gs) % 16 != 0) return false;
-    return offsets_fit(d, s);
+    return offsets_fit(d, s) && rows_disjoint(d->B, heads, d->T, s, d->D);
   };
-  if (!grad_ok(dv, d->stride_dv)) return SA_ERR_INVALID_ARG;
+  const int64_t hkv = kv_heads(d);
+  if (!grad_ok(dv, d->stride_dv, hkv)) return SA_ERR_INVALID_ARG;
   if (d->score == SA_SCORE_DOT) {
     if (dq == nullptr || dk == nullptr) return SA_ERR_INVALID_ARG;
-    if (!grad_ok(dq, d->stride_dq) || !grad_ok(dk, d->stride_dk)) return SA_ERR_INVALID_ARG;
+    if (!grad_ok(dq, d->stride_dq, d->H) || !grad_ok(dk, d->stride_dk, hkv)) return SA_ERR_INVALID_ARG;
   } else if (coord) {
     if (dcq == nullptr || dck == nullptr || dgamma == nullptr || dbeta == nullptr)
       return SA_ERR_INVALID_ARG;
@@ -299,7 +325,8 @@ extern "C" sa_status sa_decode(const sa_graph* g, const sa_attn_desc* d, const i
     if (cq == nullptr || ck == nullptr || gamma == nullptr || beta == nullptr) return SA_ERR_INVALID_ARG;
   }
   if (o == nullptr || lse == nullptr || !lists_ready(g)) return SA_ERR_INVALID_ARG;
-  if (!aligned_rows(o, o_row, es) || !offsets_fit(d, o_row)) return SA_ERR_INVALID_ARG;
+  if (!aligned_rows(o, o_row, es) || !offsets_fit(d, o_row) || !rows_disjoint(d->B, d->H, 1, o_row, d->D))
+    return SA_ERR_INVALID_ARG;
   sa::Params p;
   fill_common(&p, g, d);
   p.q = q; SET_STRIDES(sq, d->stride_q);

@@ -132,6 +132,9 @@ extern "C" sa_status sa_graph_upload(sa_graph* g, void* device_buf, size_t bytes
   if (device_buf == nullptr || (reinterpret_cast<uintptr_t>(device_buf) & 255u) != 0 ||
       bytes < 2 * (pb + cb))
     return SA_ERR_INVALID_ARG;
+  // the device lists are fixed once uploaded: calls in flight on another
+  // stream may be reading them, so the handle is never re-pointed
+  if (g->d_rp != nullptr) return SA_ERR_INVALID_ARG;
   char* base = static_cast<char*>(device_buf);
   int32_t* d_rp = reinterpret_cast<int32_t*>(base);
   int32_t* d_cols = reinterpret_cast<int32_t*>(base + pb);

@@ -277,3 +277,134 @@ def test_explicit_lists_need_an_upload_and_pick_indexed_kernels():
     kind = ctypes.c_int32(-1)
     assert L.sa_graph_kind(g.handle, ctypes.byref(kind)) == E.SA_OK and kind.value == E.SA_GRAPH_CSR
     assert L.sa_graph_kind(None, ctypes.byref(kind)) == E.SA_ERR_INVALID_ARG
+
+
+def test_overlapping_outputs_are_rejected(g64):
+    """Output rows must be disjoint: a zero or too-small stride would let
+    several workgroups store the same row in no fixed order.  Inputs may
+    alias (broadcast k, v over heads with a zero head stride, say)."""
+    E = _abi
+    d = desc()
+    d.stride_o[2] = 0  # every t of a head on one row
+    assert fwd(g64, d) == E.SA_ERR_INVALID_ARG
+    d = desc()
+    d.stride_o[1] = 0  # both heads on the same rows
+    assert fwd(g64, d) == E.SA_ERR_INVALID_ARG
+    d = desc()
+    d.stride_o[2] = 16  # rows of 32 elements 16 apart: overlap
+    assert fwd(g64, d) == E.SA_ERR_INVALID_ARG
+    d = desc()
+    d.stride_k[1] = 0  # an input broadcast over heads is fine: the call gets past
+    d.stride_o[2] = 0  # ... the inputs and fails on the output
+    assert fwd(g64, d) == E.SA_ERR_INVALID_ARG
+    for name in ("dq", "dk", "dv"):
+        d = desc()
+        getattr(d, "stride_" + name)[2] = 0
+        assert bwd(g64, d) == E.SA_ERR_INVALID_ARG, name
+        d = desc()
+        getattr(d, "stride_" + name)[1] = 8  # heads overlapping within a row
+        assert bwd(g64, d) == E.SA_ERR_INVALID_ARG, name
+        # disjoint layouts pass the gradient checks and reach the workspace check
+        d = desc()
+        getattr(d, "stride_" + name)[:] = (2 * 64 * 32, 32, 2 * 32)  # [B, T, H, D] storage
+        assert bwd(g64, d, ws=None) == E.SA_ERR_WORKSPACE, name
+        d = desc(B=1)
+        getattr(d, "stride_" + name)[0] = 0  # an extent-1 dimension may have any stride
+        assert bwd(g64, d, ws=None) == E.SA_ERR_WORKSPACE, name
+
+
+def test_grid_must_fit_int32():
+    """Workgroup counts are int32: B * H * ceil(T / 8) must stay below 2^31."""
+    E = _abi
+    T = 1 << 30
+    g = sa_build_graph(T, 4, [])
+    d = desc(B=1, H=16, T=T)
+    assert fwd(g, d) == E.SA_ERR_UNSUPPORTED  # 16 * 2^27 = 2^31 workgroups
+    d = desc(B=1, H=8, T=T)  # 2^30: fits, so the check passes and a later one fails
+    assert fwd(g, d, lse=None) == E.SA_ERR_INVALID_ARG
+
+
+def test_second_upload_is_refused_by_the_binding():
+    """A graph's device lists are fixed at its first upload: the binding
+    refuses to move an uploaded graph to another device (the library refuses a
+    second sa_graph_upload; that half runs in the GPU tests)."""
+    import torch
+
+    from sparse_causal_attention_amd import sa_build_graph_csr
+
+    g = sa_build_graph_csr(3, [0, 1, 2, 3], [0, 1, 2])
+
+    class FakeBuf:  # stands in for the uploaded buffer on cuda:0
+        device = torch.device("cuda", 0)
+
+    g._dev = FakeBuf()
+    assert g.upload("cuda:0") is g  # already there: nothing to do
+    with pytest.raises(ValueError, match="build another graph"):
+        g.upload("cuda:1")
+    with pytest.raises(ValueError):
+        g.upload("cpu")
+    g._dev = None
+
+
+def test_side_stream_marshalling(monkeypatch):
+    """With stream= another stream than torch's current one, the launch stream
+    waits for the current stream and the binding's allocations happen on the
+    launch stream (so the caching allocator does not hand the memory to
+    other work before those kernels finish); with the current stream nothing
+    extra happens.  torch.cuda is replaced by fakes: no GPU is needed."""
+    import torch
+
+    import sparse_causal_attention_amd as pkg
+
+    log = []
+
+    class FakeStream:
+        def __init__(self, h):
+            self.cuda_stream = h
+
+        def wait_stream(self, other):
+            log.append(("wait", self.cuda_stream, other.cuda_stream))
+
+    current = FakeStream(1)
+
+    class FakeCtx:
+        def __init__(self, s):
+            self.s = s
+
+        def __enter__(self):
+            log.append(("enter", self.s.cuda_stream))
+
+        def __exit__(self, *a):
+            log.append(("exit", self.s.cuda_stream))
+
+    monkeypatch.setattr(torch.cuda, "current_stream", lambda device=None: current)
+    monkeypatch.setattr(torch.cuda, "stream", lambda s: FakeCtx(s))
+    with pkg._on_stream(FakeStream(1), None):
+        log.append("alloc")
+    assert log == ["alloc"]
+    log.clear()
+    with pkg._on_stream(None, None):
+        log.append("alloc")
+    assert log == ["alloc"]
+    log.clear()
+    with pkg._on_stream(FakeStream(7), None):
+        log.append("alloc")
+    assert log == [("wait", 7, 1), ("enter", 7), "alloc", ("exit", 7)]
+
+    # the uploaded lists of an explicit-list graph are recorded on the side stream
+    recorded = []
+
+    class FakeBuf:
+        device = None
+
+        def record_stream(self, s):
+            recorded.append(s.cuda_stream)
+
+    g = pkg.sa_build_graph_csr(2, [0, 1, 2], [0, 1])
+    g._dev = FakeBuf()
+    g._used_on(FakeStream(1))
+    g._used_on(None)
+    assert recorded == []
+    g._used_on(FakeStream(9))
+    assert recorded == [9]
+    g._dev = None

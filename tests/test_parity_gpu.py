@@ -4,6 +4,10 @@ Tolerances (max-abs over every output element): 1e-4 for fp32 inputs and
 2e-2 for bf16 inputs with fp32 accumulation.  The per-head coordinate-score
 parameter gradients (sums over up to 8M edges) use
 |err| <= max(tol, 1e-6 * sum_edges |dS| (1 + ||c_q - c_k||^2)).
+Gradients requested in bf16 are rounded once more, to nearest even, after
+the fp32 computation: each element may differ from the oracle by the tolerance
+plus half a bf16 unit in the last place at the magnitude the fp32 result can
+have, |g| + tol (see bf16_stored_excess).
 """
 import sys
 
@@ -43,6 +47,34 @@ def maxabs(t, ref):
     return float(np.max(np.abs(t.detach().double().cpu().numpy() - ref))) if ref.size else 0.0
 
 
+def bf16_half_ulp(x):
+    """Half a bf16 unit in the last place at magnitude |x| (8 significant
+    bits: for |x| in [2^e, 2^(e+1)) the unit is 2^(e-7)); 0 at 0."""
+    ax = np.abs(np.asarray(x, dtype=np.float64))
+    _, e = np.frexp(ax)  # ax = f * 2^e with f in [0.5, 1): binade 2^(e-1)
+    return np.where(ax > 0, np.ldexp(1.0, e - 9), 0.0)
+
+
+def bf16_stored_excess(t, ref, tol):
+    """Largest error of a bf16-stored result beyond its final rounding: the
+    kernel computes g in fp32 within tol of the oracle's value ref, then
+    stores RNE(g), which moves it by at most half a bf16 ulp of |g| <= |ref| + tol.
+    Returns max(|t - ref| - half_ulp(|ref| + tol)), to be compared with tol."""
+    if not ref.size:
+        return 0.0
+    err = np.abs(t.detach().double().cpu().numpy() - ref)
+    return float(np.max(err - bf16_half_ulp(np.abs(ref) + tol)))
+
+
+def grad_err(t, ref, tol, grad_dtype):
+    """Max-abs error of a gradient; for bf16-stored gradients, the error
+    beyond the final rounding (bf16_stored_excess)."""
+    if grad_dtype == torch.bfloat16:
+        assert t.dtype == torch.bfloat16
+        return bf16_stored_excess(t, ref, tol)
+    return maxabs(t, ref)
+
+
 def run_and_compare(w: Workload, algo="auto", backward=True, grad_dtype=None, **shape):
     x = make_inputs(w, device="cpu", backward=backward, **shape)
     B, H, T, D = x["v"].shape
@@ -77,7 +109,7 @@ def run_and_compare(w: Workload, algo="auto", backward=True, grad_dtype=None, **
                                 gamma=hv["gamma"], beta=hv["beta"])
             torch.cuda.synchronize()
             for key in ("dv", "dcq", "dck"):
-                errs[key] = maxabs(gr[key], ref[key])
+                errs[key] = grad_err(gr[key], ref[key], tol, grad_dtype if key == "dv" else None)
             for key in ("dgamma", "dbeta"):
                 err = np.abs(gr[key].double().cpu().numpy() - ref[key])
                 bound = np.maximum(tol, 1e-6 * ref["l1"])
@@ -87,17 +119,18 @@ def run_and_compare(w: Workload, algo="auto", backward=True, grad_dtype=None, **
             ref = oracle.bwd_bh(w.window, w.offsets, hv["v"], hv["do"])
             torch.cuda.synchronize()
             assert sorted(gr) == ["dv"]
-            errs["dv"] = maxabs(gr["dv"], ref["dv"])
+            errs["dv"] = grad_err(gr["dv"], ref["dv"], tol, grad_dtype)
         else:
             gr = sa_bwd(g, xd["q"], xd["k"], xd["v"], o, lse, xd["do"], algo=algo, grad_dtype=grad_dtype)
             ref = oracle.bwd_bh(w.window, w.offsets, hv["v"], hv["do"], q=hv["q"], k=hv["k"])
             torch.cuda.synchronize()
             for key in ("dq", "dk", "dv"):
-                errs[key] = maxabs(gr[key], ref[key])
-    _say("%s errors %s (tol %g)" % (w.name, {k: "%.2e" % v for k, v in errs.items()}, tol))
-    gtol = tol if grad_dtype in (None, torch.float32) else max(tol, 5e-2)
+                errs[key] = grad_err(gr[key], ref[key], tol, grad_dtype)
+    _say("%s errors %s (tol %g%s)" % (w.name, {k: "%.2e" % v for k, v in errs.items()}, tol,
+                                      ", gradient errors beyond their bf16 rounding"
+                                      if grad_dtype == torch.bfloat16 else ""))
     for key, e in errs.items():
-        assert e <= (tol if key in ("o", "lse") else gtol), (w.name, key, e)
+        assert e <= tol, (w.name, key, e)
     return o, lse
 
 
@@ -533,11 +566,10 @@ def run_csr(rp, cols, B, H, Hkv, D, dt, score, seed, grad_dtype=None):
             err = np.abs(gr[key].double().cpu().numpy() - ref[key])
             errs[key] = float(np.max(err / np.maximum(tol, 1e-6 * ref["l1"]))) * tol
         else:
-            errs[key] = maxabs(gr[key], ref[key])
+            errs[key] = grad_err(gr[key], ref[key], tol, grad_dtype if key in ("dq", "dk", "dv") else None)
     _say("csr errors %s (tol %g)" % ({k_: "%.2e" % e for k_, e in errs.items()}, tol))
-    gtol = tol if grad_dtype in (None, torch.float32) else max(tol, 5e-2)
     for key, e in errs.items():
-        assert e <= (tol if key in ("o", "lse") else gtol), (key, e)
+        assert e <= tol, (key, e)
     return g, xd, o, lse, gr
 
 
@@ -698,10 +730,10 @@ def test_explicit_lists_edge_cases():
     hv = {k_: host_view(t.transpose(1, 2).contiguous()) for k_, t in base.items()}
     O, L, ref = csr_reference(rp, cols, 1, hv["v"], hv["do"], q=hv["q"], k=hv["k"])
     errs = {"o": maxabs(o, O), "lse": maxabs(lse, L)}
-    errs.update({k_: maxabs(gr[k_], ref[k_]) for k_ in ("dq", "dk", "dv")})
-    _say("csr strided / bf16 gradients errors %s" % {k_: "%.2e" % e for k_, e in errs.items()})
-    assert errs["o"] <= 2e-2 and errs["lse"] <= 2e-2
-    assert all(errs[k_] <= 5e-2 for k_ in ("dq", "dk", "dv")), errs
+    errs.update({k_: grad_err(gr[k_], ref[k_], 2e-2, torch.bfloat16) for k_ in ("dq", "dk", "dv")})
+    _say("csr strided / bf16 gradients errors %s (gradients: beyond their bf16 rounding)"
+         % {k_: "%.2e" % e for k_, e in errs.items()})
+    assert all(e <= 2e-2 for e in errs.values()), errs
 
 
 @pytest.mark.parametrize("kind", ["band", "dilated", "lists"])
@@ -748,3 +780,42 @@ def test_graph_capture_replays_match_eager(kind):
 def sa_bwd_workspace_size_of(g, v):
     from sparse_causal_attention_amd import sa_bwd_workspace_size
     return sa_bwd_workspace_size(g, v)
+
+
+def test_side_stream_and_fixed_upload():
+    """Calls on a stream other than torch's current one give the same bits as
+    on the current stream (the binding makes the launch stream wait for the
+    current one and allocates outputs and workspace on it), and an explicit-list
+    graph's device lists are fixed by its first upload: the library refuses a
+    second sa_graph_upload, with nothing copied."""
+    import ctypes
+
+    from sparse_causal_attention_amd import _abi
+
+    B, H, T, D = 1, 2, 700, 64
+    rp, cols = random_causal_lists(T, 4, 12, 4242)
+    for g in (sa_build_graph(T, 64, (128, 256)), sa_build_graph_csr(T, rp, cols)):
+        gen = torch.Generator().manual_seed(31337)
+        x = {k_: torch.randn((B, H, T, D), generator=gen).to(torch.bfloat16).to(DEV)
+             for k_ in ("q", "k", "v", "do")}
+        o, lse = sa_fwd(g, x["q"], x["k"], x["v"])
+        gr = sa_bwd(g, x["q"], x["k"], x["v"], o, lse, x["do"])
+        torch.cuda.synchronize()
+        s = torch.cuda.Stream()
+        # inputs produced on the current stream just before the side-stream call
+        xs = {k_: t * 1 for k_, t in x.items()}
+        o2, lse2 = sa_fwd(g, xs["q"], xs["k"], xs["v"], stream=s)
+        gr2 = sa_bwd(g, xs["q"], xs["k"], xs["v"], o2, lse2, xs["do"], stream=s)
+        s.synchronize()
+        assert torch.equal(o, o2) and torch.equal(lse, lse2)
+        assert all(torch.equal(gr[k_], gr2[k_]) for k_ in gr)
+        if g.is_csr:
+            n = g.device_bytes()
+            other = torch.empty(n + 256, dtype=torch.uint8, device=DEV)
+            ptr = other.data_ptr() + (-other.data_ptr()) % 256
+            st = _abi.lib().sa_graph_upload(g.handle, ctypes.c_void_p(ptr), n, None)
+            assert st == _abi.SA_ERR_INVALID_ARG
+            o3, _ = sa_fwd(g, x["q"], x["k"], x["v"])  # still reads the first upload
+            torch.cuda.synchronize()
+            assert torch.equal(o3, o)
+    _say("side stream: bitwise equal to the current stream; second upload refused")
