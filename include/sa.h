@@ -269,6 +269,30 @@ sa_status sa_bwd(const sa_graph* g, const sa_attn_desc* desc, const void* q, con
                  void* dk, void* dv, float* dcq, float* dck, float* dgamma, float* dbeta,
                  void* workspace, size_t workspace_bytes, sa_stream stream);
 
+/* Bytes of the built-in device scratch sa_bwd_noalloc uses in place of a
+ * workspace (16 MiB: enough for B * H * T up to about two million rows). */
+#define SA_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/* sa_bwd without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  Same arguments, results (bitwise: the same
+ * kernels), validation and status rules as sa_bwd, except that the workspace
+ * is a static device array of SA_NOALLOC_SCRATCH_BYTES inside the library:
+ * each GPU the library runs on holds one copy until the process ends, found on
+ * the first call on that device.  A shape whose workspace
+ * (sa_bwd_workspace_size) exceeds SA_NOALLOC_SCRATCH_BYTES is
+ * SA_ERR_WORKSPACE; use sa_bwd with a workspace of your own instead.  The
+ * call allocates nothing and clears nothing (no part of the scratch needs to
+ * start at zero).  Every call on one GPU shares that GPU's scratch: calls that
+ * overlap on one GPU (on different streams, or from several threads) race and
+ * corrupt each other's gradients -- order them on one stream.  A failed
+ * lookup of the scratch is SA_ERR_HIP. */
+sa_status sa_bwd_noalloc(const sa_graph* g, const sa_attn_desc* desc, const void* q, const void* k,
+                         const void* v, const float* cq, const float* ck, const float* gamma,
+                         const float* beta, const void* o, const float* lse, const void* dout,
+                         void* dq, void* dk, void* dv, float* dcq, float* dck, float* dgamma,
+                         float* dbeta, sa_stream stream);
+
 /* Decode step with a key/value cache: for every (b, h), the one new token at
  * row t_b = positions[b] of the cache attends to its neighbour list N(t_b)
  * (the window t_b .. t_b - W + 1 and t_b - d for the long-range distances

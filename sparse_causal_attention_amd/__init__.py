@@ -38,8 +38,8 @@ from ._abi import (SA_ALGO_AUTO, SA_ALGO_BAND, SA_ALGO_GATHER, SA_BF16, SA_F32, 
                    SA_GRAPH_DISTANCE, SA_MAX_DILATED, SA_SCORE_COORD, SA_SCORE_DOT, SA_SCORE_UNIFORM,
                    SaError)
 
-__all__ = ["sa_build_graph", "sa_build_graph_csr", "sa_fwd", "sa_bwd", "sa_decode", "sa_decode_prepared", "sa_fwd_prepared",
-           "sa_bwd_prepared",
+__all__ = ["sa_build_graph", "sa_build_graph_csr", "sa_fwd", "sa_bwd", "sa_bwd_noalloc", "sa_decode",
+           "sa_decode_prepared", "sa_fwd_prepared", "sa_bwd_prepared",
            "sa_bwd_workspace_size", "sa_describe_plan", "Graph", "SaError"]
 
 _ALGOS = {"auto": SA_ALGO_AUTO, "gather": SA_ALGO_GATHER, "band": SA_ALGO_BAND}
@@ -360,6 +360,9 @@ def _dtype_code_of(dt) -> int:
     return {torch.float32: SA_F32, torch.bfloat16: SA_BF16}[dt]
 
 
+_NO_WORKSPACE = object()  # marks a backward marshalled for sa_bwd_noalloc
+
+
 def _bwd_args(graph, q, k, v, o, lse, dout, cq, ck, gamma, beta, scale, grad_dtype, dq, dk, dv,
               dcq, dck, dgamma, dbeta, workspace, algo, stream):
     torch = _torch()
@@ -396,9 +399,14 @@ def _bwd_args(graph, q, k, v, o, lse, dout, cq, ck, gamma, beta, scale, grad_dty
     n = ctypes.c_size_t()
     _abi.check(L.sa_bwd_workspace_size(graph.handle, ctypes.byref(d), ctypes.byref(n)),
                "sa_bwd_workspace_size")
-    if workspace is None:
-        with _on_stream(stream, dev):  # freed after the call, on the stream that used it
-            workspace = torch.empty(max(n.value, 256), dtype=torch.uint8, device=dev)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is _NO_WORKSPACE:  # the allocation-free entry point brings its own
+        workspace = None
+    else:
+        if workspace is None:
+            with _on_stream(stream, dev):  # freed after the call, on the stream that used it
+                workspace = torch.empty(max(n.value, 256), dtype=torch.uint8, device=dev)
+        ws_ptr, ws_bytes = _ptr(workspace), workspace.numel() * workspace.element_size()
     graph.upload(dev, stream)
     graph._used_on(stream)
     args = (graph.handle, ctypes.byref(d), _ptr(None if coord else q), _ptr(None if coord else k),
@@ -406,7 +414,7 @@ def _bwd_args(graph, q, k, v, o, lse, dout, cq, ck, gamma, beta, scale, grad_dty
             _ptr(None if coord else dq), _ptr(None if coord else dk), _ptr(dv),
             _ptr(dcq if coord else None), _ptr(dck if coord else None),
             _ptr(dgamma if coord else None), _ptr(dbeta if coord else None),
-            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+            ws_ptr, ws_bytes, _stream(stream))
     if coord:
         out = {"dv": dv, "dcq": dcq, "dck": dck, "dgamma": dgamma, "dbeta": dbeta}
     elif uniform:
@@ -426,6 +434,21 @@ def sa_bwd(graph: Graph, q=None, k=None, v=None, o=None, lse=None, dout=None, *,
                                      grad_dtype, dq, dk, dv, dcq, dck, dgamma, dbeta, workspace,
                                      algo, stream)
     _abi.check(_abi.lib().sa_bwd(*args), "sa_bwd")
+    return out
+
+
+def sa_bwd_noalloc(graph: Graph, q=None, k=None, v=None, o=None, lse=None, dout=None, *, cq=None, ck=None,
+                   gamma=None, beta=None, scale=None, grad_dtype=None, dq=None, dk=None, dv=None,
+                   dcq=None, dck=None, dgamma=None, dbeta=None, algo="auto", stream=None):
+    """sa_bwd through the library's allocation-free entry point: the workspace
+    is the library's built-in device scratch (SA_NOALLOC_SCRATCH_BYTES per GPU),
+    so with every output given (dq, dk, dv, or the coordinate-mode ones) the
+    call allocates no device memory.  Calls that overlap on one GPU share that
+    scratch and race: keep them on one stream."""
+    args, (_d, _ws, out) = _bwd_args(graph, q, k, v, o, lse, dout, cq, ck, gamma, beta, scale,
+                                     grad_dtype, dq, dk, dv, dcq, dck, dgamma, dbeta, _NO_WORKSPACE,
+                                     algo, stream)
+    _abi.check(_abi.lib().sa_bwd_noalloc(*(args[:19] + args[21:])), "sa_bwd_noalloc")
     return out
 
 

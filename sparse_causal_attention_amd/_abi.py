@@ -18,6 +18,7 @@ SA_SCORE_DOT, SA_SCORE_COORD, SA_SCORE_UNIFORM = 0, 1, 2
 SA_ALGO_AUTO, SA_ALGO_GATHER, SA_ALGO_BAND = 0, 1, 2
 SA_GRAPH_DISTANCE, SA_GRAPH_CSR = 0, 1
 SA_MAX_DILATED = 64
+SA_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 i64 = ctypes.c_int64
 i32 = ctypes.c_int32
@@ -39,7 +40,8 @@ class SaAttnDesc(ctypes.Structure):
 EXPORTED = (
     "sa_build_graph", "sa_build_graph_csr", "sa_graph_kind", "sa_graph_device_bytes", "sa_graph_upload",
     "sa_graph_info", "sa_graph_rows", "sa_graph_rows_reverse", "sa_graph_free",
-    "sa_fwd", "sa_bwd_workspace_size", "sa_bwd", "sa_decode", "sa_describe_plan", "sa_status_str",
+    "sa_fwd", "sa_bwd_workspace_size", "sa_bwd", "sa_bwd_noalloc", "sa_decode", "sa_describe_plan",
+    "sa_status_str",
 )
 
 _lib = None
@@ -85,6 +87,8 @@ def lib():
     L.sa_bwd_workspace_size.argtypes = [vp, ctypes.POINTER(SaAttnDesc), ctypes.POINTER(ctypes.c_size_t)]
     L.sa_bwd.restype = i32
     L.sa_bwd.argtypes = [vp, ctypes.POINTER(SaAttnDesc)] + [vp] * 17 + [vp, ctypes.c_size_t, vp]
+    L.sa_bwd_noalloc.restype = i32
+    L.sa_bwd_noalloc.argtypes = [vp, ctypes.POINTER(SaAttnDesc)] + [vp] * 17 + [vp]
     L.sa_decode.restype = i32
     L.sa_decode.argtypes = [vp, ctypes.POINTER(SaAttnDesc)] + [vp] * 11
     L.sa_describe_plan.restype = i32

@@ -231,18 +231,20 @@ extern "C" sa_status sa_bwd_workspace_size(const sa_graph* g, const sa_attn_desc
   return SA_OK;
 }
 
-extern "C" sa_status sa_bwd(const sa_graph* g, const sa_attn_desc* d, const void* q, const void* k,
-                            const void* v, const float* cq, const float* ck, const float* gamma,
-                            const float* beta, const void* o, const float* lse, const void* dout,
-                            void* dq, void* dk, void* dv, float* dcq, float* dck, float* dgamma,
-                            float* dbeta, void* workspace, size_t workspace_bytes,
-                            sa_stream stream) {
-  Plan plan;
-  sa_status st = check_common(g, d, q, k, v, cq, ck, gamma, beta, &plan);
+namespace {
+
+// Everything sa_bwd checks except the workspace: the graph, shapes, dtypes,
+// pointers and strides of inputs and outputs.  Chooses the kernel path.
+sa_status bwd_validate(const sa_graph* g, const sa_attn_desc* d, const void* q, const void* k,
+                       const void* v, const float* cq, const float* ck, const float* gamma,
+                       const float* beta, const void* o, const float* lse, const void* dout, void* dq,
+                       void* dk, void* dv, float* dcq, float* dck, float* dgamma, float* dbeta,
+                       Plan* plan) {
+  sa_status st = check_common(g, d, q, k, v, cq, ck, gamma, beta, plan);
   if (st != SA_OK) return st;
-  if (plan.path == Path::Band && !band_bwd_slices_fit(d)) {
+  if (plan->path == Path::Band && !band_bwd_slices_fit(d)) {
     if (d->algo == SA_ALGO_BAND) return SA_ERR_UNSUPPORTED;
-    plan.path = Path::Gather;
+    plan->path = Path::Gather;
   }
   const bool coord = d->score == SA_SCORE_COORD;
   const int es = esize(d->dtype), gs = esize(d->grad_dtype);
@@ -267,11 +269,18 @@ extern "C" sa_status sa_bwd(const sa_graph* g, const sa_attn_desc* d, const void
     if (dcq == nullptr || dck == nullptr || dgamma == nullptr || dbeta == nullptr)
       return SA_ERR_INVALID_ARG;
   }  // uniform mode writes dv alone
-  if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-    return SA_ERR_WORKSPACE;
-  const size_t need = workspace_bytes_for(d);
-  if (workspace_bytes < need) return SA_ERR_WORKSPACE;
+  return SA_OK;
+}
 
+// Packs the parameters of a validated backward and launches its kernels with
+// `ws` (256-byte aligned, workspace_bytes_for(d) bytes) as the workspace.
+// Nothing in the workspace needs to start at zero: every kernel writes the
+// per-row and per-block values it later reads within the same call.
+sa_status bwd_launch(const sa_graph* g, const sa_attn_desc* d, Path path, const void* q, const void* k,
+                     const void* v, const float* cq, const float* ck, const float* gamma,
+                     const float* beta, const void* o, const float* lse, const void* dout, void* dq,
+                     void* dk, void* dv, float* dcq, float* dck, float* dgamma, float* dbeta, char* ws,
+                     sa_stream stream) {
   sa::Params p;
   fill_common(&p, g, d);
   p.q = q; SET_STRIDES(sq, d->stride_q);
@@ -285,17 +294,80 @@ extern "C" sa_status sa_bwd(const sa_graph* g, const sa_attn_desc* d, const void
   p.cq = cq; p.ck = ck; p.gamma = gamma; p.beta = beta;
   p.dcq = dcq; p.dck = dck; p.dgamma = dgamma; p.dbeta = dbeta;
   p.lse = const_cast<float*>(lse);
-  char* ws = static_cast<char*>(workspace);
   const size_t row_bytes = align256((size_t)d->B * d->H * d->T * sizeof(float));
   p.delta = reinterpret_cast<float*>(ws);
   p.ndelta = p.delta;
   p.lse2 = reinterpret_cast<float*>(ws + row_bytes);
   p.partials = reinterpret_cast<float*>(ws + 2 * row_bytes);
   const int dt = d->dtype == SA_BF16 ? sa::DT_BF16 : sa::DT_F32;
-  hipError_t e = plan.path == Path::Band  ? sa::launch_band_bwd(p, as_stream(stream))
-                 : plan.path == Path::Csr ? sa::launch_csr_bwd(p, dt, d->score, as_stream(stream))
-                                          : sa::launch_gather_bwd(p, dt, d->score, as_stream(stream));
+  hipError_t e = path == Path::Band  ? sa::launch_band_bwd(p, as_stream(stream))
+                 : path == Path::Csr ? sa::launch_csr_bwd(p, dt, d->score, as_stream(stream))
+                                     : sa::launch_gather_bwd(p, dt, d->score, as_stream(stream));
   return e == hipSuccess ? SA_OK : SA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" sa_status sa_bwd(const sa_graph* g, const sa_attn_desc* d, const void* q, const void* k,
+                            const void* v, const float* cq, const float* ck, const float* gamma,
+                            const float* beta, const void* o, const float* lse, const void* dout,
+                            void* dq, void* dk, void* dv, float* dcq, float* dck, float* dgamma,
+                            float* dbeta, void* workspace, size_t workspace_bytes,
+                            sa_stream stream) {
+  Plan plan;
+  const sa_status st = bwd_validate(g, d, q, k, v, cq, ck, gamma, beta, o, lse, dout, dq, dk, dv, dcq, dck,
+                                    dgamma, dbeta, &plan);
+  if (st != SA_OK) return st;
+  if (workspace == nullptr || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return SA_ERR_WORKSPACE;
+  if (workspace_bytes < workspace_bytes_for(d)) return SA_ERR_WORKSPACE;
+  return bwd_launch(g, d, plan.path, q, k, v, cq, ck, gamma, beta, o, lse, dout, dq, dk, dv, dcq, dck,
+                    dgamma, dbeta, static_cast<char*>(workspace), stream);
+}
+
+// ------------------------------------------------------------------ allocation-free backward
+// The backward's workspace as a file-scope device array, for callers that
+// cannot allocate (graph capture, tight serving loops).  In host code the
+// name `scratch` is only a host-side stand-in: kernels get the device address
+// that hipGetSymbolAddress returns for the current device, looked up on the
+// first call on each device and kept per device (every GPU has its own copy).
+static __device__ __align__(256) char scratch[SA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::atomic<char*> g_scratch_ptr[kMaxScratchDevices];
+
+// Device address of this device's `scratch`, or nullptr when the lookup fails.
+char* scratch_on_current_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices) return nullptr;
+  char* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (ptr != nullptr) return ptr;
+  void* addr = nullptr;
+  if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || addr == nullptr) return nullptr;
+  ptr = static_cast<char*>(addr);
+  g_scratch_ptr[dev].store(ptr, std::memory_order_release);  // racing first calls store the same address
+  return ptr;
+}
+
+}  // namespace
+
+extern "C" sa_status sa_bwd_noalloc(const sa_graph* g, const sa_attn_desc* d, const void* q,
+                                    const void* k, const void* v, const float* cq, const float* ck,
+                                    const float* gamma, const float* beta, const void* o,
+                                    const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                                    float* dcq, float* dck, float* dgamma, float* dbeta,
+                                    sa_stream stream) {
+  Plan plan;
+  const sa_status st = bwd_validate(g, d, q, k, v, cq, ck, gamma, beta, o, lse, dout, dq, dk, dv, dcq, dck,
+                                    dgamma, dbeta, &plan);
+  if (st != SA_OK) return st;
+  if (workspace_bytes_for(d) > (size_t)SA_NOALLOC_SCRATCH_BYTES) return SA_ERR_WORKSPACE;
+  char* ws = scratch_on_current_device();
+  if (ws == nullptr) return SA_ERR_HIP;
+  return bwd_launch(g, d, plan.path, q, k, v, cq, ck, gamma, beta, o, lse, dout, dq, dk, dv, dcq, dck,
+                    dgamma, dbeta, ws, stream);
 }
 
 extern "C" sa_status sa_decode(const sa_graph* g, const sa_attn_desc* d, const int32_t* positions,

@@ -408,3 +408,33 @@ def test_side_stream_marshalling(monkeypatch):
     g._used_on(FakeStream(9))
     assert recorded == [9]
     g._dev = None
+
+
+def test_noalloc_validation():
+    """sa_bwd_noalloc validates like sa_bwd (no workspace arguments) and
+    rejects, before any HIP call, a shape whose workspace exceeds its built-in
+    scratch."""
+    E = _abi
+    L = _abi.lib()
+
+    def noalloc(g, d, **kw):
+        args = dict(q=FAKE, k=FAKE, v=FAKE, cq=None, ck=None, gm=None, bt=None, o=FAKE, lse=FAKE, do=FAKE,
+                    dq=FAKE, dk=FAKE, dv=FAKE, dcq=None, dck=None, dg=None, db=None)
+        args.update(kw)
+        return L.sa_bwd_noalloc(g.handle, ctypes.byref(d), *args.values(), None)
+
+    T = 1 << 16
+    g = sa_build_graph(T, 4, [])
+    need = ctypes.c_size_t()
+    big = desc(B=1, H=40, T=T, D=64, dtype=1)
+    assert L.sa_bwd_workspace_size(g.handle, ctypes.byref(big), ctypes.byref(need)) == 0
+    assert need.value > E.SA_NOALLOC_SCRATCH_BYTES
+    assert noalloc(g, big) == E.SA_ERR_WORKSPACE
+    assert noalloc(g, big, do=None) == E.SA_ERR_INVALID_ARG  # argument errors come first
+    assert noalloc(g, desc(B=1, H=40, T=T - 1, D=64, dtype=1)) == E.SA_ERR_SHAPE_MISMATCH
+    fits = desc(B=1, H=8, T=T, D=64, dtype=1)
+    assert L.sa_bwd_workspace_size(g.handle, ctypes.byref(fits), ctypes.byref(need)) == 0
+    assert need.value <= E.SA_NOALLOC_SCRATCH_BYTES
+    d = desc(B=1, H=8, T=T, D=64, dtype=1)
+    d.stride_dq[2] = 0
+    assert noalloc(g, d) == E.SA_ERR_INVALID_ARG
