@@ -39,7 +39,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workloads",
-                    default="band,dilated,coord,uniform,band_gqa,dilated_gqa,csr_dilated,csr_random,decode_band,decode_dilated,ultra")
+                    default="band,uniform,band_gqa,dilated_gqa,csr_dilated,csr_random,decode_band,decode_dilated,"
+                            "dilated,coord,ultra")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample length")
     ap.add_argument("--algo", default="auto")
@@ -47,6 +48,10 @@ def parse():
                     help="skip the cold-cache repetitions (profiled runs: keeps per-kernel averages warm)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (scales profiler byte counters)")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the measured copy / MFMA-loop / empty-launch denominators")
+    ap.add_argument("--record-profiles", metavar="DIR",
+                    help="write profiles/ from the rocprofv3 CSV output under DIR/<workload>/<pass> (no GPU)")
     return ap.parse_args()
 
 
@@ -369,10 +374,46 @@ def measured_traffic(workload, kernel):
         return None
 
 
-def roofline_for(w, r, m):
-    """Roofline entry for the longer of the two calls.  The fraction is taken
-    against the gather byte model; where that exceeds 1 (rows reused from
-    cache), against the compulsory bytes instead, and `model` says which."""
+COUNTER_RECORD = os.path.join(ROOT, "profiles", "counters.json")
+
+
+def counter_mfma(workload, kernel, avg_ms):
+    """Matrix-core work of `kernel` (a plan name, "a+b" for several launches)
+    on `workload` from the committed rocprofv3 --pmc record: bf16 MFMA flops
+    per call (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512, per dispatch), those flops
+    over `avg_ms` against the spec peak, and rocprofv3's own MfmaUtil and
+    VALUBusy (percent of the kernel's time the matrix cores / vector ALUs are
+    busy; for a call of several launches, the launch with the most MFMA work).
+    None when there is no record or the kernels changed since."""
+    try:
+        rec = json.load(open(COUNTER_RECORD))
+        from sparse_causal_attention_amd.build import source_digest
+        if rec.get("source_sha256") != source_digest():
+            return None
+        ents = [rec["kernels"][workload][name] for name in kernel.split("+")]
+        flops = 512.0 * sum(e.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) for e in ents)
+        main = max(ents, key=lambda e: e.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0))
+        out = {"flops_per_call": flops,
+               "mfma_bf16_frac": round(flops / (avg_ms * 1e9) / MFMA_BF16_PEAK_TFS, 4)}
+        for key in ("MfmaUtil", "VALUBusy"):
+            if key in main:
+                out[key + "_pct"] = round(main[key], 2)
+        return out
+    except (OSError, KeyError, ValueError, TypeError, ZeroDivisionError):
+        return None
+
+
+RIDGE = MFMA_BF16_PEAK_TFS * 1e12 / (HBM_PEAK_GBS * 1e9)  # flop per byte where the two roofs meet
+
+
+def roofline_for(w, r, m, peaks=None):
+    """Roofline entry for the longer of the two calls.  The bound is the roof
+    the call's algorithmic intensity (flops over compulsory bytes) falls under:
+    HBM below the ridge (MFMA peak / HBM peak = 312.5 flop/B), the bf16 matrix
+    cores above it.  Against HBM the fraction is taken with the gather byte
+    model; where that exceeds 1 (rows reused from cache), with the compulsory
+    bytes instead, and `model` says which.  `peaks`: measured denominators
+    (copy bandwidth, MFMA loop), reported beside the spec fractions."""
     use_bwd = r["bwd_ms"] > r["fwd_ms"]
     ms = r["bwd_ms"] if use_bwd else r["fwd_ms"]
     call = "bwd" if use_bwd else "fwd"
@@ -384,16 +425,39 @@ def roofline_for(w, r, m):
     frac_c = byt_c / (ms * 1e6) / HBM_PEAK_GBS
     model = "gather" if frac_g <= 1.0 else "compulsory"
     byt = byt_g if model == "gather" else byt_c
-    achieved = byt / (ms * 1e6)
-    return {
-        "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(w.name, kernel),
+    gbs = byt / (ms * 1e6)
+    tfs = fl / (ms * 1e9)
+    dot_mfma = not (w.coord or w.uniform or w.decode)  # bf16 dot scores run on the matrix cores
+    intensity = fl / byt_c if byt_c else 0.0
+    bound = "mfma" if dot_mfma and intensity > RIDGE else "hbm"
+    if bound == "mfma":
+        head = {"bound": "mfma", "achieved": round(tfs, 1), "peak": MFMA_BF16_PEAK_TFS, "unit": "TFLOP/s",
+                "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4)}
+    else:
+        head = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    traffic = measured_traffic(w.name, kernel)
+    out = dict(head)
+    out.update({
+        "traffic": traffic,
         "kernel": kernel,
         "call": "sa_" + call,
         "avg_ms": round(ms, 5), "algorithmic_bytes": byt, "model": model,
+        "intensity_flop_per_byte": round(intensity, 1),
         "frac_gather_model": round(frac_g, 4), "frac_compulsory": round(frac_c, 4),
-        "mfma_bf16_frac": round(fl / (ms * 1e9) / MFMA_BF16_PEAK_TFS, 4),
-    }
+        "mfma_bf16_frac": round(tfs / MFMA_BF16_PEAK_TFS, 4) if dot_mfma else None,
+    })
+    if traffic:
+        out["traffic_over_algorithmic"] = round(traffic / byt, 3)
+        out["traffic_GBs"] = round(traffic / (ms * 1e6), 1)
+    cm = counter_mfma(w.name, kernel, ms) if dot_mfma else None
+    if cm:
+        out["mfma_counters"] = cm
+    if peaks:
+        out["frac_of_measured_copy"] = round(gbs / peaks["copy_GBs"], 4)
+        if dot_mfma:
+            out["mfma_frac_of_measured_loop"] = round(tfs / peaks["mfma_bf16_TFs"], 4)
+    return out
 
 
 # ------------------------------------------------------------------ CPU baseline (oracle)
@@ -467,21 +531,321 @@ def cpu_baseline(w, inputs, target_s):
             "cpu_model": cpu_model()}
 
 
-def copy_probe():
+_PROBE = None
+
+
+def probe_lib():
+    """libsa_probe.so (include/sa_probe.h): copy, MFMA-loop and empty-launch
+    probes built beside libsa.so."""
+    global _PROBE
+    if _PROBE is None:
+        import ctypes
+        path = os.path.join(ROOT, "sparse_causal_attention_amd", "libsa_probe.so")
+        if not os.path.exists(path):
+            raise ImportError("libsa_probe.so is not built; run python -m sparse_causal_attention_amd.build")
+        L = ctypes.CDLL(path)
+        vp = ctypes.c_void_p
+        L.sa_probe_copy.argtypes = [vp, vp, ctypes.c_size_t, vp]
+        L.sa_probe_mfma.argtypes = [vp, ctypes.c_int, ctypes.c_int, vp]
+        L.sa_probe_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
+        L.sa_probe_empty.argtypes = [vp]
+        _PROBE = L
+    return _PROBE
+
+
+def _stream_handle():
+    import ctypes
     import torch
-    n = 1 << 30
-    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+COPY_PROBE_BYTES = 1 << 30
+
+
+def copy_probe(reps=3):
+    """The probe's plain 1 GiB device copy (the counters' scale reference):
+    returns the median copy time in ms over `reps` launches."""
+    import ctypes
+    import torch
+    L = probe_lib()
+    a = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device="cuda")
     b = torch.empty_like(a)
     a.fill_(1)
     torch.cuda.synchronize()
-    for _ in range(3):
-        b.copy_(a)
-    torch.cuda.synchronize()
+    ms = []
+    for _ in range(reps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record()
+        assert L.sa_probe_copy(ctypes.c_void_p(b.data_ptr()), ctypes.c_void_p(a.data_ptr()), COPY_PROBE_BYTES,
+                               _stream_handle()) == 0
+        e[1].record()
+        torch.cuda.synchronize()
+        ms.append(e[0].elapsed_time(e[1]))
     del a, b
+    return median(ms)
+
+
+def measured_peaks():
+    """Measured denominators beside the published peaks: a plain device copy
+    (read + write bytes over its time), a loop of independent bf16 MFMAs, and
+    an empty launch (alone between two events, and back to back)."""
+    import ctypes
+    import torch
+    L = probe_lib()
+    copy_probe(2)  # warm
+    copy_ms = copy_probe(5)
+    blocks, iters = 256 * 8, 2000
+    out = torch.empty(blocks * 4, dtype=torch.float32, device="cuda")
+    fl = ctypes.c_double()
+    L.sa_probe_mfma_flops(blocks, iters, ctypes.byref(fl))
+    ms = []
+    for r in range(6):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record()
+        assert L.sa_probe_mfma(ctypes.c_void_p(out.data_ptr()), blocks, iters, _stream_handle()) == 0
+        e[1].record()
+        torch.cuda.synchronize()
+        if r:
+            ms.append(e[0].elapsed_time(e[1]))
+    mfma_ms = median(ms)
+    alone = []
+    for _ in range(50):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record()
+        L.sa_probe_empty(_stream_handle())
+        e[1].record()
+        torch.cuda.synchronize()
+        alone.append(e[0].elapsed_time(e[1]))
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    e[0].record()
+    for _ in range(200):
+        L.sa_probe_empty(_stream_handle())
+    e[1].record()
+    torch.cuda.synchronize()
+    return {"copy_GBs": round(2 * COPY_PROBE_BYTES / (copy_ms * 1e6), 1),
+            "copy_how": "probe copy kernel, 1 GiB read + 1 GiB written, median of 5",
+            "mfma_bf16_TFs": round(fl.value / (mfma_ms * 1e9), 1),
+            "mfma_how": "%d workgroups x 4 wavefronts x 4 independent chains x %d v_mfma_f32_32x32x16_bf16, "
+                        "median of 5" % (blocks, iters),
+            "empty_launch_us": round(1e3 * median(alone), 2),
+            "empty_launch_us_back_to_back": round(1e3 * e[0].elapsed_time(e[1]) / 200, 2),
+            "spec": {"hbm_GBs": HBM_PEAK_GBS, "mfma_bf16_TFs": MFMA_BF16_PEAK_TFS}}
+
+
+# ------------------------------------------------------------------ profile records
+# The rocprofv3 runs behind profiles/ (each from /tmp with TMPDIR=/tmp, one
+# bench process per workload, into <dir>/<workload>/<pass>), and the bench
+# command each profiles.  `python bench.py --record-profiles <dir>` turns their
+# CSV output into profiles/<family>__<workload>.txt (kernel-trace statistics),
+# profiles/counters__<workload>.txt and the JSON records bench.py reads back
+# (profiles/traffic.json, profiles/counters.json).
+PROFILE_PASSES = {
+    "trace": ("rocprofv3 --kernel-trace --stats --output-format csv -d <dir>/<workload>/trace -o run --",
+              "--steps 10 --warmup 2 --no-cpu-baseline --no-cold --no-peaks"),
+    "fetch": ("rocprofv3 --pmc FETCH_SIZE --output-format csv -d <dir>/<workload>/fetch -o run --",
+              "--steps 3 --warmup 1 --no-cpu-baseline --no-cold --no-peaks --copy-probe"),
+    "write": ("rocprofv3 --pmc WRITE_SIZE --output-format csv -d <dir>/<workload>/write -o run --",
+              "--steps 3 --warmup 1 --no-cpu-baseline --no-cold --no-peaks --copy-probe"),
+    "mfma": ("rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 MfmaUtil VALUBusy --output-format csv "
+             "-d <dir>/<workload>/mfma -o run --",
+             "--steps 3 --warmup 1 --no-cpu-baseline --no-cold --no-peaks"),
+}
+
+
+def profile_command(pass_name, workload):
+    tool, args = PROFILE_PASSES[pass_name]
+    return "%s python3 <repo>/bench.py %s --workloads %s" % (tool.replace("<workload>", workload), args, workload)
+
+
+def _csv_rows(path):
+    import csv
+    with open(path) as f:
+        return list(csv.DictReader(f))
+
+
+def _plain_name(full):
+    """'void sa::(anonymous namespace)::band_fwd_kernel<false, 1>(sa::Params)'
+    -> 'band_fwd_kernel<false, 1>' (the name with its template arguments and
+    without namespaces, return type or parameter list)."""
+    name = full.replace("(anonymous namespace)", "")
+    if name.startswith("void "):
+        name = name[5:]
+    depth, cut = 0, len(name)
+    for i, ch in enumerate(name):  # the parameter list starts at the first '(' outside <...>
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            cut = i
+            break
+    name = name[:cut]
+    head = name.split("<", 1)[0]
+    return head.split("::")[-1] + (name[len(head):] if "<" in name else "")
+
+
+def _plan_names(workload):
+    """Plan names of the workload's calls, each with the symbol prefix of its
+    kernel, in launch order (forward first)."""
+    from sparse_causal_attention_amd.inputs import WORKLOADS
+    w = WORKLOADS[workload]
+    if w.decode:
+        return ["decode_kernel(dot)"]
+    import torch
+
+    from sparse_causal_attention_amd import sa_describe_plan
+    g = make_graph(w)
+    v = torch.empty((w.B, w.kv_heads, w.T, w.D), dtype=w.dtype, device="meta")  # shape only, no memory
+    plans = sa_describe_plan(g, v, score=score_name(w), which="fwd", heads=w.H).split("+")
+    if w.backward:
+        plans += sa_describe_plan(g, v, score=score_name(w), which="bwd", heads=w.H).split("+")
+    return plans
+
+
+def _symbol_plan(symbol, plans):
+    """The plan name a kernel symbol belongs to: the plan whose kernel name
+    the symbol starts with (for a family launched once per call)."""
+    base = symbol.split("<")[0]
+    for pl in plans:
+        if pl.split("(")[0] == base:
+            return pl
+    return None
+
+
+def record_profiles(root):
+    """Reads <root>/<workload>/{trace,fetch,write,mfma}/run_*.csv and writes
+    the profile summaries and records under profiles/."""
+    from sparse_causal_attention_amd.build import source_digest
+    from sparse_causal_attention_amd.inputs import WORKLOADS
+    prof = os.path.join(ROOT, "profiles")
+    digest = source_digest()
+    traffic = {"source_sha256": digest,
+               "note": "FETCH_SIZE and WRITE_SIZE in KiB per dispatch (mean over dispatches), from two rocprofv3 "
+                       "--pmc runs per workload; copy = the probe's plain 1 GiB device copy in the same process, "
+                       "used to scale each counter to bytes",
+               "commands": {p: profile_command(p, "<workload>") for p in ("fetch", "write")},
+               "copy": None, "kernels": {}}
+    counters = {"source_sha256": digest,
+                "note": "per dispatch means: SQ_INSTS_VALU_MFMA_MOPS_BF16 (bf16 MFMA flops / 512), MfmaUtil and "
+                        "VALUBusy (rocprofv3 derived metrics, percent)",
+                "command": profile_command("mfma", "<workload>"), "kernels": {}}
+    for workload in sorted(os.listdir(root)):
+        wdir = os.path.join(root, workload)
+        if workload not in WORKLOADS or not os.path.isdir(wdir):
+            continue
+        w = WORKLOADS[workload]
+        plans = _plan_names(workload)
+        # kernel trace statistics
+        stats = os.path.join(wdir, "trace", "run_kernel_stats.csv")
+        if os.path.exists(stats):
+            rows = [r for r in _csv_rows(stats) if "sa::" in r["Name"]]
+            fam = {"band": "band_kernels", "gather": "gather_kernels", "csr": "csr_kernels",
+                   "decode": "decode_kernel"}[plans[0].split("_")[0]]
+            lines = ["# rocprofv3 kernel-trace statistics, %s: B=%d H=%d H_kv=%d T=%d D=%d W=%d offsets=%s %s %s "
+                     "score, %s" % (workload, w.B, w.H, w.kv_heads, w.T, w.D, w.window, list(w.offsets),
+                                    w.dtype_name, score_name(w), "fwd+bwd" if w.backward else "fwd"),
+                     "# one MI355X (gfx950); calls per kernel = warm-up + timed steps of bench.py",
+                     "# command, run from /tmp with TMPDIR=/tmp on the repository as committed:",
+                     "#   " + profile_command("trace", workload),
+                     "# libsa.so source sha256: " + digest,
+                     "%-64s %6s %12s %12s %12s" % ("kernel", "calls", "avg_us", "min_us", "max_us")]
+            for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+                lines.append("%-64s %6d %12.2f %12.2f %12.2f" % (
+                    _plain_name(r["Name"]), int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+                    float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3))
+            open(os.path.join(prof, "%s__%s.txt" % (fam, workload)), "w").write("\n".join(lines) + "\n")
+        # counters: mean per dispatch of each counter per kernel symbol
+        per = {}
+        for pass_name in ("fetch", "write", "mfma"):
+            path = os.path.join(wdir, pass_name, "run_counter_collection.csv")
+            if not os.path.exists(path):
+                continue
+            acc = {}
+            for r in _csv_rows(path):
+                key = (_plain_name(r["Kernel_Name"]), r["Counter_Name"])
+                acc.setdefault(key, []).append(float(r["Counter_Value"]))
+            for (sym, cname), vals in acc.items():
+                per.setdefault(sym, {})[cname] = sum(vals) / len(vals)
+        copy = per.get("probe_copy_kernel")
+        if copy and "FETCH_SIZE" in copy and "WRITE_SIZE" in copy and traffic["copy"] is None:
+            traffic["copy"] = {"bytes": COPY_PROBE_BYTES, "fetch_kib": copy["FETCH_SIZE"],
+                               "write_kib": copy["WRITE_SIZE"], "workload_run": workload}
+        for sym, vals in per.items():
+            plan = _symbol_plan(sym, plans)
+            if plan is None:
+                continue
+            if "FETCH_SIZE" in vals and "WRITE_SIZE" in vals:
+                traffic["kernels"].setdefault(workload, {})[plan] = {
+                    "fetch_kib": vals["FETCH_SIZE"], "write_kib": vals["WRITE_SIZE"], "symbol": sym}
+            m = {k: vals[k] for k in ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "MfmaUtil", "VALUBusy") if k in vals}
+            if m:
+                counters["kernels"].setdefault(workload, {})[plan] = dict(m, symbol=sym)
+    json.dump(traffic, open(os.path.join(prof, "traffic.json"), "w"), indent=1)
+    json.dump(counters, open(os.path.join(prof, "counters.json"), "w"), indent=1)
+    # a readable summary per workload
+    cf = cw = None
+    if traffic["copy"]:
+        cf = traffic["copy"]["bytes"] / (traffic["copy"]["fetch_kib"] * 1024.0)
+        cw = traffic["copy"]["bytes"] / (traffic["copy"]["write_kib"] * 1024.0)
+    for workload in sorted(set(traffic["kernels"]) | set(counters["kernels"])):
+        lines = ["# rocprofv3 --pmc counters per dispatch, workload %s, one MI355X (gfx950)" % workload,
+                 "# commands (from /tmp, TMPDIR=/tmp, on the repository as committed):"]
+        for p in ("fetch", "write", "mfma"):
+            lines.append("#   " + profile_command(p, workload))
+        lines.append("# libsa.so source sha256: " + digest)
+        if cf:
+            lines.append("# bytes = FETCH_SIZE KiB x 1024 x %.4f + WRITE_SIZE KiB x 1024 x %.4f (the probe's 1 GiB "
+                         "copy reads %.1f / %.1f KiB on these counters)" % (
+                             cf, cw, traffic["copy"]["fetch_kib"], traffic["copy"]["write_kib"]))
+        lines.append("%-34s %14s %14s %12s %16s %10s %10s" % ("kernel (plan name)", "FETCH_SIZE_KiB",
+                                                             "WRITE_SIZE_KiB", "HBM_MB", "MFMA_bf16_GFLOP",
+                                                             "MfmaUtil%", "VALUBusy%"))
+        names = sorted(set(traffic["kernels"].get(workload, {})) | set(counters["kernels"].get(workload, {})))
+        for plan in names:
+            t = traffic["kernels"].get(workload, {}).get(plan, {})
+            c = counters["kernels"].get(workload, {}).get(plan, {})
+            hbm = (t["fetch_kib"] * cf + t["write_kib"] * cw) * 1024 / 1e6 if (t and cf) else float("nan")
+            lines.append("%-34s %14.1f %14.1f %12.2f %16.3f %10.2f %10.2f" % (
+                plan, t.get("fetch_kib", float("nan")), t.get("write_kib", float("nan")), hbm,
+                512 * c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", float("nan")) / 1e9,
+                c.get("MfmaUtil", float("nan")), c.get("VALUBusy", float("nan"))))
+        open(os.path.join(prof, "counters__%s.txt" % workload), "w").write("\n".join(lines) + "\n")
+
+
+# Workloads the oracle is also timed on (besides the headline): the dilated
+# training shape, its coordinate-score variant and the tiny fp32 case (CPU
+# only), each with a single-thread slice.
+CPU_EXTRA = ("dilated", "coord", "tiny")
+CPU_EXTRA_SECONDS = 6.0
+
+# Order of the compact per-workload summary that closes the JSON line: the
+# configurations the metric is quoted on come last.
+SUMMARY_LAST = ("band", "dilated", "coord", "ultra")
+
+
+def compact(s):
+    """One short entry per workload for the end of the line."""
+    rf = s["roofline"]
+    e = {"tok_s": round(s["tokens_per_s"], 1), "edges_s": round(s["edges_per_s"], 1),
+         "fwd_us": round(1e3 * s["fwd_ms"], 1), "bwd_us": round(1e3 * s["bwd_ms"], 1),
+         "bound": rf["bound"], "frac": rf["frac"], "model": rf["model"],
+         "frac_compulsory": rf["frac_compulsory"]}
+    if rf.get("traffic"):
+        e["traffic_ratio"] = rf["traffic_over_algorithmic"]
+    if rf.get("mfma_bf16_frac") is not None:
+        e["mfma_frac"] = rf["mfma_bf16_frac"]
+    if rf.get("mfma_counters"):
+        e["mfma_frac_counters"] = rf["mfma_counters"]["mfma_bf16_frac"]
+        if "MfmaUtil_pct" in rf["mfma_counters"]:
+            e["MfmaUtil_pct"] = rf["mfma_counters"]["MfmaUtil_pct"]
+    return e
 
 
 def main():
     args = parse()
+    if args.record_profiles:
+        record_profiles(args.record_profiles)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         sys.stderr.write("bench.py measures one GPU only: this build has no multi-GPU path "
                          "(independent (batch, head) slices would shard without communication; "
@@ -490,14 +854,19 @@ def main():
     import torch
 
     from sparse_causal_attention_amd import _abi
-    from sparse_causal_attention_amd.inputs import WORKLOADS
+    from sparse_causal_attention_amd.inputs import WORKLOADS, make_inputs
 
     _abi.lib()
     if args.copy_probe:
         copy_probe()
+    peaks = None
+    if not args.no_peaks:
+        print("[bench] measured peaks (copy, MFMA loop, empty launch)", file=sys.stderr, flush=True)
+        peaks = measured_peaks()
     names = [n for n in args.workloads.split(",") if n]
     headline = names[0]
     results = {}
+    host_inputs = {}
     for name in names:
         w = WORKLOADS[name]
         steps = args.steps if name != "ultra" else max(2, min(args.steps, 5))
@@ -508,10 +877,15 @@ def main():
         r = (run_decode(w, steps, warm, args.no_cold) if w.decode
              else run_workload(w, steps, warm, args.algo, no_cold=args.no_cold))
         s, m = summarize(w, r, steps)
-        s["roofline"] = roofline_for(w, r, m)
+        s["roofline"] = roofline_for(w, r, m, peaks)
         s["steps"] = steps
+        if w.decode and peaks:
+            s["launch_floor_us"] = peaks["empty_launch_us"]
+            s["over_launch_floor"] = round(1e3 * r["fwd_ms"] / peaks["empty_launch_us"], 2)
         results[name] = (w, r, s)
         if name != headline:
+            if name in CPU_EXTRA and not args.no_cpu_baseline:
+                host_inputs[name] = {k: t.cpu() for k, t in r["inputs"].items()}
             del r["inputs"]
             torch.cuda.empty_cache()
     w, r, s = results[headline]
@@ -534,14 +908,32 @@ def main():
             "global_batch": w.B, "seq_len": w.T, "heads": w.H, "head_dim": w.D},
         "edges_per_s": s["edges_per_s"],
         "roofline": s["roofline"],
+        "measured_peaks": peaks,
         "detail": {k: v for k, v in s.items() if k not in ("roofline",)},
     }
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle) on %s" % w.name, file=sys.stderr, flush=True)
-        line["cpu_baseline"] = cpu_baseline(w, r["inputs"], args.cpu_seconds)
+        cb = cpu_baseline(w, r["inputs"], args.cpu_seconds)
+        others = {}
+        for name in CPU_EXTRA:
+            wx = WORKLOADS[name]
+            xin = host_inputs.get(name)
+            if xin is None and name not in results:
+                xin = make_inputs(wx)  # a workload the GPU leg did not run (the tiny fp32 case)
+            if xin is None:
+                continue
+            print("[bench] cpu baseline (oracle) on %s" % name, file=sys.stderr, flush=True)
+            c = cpu_baseline(wx, xin, CPU_EXTRA_SECONDS)
+            if name in results:
+                c["gpu_over_cpu"] = round(results[name][2]["tokens_per_s"] / c["value"], 1)
+            others[name] = c
+        cb["other_workloads"] = others
+        line["cpu_baseline"] = cb
     else:
         line["cpu_baseline"] = None
     line["extra"] = {n: s2 for n, (_, _, s2) in results.items() if n != headline}
+    order = [n for n in results if n not in SUMMARY_LAST] + [n for n in SUMMARY_LAST if n in results]
+    line["summary"] = {n: compact(results[n][2]) for n in order}
     print(json.dumps(line), flush=True)
 
 

@@ -10,7 +10,9 @@ import ctypes
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libsa.so")
+# the in-tree build; SA_LIBRARY names another build of the same sources (for
+# comparing two builds in one process tree on one GPU)
+LIB_PATH = os.environ.get("SA_LIBRARY") or os.path.join(_PKG, "libsa.so")
 
 SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_SHAPE_MISMATCH, SA_ERR_WORKSPACE, SA_ERR_HIP = range(6)
 SA_F32, SA_BF16 = 0, 1

@@ -88,12 +88,31 @@ def stale() -> bool:
     return any(os.path.getmtime(f) > t for f in sources() + headers())
 
 
+PROBE_SRC = os.path.join(PKG, "probe", "probe.hip")
+PROBE_LIB = os.path.join(PKG, "libsa_probe.so")
+
+
+def build_probe() -> str:
+    """libsa_probe.so: the benchmark's measurement probes (copy, MFMA loop,
+    empty launch), a library of their own beside libsa.so."""
+    obj = _compile(PROBE_SRC)
+    tmp = PROBE_LIB + ".tmp%d" % os.getpid()
+    r = subprocess.run([HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp, obj],
+                       capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("probe link failed:\n%s" % r.stderr)
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
+
+
 def build(jobs: int | None = None) -> str:
     os.makedirs(BUILD, exist_ok=True)
     srcs = sources()
-    jobs = jobs or min(len(srcs), max(1, (os.cpu_count() or 4)))
+    jobs = jobs or min(len(srcs) + 1, max(1, (os.cpu_count() or 4)))
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        probe = ex.submit(build_probe)
         objs = list(ex.map(_compile, srcs))
+        probe.result()
     tmp = LIB + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -96,6 +96,19 @@ struct Frag<DT_BF16> {
   }
 };
 
+// 16-byte fragments per lane of a gather-kernel row.  One (a row spans
+// D * bytes / 16 lanes, so a wavefront's load covers whole rows) except for
+// the coordinate score on bf16 rows of 64 or more elements: there the vector
+// ALUs, not the loads, bound the kernels, and two fragments per lane halve the
+// lanes that repeat each edge's score and softmax work (measured on the
+// coordinate training workload: forward 78.7 -> 73.4 us, backward 188 -> 169
+// us).  With the dot and fixed-weight scores two fragments were slower (the
+// dilated backward 274 -> 304 us): a row's 128-byte cache line is then split
+// over two load instructions, which doubles the load path's line requests.
+constexpr int gather_frags_per_lane(int dt, int D, int score_mode) {
+  return dt == DT_BF16 && D >= 64 && score_mode == SM_COORD ? 2 : 1;
+}
+
 __device__ __forceinline__ uint4 ld16(const char* p) {
   return *reinterpret_cast<const uint4*>(p);
 }

@@ -28,10 +28,13 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 
-template <int DT, int D>
+// Row layout as in the gather forward: NF 16-byte fragments per lane
+// (fragment f of lane s at bytes 16 (f LG + s)), LG lanes per row.
+template <int DT, int D, int SM>
 struct Geo {
   static constexpr int EPL = Frag<DT>::EPL;
-  static constexpr int LG = D / EPL;
+  static constexpr int NF = gather_frags_per_lane(DT, D, SM);
+  static constexpr int LG = D / (EPL * NF);
   static constexpr int RPW = 64 / LG;
   static constexpr int RPB = RPW * kWaves;
 };
@@ -41,9 +44,10 @@ struct Geo {
 template <int DT, int D, bool COORD, int G, bool OFF32>
 __global__ __launch_bounds__(kThreads) void gather_bwd_q_kernel(Params p) {
   using F = Frag<DT>;
-  using Gm = Geo<DT, D>;
-  constexpr int EPL = Gm::EPL, LG = Gm::LG, RPW = Gm::RPW, RPB = Gm::RPB;
+  using Gm = Geo<DT, D, COORD ? SM_COORD : SM_DOT>;
+  constexpr int EPL = Gm::EPL, NF = Gm::NF, LG = Gm::LG, RPW = Gm::RPW, RPB = Gm::RPB;
   constexpr int EB = F::BYTES;
+  constexpr int FS = 16 * LG;  // bytes between a lane's fragments
 
   const int nblk = (p.T + RPB - 1) / RPB;
   const int logical = xcd_logical_block(p.B * p.H * nblk);
@@ -69,11 +73,15 @@ __global__ __launch_bounds__(kThreads) void gather_bwd_q_kernel(Params p) {
   const uint32_t sub16 = (uint32_t)sub * 16u;
 
   // dout and q fragments as stored (dot operands)
-  uint4 doraw, qraw = make_uint4(0u, 0u, 0u, 0u);
+  uint4 doraw[NF], qraw[NF];
   {
     const char* dorow = static_cast<const char*>(p.dout) +
                         (b * p.sdo_b + h * p.sdo_h + i * p.sdo_t) * EB + sub * 16;
-    doraw = ld16(dorow);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      doraw[f] = ld16(dorow + f * FS);
+      qraw[f] = make_uint4(0u, 0u, 0u, 0u);
+    }
   }
   // lse includes beta in coordinate mode; the scores below omit it
   const float lse2 =
@@ -85,7 +93,8 @@ __global__ __launch_bounds__(kThreads) void gather_bwd_q_kernel(Params p) {
   if constexpr (!COORD) {
     const char* qrow = static_cast<const char*>(p.q) + (b * p.sq_b + h * p.sq_h + i * p.sq_t) * EB +
                        sub * 16;
-    qraw = ld16(qrow);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) qraw[f] = ld16(qrow + f * FS);
   } else {
     const float* cqr = p.cq + ((int64_t)bh * p.T + i) * 3;
     cqi[0] = cqr[0]; cqi[1] = cqr[1]; cqi[2] = cqr[2];
@@ -98,15 +107,17 @@ __global__ __launch_bounds__(kThreads) void gather_bwd_q_kernel(Params p) {
   // (k_j in dot mode; c_q,i - c_k,j and ||.||^2 in coordinate mode)
   // sum P dP x and sum P x
   float delta = 0.f;
-  float pdx[EPL], px[EPL];
+  float pdx[NF][EPL], px[NF][EPL];
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) pdx[e] = px[e] = 0.f;
+  for (int f = 0; f < NF; ++f)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) pdx[f][e] = px[f][e] = 0.f;
   float cdx[3] = {0.f, 0.f, 0.f}, cx[3] = {0.f, 0.f, 0.f};
   float r2dx = 0.f, r2x = 0.f, psum = 0.f;
 
   auto group = [&](const int (&dist)[G]) {
     int j[G];
-    uint4 kraw[G], vraw[G];
+    uint4 kraw[G][NF], vraw[G][NF];
     float s[G], dp[G], r2[G], dif[G][3];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -115,13 +126,19 @@ __global__ __launch_bounds__(kThreads) void gather_bwd_q_kernel(Params p) {
       if constexpr (OFF32) {
         const uint32_t ko = ok ? kl32 - (uint32_t)dist[g] * (uint32_t)skt : sub16;
         const uint32_t vo = ok ? vl32 - (uint32_t)dist[g] * (uint32_t)svt : sub16;
-        if constexpr (!COORD) kraw[g] = ld16(khead + ko);
-        vraw[g] = ld16(vhead + vo);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          if constexpr (!COORD) kraw[g][f] = ld16(khead + ko + f * FS);
+          vraw[g][f] = ld16(vhead + vo + f * FS);
+        }
       } else {
         const int64_t ko = ok ? kl - (int64_t)dist[g] * skt : (int64_t)sub16;
         const int64_t vo = ok ? vl - (int64_t)dist[g] * svt : (int64_t)sub16;
-        if constexpr (!COORD) kraw[g] = ld16(khead + ko);
-        vraw[g] = ld16(vhead + vo);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          if constexpr (!COORD) kraw[g][f] = ld16(khead + ko + f * FS);
+          vraw[g][f] = ld16(vhead + vo + f * FS);
+        }
       }
       if constexpr (COORD) {
         const float* c = ckb + (int64_t)(ok ? j[g] : 0) * 3;
@@ -134,8 +151,13 @@ __global__ __launch_bounds__(kThreads) void gather_bwd_q_kernel(Params p) {
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      dp[g] = F::dot(doraw, vraw[g], 0.f);
-      if constexpr (!COORD) s[g] = F::dot(qraw, kraw[g], 0.f);
+      dp[g] = F::dot(doraw[0], vraw[g][0], 0.f);
+      if constexpr (!COORD) s[g] = F::dot(qraw[0], kraw[g][0], 0.f);
+#pragma unroll
+      for (int f = 1; f < NF; ++f) {
+        dp[g] = F::dot(doraw[f], vraw[g][f], dp[g]);
+        if constexpr (!COORD) s[g] = F::dot(qraw[f], kraw[g][f], s[g]);
+      }
     }
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -148,12 +170,15 @@ __global__ __launch_bounds__(kThreads) void gather_bwd_q_kernel(Params p) {
       const float pd = pr * dp[g];
       delta += pd;
       if constexpr (!COORD) {
-        float kf[EPL];
-        F::unpack(kraw[g], kf);
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) {
-          pdx[e] = fmaf(pd, kf[e], pdx[e]);
-          px[e] = fmaf(pr, kf[e], px[e]);
+        for (int f = 0; f < NF; ++f) {
+          float kf[EPL];
+          F::unpack(kraw[g][f], kf);
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) {
+            pdx[f][e] = fmaf(pd, kf[e], pdx[f][e]);
+            px[f][e] = fmaf(pr, kf[e], px[f][e]);
+          }
         }
       } else {
 #pragma unroll
@@ -186,13 +211,16 @@ __global__ __launch_bounds__(kThreads) void gather_bwd_q_kernel(Params p) {
 
   if constexpr (!COORD) {
     if (row_ok) {
-      float dq[EPL];
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) dq[e] = p.scale * (pdx[e] - delta * px[e]);
       const int gb = p.grad_bf16 ? 2 : 4;
       char* dqrow = static_cast<char*>(p.dq) + (b * p.sdq_b + h * p.sdq_h + i * p.sdq_t) * gb +
                     sub * EPL * gb;
-      store_vals<EPL>(dqrow, dq, p.grad_bf16 != 0);
+#pragma unroll
+      for (int f = 0; f < NF; ++f) {
+        float dq[EPL];
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) dq[e] = p.scale * (pdx[f][e] - delta * px[f][e]);
+        store_vals<EPL>(dqrow + f * LG * EPL * gb, dq, p.grad_bf16 != 0);
+      }
     }
   } else {
     if (row_ok && sub == 0) {
@@ -231,9 +259,10 @@ __global__ __launch_bounds__(kThreads) void gather_bwd_kv_kernel(Params p) {
   constexpr bool COORD = SM == SM_COORD;
   constexpr bool UNIFORM = SM == SM_UNIFORM;  // dv only: no score parameters
   using F = Frag<DT>;
-  using Gm = Geo<DT, D>;
-  constexpr int EPL = Gm::EPL, LG = Gm::LG, RPW = Gm::RPW, RPB = Gm::RPB;
+  using Gm = Geo<DT, D, SM>;
+  constexpr int EPL = Gm::EPL, NF = Gm::NF, LG = Gm::LG, RPW = Gm::RPW, RPB = Gm::RPB;
   constexpr int EB = F::BYTES;
+  constexpr int FS = 16 * LG;  // bytes between a lane's fragments
 
   // one key row per lane group of key/value head hk; the query side runs
   // over the G query heads hk G .. hk G + G - 1 that share it (G = 1 in
@@ -265,11 +294,15 @@ __global__ __launch_bounds__(kThreads) void gather_bwd_kv_kernel(Params p) {
   const float bsub = COORD ? p.beta[h0] : 0.f;  // lse includes beta in coordinate mode
 
   // own k and v fragments as stored (dot operands)
-  uint4 kraw_j = make_uint4(0u, 0u, 0u, 0u), vraw_j;
+  uint4 kraw_j[NF], vraw_j[NF];
   {
     const char* vrow = static_cast<const char*>(p.v) + (b * p.sv_b + hk * p.sv_h + j * p.sv_t) * EB +
                        sub * 16;
-    vraw_j = ld16(vrow);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+      vraw_j[f] = ld16(vrow + f * FS);
+      kraw_j[f] = make_uint4(0u, 0u, 0u, 0u);
+    }
   }
   float ckj[3] = {0.f, 0.f, 0.f};
   float gl2 = 0.f, gam = 0.f;
@@ -277,7 +310,8 @@ __global__ __launch_bounds__(kThreads) void gather_bwd_kv_kernel(Params p) {
   if constexpr (SM == SM_DOT) {
     const char* krow = static_cast<const char*>(p.k) + (b * p.sk_b + hk * p.sk_h + j * p.sk_t) * EB +
                        sub * 16;
-    kraw_j = ld16(krow);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) kraw_j[f] = ld16(krow + f * FS);
   } else if constexpr (COORD) {
     const float* ckr = p.ck + ((int64_t)bh * p.T + j) * 3;
     ckj[0] = ckr[0]; ckj[1] = ckr[1]; ckj[2] = ckr[2];
@@ -286,14 +320,16 @@ __global__ __launch_bounds__(kThreads) void gather_bwd_kv_kernel(Params p) {
     cqb = p.cq + (int64_t)bh * p.T * 3;
   }
 
-  float dk[EPL], dv[EPL];
+  float dk[NF][EPL], dv[NF][EPL];
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) dk[e] = dv[e] = 0.f;
+  for (int f = 0; f < NF; ++f)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) dk[f][e] = dv[f][e] = 0.f;
   float dc[3] = {0.f, 0.f, 0.f};
 
   auto group = [&](const int (&dist)[G]) {
     int i[G];
-    uint4 qraw[G], doraw[G];
+    uint4 qraw[G][NF], doraw[G][NF];
     float s[G], dp[G], lse2[G], del[G], dif[G][3];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -303,13 +339,19 @@ __global__ __launch_bounds__(kThreads) void gather_bwd_kv_kernel(Params p) {
       if constexpr (OFF32) {
         const uint32_t qo = ok ? ql32 + (uint32_t)dist[g] * (uint32_t)sqt : ql32;
         const uint32_t doo = ok ? dl32 + (uint32_t)dist[g] * (uint32_t)sdot : dl32;
-        if constexpr (SM == SM_DOT) qraw[g] = ld16(qhead + qo);
-        doraw[g] = ld16(dohead + doo);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          if constexpr (SM == SM_DOT) qraw[g][f] = ld16(qhead + qo + f * FS);
+          doraw[g][f] = ld16(dohead + doo + f * FS);
+        }
       } else {
         const int64_t qo = ok ? ql + (int64_t)dist[g] * sqt : ql;
         const int64_t doo = ok ? dl + (int64_t)dist[g] * sdot : dl;
-        if constexpr (SM == SM_DOT) qraw[g] = ld16(qhead + qo);
-        doraw[g] = ld16(dohead + doo);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          if constexpr (SM == SM_DOT) qraw[g][f] = ld16(qhead + qo + f * FS);
+          doraw[g][f] = ld16(dohead + doo + f * FS);
+        }
       }
       lse2[g] = (lseb[ii] - bsub) * kLog2e;
       if constexpr (!UNIFORM) del[g] = delb[ii];
@@ -327,8 +369,13 @@ __global__ __launch_bounds__(kThreads) void gather_bwd_kv_kernel(Params p) {
     if constexpr (!UNIFORM) {
 #pragma unroll
       for (int g = 0; g < G; ++g) {
-        dp[g] = F::dot(doraw[g], vraw_j, 0.f);
-        if constexpr (SM == SM_DOT) s[g] = F::dot(qraw[g], kraw_j, 0.f);
+        dp[g] = F::dot(doraw[g][0], vraw_j[0], 0.f);
+        if constexpr (SM == SM_DOT) s[g] = F::dot(qraw[g][0], kraw_j[0], 0.f);
+#pragma unroll
+        for (int f = 1; f < NF; ++f) {
+          dp[g] = F::dot(doraw[g][f], vraw_j[f], dp[g]);
+          if constexpr (SM == SM_DOT) s[g] = F::dot(qraw[g][f], kraw_j[f], s[g]);
+        }
       }
 #pragma unroll
       for (int g = 0; g < G; ++g) {
@@ -339,17 +386,23 @@ __global__ __launch_bounds__(kThreads) void gather_bwd_kv_kernel(Params p) {
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const float pr = i[g] < p.T ? fast_exp2(s[g] - lse2[g]) : 0.f;
-      float dof[EPL];
-      F::unpack(doraw[g], dof);
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) dv[e] = fmaf(pr, dof[e], dv[e]);
+      for (int f = 0; f < NF; ++f) {
+        float dof[EPL];
+        F::unpack(doraw[g][f], dof);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) dv[f][e] = fmaf(pr, dof[e], dv[f][e]);
+      }
       if constexpr (UNIFORM) continue;
       const float ds = pr * (dp[g] - del[g]);
       if constexpr (SM == SM_DOT) {
-        float qf[EPL];
-        F::unpack(qraw[g], qf);
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) dk[e] = fmaf(ds, qf[e], dk[e]);
+        for (int f = 0; f < NF; ++f) {
+          float qf[EPL];
+          F::unpack(qraw[g][f], qf);
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) dk[f][e] = fmaf(ds, qf[e], dk[f][e]);
+        }
       } else {
         dc[0] = fmaf(ds, dif[g][0], dc[0]);
         dc[1] = fmaf(ds, dif[g][1], dc[1]);
@@ -383,13 +436,17 @@ __global__ __launch_bounds__(kThreads) void gather_bwd_kv_kernel(Params p) {
   const int gb = p.grad_bf16 ? 2 : 4;
   char* dvrow = static_cast<char*>(p.dv) + (b * p.sdv_b + hk * p.sdv_h + j * p.sdv_t) * gb +
                 sub * EPL * gb;
-  store_vals<EPL>(dvrow, dv, p.grad_bf16 != 0);
-  if constexpr (SM == SM_DOT) {
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) dk[e] *= p.scale;
+  for (int f = 0; f < NF; ++f) store_vals<EPL>(dvrow + f * LG * EPL * gb, dv[f], p.grad_bf16 != 0);
+  if constexpr (SM == SM_DOT) {
     char* dkrow = static_cast<char*>(p.dk) + (b * p.sdk_b + hk * p.sdk_h + j * p.sdk_t) * gb +
                   sub * EPL * gb;
-    store_vals<EPL>(dkrow, dk, p.grad_bf16 != 0);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) dk[f][e] *= p.scale;
+      store_vals<EPL>(dkrow + f * LG * EPL * gb, dk[f], p.grad_bf16 != 0);
+    }
   } else if constexpr (COORD) {
     if (sub == 0) {
       float* o = p.dck + ((int64_t)bh * p.T + j) * 3;
@@ -467,7 +524,7 @@ hipError_t launch_passes(const Params& p, hipStream_t s, int grid, int nblk) {
 
 template <int DT, int D, int SM>
 hipError_t launch_one(const Params& p, hipStream_t s) {
-  constexpr int RPB = Geo<DT, D>::RPB;
+  constexpr int RPB = Geo<DT, D, SM>::RPB;
   const int nblk = (p.T + RPB - 1) / RPB;
   const int grid = xcd_grid(p.B * p.H * nblk);
   return fits_off32(p, Frag<DT>::BYTES) ? launch_passes<DT, D, SM, true>(p, s, grid, nblk)

@@ -5,9 +5,10 @@
 // choose whom to listen to": a fixed list of distances per token), so for a
 // fixed distance delta the keys of consecutive query rows are consecutive
 // rows of K and V.  A wavefront holds 64/LG consecutive query rows, each row
-// spread over LG lanes with 16 bytes (8 bf16 or 4 fp32 elements) per lane,
-// so the K or V rows one distance needs form one contiguous, fully coalesced
-// block of 64 x 16 bytes.  Scores are reduced across the lane group with DPP,
+// spread over LG lanes with NF 16-byte fragments (8 bf16 or 4 fp32 elements
+// each) per lane: fragment f of lane s holds bytes 16 (f LG + s) .. + 15, so
+// each load instruction covers one contiguous 16 LG-byte span of every row
+// of the wavefront (all of it for NF = 1).  Scores are reduced across the lane group with DPP,
 // and the softmax over the row's neighbours runs online (running max, sum
 // and weighted value accumulator; the accumulator is rescaled only when the
 // max grows by more than 2^8).
@@ -23,10 +24,13 @@ namespace {
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 
-template <int DT, int D>
+template <int DT, int D, int SM>
 struct Geo {
-  static constexpr int EPL = Frag<DT>::EPL;  // elements per lane
-  static constexpr int LG = D / EPL;         // lanes per row
+  static constexpr int EPL = Frag<DT>::EPL;  // elements per 16-byte fragment
+  // fragments per lane (gather_frags_per_lane): two shares a row's repeated
+  // per-edge work (score, softmax bookkeeping) between half as many lanes
+  static constexpr int NF = gather_frags_per_lane(DT, D, SM);
+  static constexpr int LG = D / (EPL * NF);  // lanes per row
   static constexpr int RPW = 64 / LG;        // rows per wavefront
   static constexpr int RPB = RPW * kWaves;   // rows per workgroup
   static_assert(LG >= 1 && LG <= 32 && (LG & (LG - 1)) == 0, "row must span 1..32 lanes");
@@ -36,9 +40,10 @@ struct Geo {
 template <int DT, int D, int SM, int G, bool OFF32>
 __global__ __launch_bounds__(kThreads) void gather_fwd_kernel(Params p) {
   using F = Frag<DT>;
-  using Gm = Geo<DT, D>;
-  constexpr int EPL = Gm::EPL, LG = Gm::LG, RPW = Gm::RPW, RPB = Gm::RPB;
+  using Gm = Geo<DT, D, SM>;
+  constexpr int EPL = Gm::EPL, NF = Gm::NF, LG = Gm::LG, RPW = Gm::RPW, RPB = Gm::RPB;
   constexpr int EB = F::BYTES;
+  constexpr int FS = 16 * LG;  // bytes between a lane's fragments
 
   const int nblk = (p.T + RPB - 1) / RPB;
   const int logical = xcd_logical_block(p.B * p.H * nblk);
@@ -65,14 +70,17 @@ __global__ __launch_bounds__(kThreads) void gather_fwd_kernel(Params p) {
   asm volatile("" : "+v"(kl32), "+v"(vl32), "+v"(kl), "+v"(vl));
   const uint32_t sub16 = (uint32_t)sub * 16u;
 
-  uint4 qraw = make_uint4(0u, 0u, 0u, 0u);  // q fragment as stored (dot operand)
+  uint4 qraw[NF];  // q fragments as stored (dot operands)
+#pragma unroll
+  for (int f = 0; f < NF; ++f) qraw[f] = make_uint4(0u, 0u, 0u, 0u);
   float cqi[3] = {0.f, 0.f, 0.f};
   float gl2 = 0.f;  // gamma * log2(e)
   const float* ckb = nullptr;
   if constexpr (SM == SM_DOT) {
     const char* qrow = static_cast<const char*>(p.q) + (b * p.sq_b + h * p.sq_h + i * p.sq_t) * EB +
                        sub * 16;
-    qraw = ld16(qrow);
+#pragma unroll
+    for (int f = 0; f < NF; ++f) qraw[f] = ld16(qrow + f * FS);
   } else if constexpr (SM == SM_COORD) {
     const float* cqr = p.cq + ((int64_t)bh * p.T + i) * 3;
     cqi[0] = cqr[0]; cqi[1] = cqr[1]; cqi[2] = cqr[2];
@@ -81,16 +89,18 @@ __global__ __launch_bounds__(kThreads) void gather_fwd_kernel(Params p) {
   }
 
   float m = -INFINITY, l = 0.f;  // running max (log2 units), row sum
-  float acc[EPL];
+  float acc[NF][EPL];
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) acc[e] = 0.f;
+  for (int f = 0; f < NF; ++f)
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[f][e] = 0.f;
 
   const int imax = i0w + RPW - 1 < p.T - 1 ? i0w + RPW - 1 : p.T - 1;
   // One group of G distances (wave-uniform, ascending; kUnreachable past
   // the end of the list): gather, score, online softmax, accumulate.
   auto group = [&](const int (&dist)[G]) {
     int j[G];
-    uint4 kraw[G], vraw[G];
+    uint4 kraw[G][NF], vraw[G][NF];
     float s[G];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -99,13 +109,19 @@ __global__ __launch_bounds__(kThreads) void gather_fwd_kernel(Params p) {
       if constexpr (OFF32) {
         const uint32_t ko = ok ? kl32 - (uint32_t)dist[g] * (uint32_t)skt : sub16;
         const uint32_t vo = ok ? vl32 - (uint32_t)dist[g] * (uint32_t)svt : sub16;
-        if constexpr (SM == SM_DOT) kraw[g] = ld16(khead + ko);
-        vraw[g] = ld16(vhead + vo);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          if constexpr (SM == SM_DOT) kraw[g][f] = ld16(khead + ko + f * FS);
+          vraw[g][f] = ld16(vhead + vo + f * FS);
+        }
       } else {
         const int64_t ko = ok ? kl - (int64_t)dist[g] * skt : (int64_t)sub16;
         const int64_t vo = ok ? vl - (int64_t)dist[g] * svt : (int64_t)sub16;
-        if constexpr (SM == SM_DOT) kraw[g] = ld16(khead + ko);
-        vraw[g] = ld16(vhead + vo);
+#pragma unroll
+        for (int f = 0; f < NF; ++f) {
+          if constexpr (SM == SM_DOT) kraw[g][f] = ld16(khead + ko + f * FS);
+          vraw[g][f] = ld16(vhead + vo + f * FS);
+        }
       }
       if constexpr (SM == SM_COORD) {
         const float* c = ckb + (int64_t)(ok ? j[g] : 0) * 3;
@@ -117,7 +133,11 @@ __global__ __launch_bounds__(kThreads) void gather_fwd_kernel(Params p) {
     }
     if constexpr (SM == SM_DOT) {
 #pragma unroll
-      for (int g = 0; g < G; ++g) s[g] = F::dot(qraw, kraw[g], 0.f);
+      for (int g = 0; g < G; ++g) {
+        s[g] = F::dot(qraw[0], kraw[g][0], 0.f);
+#pragma unroll
+        for (int f = 1; f < NF; ++f) s[g] = F::dot(qraw[f], kraw[g][f], s[g]);
+      }
 #pragma unroll
       for (int g = 0; g < G; ++g) s[g] = group_sum<LG>(s[g]) * p.scale_log2;
     }
@@ -135,7 +155,9 @@ __global__ __launch_bounds__(kThreads) void gather_fwd_kernel(Params p) {
       const float alpha = m == -INFINITY ? 0.f : fast_exp2(m - mnew);
       l *= alpha;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[e] *= alpha;
+      for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[f][e] *= alpha;
       m = mnew;
     }
     const float neg = m == -INFINITY ? 0.f : -m;
@@ -143,10 +165,13 @@ __global__ __launch_bounds__(kThreads) void gather_fwd_kernel(Params p) {
     for (int g = 0; g < G; ++g) {
       const float pg = fast_exp2(s[g] + neg);
       l += pg;
-      float vf[EPL];
-      F::unpack(vraw[g], vf);
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) acc[e] = fmaf(pg, vf[e], acc[e]);
+      for (int f = 0; f < NF; ++f) {
+        float vf[EPL];
+        F::unpack(vraw[g][f], vf);
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) acc[f][e] = fmaf(pg, vf[e], acc[f][e]);
+      }
     }
   };
 
@@ -169,10 +194,13 @@ __global__ __launch_bounds__(kThreads) void gather_fwd_kernel(Params p) {
 
   if (!row_ok) return;
   const float inv_l = 1.f / l;
-#pragma unroll
-  for (int e = 0; e < EPL; ++e) acc[e] *= inv_l;
   char* orow = static_cast<char*>(p.o) + (b * p.so_b + h * p.so_h + i * p.so_t) * EB + sub * 16;
-  st16_stream(orow, F::pack(acc));
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) acc[f][e] *= inv_l;
+    st16_stream(orow + f * FS, F::pack(acc[f]));
+  }
   if (sub == 0) {
     float lse = (m + fast_log2(l)) * kLn2;
     if constexpr (SM == SM_COORD) lse += p.beta[h];
@@ -189,13 +217,15 @@ inline bool fits_off32(const Params& p, int eb) {
 
 template <int DT, int D, int SM>
 hipError_t launch_one(const Params& p, hipStream_t s) {
-  constexpr int RPB = Geo<DT, D>::RPB;
+  constexpr int RPB = Geo<DT, D, SM>::RPB;
   const int nblk = (p.T + RPB - 1) / RPB;
   const int grid = xcd_grid(p.B * p.H * nblk);
+  // distances per step: four 16-byte fragments of K and V in flight per lane
+  constexpr int G = 4 / Geo<DT, D, SM>::NF;
   if (fits_off32(p, Frag<DT>::BYTES))
-    hipLaunchKernelGGL((gather_fwd_kernel<DT, D, SM, 4, true>), dim3(grid), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((gather_fwd_kernel<DT, D, SM, G, true>), dim3(grid), dim3(kThreads), 0, s, p);
   else
-    hipLaunchKernelGGL((gather_fwd_kernel<DT, D, SM, 4, false>), dim3(grid), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((gather_fwd_kernel<DT, D, SM, G, false>), dim3(grid), dim3(kThreads), 0, s, p);
   return hipGetLastError();
 }
 
@@ -213,6 +243,8 @@ hipError_t launch_d(const Params& p, hipStream_t s) {
 }  // namespace
 
 int gather_rows_per_block(int dtype, int D) {
+  // the smallest query-side block of the gather and explicit-list kernels
+  // (one fragment per lane): sizes the per-block partials in the workspace
   const int epl = dtype == DT_BF16 ? 8 : 4;
   return (64 / (D / epl)) * kWaves;
 }
