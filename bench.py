@@ -39,8 +39,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workloads",
-                    default="band,uniform,band_gqa,dilated_gqa,csr_dilated,csr_random,decode_band,decode_dilated,"
-                            "dilated,coord,ultra")
+                    default="band,band_bf16grad,uniform,band_gqa,dilated_gqa,csr_dilated,csr_random,decode_band,"
+                            "decode_dilated,ultra_band,dilated,coord,ultra")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle sample length")
     ap.add_argument("--algo", default="auto")
@@ -178,19 +178,21 @@ def run_workload(w, steps, warmup, algo, with_backward=True, no_cold=False):
     if bwd:
         gshape = (w.B, w.H, w.T, w.D)
         kvshape = (w.B, w.kv_heads, w.T, w.D)
-        grads = {"dv": torch.empty(kvshape, dtype=torch.float32, device=dev)}
+        gdt = torch.bfloat16 if w.grad_bf16 else torch.float32
+        grads = {"dv": torch.empty(kvshape, dtype=gdt, device=dev)}
         if coord:
             grads.update(dcq=torch.empty((w.B, w.H, w.T, 3), dtype=torch.float32, device=dev),
                          dck=torch.empty((w.B, w.H, w.T, 3), dtype=torch.float32, device=dev),
                          dgamma=torch.empty((w.H,), dtype=torch.float32, device=dev),
                          dbeta=torch.empty((w.H,), dtype=torch.float32, device=dev))
         elif not w.uniform:
-            grads.update(dq=torch.empty(gshape, dtype=torch.float32, device=dev),
-                         dk=torch.empty(kvshape, dtype=torch.float32, device=dev))
+            grads.update(dq=torch.empty(gshape, dtype=gdt, device=dev),
+                         dk=torch.empty(kvshape, dtype=gdt, device=dev))
         from sparse_causal_attention_amd import sa_bwd_workspace_size
         ws = torch.empty(sa_bwd_workspace_size(g, x["v"], heads=w.H), dtype=torch.uint8, device=dev)
         bkw = dict(v=x["v"], o=o, lse=lse, dout=x["do"], cq=x.get("cq"), ck=x.get("ck"),
-                   gamma=x.get("gamma"), beta=x.get("beta"), workspace=ws, algo=algo, **grads)
+                   gamma=x.get("gamma"), beta=x.get("beta"), workspace=ws, algo=algo,
+                   grad_dtype=gdt, **grads)
         if not coord and not w.uniform:
             bkw.update(q=x["q"], k=x["k"])
 
@@ -312,7 +314,7 @@ def run_decode(w, steps, warmup, no_cold=False):
 
 
 def summarize(w, r, steps):
-    m = models(w)
+    m = models(w, grad_bytes=2 if w.grad_bf16 else 4)
     tokens = w.B if w.decode else w.B * w.T  # a decode step makes one token per sequence
     fb = r["fwd_ms"] + r["bwd_ms"]
     wall = r["wall_s"]
@@ -320,7 +322,8 @@ def summarize(w, r, steps):
         "workload": w.name,
         "shape": {"B": w.B, "H": w.H, "H_kv": w.kv_heads, "T": w.T, "D": w.D, "window": w.window,
                   "offsets": list(w.offsets), "graph": w.graph, "dtype": w.dtype_name,
-                  "score": score_name(w), "backward": w.backward},
+                  "score": score_name(w), "backward": w.backward,
+                  "grad_dtype": ("bf16" if w.grad_bf16 else "f32") if w.backward else None},
         # decode steps last microseconds: their rate comes from the kernel events
         "tokens_per_s": tokens / (r["fwd_ms"] * 1e-3) if w.decode else tokens * steps / wall,
         "edges_per_s": m["edges"] / (r["fwd_ms"] * 1e-3) if w.decode else m["edges"] * steps / wall,
@@ -869,8 +872,9 @@ def main():
     host_inputs = {}
     for name in names:
         w = WORKLOADS[name]
-        steps = args.steps if name != "ultra" else max(2, min(args.steps, 5))
-        warm = args.warmup if name != "ultra" else min(args.warmup, 2)
+        long_t = w.T > (1 << 24)  # the 2^26-token workloads: tens of ms per call
+        steps = args.steps if not long_t else max(2, min(args.steps, 5))
+        warm = args.warmup if not long_t else min(args.warmup, 2)
         if w.decode:
             steps, warm = max(steps, 200), max(warm, 20)  # microsecond steps
         print("[bench] %s: %d warmup + %d timed steps" % (name, warm, steps), file=sys.stderr, flush=True)

@@ -192,14 +192,41 @@ __global__ __launch_bounds__(kThreads) void gather_fwd_kernel(Params p) {
     group(dist);
   }
 
-  if (!row_ok) return;
   const float inv_l = 1.f / l;
-  char* orow = static_cast<char*>(p.o) + (b * p.so_b + h * p.so_h + i * p.so_t) * EB + sub * 16;
+  if constexpr (NF == 1) {
+    if (!row_ok) return;
 #pragma unroll
-  for (int f = 0; f < NF; ++f) {
+    for (int e = 0; e < EPL; ++e) acc[0][e] *= inv_l;
+    char* orow = static_cast<char*>(p.o) + (b * p.so_b + h * p.so_h + i * p.so_t) * EB + sub * 16;
+    st16_stream(orow, F::pack(acc[0]));
+  } else {
+    // Two fragments per lane cover half of each row per instruction; one
+    // cross-half swap (v_permlane32_swap) turns them into two stores that each
+    // write whole rows: the first the wavefront's rows 0 .. RPW/2 - 1, the
+    // second the rest (lanes l and l + 32 hold the two halves of a row), so
+    // no row is written as two partial lines.
+    static_assert(NF == 2 && RPW % 2 == 0, "two fragments per lane");
+    uint4 x[2];
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) acc[f][e] *= inv_l;
-    st16_stream(orow + f * FS, F::pack(acc[f]));
+    for (int f = 0; f < 2; ++f) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) acc[f][e] *= inv_l;
+      x[f] = F::pack(acc[f]);
+    }
+    uint32_t* x0 = &x[0].x;
+    uint32_t* x1 = &x[1].x;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const auto r = __builtin_amdgcn_permlane32_swap(x0[c], x1[c], false, false);
+      x0[c] = r[0];  // lanes 0..31: fragment 0 of rows 0..RPW/2-1; lanes 32..63: their fragment 1
+      x1[c] = r[1];  // the same for rows RPW/2 .. RPW-1
+    }
+    const int half = lane >> 5;
+    const int ra = i0w + (lane & 31) / LG;  // row of x[0]; x[1] holds row ra + RPW / 2
+    char* obase = static_cast<char*>(p.o) + (b * p.so_b + h * p.so_h) * EB + sub * 16 + half * FS;
+    if (ra < p.T) st16_stream(obase + (int64_t)ra * p.so_t * EB, x[0]);
+    if (ra + RPW / 2 < p.T) st16_stream(obase + (int64_t)(ra + RPW / 2) * p.so_t * EB, x[1]);
+    if (!row_ok) return;
   }
   if (sub == 0) {
     float lse = (m + fast_log2(l)) * kLn2;

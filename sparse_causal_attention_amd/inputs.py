@@ -51,6 +51,7 @@ class Workload:
     Hkv: int = 0           # key/value heads (0: H)
     graph: str = "distance"  # "distance", "lists" (same graph as lists) or "random" lists
     extra: int = 0           # random lists: distinct earlier keys per row beyond the window
+    grad_bf16: bool = False  # gradients stored in bf16 (else fp32)
 
     @property
     def kv_heads(self) -> int:
@@ -100,6 +101,12 @@ WORKLOADS = {
     # ultra-long single head, forward only: window 64 + distances 2^6..2^25
     "ultra": Workload("ultra", 5, 1, 1, 2 ** 26, 64, torch.bfloat16, 64, _pow2(6, 25),
                       backward=False),
+    # the same inputs with the window alone (the ultra workload's time and
+    # traffic split into its window and long-range parts)
+    "ultra_band": Workload("ultra_band", 5, 1, 1, 2 ** 26, 64, torch.bfloat16, 64, (), backward=False),
+    # the band workload with gradients stored in bf16 (the gradient dtype of
+    # a bf16 model); the fp32-gradient band workload stays the reference
+    "band_bf16grad": Workload("band_bf16grad", 2, 1, 8, 16384, 64, torch.bfloat16, 256, (), grad_bf16=True),
 }
 
 

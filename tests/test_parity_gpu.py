@@ -176,6 +176,12 @@ def test_dilated_bf16_gradients():
     run_and_compare(WORKLOADS["dilated"], grad_dtype=torch.bfloat16, B=1, H=4)
 
 
+def test_band_bf16_gradients_full_size():
+    """The band kernels' bf16-gradient path (the bench's band_bf16grad
+    workload) on every element of the full-size band workload."""
+    run_and_compare(WORKLOADS["band_bf16grad"], grad_dtype=torch.bfloat16)
+
+
 def test_ultra_long_sampled_rows():
     w = WORKLOADS["ultra"]
     _say("ultra: generating %d x %d bf16 inputs on device" % (w.T, w.D))
@@ -242,6 +248,16 @@ def test_uniform_full_size():
 @pytest.mark.parametrize("dt", [torch.float32, torch.bfloat16])
 def test_coord_small(dt):
     w = Workload("coord_small", 8, 2, 3, 300, 32, dt, 3, (4, 8, 16, 32, 64, 128), coord=True)
+    run_and_compare(w)
+
+
+@pytest.mark.parametrize("T, D", [(300, 64), (77, 128), (16, 64)])
+def test_coord_two_fragments_per_lane(T, D):
+    """The coordinate score on bf16 rows of 64 and 128 elements (two 16-byte
+    fragments per lane, whole-row output stores after a cross-half swap), with
+    ragged last wavefronts: rows past T are neither stored nor mixed into
+    stored rows."""
+    w = Workload("coord_wide", 8, 2, 3, T, D, torch.bfloat16, 5, (8, 16, 32, 64), coord=True)
     run_and_compare(w)
 
 
