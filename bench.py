@@ -430,7 +430,7 @@ def roofline_for(w, r, m, peaks=None):
     byt = byt_g if model == "gather" else byt_c
     gbs = byt / (ms * 1e6)
     tfs = fl / (ms * 1e9)
-    dot_mfma = not (w.coord or w.uniform or w.decode)  # bf16 dot scores run on the matrix cores
+    dot_mfma = kernel.startswith("band_")  # the band kernels run their products on the matrix cores
     intensity = fl / byt_c if byt_c else 0.0
     bound = "mfma" if dot_mfma and intensity > RIDGE else "hbm"
     if bound == "mfma":
@@ -826,6 +826,11 @@ CPU_EXTRA_SECONDS = 6.0
 SUMMARY_LAST = ("band", "dilated", "coord", "ultra")
 
 
+def summary_order(names):
+    """Workload names with the configurations the metric is quoted on last."""
+    return [n for n in names if n not in SUMMARY_LAST] + [n for n in SUMMARY_LAST if n in names]
+
+
 def compact(s):
     """One short entry per workload for the end of the line."""
     rf = s["roofline"]
@@ -936,8 +941,7 @@ def main():
     else:
         line["cpu_baseline"] = None
     line["extra"] = {n: s2 for n, (_, _, s2) in results.items() if n != headline}
-    order = [n for n in results if n not in SUMMARY_LAST] + [n for n in SUMMARY_LAST if n in results]
-    line["summary"] = {n: compact(results[n][2]) for n in order}
+    line["summary"] = {n: compact(results[n][2]) for n in summary_order(list(results))}
     print(json.dumps(line), flush=True)
 
 

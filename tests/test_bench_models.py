@@ -116,3 +116,35 @@ def test_summary_carries_warm_and_cold_figures():
 def test_median():
     assert bench.median([3.0, 1.0, 2.0]) == 2.0
     assert bench.median([4.0, 1.0, 2.0, 3.0]) == 2.5
+
+
+def test_roofline_bound_follows_intensity():
+    """The roof is the one the call's intensity (flops over compulsory bytes)
+    falls under: the band workload (W = 256, about 115-126 flop/B) sits under
+    the HBM roof, the dense W = T = 2048 variant (about 500 flop/B) above the
+    ridge of 312.5 flop/B, under the bf16 matrix-core roof; the gather
+    kernels report no matrix-core fraction."""
+    assert abs(bench.RIDGE - 312.5) < 1e-9
+    band = WORKLOADS["band"]
+    r = {"fwd_ms": 0.02, "bwd_ms": 0.07, "plan_fwd": "band_fwd_kernel",
+         "plan_bwd": "band_bwd_prepass_kernel+band_bwd_kernel"}
+    e = bench.roofline_for(band, r, bench.models(band))
+    assert e["bound"] == "hbm" and e["unit"] == "GB/s" and e["intensity_flop_per_byte"] < bench.RIDGE
+    assert e["mfma_bf16_frac"] is not None
+    dense = WORKLOADS["band_dense"]
+    e = bench.roofline_for(dense, r, bench.models(dense))
+    assert e["bound"] == "mfma" and e["unit"] == "TFLOP/s" and e["peak"] == bench.MFMA_BF16_PEAK_TFS
+    assert abs(e["frac"] - bench.models(dense)["bwd_flops"] / 0.07e9 / bench.MFMA_BF16_PEAK_TFS) < 1e-3
+    dil = WORKLOADS["dilated"]
+    r = {"fwd_ms": 0.09, "bwd_ms": 0.3, "plan_fwd": "gather_fwd_kernel(dot)",
+         "plan_bwd": "gather_bwd_q_kernel(dot)+gather_bwd_kv_kernel(dot)"}
+    e = bench.roofline_for(dil, r, bench.models(dil), {"copy_GBs": 5500.0, "mfma_bf16_TFs": 1800.0})
+    assert e["bound"] == "hbm" and e["mfma_bf16_frac"] is None and "mfma_frac_of_measured_loop" not in e
+    assert abs(e["frac_of_measured_copy"] - e["achieved"] / 5500.0) < 1e-3
+
+
+def test_summary_keeps_the_quoted_configs_last():
+    names = ["band", "band_bf16grad", "uniform", "decode_dilated", "ultra_band", "dilated", "coord", "ultra"]
+    order = bench.summary_order(names)
+    assert order[-4:] == ["band", "dilated", "coord", "ultra"] and sorted(order) == sorted(names)
+    assert bench.summary_order(["uniform", "band"]) == ["uniform", "band"]
