@@ -652,7 +652,19 @@ PROFILE_PASSES = {
     "mfma": ("rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 MfmaUtil VALUBusy --output-format csv "
              "-d <dir>/<workload>/mfma -o run --",
              "--steps 3 --warmup 1 --no-cpu-baseline --no-cold --no-peaks"),
+    "insts": ("rocprofv3 --pmc SQ_INSTS_VALU SQ_INSTS_VMEM_RD SQ_INSTS_LDS SQ_INSTS_SALU SQ_INSTS_MFMA SQ_WAVES "
+              "--output-format csv -d <dir>/<workload>/insts -o run --",
+              "--steps 3 --warmup 1 --no-cpu-baseline --no-cold --no-peaks"),
+    "loadpath": ("rocprofv3 --pmc TA_TA_BUSY_sum TA_DATA_STALLED_BY_TC_CYCLES_sum TCC_HIT_sum TCC_MISS_sum "
+                 "GRBM_GUI_ACTIVE --output-format csv -d <dir>/<workload>/loadpath -o run --",
+                 "--steps 3 --warmup 1 --no-cpu-baseline --no-cold --no-peaks"),
 }
+# Per-dispatch counters kept in profiles/counters.json (besides FETCH_SIZE and
+# WRITE_SIZE, which go to profiles/traffic.json).
+COUNTER_KEYS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "MfmaUtil", "VALUBusy", "SQ_INSTS_VALU", "SQ_INSTS_VMEM_RD",
+                "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_INSTS_MFMA", "SQ_WAVES", "TA_TA_BUSY_sum",
+                "TA_DATA_STALLED_BY_TC_CYCLES_sum", "TCC_HIT_sum", "TCC_MISS_sum", "GRBM_GUI_ACTIVE")
+CUS, XCDS, SIMDS = 256, 8, 1024  # MI355X: compute units, accelerator dies, SIMDs
 
 
 def profile_command(pass_name, workload):
@@ -730,8 +742,12 @@ def record_profiles(root):
                "copy": None, "kernels": {}}
     counters = {"source_sha256": digest,
                 "note": "per dispatch means: SQ_INSTS_VALU_MFMA_MOPS_BF16 (bf16 MFMA flops / 512), MfmaUtil and "
-                        "VALUBusy (rocprofv3 derived metrics, percent)",
-                "command": profile_command("mfma", "<workload>"), "kernels": {}}
+                        "VALUBusy (rocprofv3 derived metrics, percent), instruction counts (wavefront "
+                        "instructions, summed over the GPU), TA_TA_BUSY_sum (texture-addresser busy cycles "
+                        "summed over the 256 compute units), TCC hits and misses, GRBM_GUI_ACTIVE (GPU-busy "
+                        "cycles summed over the 8 dies)",
+                "commands": {p: profile_command(p, "<workload>") for p in ("mfma", "insts", "loadpath")},
+                "kernels": {}}
     for workload in sorted(os.listdir(root)):
         wdir = os.path.join(root, workload)
         if workload not in WORKLOADS or not os.path.isdir(wdir):
@@ -759,7 +775,7 @@ def record_profiles(root):
             open(os.path.join(prof, "%s__%s.txt" % (fam, workload)), "w").write("\n".join(lines) + "\n")
         # counters: mean per dispatch of each counter per kernel symbol
         per = {}
-        for pass_name in ("fetch", "write", "mfma"):
+        for pass_name in ("fetch", "write", "mfma", "insts", "loadpath"):
             path = os.path.join(wdir, pass_name, "run_counter_collection.csv")
             if not os.path.exists(path):
                 continue
@@ -780,7 +796,7 @@ def record_profiles(root):
             if "FETCH_SIZE" in vals and "WRITE_SIZE" in vals:
                 traffic["kernels"].setdefault(workload, {})[plan] = {
                     "fetch_kib": vals["FETCH_SIZE"], "write_kib": vals["WRITE_SIZE"], "symbol": sym}
-            m = {k: vals[k] for k in ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "MfmaUtil", "VALUBusy") if k in vals}
+            m = {k: vals[k] for k in COUNTER_KEYS if k in vals}
             if m:
                 counters["kernels"].setdefault(workload, {})[plan] = dict(m, symbol=sym)
     json.dump(traffic, open(os.path.join(prof, "traffic.json"), "w"), indent=1)
@@ -793,7 +809,7 @@ def record_profiles(root):
     for workload in sorted(set(traffic["kernels"]) | set(counters["kernels"])):
         lines = ["# rocprofv3 --pmc counters per dispatch, workload %s, one MI355X (gfx950)" % workload,
                  "# commands (from /tmp, TMPDIR=/tmp, on the repository as committed):"]
-        for p in ("fetch", "write", "mfma"):
+        for p in ("fetch", "write", "mfma", "insts", "loadpath"):
             lines.append("#   " + profile_command(p, workload))
         lines.append("# libsa.so source sha256: " + digest)
         if cf:
@@ -812,6 +828,23 @@ def record_profiles(root):
                 plan, t.get("fetch_kib", float("nan")), t.get("write_kib", float("nan")), hbm,
                 512 * c.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", float("nan")) / 1e9,
                 c.get("MfmaUtil", float("nan")), c.get("VALUBusy", float("nan"))))
+        # issue and load-path figures: per SIMD instruction counts, and the texture addresser's
+        # busy fraction = TA_TA_BUSY_sum / CUs over GRBM_GUI_ACTIVE / dies
+        lines.append("%-34s %12s %12s %10s %10s %10s %9s %9s" % (
+            "kernel (plan name)", "VALU/SIMD", "VMEM_RD/SIMD", "LDS/SIMD", "SALU/SIMD", "MFMA/SIMD",
+            "TA_busy%", "L2_hit%"))
+        for plan in names:
+            c = counters["kernels"].get(workload, {}).get(plan, {})
+            if "SQ_INSTS_VALU" not in c:
+                continue
+            ta = (100.0 * c["TA_TA_BUSY_sum"] / CUS / (c["GRBM_GUI_ACTIVE"] / XCDS)
+                  if c.get("GRBM_GUI_ACTIVE") and "TA_TA_BUSY_sum" in c else float("nan"))
+            hm = c.get("TCC_HIT_sum", 0.0) + c.get("TCC_MISS_sum", 0.0)
+            l2 = 100.0 * c["TCC_HIT_sum"] / hm if hm else float("nan")
+            lines.append("%-34s %12.0f %12.0f %10.0f %10.0f %10.0f %9.1f %9.1f" % (
+                plan, c["SQ_INSTS_VALU"] / SIMDS, c.get("SQ_INSTS_VMEM_RD", 0.0) / SIMDS,
+                c.get("SQ_INSTS_LDS", 0.0) / SIMDS, c.get("SQ_INSTS_SALU", 0.0) / SIMDS,
+                c.get("SQ_INSTS_MFMA", 0.0) / SIMDS, ta, l2))
         open(os.path.join(prof, "counters__%s.txt" % workload), "w").write("\n".join(lines) + "\n")
 
 
