@@ -66,8 +66,8 @@ __global__ __launch_bounds__(kThreads) void csr_fwd_kernel(Params p) {
   const int nblk = (p.T + RPB - 1) / RPB;
   const int logical = xcd_logical_block(p.B * p.H * nblk);
   if (logical < 0) return;
-  const int bh = logical / nblk, rb = logical - bh * nblk;
-  const int b = bh / p.H, h = bh - b * p.H;
+  const QueryBlock qb = query_block(logical, nblk, p.H, p.G);
+  const int bh = qb.bh, rb = qb.rb, b = qb.b, h = qb.h;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int sub = lane % LG;
@@ -178,8 +178,8 @@ __global__ __launch_bounds__(kThreads) void csr_bwd_q_kernel(Params p) {
   const int nblk = (p.T + RPB - 1) / RPB;
   const int logical = xcd_logical_block(p.B * p.H * nblk);
   if (logical < 0) return;
-  const int bh = logical / nblk, rb = logical - bh * nblk;
-  const int b = bh / p.H, h = bh - b * p.H;
+  const QueryBlock qb = query_block(logical, nblk, p.H, p.G);
+  const int bh = qb.bh, rb = qb.rb, b = qb.b, h = qb.h;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int sub = lane % LG;

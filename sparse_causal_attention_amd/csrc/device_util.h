@@ -314,6 +314,26 @@ __device__ __forceinline__ int xcd_logical_block(int total) {
   const int logical = (b % kNumXcd) * per + b / kNumXcd;
   return logical < total ? logical : -1;
 }
+// Query-side block order for grouped key/value heads: logical block
+// ((b H_kv + hk) nblk + rb) G + g is row block rb of query head hk G + g of
+// batch b, so the G query heads that read one key/value head take the same
+// row block one after another (on the same XCD), and the key/value rows they
+// gather are fetched into that XCD's L2 once for the group instead of once per
+// query head.  With G = 1 this is the plain (b, h, rb) order.
+struct QueryBlock {
+  int b, h, bh, rb;
+};
+__device__ __forceinline__ QueryBlock query_block(int logical, int nblk, int H, int G) {
+  QueryBlock q;
+  const int g = logical % G, t = logical / G;
+  const int bk = t / nblk;
+  q.rb = t - bk * nblk;
+  const int Hkv = H / G;
+  q.b = bk / Hkv;
+  q.h = (bk - q.b * Hkv) * G + g;
+  q.bh = q.b * H + q.h;
+  return q;
+}
 inline int xcd_grid(int total) {
   const int per = (total + kNumXcd - 1) / kNumXcd;
   return per * kNumXcd;

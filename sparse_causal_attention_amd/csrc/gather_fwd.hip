@@ -48,8 +48,8 @@ __global__ __launch_bounds__(kThreads) void gather_fwd_kernel(Params p) {
   const int nblk = (p.T + RPB - 1) / RPB;
   const int logical = xcd_logical_block(p.B * p.H * nblk);
   if (logical < 0) return;
-  const int bh = logical / nblk, rb = logical - bh * nblk;
-  const int b = bh / p.H, h = bh - b * p.H;
+  const QueryBlock qb = query_block(logical, nblk, p.H, p.G);
+  const int bh = qb.bh, rb = qb.rb, b = qb.b, h = qb.h;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform
   const int sub = lane % LG;
