@@ -830,21 +830,25 @@ def record_profiles(root):
                 c.get("MfmaUtil", float("nan")), c.get("VALUBusy", float("nan"))))
         # issue and load-path figures: per SIMD instruction counts, and the texture addresser's
         # busy fraction = TA_TA_BUSY_sum / CUs over GRBM_GUI_ACTIVE / dies
-        lines.append("%-34s %12s %12s %10s %10s %10s %9s %9s" % (
+        # TA_floor%: the share of the kernel's time the texture addresser would need at its nominal
+        # 16 cycles per 64-lane load instruction (64 B per cycle for 16-byte lanes)
+        lines.append("%-34s %12s %12s %10s %10s %10s %9s %9s %9s" % (
             "kernel (plan name)", "VALU/SIMD", "VMEM_RD/SIMD", "LDS/SIMD", "SALU/SIMD", "MFMA/SIMD",
-            "TA_busy%", "L2_hit%"))
+            "TA_busy%", "TA_floor%", "L2_hit%"))
         for plan in names:
             c = counters["kernels"].get(workload, {}).get(plan, {})
             if "SQ_INSTS_VALU" not in c:
                 continue
             ta = (100.0 * c["TA_TA_BUSY_sum"] / CUS / (c["GRBM_GUI_ACTIVE"] / XCDS)
                   if c.get("GRBM_GUI_ACTIVE") and "TA_TA_BUSY_sum" in c else float("nan"))
+            floor = (100.0 * c.get("SQ_INSTS_VMEM_RD", 0.0) * 16 / CUS / (c["GRBM_GUI_ACTIVE"] / XCDS)
+                     if c.get("GRBM_GUI_ACTIVE") else float("nan"))
             hm = c.get("TCC_HIT_sum", 0.0) + c.get("TCC_MISS_sum", 0.0)
             l2 = 100.0 * c["TCC_HIT_sum"] / hm if hm else float("nan")
-            lines.append("%-34s %12.0f %12.0f %10.0f %10.0f %10.0f %9.1f %9.1f" % (
+            lines.append("%-34s %12.0f %12.0f %10.0f %10.0f %10.0f %9.1f %9.1f %9.1f" % (
                 plan, c["SQ_INSTS_VALU"] / SIMDS, c.get("SQ_INSTS_VMEM_RD", 0.0) / SIMDS,
                 c.get("SQ_INSTS_LDS", 0.0) / SIMDS, c.get("SQ_INSTS_SALU", 0.0) / SIMDS,
-                c.get("SQ_INSTS_MFMA", 0.0) / SIMDS, ta, l2))
+                c.get("SQ_INSTS_MFMA", 0.0) / SIMDS, ta, floor, l2))
         open(os.path.join(prof, "counters__%s.txt" % workload), "w").write("\n".join(lines) + "\n")
 
 
