@@ -892,7 +892,7 @@ def main():
         record_profiles(args.record_profiles)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        sys.stderr.write("bench.py measures one GPU only: this build has no multi-GPU path "
+        sys.stderr.write("bench.py measures one GPU only: the library has no multi-GPU path "
                          "(independent (batch, head) slices would shard without communication; "
                          "see the sharding notes in the design document).\n")
         sys.exit(2)

@@ -66,7 +66,7 @@ extern "C" {
 typedef enum {
   SA_OK = 0,
   SA_ERR_INVALID_ARG = 1,    /* null pointer, size < 1, negative offset, bad alignment, ... */
-  SA_ERR_UNSUPPORTED = 2,    /* a valid request this build does not implement (e.g. D = 48) */
+  SA_ERR_UNSUPPORTED = 2,    /* a valid request the library does not implement (e.g. D = 48) */
   SA_ERR_SHAPE_MISMATCH = 3, /* graph T differs from the descriptor's T */
   SA_ERR_WORKSPACE = 4,      /* backward workspace missing or too small */
   SA_ERR_HIP = 5             /* a kernel launch reported an error */
