@@ -39,9 +39,11 @@
  *  - Coordinates c_q, c_k (and their gradients) are [B, H, T, 3] fp32,
  *    contiguous.  gamma, beta (and dgamma, dbeta) are [H] fp32.
  *  - Every pointer passed to sa_fwd / sa_bwd is a device pointer owned by the
- *    caller.  The library never allocates or frees device memory; the one
- *    device region it refers to beyond a call is the buffer an explicit-list
- *    graph was uploaded into (sa_graph_upload), which stays the caller's.
+ *    caller.  The library never allocates or frees device memory; the device
+ *    regions it refers to beyond a call are the buffer an explicit-list graph
+ *    was uploaded into (sa_graph_upload), which stays the caller's, and its
+ *    own static scratch array for sa_bwd_noalloc (SA_NOALLOC_SCRATCH_BYTES per
+ *    GPU, part of the library's device code, held until the process ends).
  *  - Calls are asynchronous on the given stream (a hipStream_t; NULL is the
  *    null stream).  SA_OK means the work was validated and enqueued.  sa_fwd,
  *    sa_bwd and sa_decode only launch kernels (no allocation, memset or
