@@ -230,6 +230,23 @@ def test_ragged_shapes(B, H, T, D, dt, W, offs):
     run_and_compare(w)
 
 
+# Windows narrower than a 64-key tile, forced onto the band kernels (the call
+# fails if they do not apply): a 32 x 32 block of keys and queries can then
+# cross both bounds of the window at once, and a wavefront's first and
+# diagonal blocks are the same or adjacent -- the two-sided mask case of the
+# forward, the dq units and the dk/dv units.
+@pytest.mark.parametrize("T,W,offs", [
+    (300, 16, ()),
+    (517, 17, (64, 256)),
+    (1000, 31, ()),
+    (777, 33, (40, 100, 500)),
+    (1200, 63, ()),
+])
+def test_band_narrow_windows(T, W, offs):
+    w = Workload("band_narrow", 13, 2, 2, T, 64, torch.bfloat16, W, offs)
+    run_and_compare(w, algo="band")
+
+
 @pytest.mark.parametrize("B,H,T,D,dt,W,offs", [
     (2, 3, 300, 32, torch.float32, 3, (4, 8, 16, 32, 64, 128)),
     (1, 2, 1000, 64, torch.bfloat16, 4, tuple(2 ** k for k in range(10))),
