@@ -241,6 +241,9 @@ def test_ragged_shapes(B, H, T, D, dt, W, offs):
     (1000, 31, ()),
     (777, 33, (40, 100, 500)),
     (1200, 63, ()),
+    (16, 16, ()),          # the smallest band graph: T = W = 16
+    (40, 16, (32,)),       # shorter than one tile, one long-range distance
+    (100, 5000, ()),       # window far past T: dense causal
 ])
 def test_band_narrow_windows(T, W, offs):
     w = Workload("band_narrow", 13, 2, 2, T, 64, torch.bfloat16, W, offs)
