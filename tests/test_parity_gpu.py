@@ -281,13 +281,18 @@ def test_coord_two_fragments_per_lane(T, D):
     run_and_compare(w)
 
 
-def test_strided_inputs():
-    """q, k, v, dout as [B, T, H, D] storage viewed as [B, H, T, D]."""
-    B, H, T, D, W, offs = 2, 4, 777, 64, 6, (8, 16, 32, 64, 128, 256)
+@pytest.mark.parametrize("W,kernels", [(6, "gather"), (64, "band")])
+def test_strided_inputs(W, kernels):
+    """q, k, v, dout as [B, T, H, D] storage viewed as [B, H, T, D] (row
+    stride H D), on the gather kernels (W = 6) and on the band kernels
+    (W = 64), both with long-range distances."""
+    B, H, T, D, offs = 2, 4, 777, 64, (8, 16, 32, 64, 128, 256)
     gen = torch.Generator().manual_seed(77)
     base = {n: torch.randn((B, T, H, D), generator=gen).to(torch.bfloat16) for n in ("q", "k", "v", "do")}
     xd = {n: t.to(DEV).permute(0, 2, 1, 3) for n, t in base.items()}
     g = sa_build_graph(T, W, offs)
+    for which in ("fwd", "bwd"):
+        assert sa_describe_plan(g, xd["v"], which=which).startswith(kernels), which
     o, lse = sa_fwd(g, xd["q"], xd["k"], xd["v"])
     gr = sa_bwd(g, xd["q"], xd["k"], xd["v"], o, lse, xd["do"])
     hv = {n: host_view(t.permute(0, 2, 1, 3).contiguous()) for n, t in base.items()}
