@@ -303,10 +303,17 @@ def test_strided_inputs(W, kernels):
         assert maxabs(gr[key], ref[key]) <= 2e-2, key
 
 
-def test_row_zero_identity_and_determinism():
+@pytest.mark.parametrize("W,offs,kernels", [(4, tuple(2 ** k for k in range(14)), "gather"),
+                                             (256, (), "band"), (64, (128, 1024), "band")])
+def test_row_zero_identity_and_determinism(W, offs, kernels):
+    """Row 0 (one key) returns v_0 exactly; forward and backward are bitwise
+    identical from run to run (no atomics, fixed summation order), on the
+    gather kernels and on the band kernels (persistent backward)."""
     w = WORKLOADS["dilated"]
     x = {k: v.to(DEV) for k, v in make_inputs(w, B=1, H=2, T=4096).items()}
-    g = sa_build_graph(4096, w.window, w.offsets)
+    g = sa_build_graph(4096, W, offs)
+    for which in ("fwd", "bwd"):
+        assert sa_describe_plan(g, x["v"], which=which).startswith(kernels), which
     o1, l1 = sa_fwd(g, x["q"], x["k"], x["v"])
     o2, l2 = sa_fwd(g, x["q"], x["k"], x["v"])
     # row 0 has one key: o_0 = v_0 exactly, lse_0 = s_00
@@ -320,11 +327,16 @@ def test_row_zero_identity_and_determinism():
         assert torch.equal(g1[key], g2[key]), key
 
 
-def test_outputs_stay_in_bounds():
-    """Canaries around every output: nothing outside the tensors is written."""
-    B, H, T, D, W, offs = 1, 2, 1001, 64, 4, (4, 8, 16, 32, 64)
+@pytest.mark.parametrize("W,offs,kernels", [(4, (4, 8, 16, 32, 64), "gather"), (256, (), "band"),
+                                             (64, (100, 700), "band")])
+def test_outputs_stay_in_bounds(W, offs, kernels):
+    """Canaries around every output: nothing outside the tensors is written
+    (T = 1001 is not a multiple of any row block or tile)."""
+    B, H, T, D = 1, 2, 1001, 64
     x = {k: v.to(DEV) for k, v in make_inputs(WORKLOADS["dilated"], B=B, H=H, T=T).items()}
     g = sa_build_graph(T, W, offs)
+    for which in ("fwd", "bwd"):
+        assert sa_describe_plan(g, x["v"], which=which).startswith(kernels), which
     n = B * H * T * D
     pad = 4096
     canary = -1536.0  # exact in bf16 and fp32
