@@ -50,6 +50,9 @@ def parse():
                     help="also run a plain 1 GiB device copy (scales profiler byte counters)")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the measured copy / MFMA-loop / empty-launch denominators")
+    ap.add_argument("--probe-rates", action="store_true",
+                    help="only run the issue-rate probes (MFMA and vector-ALU overlap on one SIMD) and print "
+                         "one JSON line")
     ap.add_argument("--record-profiles", metavar="DIR",
                     help="write profiles/ from the rocprofv3 CSV output under DIR/<workload>/<pass> (no GPU)")
     return ap.parse_args()
@@ -552,6 +555,10 @@ def probe_lib():
         L.sa_probe_mfma.argtypes = [vp, ctypes.c_int, ctypes.c_int, vp]
         L.sa_probe_mfma_flops.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
         L.sa_probe_empty.argtypes = [vp]
+        ip = ctypes.POINTER(ctypes.c_int)
+        L.sa_probe_mix_variants.argtypes = []
+        L.sa_probe_mix_counts.argtypes = [ctypes.c_int, ip, ip, ip]
+        L.sa_probe_mix.argtypes = [ctypes.c_int, vp, ctypes.c_int, ctypes.c_int, vp]
         _PROBE = L
     return _PROBE
 
@@ -563,6 +570,57 @@ def _stream_handle():
 
 
 COPY_PROBE_BYTES = 1 << 30
+
+
+def probe_rates(iters=512, reps=5):
+    """The issue-rate probes (include/sa_probe.h), four workgroups of four
+    wavefronts per compute unit, so each SIMD processes four wavefronts'
+    rounds.  Per variant: the launch's HIP-event time per round (median of
+    `reps` launches after one warm-up launch), i.e. one SIMD's time for four
+    rounds, and the shader clock from the wavefronts' s_memtime against
+    s_memrealtime (100 MHz) ticks; cycles = time x clock.  Comparing the
+    MFMA-only, FMA-only and mixed rounds shows how far the matrix core and the
+    vector ALU overlap; the per-instruction figures are cycles / (4 x count)
+    for the single-kind rounds.  (The wavefronts of a SIMD do not all run
+    side by side for the whole launch, so per-wavefront spans are not used.)"""
+    import ctypes
+    import torch
+    L = probe_lib()
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks = 4 * cus
+    out = torch.empty(16 * blocks, dtype=torch.float32, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def launch(v):
+        assert L.sa_probe_mix(v, ctypes.c_void_p(out.data_ptr()), blocks, iters, _stream_handle()) == 0
+
+    rows = []
+    for v in range(L.sa_probe_mix_variants()):
+        nm, nf, ne = ctypes.c_int(), ctypes.c_int(), ctypes.c_int()
+        assert L.sa_probe_mix_counts(v, ctypes.byref(nm), ctypes.byref(nf), ctypes.byref(ne)) == 0
+        launch(v)
+        torch.cuda.synchronize()
+        ns, ghz = [], []
+        for _ in range(reps):
+            e0.record()
+            launch(v)
+            e1.record()
+            torch.cuda.synchronize()
+            ns.append(e0.elapsed_time(e1) * 1e6 / iters)
+            w = out.view(-1, 4).double()
+            ghz.append(float((w[:, 0] / (w[:, 1] * 10.0)).median()))  # memtime ticks per ns
+        ns.sort()
+        ghz.sort()
+        t, f = ns[len(ns) // 2], ghz[len(ghz) // 2]
+        rows.append({"mfma": nm.value, "fma": nf.value, "exp": ne.value, "ns_per_round": round(t, 1),
+                     "shader_ghz": round(f, 3), "simd_cycles_per_round": round(t * f, 1)})
+    per = {}
+    for r in rows:
+        kinds = [k for k in ("mfma", "fma", "exp") if r[k]]
+        if len(kinds) == 1:
+            per[kinds[0]] = round(r["simd_cycles_per_round"] / (4 * r[kinds[0]]), 2)
+    return {"probe": "issue rates", "workgroups_per_cu": 4, "wavefronts_per_simd": 4, "iters": iters,
+            "rounds": rows, "simd_cycles_per_wavefront_instruction": per}
 
 
 def copy_probe(reps=3):
@@ -902,6 +960,9 @@ def main():
     from sparse_causal_attention_amd.inputs import WORKLOADS, make_inputs
 
     _abi.lib()
+    if args.probe_rates:
+        print(json.dumps(probe_rates()))
+        return
     if args.copy_probe:
         copy_probe()
     peaks = None

@@ -4,7 +4,8 @@
  * them for measured roofline denominators next to the chip's published peaks:
  * the bandwidth of a plain device copy, the bf16 matrix-core rate of a loop of
  * independent MFMAs, and the cost of an empty kernel launch (the floor under
- * microsecond calls such as a decode step).  None comes from the pages; they
+ * microsecond calls such as a decode step); and issue-rate probes of mixed
+ * matrix-core and vector-ALU work (how far one SIMD overlaps them).  None comes from the pages; they
  * characterise the machine the attention kernels run on.
  *
  * Pointers are device pointers, `stream` a hipStream_t (NULL: null stream);
@@ -34,6 +35,21 @@ int sa_probe_mfma_flops(int blocks, int iters, double* flops);
 
 /* One empty kernel (one wavefront). */
 int sa_probe_empty(void* stream);
+
+/* Issue-rate probes: does the SIMD overlap independent matrix-core and
+ * vector-ALU work, and what does each cost?  Variant v (0 <= v <
+ * sa_probe_mix_variants()) runs, per round, the counts sa_probe_mix_counts
+ * names: MFMAs (v_mfma_f32_32x32x16_bf16, two independent chains), v_fma_f32
+ * and v_exp_f32 (sixteen independent chains each), none depending on another.
+ * sa_probe_mix launches `blocks` workgroups of four wavefronts running `iters`
+ * rounds; out receives four floats per wavefront (16 * blocks floats): the
+ * ticks of s_memtime and of s_memrealtime (constant rate, see the device's
+ * wall-clock frequency) its rounds took, a value that keeps the work, and 0.
+ * With four workgroups per compute unit (blocks = 4 x CUs), time / iters is
+ * one SIMD's time for one round of each of its four wavefronts. */
+int sa_probe_mix_variants(void);
+int sa_probe_mix_counts(int variant, int* n_mfma, int* n_fma, int* n_exp);
+int sa_probe_mix(int variant, float* out, int blocks, int iters, void* stream);
 
 #ifdef __cplusplus
 }

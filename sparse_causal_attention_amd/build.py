@@ -53,6 +53,12 @@ def headers():
     return sorted(glob.glob(os.path.join(CSRC, "*.h")) + glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 
+def lib_headers():
+    """The headers libsa.so is built from (its own and include/sa.h; not the
+    probe library's header)."""
+    return sorted(glob.glob(os.path.join(CSRC, "*.h")) + [os.path.join(ROOT, "include", "sa.h")])
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
     cmd = [HIPCC] + COMMON + DEVICE + PER_FILE.get(os.path.basename(src), []) + ["-c", src, "-o", obj]
@@ -71,7 +77,7 @@ def source_digest() -> str:
     import hashlib
 
     h = hashlib.sha256()
-    for f in sources() + headers():
+    for f in sources() + lib_headers():
         h.update(os.path.relpath(f, ROOT).encode())
         h.update(open(f, "rb").read())
     # flags with the checkout location taken out, so the digest is the same

@@ -55,6 +55,64 @@ __global__ __launch_bounds__(kThreads) void probe_mfma_kernel(float* out, int it
 
 __global__ void probe_empty_kernel() {}
 
+// Issue-rate probe: per round, NM v_mfma_f32_32x32x16_bf16 (two independent
+// chains), NV v_fma_f32 and NE v_exp_f32 (16 independent chains each), all
+// independent of each other, so the SIMD may overlap the matrix core with the
+// vector ALU.  Each wavefront stores the ticks of s_memtime and of the
+// constant-rate s_memrealtime its `iters` rounds took; with four wavefronts
+// per SIMD (a grid of four workgroups per compute unit), time / iters is the
+// SIMD time of one round of each of the four wavefronts.
+template <int NM, int NV, int NE>
+__global__ __launch_bounds__(kThreads) void probe_mix_kernel(float* out, int iters, float a, float b) {
+  bf16x8 x, y;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    x[e] = static_cast<__bf16>(1e-3f * (float)(threadIdx.x + e));
+    y[e] = static_cast<__bf16>(0.5f - 0.01f * (float)e);
+  }
+  f32x16 c0, c1;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) c0[r] = c1[r] = 0.f;
+  float v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = 1e-3f * (float)(threadIdx.x + i);
+  const uint64_t r0 = __builtin_amdgcn_s_memrealtime();
+  const uint64_t t0 = __builtin_amdgcn_s_memtime();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int m = 0; m < NM / 2; ++m) {
+      c0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x, y, c0, 0, 0, 0);
+      c1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(y, x, c1, 0, 0, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < NV / 16; ++r)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = fmaf(v[i], a, b);
+#pragma unroll
+    for (int r = 0; r < NE / 16; ++r)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) v[i] = __builtin_amdgcn_exp2f(v[i]);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s += v[i] + c0[i] + c1[i];
+  const uint64_t t1 = __builtin_amdgcn_s_memtime();
+  const uint64_t r1 = __builtin_amdgcn_s_memrealtime();
+  if ((threadIdx.x & 63) == 0) {
+    const int w = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    out[4 * w] = (float)(t1 - t0);
+    out[4 * w + 1] = (float)(r1 - r0);
+    out[4 * w + 2] = s;  // keeps the work
+    out[4 * w + 3] = 0.f;
+  }
+}
+
+struct MixVariant {
+  int nm, nv, ne;
+};
+constexpr MixVariant kMix[] = {{8, 0, 0}, {0, 128, 0}, {8, 128, 0}, {0, 0, 32}, {8, 0, 32}};
+constexpr int kNumMix = sizeof(kMix) / sizeof(kMix[0]);
+
 }  // namespace
 
 extern "C" int sa_probe_copy(void* dst, const void* src, size_t bytes, void* stream) {
@@ -85,5 +143,29 @@ extern "C" int sa_probe_mfma(float* out, int blocks, int iters, void* stream) {
 
 extern "C" int sa_probe_empty(void* stream) {
   hipLaunchKernelGGL(probe_empty_kernel, dim3(1), dim3(64), 0, reinterpret_cast<hipStream_t>(stream));
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+extern "C" int sa_probe_mix_variants(void) { return kNumMix; }
+
+extern "C" int sa_probe_mix_counts(int variant, int* n_mfma, int* n_fma, int* n_exp) {
+  if (variant < 0 || variant >= kNumMix || n_mfma == nullptr || n_fma == nullptr || n_exp == nullptr) return 1;
+  *n_mfma = kMix[variant].nm;
+  *n_fma = kMix[variant].nv;
+  *n_exp = kMix[variant].ne;
+  return 0;
+}
+
+extern "C" int sa_probe_mix(int variant, float* out, int blocks, int iters, void* stream) {
+  if (variant < 0 || variant >= kNumMix || out == nullptr || blocks < 1 || iters < 1) return 1;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  const dim3 g(blocks), b(kThreads);
+  switch (variant) {
+    case 0: hipLaunchKernelGGL((probe_mix_kernel<8, 0, 0>), g, b, 0, st, out, iters, 0.999f, 0.5f); break;
+    case 1: hipLaunchKernelGGL((probe_mix_kernel<0, 128, 0>), g, b, 0, st, out, iters, 0.999f, 0.5f); break;
+    case 2: hipLaunchKernelGGL((probe_mix_kernel<8, 128, 0>), g, b, 0, st, out, iters, 0.999f, 0.5f); break;
+    case 3: hipLaunchKernelGGL((probe_mix_kernel<0, 0, 32>), g, b, 0, st, out, iters, 0.999f, 0.5f); break;
+    default: hipLaunchKernelGGL((probe_mix_kernel<8, 0, 32>), g, b, 0, st, out, iters, 0.999f, 0.5f); break;
+  }
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }

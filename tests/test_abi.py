@@ -451,7 +451,8 @@ def test_probe_library_exports_its_header():
     lib = os.path.join(ROOT, "sparse_causal_attention_amd", "libsa_probe.so")
     out = subprocess.run(["nm", "-D", "--defined-only", lib], capture_output=True, text=True, check=True).stdout
     exported = {ln.split()[-1] for ln in out.splitlines() if " T sa_probe_" in ln}
-    assert declared == exported == {"sa_probe_copy", "sa_probe_mfma", "sa_probe_mfma_flops", "sa_probe_empty"}
+    assert declared == exported == {"sa_probe_copy", "sa_probe_mfma", "sa_probe_mfma_flops", "sa_probe_empty",
+                                    "sa_probe_mix_variants", "sa_probe_mix_counts", "sa_probe_mix"}
     L = ctypes.CDLL(lib)
     flops = ctypes.c_double()
     assert L.sa_probe_mfma_flops(2, 3, ctypes.byref(flops)) == 0
