@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--probe-rates", action="store_true",
                     help="only run the issue-rate probes (MFMA and vector-ALU overlap on one SIMD) and print "
                          "one JSON line")
+    ap.add_argument("--sweep", action="store_true",
+                    help="only time forward + backward across window sizes (band graph) and sequence lengths "
+                         "(dilated graph), per edge, and print one JSON line")
     ap.add_argument("--record-profiles", metavar="DIR",
                     help="write profiles/ from the rocprofv3 CSV output under DIR/<workload>/<pass> (no GPU)")
     return ap.parse_args()
@@ -251,6 +254,43 @@ def run_workload(w, steps, warmup, algo, with_backward=True, no_cold=False):
     }
     del o, lse, grads
     return res
+
+
+def sweep_workloads():
+    """The scaling sweep: the band graph (B = 1, H = 8, T = 16,384, D = 64
+    bf16) at windows 32 .. 2,048 and at W = T (dense causal attention), and
+    the dilated graph (B = 1, H = 8, window 4 plus distances 2^0 .. < T) at
+    T = 4,096 .. 65,536.  Seeded inputs of the same recipe as the named
+    workloads."""
+    import dataclasses
+
+    from sparse_causal_attention_amd.inputs import WORKLOADS
+    band, dil = WORKLOADS["band"], WORKLOADS["dilated"]
+    out = [dataclasses.replace(band, name="band_W%d" % W, window=W) for W in (32, 64, 128, 256, 512, 1024, 2048)]
+    out.append(dataclasses.replace(band, name="band_dense_causal", window=band.T))
+    for T in (4096, 8192, 16384, 32768, 65536):
+        offs = tuple(2 ** k for k in range(T.bit_length() - 1))
+        out.append(dataclasses.replace(dil, name="dilated_T%d" % T, B=1, T=T, offsets=offs))
+    return out
+
+
+def sweep(steps=50, warmup=10):
+    """Forward + backward time per workload of sweep_workloads() and per edge
+    (the work of a sparse graph should follow its edge count, not T^2)."""
+    rows = []
+    for w in sweep_workloads():
+        print("[bench] sweep %s" % w.name, file=sys.stderr, flush=True)
+        r = run_workload(w, steps, warmup, "auto", no_cold=True)
+        E, _ = edge_counts(w)
+        edges = E * w.B * w.H
+        fb_ms = r["fwd_ms"] + r["bwd_ms"]
+        rows.append({"workload": w.name, "T": w.T, "window": min(w.window, w.T), "n_offsets": len(w.offsets),
+                     "edges": edges, "fwd_us": round(1e3 * r["fwd_ms"], 1), "bwd_us": round(1e3 * r["bwd_ms"], 1),
+                     "ps_per_edge_fwd_bwd": round(1e9 * fb_ms / edges, 2),
+                     "plan": "%s | %s" % (r["plan_fwd"], r["plan_bwd"])})
+        del r
+    return {"sweep": "forward + backward per edge", "B": 1, "H": 8, "D": 64, "dtype": "bf16",
+            "steps": steps, "rows": rows}
 
 
 def median(xs):
@@ -962,6 +1002,9 @@ def main():
     _abi.lib()
     if args.probe_rates:
         print(json.dumps(probe_rates()))
+        return
+    if args.sweep:
+        print(json.dumps(sweep()))
         return
     if args.copy_probe:
         copy_probe()
