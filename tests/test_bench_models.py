@@ -148,3 +148,23 @@ def test_summary_keeps_the_quoted_configs_last():
     order = bench.summary_order(names)
     assert order[-4:] == ["band", "dilated", "coord", "ultra"] and sorted(order) == sorted(names)
     assert bench.summary_order(["uniform", "band"]) == ["uniform", "band"]
+
+
+def test_sweep_workloads_span_windows_and_lengths():
+    """The scaling sweep: band windows 32 .. 2,048 and W = T on one shape, the
+    dilated graph at T = 4,096 .. 65,536 with every power-of-two distance
+    below T; edge counts grow within each family."""
+    ws = bench.sweep_workloads()
+    band = [w for w in ws if w.name.startswith("band")]
+    dil = [w for w in ws if w.name.startswith("dilated")]
+    assert [w.window for w in band] == [32, 64, 128, 256, 512, 1024, 2048, 16384]
+    assert {(w.B, w.H, w.T, w.D) for w in band} == {(1, 8, 16384, 64)}
+    assert [w.T for w in dil] == [4096, 8192, 16384, 32768, 65536]
+    for w in dil:
+        assert w.window == 4 and w.offsets == tuple(2 ** k for k in range(w.T.bit_length() - 1))
+        assert max(w.offsets) < w.T
+    for fam in (band, dil):
+        edges = [bench.edge_counts(w)[0] for w in fam]
+        assert edges == sorted(edges) and len(set(edges)) == len(edges)
+    # W = T is dense causal attention: T (T + 1) / 2 edges per (b, h)
+    assert bench.edge_counts(band[-1])[0] == 16384 * 16385 // 2
