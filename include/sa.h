@@ -231,7 +231,10 @@ typedef struct {
  * `dtype` (bf16 rounded to nearest even) and lse in fp32 (natural log).
  * Arithmetic is fp32 with fp32 accumulation; bf16 MFMA products for the band.
  * With an explicit-list graph N(i) is row i's list, and a graph that has not
- * been uploaded is SA_ERR_INVALID_ARG (likewise for sa_bwd and sa_decode). */
+ * been uploaded is SA_ERR_INVALID_ARG (likewise for sa_bwd and sa_decode).
+ * Size limits (likewise for sa_bwd, sa_bwd_workspace_size): B, H or B * H
+ * above 2^24, or B * H * ceil(T / 8) of about 2^31 or more (workgroup counts
+ * are 32-bit), is SA_ERR_UNSUPPORTED. */
 sa_status sa_fwd(const sa_graph* g, const sa_attn_desc* desc, const void* q, const void* k,
                  const void* v, const float* cq, const float* ck, const float* gamma,
                  const float* beta, void* o, float* lse, sa_stream stream);
@@ -310,7 +313,8 @@ sa_status sa_bwd_noalloc(const sa_graph* g, const sa_attn_desc* desc, const void
  * in `dtype`, lse [B, H] fp32 (natural log).  positions is a device array of
  * B int32 (NULL: every sequence at row T - 1); a position outside [0, T)
  * cannot be checked on the host and yields NaN in that sequence's o and lse.
- * Same validation and status rules as sa_fwd. */
+ * Same validation and status rules as sa_fwd, except the size limit: B, H or
+ * B * H of 2^31 or more is SA_ERR_UNSUPPORTED (one workgroup per (b, h)). */
 sa_status sa_decode(const sa_graph* g, const sa_attn_desc* desc, const int32_t* positions,
                     const void* q, const void* k, const void* v, const float* cq, const float* ck,
                     const float* gamma, const float* beta, void* o, float* lse, sa_stream stream);

@@ -27,6 +27,14 @@ sa_status check_heads(const sa_attn_desc* d) {
 }
 int esize(int32_t dt) { return dt == SA_BF16 ? 2 : 4; }
 
+// B, H and B * H at most `limit` (< 2^31), each factor bounded first so that
+// the product cannot overflow.
+bool heads_fit(const sa_attn_desc* d, int64_t limit) {
+  return d->B <= limit && d->H <= limit && d->B * d->H <= limit;
+}
+// (batch, head) slices the attention calls accept
+constexpr int64_t kMaxSlices = (int64_t)1 << 24;
+
 // Row starts 16-byte aligned for 16-byte vector accesses.
 bool aligned_rows(const void* p, const int64_t st[3], int es) {
   if ((reinterpret_cast<uintptr_t>(p) & 15u) != 0) return false;
@@ -98,7 +106,7 @@ sa_status check_common(const sa_graph* g, const sa_attn_desc* d, const void* q, 
     return SA_ERR_INVALID_ARG;
   if (d->T != g->T) return SA_ERR_SHAPE_MISMATCH;
   if (d->D != 16 && d->D != 32 && d->D != 64 && d->D != 128) return SA_ERR_UNSUPPORTED;
-  if (d->B * d->H > (int64_t)1 << 24) return SA_ERR_UNSUPPORTED;
+  if (!heads_fit(d, kMaxSlices)) return SA_ERR_UNSUPPORTED;
   if (const sa_status hs = check_heads(d); hs != SA_OK) return hs;
   // workgroups of the smallest row tile (8 rows: fp32, D = 128), plus the
   // XCD padding of the grid, must be countable in int32
@@ -226,6 +234,7 @@ extern "C" sa_status sa_bwd_workspace_size(const sa_graph* g, const sa_attn_desc
   if (bad_dtype(d->dtype)) return SA_ERR_INVALID_ARG;
   if (d->D != 16 && d->D != 32 && d->D != 64 && d->D != 128) return SA_ERR_UNSUPPORTED;
   if (d->T != g->T) return SA_ERR_SHAPE_MISMATCH;
+  if (!heads_fit(d, kMaxSlices)) return SA_ERR_UNSUPPORTED;  // as sa_bwd: no wrapped sizes
   if (const sa_status hs = check_heads(d); hs != SA_OK) return hs;
   *bytes = workspace_bytes_for(d);
   return SA_OK;
@@ -381,7 +390,7 @@ extern "C" sa_status sa_decode(const sa_graph* g, const sa_attn_desc* d, const i
     return SA_ERR_INVALID_ARG;
   if (d->T != g->T) return SA_ERR_SHAPE_MISMATCH;
   if (d->D != 16 && d->D != 32 && d->D != 64 && d->D != 128) return SA_ERR_UNSUPPORTED;
-  if (d->B * d->H > ((int64_t)1 << 31) - 1) return SA_ERR_UNSUPPORTED;
+  if (!heads_fit(d, ((int64_t)1 << 31) - 1)) return SA_ERR_UNSUPPORTED;  // one workgroup per (b, h)
   if (const sa_status hs = check_heads(d); hs != SA_OK) return hs;
   const int es = esize(d->dtype);
   const int64_t row_only[3] = {d->stride_q[0], d->stride_q[1], 0};

@@ -459,3 +459,33 @@ def test_probe_library_exports_its_header():
     assert flops.value == 2 * 4 * 3 * 4 * 2 * 32 * 32 * 16  # workgroups x waves x iters x chains x flops
     assert L.sa_probe_mfma_flops(0, 3, ctypes.byref(flops)) == 1
     assert L.sa_probe_copy(None, None, ctypes.c_size_t(16), None) == 1  # validated before any launch
+
+
+def test_huge_batch_and_heads_are_refused_before_any_product():
+    """B and H are bounded one by one before B * H is formed (a product of two
+    int64 values near 2^33 would overflow): with broadcast (stride 0) inputs,
+    which pass every offset check, such shapes are SA_ERR_UNSUPPORTED for the
+    forward, the backward, the workspace size and the decode step."""
+    E = _abi
+    g = sa_build_graph(64, 4, [])
+    for B, H in ((1 << 33, 1 << 33), (1 << 40, 1), (1, 1 << 40), ((1 << 24) + 1, 1), (1 << 12, (1 << 12) + 1)):
+        d = desc(B=B, H=H, T=64, D=32)
+        for name in ("q", "k", "v", "do"):
+            getattr(d, "stride_" + name)[:] = (0, 0, 32)
+        assert fwd(g, d) == E.SA_ERR_UNSUPPORTED, (B, H)
+        assert bwd(g, d) == E.SA_ERR_UNSUPPORTED, (B, H)
+        n = ctypes.c_size_t(0)
+        assert _abi.lib().sa_bwd_workspace_size(g.handle, ctypes.byref(d), ctypes.byref(n)) == \
+            E.SA_ERR_UNSUPPORTED, (B, H)
+    for B, H in ((1 << 33, 1 << 33), (1 << 31, 1), ((1 << 16), (1 << 15))):
+        d = desc(B=B, H=H, T=64, D=32)
+        for name in ("q", "k", "v", "o"):
+            getattr(d, "stride_" + name)[:] = (0, 0, 32)
+        st = _abi.lib().sa_decode(g.handle, ctypes.byref(d), None, FAKE, FAKE, FAKE, None, None, None, None,
+                                  FAKE, FAKE, None)
+        assert st == E.SA_ERR_UNSUPPORTED, (B, H)
+    # the largest accepted slice count still validates (and fails later, on the null lse)
+    d = desc(B=1 << 12, H=1 << 12, T=64, D=32)
+    for name in ("q", "k", "v", "do"):
+        getattr(d, "stride_" + name)[:] = (0, 0, 32)
+    assert fwd(g, d, lse=None) == E.SA_ERR_INVALID_ARG
