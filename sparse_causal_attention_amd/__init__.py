@@ -35,8 +35,7 @@ import numpy as np
 
 from . import _abi
 from ._abi import (SA_ALGO_AUTO, SA_ALGO_BAND, SA_ALGO_GATHER, SA_BF16, SA_F32, SA_GRAPH_CSR,
-                   SA_GRAPH_DISTANCE, SA_MAX_DILATED, SA_SCORE_COORD, SA_SCORE_DOT, SA_SCORE_UNIFORM,
-                   SaError)
+                   SA_MAX_DILATED, SA_SCORE_COORD, SA_SCORE_DOT, SA_SCORE_UNIFORM, SaError)
 
 __all__ = ["sa_build_graph", "sa_build_graph_csr", "sa_fwd", "sa_bwd", "sa_bwd_noalloc", "sa_decode",
            "sa_decode_prepared", "sa_fwd_prepared", "sa_bwd_prepared",
@@ -115,7 +114,6 @@ class Graph:
             self._dev.record_stream(stream)
 
     def _rows(self, fn, r0, r1):
-        L = _abi.lib()
         r1 = self.T if r1 is None else r1
         rp = np.zeros(max(r1 - r0, 0) + 1, dtype=np.int64)
         st = fn(self._h, r0, r1, rp.ctypes.data, None, 0)

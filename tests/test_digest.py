@@ -1,6 +1,5 @@
 """The source digest that ties profiler counters to the kernels they were
 taken on does not depend on where the repository is checked out."""
-import importlib
 import os
 import shutil
 import subprocess
