@@ -21,11 +21,15 @@
 // -Delta, so dP - Delta comes out of the matrix cores.
 //
 // Scheduling.  The grid is a fixed number of workgroups (two per compute
-// unit).  Workgroup i of XCD x takes the (dq, dk/dv) unit pairs i, i + G,
-// i + 2G, ... of that XCD's contiguous share of row blocks (G workgroups per
-// XCD), so workgroups running side by side work on neighbouring row blocks
-// and share K, V, Q, dO rows in the XCD's L2; a dq unit and a dk/dv unit of
-// the same row block together have nearly the same work at every position.
+// unit), G per XCD, each XCD owning a contiguous share of row blocks.  With
+// G even, workgroups 2h and 2h + 1 take the dq unit and the dk/dv unit of the
+// same row block at the same time, row blocks h, h + G/2, h + G/2 * 2, ... of
+// the share, swapping the two roles each round: workgroups running side by
+// side work on neighbouring row blocks and share K, V, Q, dO rows in the XCD's
+// L2, an XCD has G/2 row blocks in flight (a working set that fits its L2
+// better than G), and every workgroup alternates the two kinds of unit, which
+// together have nearly the same work at every position.  (With G odd,
+// workgroup i takes the (dq, dk/dv) pairs i, i + G, ... in turn.)
 // Streamed 64-row tiles are double-buffered in LDS and filled by direct
 // buffer -> LDS loads; the stream runs on across units: while a unit's last
 // tile is computed, the first tile of the next unit is loaded, together with
@@ -644,7 +648,16 @@ __global__ __launch_bounds__(kThreads, 2) void band_bwd_kernel(Params p) {
   const int wh = wgs_per_xcd / 2, wd = wgs_per_xcd - wh;  // grouped: >= 1 each
   const bool kv_wg = grouped && g < wh;
   auto unit_at = [&](int k) {
-    if (!grouped) {  // unit k: pair ibeg + g + (k / 2) wgs_per_xcd, dq unit then dk/dv unit
+    if (!grouped) {
+      if ((wgs_per_xcd & 1) == 0) {
+        // workgroups 2h and 2h + 1 take the dq and the dk/dv unit of the same
+        // row block at the same time (roles swapping each round): an XCD works
+        // on half as many row blocks at once, a smaller working set in its L2,
+        // and every workgroup still alternates the two kinds of unit
+        const int pair = ibeg + (g >> 1) + k * (wgs_per_xcd >> 1);
+        return pair < iend ? make_unit(p, pair, (k + g) & 1, nblk) : none;
+      }
+      // unit k: pair ibeg + g + (k / 2) wgs_per_xcd, dq unit then dk/dv unit
       const int pair = ibeg + g + (k >> 1) * wgs_per_xcd;
       return pair < iend ? make_unit(p, pair, k & 1, nblk) : none;
     }
